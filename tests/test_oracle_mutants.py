@@ -1,0 +1,89 @@
+"""The pins are strong enough: each plausible slip planted in a copy of the
+oracle's C source (a dropped term, a wrong sign, a swapped index, a transposed
+operand, the state read after instead of before its update) makes at least one
+pin fail.  Mutants are built from a temporary copy on the CPU; the oracle
+itself is never modified."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as P
+
+MUTANTS = {
+    "rwkv4_decay_sign": ("double decay = exp(-(double)w[c]);",
+                         "double decay = exp((double)w[c]);"),
+    "rwkv4_no_bonus": ("double cur = exp(bonus + kt);", "double cur = exp(kt);"),
+    "rwkv4_no_decay_num": ("num = decay * num + ek * vt;", "num = num + ek * vt;"),
+    "rwkv4_den_drops_k": ("den = decay * den + ek;", "den = decay * den + 1.0;"),
+    "rwkv4_den_drops_current": ("y[idx] = (num + cur * vt) / (den + cur);",
+                                "y[idx] = (num + cur * vt) / (den + 1.0);"),
+    "rwkv4_output_after_update": (
+        "y[idx] = (num + cur * vt) / (den + cur);",
+        "y[idx] = (decay * num + exp(kt) * vt + cur * vt) / "
+        "(decay * den + exp(kt) + cur);"),
+    "matrix_decay_sign": ("wt[i] = exp(-exp((double)xt[i]));",
+                          "wt[i] = exp(-exp(-(double)xt[i]));"),
+    "matrix_bonus_drops_u": (
+        "ruk += (double)rt[i] * (double)uh[i] * (double)kt[i];",
+        "ruk += (double)rt[i] * (double)kt[i];"),
+    "matrix_state_transposed_in_output": ("acc += (double)rt[i] * S[i * N + j];",
+                                          "acc += (double)rt[i] * S[j * N + i];"),
+    "matrix_decay_on_value_channel": ("S[i * N + j] = wt[i] * S[i * N + j]",
+                                      "S[i * N + j] = wt[j] * S[i * N + j]"),
+    "matrix_outer_product_transposed": (
+        "+ (double)kt[i] * (double)vt[j];", "+ (double)kt[j] * (double)vt[i];"),
+    "matrix_bonus_times_k": ("o[base + j] = acc + ruk * (double)vt[j];",
+                             "o[base + j] = acc + ruk * (double)kt[j];"),
+    "matrix_output_after_update": (
+        "acc += (double)rt[i] * S[i * N + j];",
+        "acc += (double)rt[i] * (wt[i] * S[i * N + j] + (double)kt[i] * (double)vt[j]);"),
+    "matrix_static_decay_wrong_head": (
+        "const float *xt = x_per_token ? x + base : x + h * N;",
+        "const float *xt = x_per_token ? x + base : x + ((h + 1) % H) * N;"),
+    "matrix_state_in_ignores_batch": ("S[i] = s_in ? s_in[(b * H + h) * N * N + i] : 0.0;",
+                                      "S[i] = s_in ? s_in[h * N * N + i] : 0.0;"),
+}
+
+PINS = [
+    (P.test_rwkv4_bruteforce_workload1, {}),
+    (P.test_rwkv4_bruteforce_with_history, {}),
+    (P.test_rwkv4_constant_inputs_closed_form, {}),
+    (P.test_rwkv4_first_token_is_v, {}),
+    (P.test_rwkv4_golden_hand_example, {}),
+    (P.test_matrix_bruteforce, {"per_token": False}),
+    (P.test_matrix_bruteforce, {"per_token": True}),
+    (P.test_matrix_golden_hand_example, {}),
+    (P.test_matrix_geometric_closed_form, {}),
+    (P.test_matrix_no_decay_is_causal_linear_attention, {}),
+    (P.test_matrix_full_decay_keeps_only_last_token, {}),
+    (P.test_matrix_single_token, {}),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site not found once: {old}"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(str(path), lib_path)
+    lib = oracle.load(lib_path)
+    caught = []
+    for fn, kw in PINS:
+        try:
+            fn(lib, **kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_source_passes_every_pin(tmp_path):
+    lib_path = str(tmp_path / "libclean.so")
+    oracle.build(oracle.SOURCE, lib_path)
+    lib = oracle.load(lib_path)
+    for fn, kw in PINS:
+        fn(lib, **kw)

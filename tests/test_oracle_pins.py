@@ -1,0 +1,358 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each check follows from the definitions on the pages (RWKV paper summary,
+section "Temporal structure for sequential data processing": decay e^{-w},
+bonus e^{u}; RWKV-5/6 summary, sections 4.1.2 "Eagle time mixing" and 4.2.2
+"Finch time mixing": matrix state decayed per key channel, bonus u on the
+current token, r as the query) or from plain mathematics: explicit sums
+evaluated by brute force, geometric series, the w = 1 and w = 0 limits,
+hand-worked examples, exact scaling, and split / handoff invariance.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import wkv_synth as S
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------------------
+# independent brute-force forms
+
+def rwkv4_explicit(k, v, w, u):
+    """y_t = sum_{i<=t} a_{t,i} v_i / sum_{i<=t} a_{t,i} with
+    a_{t,i} = exp(-(t-1-i) w + k_i) for i < t and exp(u + k_t) for i = t."""
+    k = k.astype(np.float64)
+    v = v.astype(np.float64)
+    w = w.astype(np.float64)
+    u = u.astype(np.float64)
+    B, T, C = k.shape
+    y = np.empty((B, T, C))
+    for t in range(T):
+        i = np.arange(t)
+        expo = -(t - 1 - i)[None, :, None] * w[None, None, :] + k[:, :t, :]
+        a = np.exp(expo)
+        cur = np.exp(u[None, :] + k[:, t, :])
+        y[:, t, :] = (np.sum(a * v[:, :t, :], axis=1) + cur * v[:, t, :]) / (
+            np.sum(a, axis=1) + cur)
+    return y
+
+
+def matrix_explicit(r, k, v, x, u, s0):
+    """Unrolled Eagle/Finch: with P_i(a, b) = prod_{m=a..b} w_m[i],
+    o_t = r_t diag(P(1,t-1)) S_0
+        + sum_{s<t} (sum_i r_t[i] P_i(s+1, t-1) k_s[i]) v_s
+        + (sum_i r_t[i] u[i] k_t[i]) v_t,
+    S_T = diag(P(1,T)) S_0 + sum_{s<=T} diag(P(s+1,T)) k_s^T v_s.
+    Products are taken directly, one factor at a time."""
+    r, k, v, u, s0 = (a.astype(np.float64) for a in (r, k, v, u, s0))
+    B, T, H, N = r.shape
+    if x.shape == (H, N):
+        w = np.broadcast_to(np.exp(-np.exp(x.astype(np.float64))), (B, T, H, N))
+    else:
+        w = np.exp(-np.exp(x.astype(np.float64)))
+
+    def P(b, h, a, c):  # 1-indexed inclusive product of decays, per channel
+        out = np.ones(N)
+        for m in range(a, c + 1):
+            out = out * w[b, m - 1, h]
+        return out
+
+    o = np.zeros((B, T, H, N))
+    sT = np.zeros((B, H, N, N))
+    for b in range(B):
+        for h in range(H):
+            for t in range(1, T + 1):
+                rt = r[b, t - 1, h]
+                acc = (rt * P(b, h, 1, t - 1)) @ s0[b, h]
+                for s in range(1, t):
+                    coef = np.sum(rt * P(b, h, s + 1, t - 1) * k[b, s - 1, h])
+                    acc = acc + coef * v[b, s - 1, h]
+                acc = acc + np.sum(rt * u[h] * k[b, t - 1, h]) * v[b, t - 1, h]
+                o[b, t - 1, h] = acc
+            st = P(b, h, 1, T)[:, None] * s0[b, h]
+            for s in range(1, T + 1):
+                st = st + np.outer(P(b, h, s + 1, T) * k[b, s - 1, h], v[b, s - 1, h])
+            sT[b, h] = st
+    return o, sT
+
+
+def small_matrix_case(B, T, H, N, seed, per_token=True, s0_sigma=0.3):
+    d = S.wkv_inputs(B, T, H, N, seed, per_token, s0_sigma, rkv_sigma=0.5)
+    return (S.bf16_to_f32(d["r"]), S.bf16_to_f32(d["k"]), S.bf16_to_f32(d["v"]),
+            d["x"], d["u"], d["s0"])
+
+
+def rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# RWKV-4
+
+def test_rwkv4_bruteforce_workload1(oracle_lib):
+    d = S.workload(1)
+    out = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], lib=oracle_lib)
+    ref = rwkv4_explicit(d["k"], d["v"], d["w"], d["u"])
+    assert np.max(np.abs(out["y"] - ref) / np.maximum(np.abs(ref), out["scale"])) < 1e-12
+
+
+def test_rwkv4_bruteforce_with_history(oracle_lib):
+    # a history of P tokens given as (num, den) must equal running them inline
+    d = S.rwkv4_inputs(2, 40, 5, 11, k_sigma=2.0)
+    P = 17
+    head = oracle.rwkv4_fwd(d["k"][:, :P], d["v"][:, :P], d["w"], d["u"], lib=oracle_lib)
+    tail = oracle.rwkv4_fwd(d["k"][:, P:], d["v"][:, P:], d["w"], d["u"],
+                            head["num"], head["den"], lib=oracle_lib)
+    ref = rwkv4_explicit(d["k"], d["v"], d["w"], d["u"])
+    assert rel(tail["y"], ref[:, P:]) < 1e-12
+    assert rel(head["y"], ref[:, :P]) < 1e-12
+
+
+def test_rwkv4_constant_inputs_closed_form(oracle_lib):
+    # constant k and v: every weighted average equals v; the denominator is a
+    # geometric series: Den_T = e^k (1 - e^{-T w}) / (1 - e^{-w})
+    B, T, C = 1, 50, 4
+    k = np.full((B, T, C), 0.75, np.float32)
+    v = np.full((B, T, C), -1.25, np.float32)
+    w = np.array([0.01, 0.3, 1.0, 4.0], np.float32)
+    u = np.array([0.5, -0.5, 2.0, 0.0], np.float32)
+    out = oracle.rwkv4_fwd(k, v, w, u, lib=oracle_lib)
+    np.testing.assert_allclose(out["y"], -1.25, rtol=1e-14)
+    wd = w.astype(np.float64)
+    den = math.exp(0.75) * (1 - np.exp(-T * wd)) / (1 - np.exp(-wd))
+    np.testing.assert_allclose(out["den"][0], den, rtol=1e-13)
+    np.testing.assert_allclose(out["num"][0], -1.25 * den, rtol=1e-13)
+
+
+def test_rwkv4_first_token_is_v(oracle_lib):
+    d = S.rwkv4_inputs(3, 4, 16, 12, k_sigma=3.0)
+    out = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], lib=oracle_lib)
+    np.testing.assert_allclose(out["y"][:, 0], d["v"][:, 0].astype(np.float64), rtol=1e-15)
+
+
+def test_rwkv4_golden_hand_example(oracle_lib):
+    g = read_golden("rwkv4_hand.txt")
+    k = np.array(g["k"], np.float32).reshape(1, 3, 1)
+    v = np.array(g["v"], np.float32).reshape(1, 3, 1)
+    out = oracle.rwkv4_fwd(k, v, np.array(g["w"], np.float32),
+                           np.array(g["u"], np.float32), lib=oracle_lib)
+    np.testing.assert_allclose(out["y"].ravel(), g["y"], rtol=1e-6)
+    np.testing.assert_allclose(out["num"].ravel(), g["num"], rtol=1e-6)
+    np.testing.assert_allclose(out["den"].ravel(), g["den"], rtol=1e-6)
+
+
+def test_rwkv4_split_invariance_bitwise(oracle_lib):
+    d = S.rwkv4_inputs(2, 64, 8, 13)
+    full = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], lib=oracle_lib)
+    a = oracle.rwkv4_fwd(d["k"][:, :23], d["v"][:, :23], d["w"], d["u"], lib=oracle_lib)
+    b = oracle.rwkv4_fwd(d["k"][:, 23:], d["v"][:, 23:], d["w"], d["u"],
+                         a["num"], a["den"], lib=oracle_lib)
+    assert np.array_equal(np.concatenate([a["y"], b["y"]], 1), full["y"])
+    assert np.array_equal(b["num"], full["num"]) and np.array_equal(b["den"], full["den"])
+
+
+def test_rwkv4_is_ratio_of_two_matrix_recurrences(oracle_lib):
+    # With N = 1, r = 1, k' = e^k, w' = e^{-w} (x = ln w), u' = e^u the matrix
+    # recurrence yields Num_{t-1} + e^{u+k_t} v_t; with v = 1 it yields the
+    # denominator.  Their ratio is the RWKV-4 output.
+    d = S.rwkv4_inputs(2, 30, 6, 14)
+    B, T, C = d["k"].shape
+    k4 = np.moveaxis(np.exp(d["k"].astype(np.float64)), 2, 1).reshape(B * C, T, 1, 1)
+    v4 = np.moveaxis(d["v"], 2, 1).reshape(B * C, T, 1, 1)
+    num = []
+    den = []
+    for c in range(C):
+        sel = slice(c, B * C, C)
+        x = np.full((1, 1), math.log(float(d["w"][c])), np.float32)
+        uu = np.full((1, 1), math.exp(float(d["u"][c])), np.float32)
+        ones = np.ones_like(v4[sel], np.float32)
+        o_num, _ = oracle.wkv_matrix(ones, k4[sel], v4[sel], x, uu, lib=oracle_lib)
+        o_den, _ = oracle.wkv_matrix(ones, k4[sel], ones, x, uu, lib=oracle_lib)
+        num.append(o_num[:, :, 0, 0])
+        den.append(o_den[:, :, 0, 0])
+    y_mat = np.stack(num, -1) / np.stack(den, -1)
+    out = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], lib=oracle_lib)
+    assert np.max(np.abs(y_mat - out["y"]) / out["scale"]) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Eagle / Finch
+
+@pytest.mark.parametrize("per_token", [False, True])
+def test_matrix_bruteforce(oracle_lib, per_token):
+    r, k, v, x, u, s0 = small_matrix_case(2, 13, 2, 8, 21 + per_token, per_token)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    o_ref, s_ref = matrix_explicit(r, k, v, x, u, s0)
+    assert rel(o, o_ref) < 1e-12
+    assert rel(sT, s_ref) < 1e-12
+
+
+def test_matrix_bruteforce_head_size_64(oracle_lib):
+    r, k, v, x, u, s0 = small_matrix_case(1, 6, 1, 64, 23, True)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    o_ref, s_ref = matrix_explicit(r, k, v, x, u, s0)
+    assert rel(o, o_ref) < 1e-12
+    assert rel(sT, s_ref) < 1e-12
+
+
+def test_matrix_golden_hand_example(oracle_lib):
+    g = read_golden("wkv_matrix_hand.txt")
+    r = np.array(g["r"], np.float32).reshape(1, 2, 1, 2)
+    k = np.array(g["k"], np.float32).reshape(1, 2, 1, 2)
+    v = np.array(g["v"], np.float32).reshape(1, 2, 1, 2)
+    x = np.array(g["x"], np.float32).reshape(1, 2, 1, 2)
+    u = np.array(g["u"], np.float32).reshape(1, 2)
+    s0 = np.array(g["s0"]).reshape(1, 1, 2, 2)
+    o, s2 = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    np.testing.assert_allclose(o.ravel(), g["o"], rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(s2.ravel(), g["s2"], rtol=1e-6, atol=1e-12)
+    _, s1 = oracle.wkv_matrix(r[:, :1], k[:, :1], v[:, :1], x[:, :1], u, s0, lib=oracle_lib)
+    np.testing.assert_allclose(s1.ravel(), g["s1"], rtol=1e-6, atol=1e-12)
+
+
+def test_matrix_geometric_closed_form(oracle_lib):
+    # static w, constant k and v:
+    #   S_{t-1} = diag(w^{t-1}) S_0 + diag((1 - w^{t-1}) / (1 - w)) k^T v
+    B, T, H, N = 1, 40, 1, 4
+    rng = np.random.default_rng(5)
+    kk = rng.normal(size=N).astype(np.float32)
+    vv = rng.normal(size=N).astype(np.float32)
+    r = rng.normal(size=(B, T, H, N)).astype(np.float32)
+    k = np.broadcast_to(kk, (B, T, H, N)).copy()
+    v = np.broadcast_to(vv, (B, T, H, N)).copy()
+    x = np.array([[-4.0, -1.5, -0.5, 0.7]], np.float32)
+    u = rng.normal(size=(H, N)).astype(np.float32)
+    s0 = rng.normal(size=(B, H, N, N))
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    w = np.exp(-np.exp(x[0].astype(np.float64)))
+    kv = np.outer(kk.astype(np.float64), vv.astype(np.float64))
+    for t in range(1, T + 1):
+        wt = w ** (t - 1)
+        st = wt[:, None] * s0[0, 0] + ((1 - wt) / (1 - w))[:, None] * kv
+        rt = r[0, t - 1, 0].astype(np.float64)
+        expect = rt @ st + np.sum(rt * u[0] * kk) * vv
+        np.testing.assert_allclose(o[0, t - 1, 0], expect, rtol=1e-11, atol=1e-12)
+    wt = w ** T
+    np.testing.assert_allclose(
+        sT[0, 0], wt[:, None] * s0[0, 0] + ((1 - wt) / (1 - w))[:, None] * kv,
+        rtol=1e-11, atol=1e-12)
+
+
+def test_matrix_no_decay_is_causal_linear_attention(oracle_lib):
+    # x = -200 gives w = exp(-exp(-200)) = 1 exactly: the WKV becomes causal
+    # linear attention with a bonus diagonal:
+    #   O = tril(R K^T, -1) V + diag(R diag(u) K^T) V + R S_0
+    r, k, v, _, u, s0 = small_matrix_case(1, 24, 1, 16, 31, True)
+    x = np.full(r.shape, -200.0, np.float32)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    R, K, V = (a[0, :, 0].astype(np.float64) for a in (r, k, v))
+    A = np.tril(R @ K.T, -1)
+    bonus = np.einsum("ti,i,ti->t", R, u[0].astype(np.float64), K)
+    expect = A @ V + bonus[:, None] * V + R @ s0[0, 0]
+    np.testing.assert_allclose(o[0, :, 0], expect, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sT[0, 0], s0[0, 0] + K.T @ V, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_full_decay_keeps_only_last_token(oracle_lib):
+    # x = +10 gives w = exp(-e^10) = 0: S_t = k_t^T v_t, so
+    # o_t = (r_t . k_{t-1}) v_{t-1} + (r_t u . k_t) v_t, and o_1 = r_1 S_0 + bonus.
+    r, k, v, _, u, s0 = small_matrix_case(1, 10, 1, 8, 32, True)
+    x = np.full(r.shape, 10.0, np.float32)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    R, K, V = (a[0, :, 0].astype(np.float64) for a in (r, k, v))
+    uu = u[0].astype(np.float64)
+    for t in range(10):
+        prev = R[t] @ s0[0, 0] if t == 0 else (R[t] @ K[t - 1]) * V[t - 1]
+        expect = prev + np.sum(R[t] * uu * K[t]) * V[t]
+        np.testing.assert_allclose(o[0, t, 0], expect, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sT[0, 0], np.outer(K[-1], V[-1]), rtol=1e-15)
+
+
+def test_matrix_single_token(oracle_lib):
+    # T = 1: o = r (S_0 + diag(u) k^T v), S_1 = diag(w) S_0 + k^T v
+    r, k, v, x, u, s0 = small_matrix_case(2, 1, 3, 8, 33, True)
+    o, s1 = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    for b in range(2):
+        for h in range(3):
+            rr, kk, vv = (a[b, 0, h].astype(np.float64) for a in (r, k, v))
+            M = s0[b, h] + np.diag(u[h].astype(np.float64)) @ np.outer(kk, vv)
+            np.testing.assert_allclose(o[b, 0, h], rr @ M, rtol=1e-12, atol=1e-14)
+            w = np.exp(-np.exp(x[b, 0, h].astype(np.float64)))
+            np.testing.assert_allclose(s1[b, h], w[:, None] * s0[b, h] + np.outer(kk, vv),
+                                       rtol=1e-13, atol=1e-15)
+
+
+def test_finch_with_constant_logits_equals_eagle_bitwise(oracle_lib):
+    r, k, v, x, u, s0 = small_matrix_case(2, 20, 2, 16, 34, False)
+    xt = np.broadcast_to(x, r.shape).copy()
+    o_e, s_e = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    o_f, s_f = oracle.wkv_matrix(r, k, v, xt, u, s0, lib=oracle_lib)
+    assert np.array_equal(o_e, o_f) and np.array_equal(s_e, s_f)
+
+
+@pytest.mark.parametrize("cut", [1, 17, 31])
+def test_matrix_split_invariance_bitwise(oracle_lib, cut):
+    r, k, v, x, u, s0 = small_matrix_case(2, 32, 2, 8, 35, True)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    o1, s1 = oracle.wkv_matrix(r[:, :cut], k[:, :cut], v[:, :cut], x[:, :cut], u, s0,
+                               lib=oracle_lib)
+    o2, s2 = oracle.wkv_matrix(r[:, cut:], k[:, cut:], v[:, cut:], x[:, cut:], u, s1,
+                               lib=oracle_lib)
+    assert np.array_equal(np.concatenate([o1, o2], 1), o)
+    assert np.array_equal(s2, sT)
+
+
+def test_matrix_stepwise_equals_sequence_bitwise(oracle_lib):
+    # decoding one token per call with the state handed over equals one call
+    r, k, v, x, u, s0 = small_matrix_case(1, 12, 2, 8, 36, True)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    s = s0.astype(np.float64)
+    for t in range(12):
+        ot, s = oracle.wkv_matrix(r[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1],
+                                  x[:, t:t + 1], u, s, lib=oracle_lib)
+        assert np.array_equal(ot[:, 0], o[:, t])
+    assert np.array_equal(s, sT)
+
+
+def test_matrix_scaling_exact(oracle_lib):
+    # linear in (v, S_0) jointly and in r alone; powers of two scale exactly
+    r, k, v, x, u, s0 = small_matrix_case(1, 16, 2, 8, 37, True)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    o2, s2 = oracle.wkv_matrix(r, k, 2 * v, x, u, 2 * s0, lib=oracle_lib)
+    assert np.array_equal(o2, 2 * o) and np.array_equal(s2, 2 * sT)
+    o4, s4 = oracle.wkv_matrix(4 * r, k, v, x, u, s0, lib=oracle_lib)
+    assert np.array_equal(o4, 4 * o) and np.array_equal(s4, sT)
+
+
+def test_matrix_additive_in_v(oracle_lib):
+    r, k, v, x, u, s0 = small_matrix_case(1, 16, 2, 8, 38, True)
+    _, _, v2, _, _, s02 = small_matrix_case(1, 16, 2, 8, 39, True)
+    oa, sa = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    ob, sb = oracle.wkv_matrix(r, k, v2, x, u, s02, lib=oracle_lib)
+    vs = v + v2  # exact: sums of two bf16 values of similar size fit in fp32
+    assert np.array_equal(vs.astype(np.float64), v.astype(np.float64) + v2.astype(np.float64))
+    oc, sc = oracle.wkv_matrix(r, k, vs, x, u, s0.astype(np.float64) + s02, lib=oracle_lib)
+    np.testing.assert_allclose(oc, oa + ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sc, sa + sb, rtol=1e-12, atol=1e-13)
+
+
+def test_matrix_heads_and_batches_are_independent(oracle_lib):
+    r, k, v, x, u, s0 = small_matrix_case(2, 9, 3, 8, 40, True)
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
+    for b in range(2):
+        for h in range(3):
+            ob, sb = oracle.wkv_matrix(r[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1],
+                                       v[b:b + 1, :, h:h + 1], x[b:b + 1, :, h:h + 1],
+                                       u[h:h + 1], s0[b:b + 1, h:h + 1], lib=oracle_lib)
+            assert np.array_equal(ob[0, :, 0], o[b, :, h])
+            assert np.array_equal(sb[0, 0], sT[b, h])
+
+
+def test_thread_count_does_not_change_results(oracle_lib):
+    r, k, v, x, u, s0 = small_matrix_case(2, 10, 3, 8, 41, True)
+    a = oracle.wkv_matrix(r, k, v, x, u, s0, nthreads=1, lib=oracle_lib)
+    b = oracle.wkv_matrix(r, k, v, x, u, s0, nthreads=5, lib=oracle_lib)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
