@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Throughput of the RWKV WKV operators on one MI355X.
+
+One step = one rwkv6_wkv_fwd call (Finch, time-parallel mode) over the Finch
+workload: B=8 sequences x T=4096 tokens x D=2560 channels (H=40 heads of 64),
+bf16 r/k/v, fp32 per-token decay logits and fp32 state, inputs resident in
+HBM.  The JSON line reports tokens*channels/s of the timed steps, the
+roofline of the chunked kernel (algorithmic bytes / average kernel time vs
+8 TB/s), the fp64 oracle timed on the host cores, and the other operators on
+their own workloads under "paths" (RWKV-4 scan, Eagle chunked, Finch decode).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-paths]
+                       [--skip-cpu] [--only PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, vendor figure
+FLUSH_BYTES = 1 << 30        # > 256 MiB Infinity Cache
+
+METRIC = "WKV tokens*channels/s & % HBM/MFMA roofline, Finch D2560 T4096; decode steps/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
+    ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
+    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode"],
+                    help="time one path only (for profiling)")
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    return ap.parse_args()
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "linear_attention_rnn_wkv_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_src, per_launch_key):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[per_launch_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events around each launch on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        s = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        self.pairs.append([s, None])
+        return self
+
+    def __exit__(self, *exc):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def flush(torch, buf):
+    buf.zero_()
+
+
+def time_launches(torch, launch, steps, warmup, flush_buf=None):
+    for _ in range(warmup):
+        if flush_buf is not None:
+            flush(torch, flush_buf)
+        launch()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush_buf is not None:
+            flush(torch, flush_buf)
+        with timer:
+            launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = timer.ms()
+    return {"kernel_ms_mean": sum(ms) / len(ms), "kernel_ms_min": min(ms),
+            "kernel_ms_max": max(ms), "wall_s": wall}
+
+
+# ---------------------------------------------------------------------------
+# paths
+
+def finch_bytes(B, T, H, N=64):
+    tok = B * T * H * N
+    return tok * (2 * 3 + 4 + 2) + 2 * B * H * N * N * 4 + H * N * 4
+
+
+def eagle_bytes(B, T, H, N=64):
+    tok = B * T * H * N
+    return tok * (2 * 3 + 2) + 2 * B * H * N * N * 4 + 2 * H * N * 4
+
+
+def rwkv4_bytes(B, T, C):
+    return B * T * C * 12 + 2 * B * 3 * C * 4 + 2 * C * 4
+
+
+def decode_bytes_per_step(B, H, N=64):
+    tok = B * H * N
+    return 2 * B * H * N * N * 4 + tok * (2 * 3 + 4 + 2) + H * N * 4
+
+
+def chunk_mfma_flops(B, T, H, N=64, L=64):
+    # per chunk and head, as executed: A^T (lower-triangular 16x16 tiles,
+    # K = N), A V (causal K-blocks), Q S, Kh_hi V + Kh_lo V, all bf16 MFMA
+    chunks = (T + L - 1) // L
+    per_chunk = 2 * 16 * 16 * 32 * (2 * 10 + 4 * (1 + 1 + 2 + 2) + 8 * 4 + 16 * 4)
+    return B * H * chunks * per_chunk
+
+
+def run_finch(torch, W, S, H2D, args, cfg=4):
+    spec = S.WORKLOADS[cfg]
+    d = S.workload(cfg)
+    g = H2D(d)
+    o = torch.empty_like(g["r"])
+    so = torch.empty_like(g["s0"])
+    fn = W.rwkv6_wkv_fwd if cfg == 4 else W.rwkv5_wkv_fwd
+
+    def launch():
+        fn(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"], state_out=so, o=o)
+
+    res = time_launches(torch, launch, args.steps, args.warmup)
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    nbytes = finch_bytes(B, T, H) if cfg == 4 else eagle_bytes(B, T, H)
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({
+        "workload": S.WORKLOAD_NAMES[cfg],
+        "tokens_channels_per_s": B * T * H * 64 / sec,
+        "algorithmic_bytes": nbytes,
+        "hbm_GBps": nbytes / sec / 1e9,
+        "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+        "mfma_TFLOPs": chunk_mfma_flops(B, T, H) / sec / 1e12,
+        "mfma_frac": chunk_mfma_flops(B, T, H) / sec / 1e12 / MFMA_BF16_PEAK_TFS,
+    })
+    return res, d
+
+
+def run_rwkv4(torch, W, S, H2D, args, flush_buf):
+    spec = S.WORKLOADS[2]
+    d = S.workload(2)
+    k, v, w, u = (H2D({"a": d[n]})["a"] for n in ("k", "v", "w", "u"))
+    y = torch.empty_like(k)
+    so = torch.empty((spec["B"], 3, spec["C"]), dtype=torch.float32, device="cuda")
+
+    def launch():
+        W.rwkv4_wkv_fwd(k, v, w, u, state_out=so, y=y)
+
+    res = time_launches(torch, launch, max(args.steps, 20), args.warmup, flush_buf)
+    nbytes = rwkv4_bytes(spec["B"], spec["T"], spec["C"])
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({"workload": S.WORKLOAD_NAMES[2], "cache": "flushed before each launch",
+                "tokens_channels_per_s": spec["B"] * spec["T"] * spec["C"] / sec,
+                "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+    return res
+
+
+def run_decode(torch, W, S, H2D, args):
+    spec = S.WORKLOADS[5]
+    steps = args.decode_steps
+    d = S.workload(5, steps=steps)
+    g = H2D(d)
+    st = g["s0"].clone()
+    o = torch.empty_like(g["r"])
+    views = [(g["r"][s].unsqueeze(1), g["k"][s].unsqueeze(1), g["v"][s].unsqueeze(1),
+              g["x"][s].unsqueeze(1), o[s].unsqueeze(1)) for s in range(steps)]
+
+    def one(s):
+        r, k, v, x, os_ = views[s]
+        W.rwkv6_wkv_step(r, k, v, x, g["u"], st, o=os_)
+
+    for s in range(min(8, steps)):  # warm-up on a scratch copy of the state
+        one(s)
+    st.copy_(g["s0"])
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        with timer:
+            one(s)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms = timer.ms()
+    per = sum(ms) / len(ms)
+    nbytes = decode_bytes_per_step(spec["B"], spec["H"])
+    return {"workload": S.WORKLOAD_NAMES[5], "steps": steps,
+            "steps_per_s": steps / (total_ms / 1e3), "interval_ms": total_ms,
+            "kernel_ms_mean": per, "wall_s": wall,
+            "algorithmic_bytes_per_step": nbytes,
+            "hbm_GBps": nbytes / (per / 1e3) / 1e9,
+            "hbm_frac": nbytes / (per / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(S, d4):
+    """The fp64 oracle on the whole Finch workload, all host threads."""
+    import oracle
+    r, k, v = (S.bf16_to_f32(d4[n]) for n in ("r", "k", "v"))
+    nthreads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.wkv_matrix(r, k, v, d4["x"], d4["u"], d4["s0"], nthreads=nthreads)
+    sec = time.perf_counter() - t0
+    B, T, H, N = d4["r"].shape
+    return {"value": B * T * H * N / sec, "unit": "tokens*channels/s", "cores": nthreads,
+            "kind": "oracle", "seconds": sec,
+            "sample": f"the full Finch workload (B={B}, T={T}, H={H}, N={N}), one pass"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the operator shards by sequence and head with no exchange; see the "
+              "design notes)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import linear_attention_rnn_wkv_amd as W
+    import wkv_synth as S
+
+    W.lib()
+    torch.cuda.set_device(0)
+
+    def H2D(d):
+        out = {}
+        for n, a in d.items():
+            a = np.ascontiguousarray(a)
+            t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+            t = t.cuda()
+            out[n] = t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+        return out
+
+    paths = {}
+    only = args.only
+    d4 = None
+    if only in (None, "finch"):
+        print("finch forward ...", file=sys.stderr, flush=True)
+        finch, d4 = run_finch(torch, W, S, H2D, args, cfg=4)
+        paths["finch_fwd"] = finch
+    flush_buf = None
+    if not args.skip_paths and only in (None, "eagle"):
+        print("eagle forward ...", file=sys.stderr, flush=True)
+        paths["eagle_fwd"], _ = run_finch(torch, W, S, H2D, args, cfg=3)
+    if not args.skip_paths and only in (None, "rwkv4"):
+        print("rwkv4 forward ...", file=sys.stderr, flush=True)
+        flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        paths["rwkv4_fwd"] = run_rwkv4(torch, W, S, H2D, args, flush_buf)
+        del flush_buf
+    if not args.skip_paths and only in (None, "decode"):
+        print("finch decode ...", file=sys.stderr, flush=True)
+        paths["finch_decode"] = run_decode(torch, W, S, H2D, args)
+    torch.cuda.synchronize()
+
+    if "finch_fwd" not in paths:
+        print(json.dumps({"paths": paths}))
+        return 0
+
+    finch = paths["finch_fwd"]
+    spec = S.WORKLOADS[4]
+    ms = finch["wall_s"] / args.steps * 1e3
+    cpu = None
+    if not args.skip_cpu:
+        print("oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(S, d4)
+    traffic = measured_traffic("wkv_chunk.hip", "finch_fwd")
+    line = {
+        "metric": METRIC,
+        "value": spec["B"] * spec["T"] * spec["H"] * spec["N"] / (ms / 1e3),
+        "unit": "tokens*channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": S.WORKLOAD_NAMES[4], "B": spec["B"], "T": spec["T"],
+                   "H": spec["H"], "N": spec["N"], "D": spec["H"] * spec["N"],
+                   "state": "fp32", "decay_logits": "fp32 per token"},
+        "roofline": {"bound": "hbm", "achieved": finch["hbm_GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": finch["hbm_frac"], "traffic": traffic},
+        "cpu_baseline": cpu,
+        "paths": paths,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,154 @@
+/*
+ * rwkv_wkv.h -- C ABI of the RWKV WKV time-mixing operators for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library computes the WKV recurrence of three RWKV generations:
+ *
+ *  RWKV-4: per-channel decayed weighted average (RWKV paper summary,
+ *    cafeforensic.com zhuanlan/310315, section "Temporal structure for
+ *    sequential data processing": decay e^{-w} and current-token bonus e^{u}
+ *    of the WKV; section "Gradient stability and layer stacking": evaluated
+ *    as a time-dependent softmax for numerical stability):
+ *        y_t = (sum_{i<t} e^{-(t-1-i)w + k_i} v_i + e^{u+k_t} v_t)
+ *            / (sum_{i<t} e^{-(t-1-i)w + k_i}     + e^{u+k_t})
+ *
+ *  Eagle (RWKV-5) and Finch (RWKV-6): per-head matrix-valued state
+ *    (RWKV-5/6 summary, blob.wenxiaobai.com, section 4 notation: per-head row
+ *    vectors, matrices act on the right; 4.1.2 "Eagle time mixing":
+ *    w = exp(-exp(omega)) per key channel, bonus u on the current token's
+ *    k^T v, r used like a query; 4.2.2 "Finch time mixing": w_t varies per
+ *    token and channel):
+ *        o_t = r_t (S_{t-1} + diag(u) k_t^T v_t)
+ *        S_t = diag(w_t) S_{t-1} + k_t^T v_t,     w_t = exp(-exp(x_t))
+ *    with S[i][j], i = key channel, j = value channel.
+ *
+ * Both modes the pages describe are provided: the time-parallel (chunked)
+ * mode for prefill / training forward (RWKV paper summary, section
+ * "Transformer-like parallelization"), and the serial RNN mode for decoding
+ * (section "RNN-like sequential decoding": each output depends only on the
+ * latest state, so speed and memory per token are constant in sequence
+ * length).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing and keeps no state between calls.
+ *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
+ *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
+ *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
+ *    nearest, ties to even.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; nothing waits for it.  Errors raised by a running kernel
+ *    surface at the caller's next synchronisation.
+ *  - Return value: RWKV_OK, or a negative status.  Arguments are validated on
+ *    the host before any HIP call; on a validation error nothing is
+ *    launched and no output is touched.
+ *  - Inputs containing Inf or NaN give unspecified results (they are not
+ *    scanned for).
+ *  - T == 0 is valid: the state is copied from state_in to state_out (or set
+ *    to the empty / zero state when state_in is NULL); r, k, v, x, y, o may
+ *    then be NULL.
+ */
+#ifndef RWKV_WKV_H
+#define RWKV_WKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rwkv_bf16; /* raw bfloat16 bits */
+
+enum rwkv_status {
+    RWKV_OK = 0,
+    RWKV_E_NULL = -1,        /* a required pointer is NULL */
+    RWKV_E_DIM = -2,         /* B, H or N < 1, T < 0, or a size overflows */
+    RWKV_E_UNSUPPORTED = -3, /* a valid shape this build does not implement */
+    RWKV_E_ALIGN = -4,       /* a pointer is not 16-byte aligned where required */
+    RWKV_E_ALIAS = -5,       /* an output overlaps an input or another output */
+    RWKV_E_HIP = -6          /* the HIP runtime rejected a launch or copy */
+};
+
+/* Static, human-readable text of a status code. */
+const char *rwkv_wkv_strerror(int status);
+
+/*
+ * RWKV-4 WKV forward, fp32.  Channels are independent: C = H*N and any
+ * factorisation of C gives identical results.
+ *
+ *   k, v       [B][T][C] fp32 keys and values
+ *   w          [C] fp32 decay RATE, w >= 0; the per-step factor is e^{-w}
+ *   u          [C] fp32 bonus of the current token
+ *   state_in   [B][3][C] fp32 history (a, b, p), or NULL for an empty one.
+ *              The history's numerator and denominator are a*e^p and b*e^p
+ *              (p is a running maximum exponent that keeps a and b finite);
+ *              the empty history is a = b = 0, p = -1e38.
+ *   state_out  [B][3][C] fp32 state after token T, or NULL.  It may equal
+ *              state_in exactly (in-place update) but not partially overlap.
+ *   y          [B][T][C] fp32 output
+ *
+ * Pointers need 4-byte alignment.  One sequence must span fewer than 2^31
+ * elements: (T + 64) * C <= INT32_MAX, else RWKV_E_UNSUPPORTED.
+ */
+int rwkv4_wkv_fwd(int B, int T, int H, int N,
+                  const float *k, const float *v,
+                  const float *w, const float *u,
+                  const float *state_in, float *state_out,
+                  float *y, void *stream);
+
+/*
+ * Eagle (RWKV-5) WKV forward, time-parallel (chunked) mode.  N must be 64.
+ *
+ *   r, k, v    [B][T][H][N] bf16 receptance, key, value
+ *   x          [H][N] fp32 decay logit omega, shared by all tokens and
+ *              sequences: w = exp(-exp(x)) lies in (0, 1)
+ *   u          [H][N] fp32 bonus
+ *   state_in   [B][H][N][N] fp32 initial state S_0 (key-major: row i is key
+ *              channel i), or NULL for zeros
+ *   state_out  [B][H][N][N] fp32 state after token T, or NULL.  It may equal
+ *              state_in exactly, but not partially overlap it.
+ *   o          [B][T][H][N] bf16 output
+ *
+ * All pointers need 16-byte alignment.
+ */
+int rwkv5_wkv_fwd(int B, int T, int H, int N,
+                  const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                  const float *x, const float *u,
+                  const float *state_in, float *state_out,
+                  rwkv_bf16 *o, void *stream);
+
+/*
+ * Finch (RWKV-6) WKV forward, time-parallel (chunked) mode.  N must be 64.
+ * As rwkv5_wkv_fwd, except that the decay logit is per token and channel:
+ *
+ *   x          [B][T][H][N] fp32: token t decays the state by
+ *              w_t = exp(-exp(x_t)) after producing o_t, so x at the last
+ *              token only affects state_out.
+ */
+int rwkv6_wkv_fwd(int B, int T, int H, int N,
+                  const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                  const float *x, const float *u,
+                  const float *state_in, float *state_out,
+                  rwkv_bf16 *o, void *stream);
+
+/*
+ * Finch (RWKV-6) WKV, serial (RNN) mode: tokens are applied one at a time to
+ * a state that stays in registers.  Decoding calls it with T == 1.  N must
+ * be 64.  Arguments as rwkv6_wkv_fwd, except:
+ *
+ *   state      [B][H][N][N] fp32, read as S_0 and overwritten with S_T
+ *              (required, never NULL).
+ *
+ * Splitting a sequence at any token and handing the state over gives
+ * bit-identical outputs and state.
+ */
+int rwkv6_wkv_step(int B, int T, int H, int N,
+                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                   const float *x, const float *u,
+                   float *state, rwkv_bf16 *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV_WKV_H */

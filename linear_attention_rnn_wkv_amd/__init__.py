@@ -1,0 +1,177 @@
+"""RWKV WKV operators on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``librwkv_wkv.so``: it checks tensor shapes, dtypes and
+devices, allocates missing outputs with torch, and passes raw device pointers
+and the current HIP stream to the C ABI declared in ``include/rwkv_wkv.h``.
+Every step of the computation runs in the library's HIP kernels; there is no
+other implementation to fall back to, and calling any operator without the
+built library raises.
+
+Operators (names as in the C ABI):
+  rwkv4_wkv_fwd   RWKV-4 per-channel WKV, fp32
+  rwkv5_wkv_fwd   Eagle matrix-state WKV, time-parallel (chunked)
+  rwkv6_wkv_fwd   Finch matrix-state WKV, time-parallel (chunked)
+  rwkv6_wkv_step  Finch matrix-state WKV, serial (decode)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librwkv_wkv.so")
+
+RWKV_OK = 0
+STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPORTED",
+          -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP"}
+EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv5_wkv_fwd", "rwkv6_wkv_fwd",
+           "rwkv6_wkv_step")
+
+_lib = None
+
+
+class WKVError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is not built; run `python -m linear_attention_rnn_wkv_amd._build`")
+        L = ctypes.CDLL(LIBRARY)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.rwkv_wkv_strerror.restype = ctypes.c_char_p
+        L.rwkv_wkv_strerror.argtypes = [I]
+        L.rwkv4_wkv_fwd.restype = I
+        L.rwkv4_wkv_fwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
+        for name in ("rwkv5_wkv_fwd", "rwkv6_wkv_fwd"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P]
+        L.rwkv6_wkv_step.restype = I
+        L.rwkv6_wkv_step.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != RWKV_OK:
+        raise WKVError(fn, status, lib().rwkv_wkv_strerror(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(name, t, shape, dtype):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rwkv4_wkv_fwd(k, v, w, u, state_in=None, state_out=None, y=None, H=1,
+                  return_state=True, stream=None):
+    """RWKV-4 WKV.  k, v: [B, T, C] fp32; w (decay rate), u: [C] fp32;
+    state_in / state_out: [B, 3, C] fp32 (a, b, p).  Returns (y, state_out)."""
+    import torch
+    B, T, C = k.shape
+    if C % H:
+        raise ValueError("C must be divisible by H")
+    f32 = torch.float32
+    _expect("k", k, (B, T, C), f32)
+    _expect("v", v, (B, T, C), f32)
+    _expect("w", w, (C,), f32)
+    _expect("u", u, (C,), f32)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, 3, C), f32)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=f32, device=k.device)
+    _expect("y", y, (B, T, C), f32)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, 3, C), dtype=f32, device=k.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, 3, C), f32)
+    _check("rwkv4_wkv_fwd", lib().rwkv4_wkv_fwd(
+        B, T, H, C // H, _ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(state_in),
+        _ptr(state_out), _ptr(y), _stream(stream)))
+    return y, state_out
+
+
+def _matrix_args(r, k, v, x, u, per_token):
+    import torch
+    B, T, H, N = r.shape
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect("r", r, (B, T, H, N), bf)
+    _expect("k", k, (B, T, H, N), bf)
+    _expect("v", v, (B, T, H, N), bf)
+    _expect("x", x, (B, T, H, N) if per_token else (H, N), f32)
+    _expect("u", u, (H, N), f32)
+    return B, T, H, N
+
+
+def _matrix_fwd(name, per_token, r, k, v, x, u, state_in, state_out, o, return_state,
+                stream):
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=r.device)
+    _expect("o", o, (B, T, H, N), torch.bfloat16)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, H, N, N), torch.float32)
+    _check(name, getattr(lib(), name)(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in),
+        _ptr(state_out), _ptr(o), _stream(stream)))
+    return o, state_out
+
+
+def rwkv5_wkv_fwd(r, k, v, x, u, state_in=None, state_out=None, o=None,
+                  return_state=True, stream=None):
+    """Eagle WKV, chunked.  r, k, v: [B, T, H, 64] bf16; x (decay logit omega),
+    u: [H, 64] fp32; state: [B, H, 64, 64] fp32.  Returns (o, state_out)."""
+    return _matrix_fwd("rwkv5_wkv_fwd", False, r, k, v, x, u, state_in, state_out, o,
+                       return_state, stream)
+
+
+def rwkv6_wkv_fwd(r, k, v, x, u, state_in=None, state_out=None, o=None,
+                  return_state=True, stream=None):
+    """Finch WKV, chunked.  As rwkv5_wkv_fwd but x: [B, T, H, 64] fp32."""
+    return _matrix_fwd("rwkv6_wkv_fwd", True, r, k, v, x, u, state_in, state_out, o,
+                       return_state, stream)
+
+
+def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):
+    """Finch WKV, serial: r, k, v: [B, T, H, 64] bf16 (T = 1 to decode);
+    x: [B, T, H, 64] fp32; u: [H, 64]; state: [B, H, 64, 64] fp32, updated in
+    place.  Returns o."""
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, True)
+    _expect("state", state, (B, H, N, N), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=r.device)
+    _expect("o", o, (B, T, H, N), torch.bfloat16)
+    _check("rwkv6_wkv_step", lib().rwkv6_wkv_step(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state), _ptr(o),
+        _stream(stream)))
+    return o

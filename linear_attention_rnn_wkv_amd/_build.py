@@ -1,0 +1,68 @@
+"""Build librwkv_wkv.so (the C-ABI library) for gfx950 with hipcc.
+
+Usage: python -m linear_attention_rnn_wkv_amd._build [--verbose]
+The library is written next to this file; objects go to <repo>/_build/.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(ROOT, "_build")
+LIBRARY = os.path.join(PKG, "librwkv_wkv.so")
+SOURCES = ["rwkv_wkv_abi.hip", "rwkv4_scan.hip", "wkv_step.hip", "wkv_chunk.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Wall", "-Wno-unused-result",
+    # no packed fp32 math (v_pk_*_f32) anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _run(cmds, verbose):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        # the host pass does not know the packed-fp32 feature: drop that note
+        lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+        if lines and (verbose or p.returncode):
+            print("\n".join(lines), file=sys.stderr)
+        if p.returncode:
+            failed.append(" ".join(cmd))
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source and link librwkv_wkv.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    _run(cmds, verbose)
+    tmp = LIBRARY + ".tmp"
+    _run([[HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

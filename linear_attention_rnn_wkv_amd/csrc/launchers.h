@@ -1,0 +1,33 @@
+// launchers.h -- host-side launch functions of the WKV kernels (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+// RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
+hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
+                        const float *w, const float *u, const float *state_in,
+                        float *state_out, float *y, hipStream_t stream);
+
+// Finch serial (RNN-mode) path, N = 64, state updated in place.
+hipError_t launch_wkv6_step(int B, int T, int H, const uint16_t *r,
+                            const uint16_t *k, const uint16_t *v, const float *x,
+                            const float *u, float *state, uint16_t *o,
+                            hipStream_t stream);
+
+// Eagle / Finch chunked (time-parallel) path, N = 64.
+hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
+                              const uint16_t *r, const uint16_t *k,
+                              const uint16_t *v, const float *x, const float *u,
+                              const float *state_in, float *state_out,
+                              uint16_t *o, hipStream_t stream);
+
+// Fill n floats with `value` (used for empty / zero states when T == 0).
+hipError_t launch_fill(float *dst, int64_t n, float value, hipStream_t stream);
+
+// RWKV-4 empty history: a = b = 0, p = -1e38 for [B][3][C].
+hipError_t launch_rwkv4_empty_state(int B, int C, float *state, hipStream_t stream);
+
+}  // namespace wkv

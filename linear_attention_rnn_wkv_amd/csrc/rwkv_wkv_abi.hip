@@ -1,0 +1,175 @@
+// rwkv_wkv_abi.hip -- the C ABI: host-side validation and dispatch.
+//
+// Every entry point validates its arguments completely before the first HIP
+// call, so a rejected call launches nothing and touches no output.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "launchers.h"
+#include "rwkv_wkv.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // per tensor; far above any HBM
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// product of non-negative factors, or -1 when it exceeds kMaxElems
+int64_t checked_mul(std::initializer_list<int64_t> f) {
+    int64_t r = 1;
+    for (int64_t x : f) {
+        if (x < 0) return -1;
+        if (x != 0 && r > kMaxElems / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RWKV_OK : RWKV_E_HIP; }
+
+// An output must not overlap any input or other output.  `same_ok` marks the
+// single permitted exact alias (state_out == state_in).
+int check_outputs(std::initializer_list<Span> outs, std::initializer_list<Span> ins,
+                  const void *same_a = nullptr, const void *same_b = nullptr) {
+    for (const Span &o : outs) {
+        for (const Span &i : ins) {
+            if (o.p != nullptr && o.p == i.p && o.p == same_a && i.p == same_b &&
+                same_a != nullptr)
+                continue;
+            if (overlaps(o, i)) return RWKV_E_ALIAS;
+        }
+    }
+    for (auto a = outs.begin(); a != outs.end(); ++a)
+        for (auto b = a + 1; b != outs.end(); ++b)
+            if (overlaps(*a, *b)) return RWKV_E_ALIAS;
+    return RWKV_OK;
+}
+
+// Shared checks of the Eagle / Finch entry points.  x_elems: elements of x.
+int check_matrix(int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                 const void *x, int64_t x_elems, const void *u, const void *s_in,
+                 const void *s_out, bool s_in_required, const void *o) {
+    if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
+    const int64_t tok = checked_mul({B, T, H, N});
+    const int64_t st = checked_mul({B, H, N, N});
+    if (tok < 0 || st < 0 || x_elems < 0) return RWKV_E_DIM;
+    if (N != 64) return RWKV_E_UNSUPPORTED;
+    if (s_in_required && s_in == nullptr) return RWKV_E_NULL;
+    if (T > 0 && (r == nullptr || k == nullptr || v == nullptr || x == nullptr ||
+                  u == nullptr || o == nullptr))
+        return RWKV_E_NULL;
+    for (const void *p : {r, k, v, x, u, s_in, s_out, o})
+        if (p != nullptr && !aligned(p, 16)) return RWKV_E_ALIGN;
+    const Span sr{r, tok * 2}, sk{k, tok * 2}, sv{v, tok * 2}, sx{x, x_elems * 4},
+        su{u, (int64_t)H * N * 4}, ssi{s_in, st * 4}, sso{s_out, st * 4}, so{o, tok * 2};
+    if (T == 0) return check_outputs({sso}, {ssi}, s_out, s_in);
+    return check_outputs({so, sso}, {sr, sk, sv, sx, su, ssi}, s_out, s_in);
+}
+
+int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
+               const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
+               const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
+    const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
+    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
+    if (st != RWKV_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (state_out == nullptr || state_out == state_in) return RWKV_OK;
+        const int64_t n = (int64_t)B * H * N * N;
+        if (state_in == nullptr) return hip_status(wkv::launch_fill(state_out, n, 0.0f, s));
+        return hip_status(hipMemcpyAsync(state_out, state_in, n * 4,
+                                         hipMemcpyDeviceToDevice, s));
+    }
+    return hip_status(wkv::launch_wkv_chunked(per_token, B, T, H, r, k, v, x, u,
+                                              state_in, state_out, o, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rwkv_wkv_strerror(int status) {
+    switch (status) {
+        case RWKV_OK: return "ok";
+        case RWKV_E_NULL: return "a required pointer is NULL";
+        case RWKV_E_DIM: return "invalid dimension (B, H, N < 1, T < 0, or size overflow)";
+        case RWKV_E_UNSUPPORTED:
+            return "unsupported shape (Eagle/Finch head size must be 64; RWKV-4 sequence too long)";
+        case RWKV_E_ALIGN: return "pointer not aligned as required";
+        case RWKV_E_ALIAS: return "an output overlaps an input or another output";
+        case RWKV_E_HIP: return "the HIP runtime rejected a launch or copy";
+        default: return "unknown status";
+    }
+}
+
+int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
+                  const float *w, const float *u, const float *state_in,
+                  float *state_out, float *y, void *stream) {
+    if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
+    const int64_t C = checked_mul({H, N});
+    const int64_t tok = checked_mul({B, T, H, N});
+    const int64_t st = checked_mul({B, 3, H, N});
+    if (C < 0 || tok < 0 || st < 0 || C > INT32_MAX / 2) return RWKV_E_DIM;
+    // the scan addresses one sequence with 32-bit element offsets
+    if (((int64_t)T + 64) * C > INT32_MAX) return RWKV_E_UNSUPPORTED;
+    if (T > 0 && (k == nullptr || v == nullptr || w == nullptr || u == nullptr ||
+                  y == nullptr))
+        return RWKV_E_NULL;
+    for (const void *p : {(const void *)k, (const void *)v, (const void *)w,
+                          (const void *)u, (const void *)state_in,
+                          (const void *)state_out, (const void *)y})
+        if (p != nullptr && !aligned(p, 4)) return RWKV_E_ALIGN;
+    const Span sk{k, tok * 4}, sv{v, tok * 4}, sw{w, C * 4}, su{u, C * 4},
+        ssi{state_in, st * 4}, sso{state_out, st * 4}, sy{y, tok * 4};
+    int chk = (T == 0) ? check_outputs({sso}, {ssi}, state_out, state_in)
+                       : check_outputs({sy, sso}, {sk, sv, sw, su, ssi}, state_out, state_in);
+    if (chk != RWKV_OK) return chk;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        if (state_out == nullptr || state_out == state_in) return RWKV_OK;
+        if (state_in == nullptr)
+            return hip_status(wkv::launch_rwkv4_empty_state(B, (int)C, state_out, s));
+        return hip_status(hipMemcpyAsync(state_out, state_in, st * 4,
+                                         hipMemcpyDeviceToDevice, s));
+    }
+    return hip_status(
+        wkv::launch_rwkv4(B, T, (int)C, k, v, w, u, state_in, state_out, y, s));
+}
+
+int rwkv5_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                  const rwkv_bf16 *v, const float *x, const float *u,
+                  const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
+    return matrix_fwd(false, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+}
+
+int rwkv6_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                  const rwkv_bf16 *v, const float *x, const float *u,
+                  const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
+    return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+}
+
+int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                   const rwkv_bf16 *v, const float *x, const float *u, float *state,
+                   rwkv_bf16 *o, void *stream) {
+    const int64_t x_elems = checked_mul({B, T, H, N});
+    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state, state, true, o);
+    if (st != RWKV_OK) return st;
+    if (T == 0) return RWKV_OK;
+    return hip_status(
+        wkv::launch_wkv6_step(B, T, H, r, k, v, x, u, state, o, (hipStream_t)stream));
+}
+
+}  // extern "C"

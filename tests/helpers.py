@@ -1,0 +1,63 @@
+"""Shared test helpers: tensor marshalling and the error metrics."""
+import numpy as np
+
+import wkv_synth as S
+
+
+def to_dev(a, bf16=False):
+    """numpy -> contiguous CUDA tensor (uint16 bf16 bits become torch.bfloat16)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if bf16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def bf16_host(t):
+    """CUDA bfloat16 tensor -> exact float64 numpy array."""
+    import torch
+    bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return S.bf16_to_f32(bits).astype(np.float64)
+
+
+def f64_host(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rel_errors(got, ref):
+    """(rms_rel, max_rel): ||g - r||_2 / ||r||_2 and
+    max_i |g_i - r_i| / max(|r_i|, rms(r))."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    nr = np.linalg.norm(ref)
+    if nr == 0:
+        return float(np.linalg.norm(got)), float(np.max(np.abs(got), initial=0.0))
+    rms = nr / np.sqrt(ref.size)
+    d = np.abs(got - ref)
+    return float(np.linalg.norm(got - ref) / nr), float(np.max(d / np.maximum(np.abs(ref), rms)))
+
+
+# tolerances for bf16-input Eagle / Finch (RMS relative, max relative)
+RMS_TOL = 5e-3
+MAX_TOL = 3e-2
+# RWKV-4 fp32: max |y - y_ref| / max(|y_ref|, |v|-weighted average)
+RWKV4_TOL = 1e-5
+
+
+def assert_matrix_close(got, ref, what):
+    rms, mx = rel_errors(got, ref)
+    assert rms <= RMS_TOL and mx <= MAX_TOL, f"{what}: rms_rel {rms:.3e}, max_rel {mx:.3e}"
+    return rms, mx
+
+
+def matrix_inputs_dev(d, per_token=True):
+    """Move a wkv_synth matrix-input dict to the GPU."""
+    return dict(r=to_dev(d["r"], True), k=to_dev(d["k"], True), v=to_dev(d["v"], True),
+                x=to_dev(d["x"]), u=to_dev(d["u"]), s0=to_dev(d["s0"]))
+
+
+def matrix_inputs_f32(d):
+    """The exact fp32 values the GPU sees, for the oracle."""
+    return (S.bf16_to_f32(d["r"]), S.bf16_to_f32(d["k"]), S.bf16_to_f32(d["v"]),
+            d["x"], d["u"], d["s0"])

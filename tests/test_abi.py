@@ -1,0 +1,167 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects invalid arguments before any HIP call (so these run
+without a GPU; dummy host addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_rnn_wkv_amd as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_DIM, E_UNSUP, E_ALIGN, E_ALIAS = 0, -1, -2, -3, -4, -5
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "rwkv_wkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rwkv\w*)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(W.LIBRARY):
+        from linear_attention_rnn_wkv_amd import _build
+        _build.build()
+    return W.lib()
+
+
+def test_header_declares_the_operators():
+    assert header_functions() == sorted(W.EXPORTS)
+
+
+def test_library_exports_every_declared_function(L):
+    out = os.popen(f"nm -D --defined-only {W.LIBRARY}").read()
+    exported = set(re.findall(r"\bT (\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_strerror_covers_every_status(L):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert L.rwkv_wkv_strerror(st).decode() != "unknown status"
+    assert L.rwkv_wkv_strerror(42).decode() == "unknown status"
+
+
+# fake, aligned host addresses: validation fails before they could be used
+BASE = 1 << 40
+SPAN = 1 << 30
+
+
+def addr(i, misalign=0):
+    return ctypes.c_void_p(BASE + i * SPAN + misalign)
+
+
+def rwkv4(L, B=2, T=8, H=1, N=16, k=1, v=2, w=3, u=4, si=5, so=6, y=7, **mis):
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
+         for n, i in dict(k=k, v=v, w=w, u=u, si=si, so=so, y=y).items()}
+    return L.rwkv4_wkv_fwd(B, T, H, N, a["k"], a["v"], a["w"], a["u"], a["si"], a["so"],
+                           a["y"], None)
+
+
+def matrix(L, fn, B=2, T=8, H=2, N=64, r=1, k=2, v=3, x=4, u=5, si=6, so=7, o=8, **mis):
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
+         for n, i in dict(r=r, k=k, v=v, x=x, u=u, si=si, so=so, o=o).items()}
+    return getattr(L, fn)(B, T, H, N, a["r"], a["k"], a["v"], a["x"], a["u"], a["si"],
+                          a["so"], a["o"], None)
+
+
+def step(L, B=2, T=1, H=2, N=64, r=1, k=2, v=3, x=4, u=5, s=6, o=7, **mis):
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
+         for n, i in dict(r=r, k=k, v=v, x=x, u=u, s=s, o=o).items()}
+    return L.rwkv6_wkv_step(B, T, H, N, a["r"], a["k"], a["v"], a["x"], a["u"], a["s"],
+                            a["o"], None)
+
+
+@pytest.mark.parametrize("dims", [(0, 8, 1, 16), (2, -1, 1, 16), (2, 8, 0, 16),
+                                  (2, 8, 1, 0), (1 << 20, 1 << 20, 1, 1 << 10)])
+def test_rwkv4_bad_dims(L, dims):
+    B, T, H, N = dims
+    assert rwkv4(L, B=B, T=T, H=H, N=N) == E_DIM
+
+
+def test_rwkv4_too_long_sequence(L):
+    assert rwkv4(L, B=1, T=1 << 21, H=1, N=1 << 10) == E_UNSUP
+
+
+@pytest.mark.parametrize("missing", ["k", "v", "w", "u", "y"])
+def test_rwkv4_null(L, missing):
+    assert rwkv4(L, **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("which", ["k", "y", "si"])
+def test_rwkv4_misaligned(L, which):
+    kw = {"k": 1, "v": 2, "w": 3, "u": 4, "si": 5, "so": 6, "y": 7}
+    a = {n: addr(i, 2 if n == which else 0) for n, i in kw.items()}
+    st = L.rwkv4_wkv_fwd(2, 8, 1, 16, a["k"], a["v"], a["w"], a["u"], a["si"], a["so"],
+                         a["y"], None)
+    assert st == E_ALIGN
+
+
+def test_rwkv4_output_overlaps_input(L):
+    assert rwkv4(L, y=1) == E_ALIAS          # y == k
+    assert rwkv4(L, so=3) == E_ALIAS         # state_out == w
+
+
+def test_rwkv4_outputs_overlap_each_other(L):
+    assert rwkv4(L, so=7) == E_ALIAS         # state_out == y
+
+
+def test_rwkv4_state_partial_overlap(L):
+    kw = {"k": 1, "v": 2, "w": 3, "u": 4}
+    a = {n: addr(i) for n, i in kw.items()}
+    si = ctypes.c_void_p(BASE + 5 * SPAN)
+    so = ctypes.c_void_p(BASE + 5 * SPAN + 4)  # overlaps but is not equal
+    assert L.rwkv4_wkv_fwd(2, 8, 1, 16, a["k"], a["v"], a["w"], a["u"], si, so,
+                           addr(7), None) == E_ALIAS
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+def test_matrix_head_size_must_be_64(L, fn):
+    assert matrix(L, fn, N=32) == E_UNSUP
+    assert matrix(L, fn, N=128) == E_UNSUP
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+@pytest.mark.parametrize("dims", [(0, 8, 2), (2, -3, 2), (2, 8, 0)])
+def test_matrix_bad_dims(L, fn, dims):
+    B, T, H = dims
+    assert matrix(L, fn, B=B, T=T, H=H) == E_DIM
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+@pytest.mark.parametrize("missing", ["r", "k", "v", "x", "u", "o"])
+def test_matrix_null(L, fn, missing):
+    assert matrix(L, fn, **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+@pytest.mark.parametrize("which", ["r", "x", "si", "so", "o"])
+def test_matrix_misaligned(L, fn, which):
+    kw = {"r": 1, "k": 2, "v": 3, "x": 4, "u": 5, "si": 6, "so": 7, "o": 8}
+    a = {n: addr(i, 8 if n == which else 0) for n, i in kw.items()}
+    st = getattr(L, fn)(2, 8, 2, 64, a["r"], a["k"], a["v"], a["x"], a["u"], a["si"],
+                        a["so"], a["o"], None)
+    assert st == E_ALIGN
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+def test_matrix_aliasing(L, fn):
+    assert matrix(L, fn, o=1) == E_ALIAS    # o == r
+    assert matrix(L, fn, o=4) == E_ALIAS    # o == x
+    assert matrix(L, fn, so=8) == E_ALIAS   # state_out == o
+
+
+def test_step_requires_state(L):
+    assert step(L, s=None) == E_NULL
+
+
+def test_step_rejects_output_on_state(L):
+    assert step(L, o=6) == E_ALIAS
+
+
+def test_step_head_size(L):
+    assert step(L, N=16) == E_UNSUP

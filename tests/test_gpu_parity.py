@@ -1,0 +1,351 @@
+"""GPU parity: every C-ABI entry point against the fp64 oracle on the same
+seeded inputs, from tiny and ragged shapes up to the full workloads (sampled
+heads at full size), plus the exact equivalences the method implies:
+split / state handoff, chunked vs serial mode, determinism, in-place state.
+
+Tolerances: RWKV-4 fp32 max relative error 1e-5 (relative to
+max(|y|, the |v|-weighted average)); bf16 Eagle / Finch RMS relative error
+5e-3 and max relative error 3e-2 (relative to max(|o|, rms(o))), on outputs
+and states."""
+import numpy as np
+import pytest
+
+import oracle
+import wkv_synth as S
+from helpers import (RWKV4_TOL, assert_matrix_close, bf16_host, f64_host, matrix_inputs_dev,
+                     matrix_inputs_f32, rel_errors, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import linear_attention_rnn_wkv_amd as W  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    W.lib()  # raises when the library is missing
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# RWKV-4
+
+def rwkv4_check(d, state_in=None, H=1):
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    si = None if state_in is None else to_dev(state_in)
+    y, so = W.rwkv4_wkv_fwd(k, v, w, u, state_in=si, H=H)
+    sync()
+    num_in = den_in = None
+    if state_in is not None:
+        num_in = state_in[:, 0].astype(np.float64) * np.exp(state_in[:, 2].astype(np.float64))
+        den_in = state_in[:, 1].astype(np.float64) * np.exp(state_in[:, 2].astype(np.float64))
+    ref = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], num_in, den_in)
+    yg = f64_host(y)
+    err = np.max(np.abs(yg - ref["y"]) / np.maximum(np.abs(ref["y"]), ref["scale"]))
+    assert err <= RWKV4_TOL, f"y max rel err {err:.3e}"
+    sg = f64_host(so)
+    den = sg[:, 1] * np.exp(sg[:, 2])
+    num = sg[:, 0] * np.exp(sg[:, 2])
+    vmax = np.max(np.abs(d["v"]), axis=1).astype(np.float64)
+    if num_in is not None:
+        vmax = np.maximum(vmax, np.abs(num_in) / np.maximum(den_in, 1e-300))
+    assert np.max(np.abs(den - ref["den"]) / ref["den"]) <= RWKV4_TOL
+    assert np.max(np.abs(num - ref["num"]) / (ref["den"] * vmax)) <= RWKV4_TOL
+    return y, so, ref
+
+
+def test_rwkv4_workload1():
+    print("rwkv4 workload 1: B=1 T=64 C=64", flush=True)
+    rwkv4_check(S.workload(1))
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 2, 5), (1, 15, 16), (1, 16, 16), (1, 17, 17),
+                                   (3, 1023, 33), (2, 1024, 64), (1, 1025, 16), (2, 2100, 40)])
+def test_rwkv4_shapes(B, T, C):
+    print(f"rwkv4 B={B} T={T} C={C}", flush=True)
+    rwkv4_check(S.rwkv4_inputs(B, T, C, 100 + T + C, k_sigma=2.0))
+
+
+def test_rwkv4_workload2_full():
+    print("rwkv4 workload 2: B=8 T=1024 C=768", flush=True)
+    rwkv4_check(S.workload(2))
+
+
+def test_rwkv4_large_keys():
+    # |k| up to ~100: the unscaled numerator would overflow fp32 without the
+    # running maximum exponent
+    print("rwkv4 large keys", flush=True)
+    rwkv4_check(S.rwkv4_inputs(2, 300, 24, 7, k_sigma=25.0))
+
+
+def test_rwkv4_state_handoff():
+    print("rwkv4 state handoff", flush=True)
+    d = S.rwkv4_inputs(2, 700, 48, 8, k_sigma=2.0)
+    head = {n: d[n][:, :333] if n in "kv" else d[n] for n in d}
+    tail = {n: d[n][:, 333:] if n in "kv" else d[n] for n in d}
+    _, s1, _ = rwkv4_check(head)
+    rwkv4_check(tail, state_in=s1.cpu().numpy())
+
+
+def test_rwkv4_channel_factorisation_is_bitwise_irrelevant():
+    d = S.rwkv4_inputs(2, 100, 64, 9)
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    y1, s1 = W.rwkv4_wkv_fwd(k, v, w, u, H=1)
+    y2, s2 = W.rwkv4_wkv_fwd(k, v, w, u, H=4)
+    sync()
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+def test_rwkv4_inplace_state_and_t0():
+    d = S.rwkv4_inputs(2, 50, 16, 10)
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    _, s = W.rwkv4_wkv_fwd(k, v, w, u)
+    s_copy = s.clone()
+    y_a, s_a = W.rwkv4_wkv_fwd(k, v, w, u, state_in=s_copy)
+    y_b, _ = W.rwkv4_wkv_fwd(k, v, w, u, state_in=s, state_out=s)  # in place
+    sync()
+    assert torch.equal(y_a, y_b) and torch.equal(s_a, s)
+    # T = 0: state copied, or the empty state when none is given
+    e = torch.empty((2, 0, 16), device="cuda")
+    _, s0 = W.rwkv4_wkv_fwd(e, e, w, u, state_in=s_a)
+    _, se = W.rwkv4_wkv_fwd(e, e, w, u)
+    sync()
+    assert torch.equal(s0, s_a)
+    assert torch.all(se[:, :2] == 0) and torch.all(se[:, 2] == -1e38)
+
+
+# ---------------------------------------------------------------------------
+# Eagle / Finch, chunked
+
+def matrix_case(B, T, H, seed, per_token, s0_sigma=0.1, **kw):
+    return S.wkv_inputs(B, T, H, 64, seed, per_token, s0_sigma, **kw)
+
+
+def run_chunked(g, per_token, state=True):
+    fn = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    return fn(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"] if state else None)
+
+
+def chunked_check(d, per_token):
+    g = matrix_inputs_dev(d)
+    o, so = run_chunked(g, per_token)
+    sync()
+    o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
+    assert_matrix_close(bf16_host(o), o_ref, "o")
+    assert_matrix_close(f64_host(so), s_ref, "state")
+    return g, o, so
+
+
+SHAPES = [(1, 1, 1), (1, 2, 1), (1, 63, 1), (1, 64, 1), (1, 65, 2), (2, 127, 3), (1, 197, 2),
+          (3, 300, 1), (1, 1000, 2)]
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", SHAPES)
+def test_chunked_shapes(per_token, B, T, H):
+    print(f"chunked {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    chunked_check(matrix_case(B, T, H, 200 + T + H, per_token), per_token)
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_chunked_zero_initial_state(per_token):
+    d = matrix_case(2, 150, 2, 11, per_token, s0_sigma=0.0)
+    g = matrix_inputs_dev(d)
+    o1, s1 = run_chunked(g, per_token, state=True)
+    o2, s2 = run_chunked(g, per_token, state=False)
+    sync()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
+    assert_matrix_close(bf16_host(o2), o_ref, "o")
+
+
+def sample_heads(B, H, n=6):
+    picks = {(0, 0), (B - 1, H - 1), (B // 2, H // 2), (1 % B, (H - 1) // 3),
+             (B - 1, 0), (0, H - 1)}
+    return sorted(picks)[:n]
+
+
+def full_workload_check(cfg, per_token):
+    spec = S.WORKLOADS[cfg]
+    d = S.workload(cfg)
+    g = matrix_inputs_dev(d)
+    o, so = run_chunked(g, per_token)
+    sync()
+    for b, h in sample_heads(spec["B"], spec["H"]):
+        head = lambda a: a[b:b + 1, :, h:h + 1]
+        xs = head(d["x"]) if per_token else d["x"][h:h + 1]
+        o_ref, s_ref = oracle.wkv_matrix(
+            S.bf16_to_f32(head(d["r"])), S.bf16_to_f32(head(d["k"])),
+            S.bf16_to_f32(head(d["v"])), xs, d["u"][h:h + 1], d["s0"][b:b + 1, h:h + 1])
+        assert_matrix_close(bf16_host(o[b:b + 1, :, h:h + 1]), o_ref, f"o head {(b, h)}")
+        assert_matrix_close(f64_host(so[b:b + 1, h:h + 1]), s_ref, f"state head {(b, h)}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(so).all()
+
+
+def test_eagle_workload3_full_size_sampled_heads():
+    print("eagle workload 3: B=8 T=4096 H=32", flush=True)
+    full_workload_check(3, False)
+
+
+def test_finch_workload4_full_size_sampled_heads():
+    print("finch workload 4: B=8 T=4096 H=40", flush=True)
+    full_workload_check(4, True)
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_chunked_split_at_chunk_boundary_is_bitwise(per_token):
+    d = matrix_case(2, 320, 3, 12, per_token)
+    g = matrix_inputs_dev(d)
+    o, so = run_chunked(g, per_token)
+    cut = 128
+    part = lambda t, a, b: t[:, a:b].contiguous()
+    x1 = part(g["x"], 0, cut) if per_token else g["x"]
+    x2 = part(g["x"], cut, 320) if per_token else g["x"]
+    fn = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    o1, s1 = fn(part(g["r"], 0, cut), part(g["k"], 0, cut), part(g["v"], 0, cut), x1, g["u"],
+                state_in=g["s0"])
+    o2, s2 = fn(part(g["r"], cut, 320), part(g["k"], cut, 320), part(g["v"], cut, 320), x2,
+                g["u"], state_in=s1)
+    sync()
+    assert torch.equal(torch.cat([o1, o2], 1), o) and torch.equal(s2, so)
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_chunked_deterministic_and_inplace(per_token):
+    d = matrix_case(3, 333, 2, 13, per_token)
+    g = matrix_inputs_dev(d)
+    o1, s1 = run_chunked(g, per_token)
+    o2, s2 = run_chunked(g, per_token)
+    st = g["s0"].clone()
+    fn = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    o3, _ = fn(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=st, state_out=st)
+    sync()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, st)
+
+
+@pytest.mark.parametrize("logit", [-200.0, 10.0, "mixed"])
+def test_chunked_extreme_decays(logit):
+    # x = -200: w = 1 (no decay); x = +10: w = 0 (state forgets everything
+    # each token): the chunk's log-decay is far outside the factorised form's
+    # range, so those chunks run token by token.
+    print(f"chunked extreme decay {logit}", flush=True)
+    d = matrix_case(2, 200, 2, 14, True)
+    if logit == "mixed":
+        x = d["x"].copy()
+        x[..., ::3] = 10.0
+        x[:, 64:128] = -200.0
+        d["x"] = x
+    else:
+        d["x"] = np.full_like(d["x"], logit)
+    chunked_check(d, True)
+
+
+def test_chunked_t0():
+    d = matrix_case(2, 1, 2, 15, True)
+    g = matrix_inputs_dev(d)
+    e = torch.empty((2, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    ex = torch.empty((2, 0, 2, 64), device="cuda")
+    _, s_copy = W.rwkv6_wkv_fwd(e, e, e, ex, g["u"], state_in=g["s0"])
+    _, s_zero = W.rwkv6_wkv_fwd(e, e, e, ex, g["u"])
+    sync()
+    assert torch.equal(s_copy, g["s0"]) and torch.all(s_zero == 0)
+
+
+# ---------------------------------------------------------------------------
+# Finch, serial mode
+
+def run_step(g, state):
+    return W.rwkv6_wkv_step(g["r"], g["k"], g["v"], g["x"], g["u"], state)
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 5, 3), (1, 64, 1), (3, 130, 2)])
+def test_step_vs_oracle(B, T, H):
+    print(f"step B={B} T={T} H={H}", flush=True)
+    d = matrix_case(B, T, H, 300 + T, True)
+    g = matrix_inputs_dev(d)
+    st = g["s0"].clone()
+    o = run_step(g, st)
+    sync()
+    o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
+    assert_matrix_close(bf16_host(o), o_ref, "o")
+    rms, mx = rel_errors(f64_host(st), s_ref)
+    assert rms < 1e-5 and mx < 1e-4, (rms, mx)  # the serial state is fp32-accurate
+
+
+def test_step_split_anywhere_is_bitwise():
+    d = matrix_case(2, 37, 2, 16, True)
+    g = matrix_inputs_dev(d)
+    st = g["s0"].clone()
+    o = run_step(g, st)
+    for cuts in ([1], [17], [5, 6, 30]):
+        s2 = g["s0"].clone()
+        outs = []
+        edges = [0] + cuts + [37]
+        for a, b in zip(edges[:-1], edges[1:]):
+            part = {n: (g[n][:, a:b].contiguous() if n in ("r", "k", "v", "x") else g[n])
+                    for n in g}
+            outs.append(run_step(part, s2))
+        sync()
+        assert torch.equal(torch.cat(outs, 1), o) and torch.equal(s2, st)
+
+
+@pytest.mark.parametrize("T", [64, 200])
+def test_step_and_chunked_agree(T):
+    d = matrix_case(2, T, 3, 17 + T, True)
+    g = matrix_inputs_dev(d)
+    o_c, s_c = run_chunked(g, True)
+    st = g["s0"].clone()
+    o_s = run_step(g, st)
+    sync()
+    assert_matrix_close(bf16_host(o_c), bf16_host(o_s), "chunked vs step o")
+    assert_matrix_close(f64_host(s_c), f64_host(st), "chunked vs step state")
+
+
+def gpu_rel_errors(got, ref):
+    got = got.double()
+    ref = ref.double()
+    nr = torch.linalg.vector_norm(ref)
+    rms = nr / ref.numel() ** 0.5
+    diff = (got - ref).abs()
+    return (float(torch.linalg.vector_norm(got - ref) / nr),
+            float(torch.max(diff / torch.maximum(ref.abs(), rms))))
+
+
+def test_decode_workload5_full():
+    """256 sequences x 64 heads x 1024 decode steps, against the oracle on
+    sampled heads and against the chunked forward over the same tokens."""
+    spec = S.WORKLOADS[5]
+    B, steps, H = spec["B"], spec["steps"], spec["H"]
+    print(f"decode workload 5: B={B} H={H} steps={steps}", flush=True)
+    d = S.workload(5)
+    g = matrix_inputs_dev(d)  # r, k, v, x: [steps, B, H, 64]
+    st = g["s0"].clone()
+    o = torch.empty((steps, B, H, 64), dtype=torch.bfloat16, device="cuda")
+    for s in range(steps):
+        W.rwkv6_wkv_step(g["r"][s].unsqueeze(1), g["k"][s].unsqueeze(1),
+                         g["v"][s].unsqueeze(1), g["x"][s].unsqueeze(1), g["u"], st,
+                         o=o[s].unsqueeze(1))
+    sync()
+    print("decode done; oracle on sampled heads", flush=True)
+    for b, h in sample_heads(B, H):
+        sl = lambda a: np.ascontiguousarray(a[:, b, h])[None, :, None]
+        o_ref, s_ref = oracle.wkv_matrix(
+            S.bf16_to_f32(sl(d["r"])), S.bf16_to_f32(sl(d["k"])), S.bf16_to_f32(sl(d["v"])),
+            sl(d["x"]), d["u"][h:h + 1], d["s0"][b:b + 1, h:h + 1])
+        assert_matrix_close(bf16_host(o[:, b, h]), o_ref[0, :, 0], f"o head {(b, h)}")
+        assert_matrix_close(f64_host(st[b, h]), s_ref[0, 0], f"state head {(b, h)}")
+    print("chunked forward over the same tokens", flush=True)
+    perm = lambda t: t.transpose(0, 1).contiguous()
+    o_c, s_c = W.rwkv6_wkv_fwd(perm(g["r"]), perm(g["k"]), perm(g["v"]), perm(g["x"]),
+                               g["u"], state_in=g["s0"])
+    sync()
+    rms, mx = gpu_rel_errors(perm(o), o_c)
+    assert rms <= 5e-3 and mx <= 3e-2, (rms, mx)
+    rms, mx = gpu_rel_errors(st, s_c)
+    assert rms <= 5e-3 and mx <= 3e-2, (rms, mx)
