@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, vendor figure
 FLUSH_BYTES = 1 << 30        # > 256 MiB Infinity Cache
+CALIB_BYTES = 1 << 30        # streaming copy used to calibrate HBM counters
 
 METRIC = "WKV tokens*channels/s & % HBM/MFMA roofline, Finch D2560 T4096; decode steps/s"
 
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
-    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode"],
+    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -242,7 +243,66 @@ def cpu_baseline(S, d4):
             "sample": f"the full Finch workload (B={B}, T={T}, H={H}, N={N}), one pass"}
 
 
+# ---------------------------------------------------------------------------
+# counter summaries
+
+PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic bytes)
+    "finch_fwd": ("wkv_chunk_kernel<true>", "wkv_chunk.hip", lambda: finch_bytes(8, 4096, 40)),
+    "eagle_fwd": ("wkv_chunk_kernel<false>", "wkv_chunk.hip", lambda: eagle_bytes(8, 4096, 32)),
+    "rwkv4_fwd": ("rwkv4_scan_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
+    "finch_decode": ("wkv6_step_kernel", "wkv_step.hip", lambda: decode_bytes_per_step(256, 64)),
+}
+PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
+            "finch_decode": "decode"}
+
+
+def _pmc_mean(csv_path, fragment, counter):
+    import csv
+    vals = []
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if fragment in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                vals.append(float(row["Counter_Value"]))
+    return sum(vals) / len(vals) if vals else None, len(vals)
+
+
+def summarize_pmc(pmc_dir):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (one directory per
+    path and counter: <pmc_dir>/<path>_<COUNTER>/run_counter_collection.csv,
+    made by `rocprofv3 --pmc <COUNTER> --output-format csv -d <that dir>
+    -o run -- python bench.py --only <path> --steps 2 --warmup 1 --skip-cpu
+    --decode-steps 8`) into profiles/traffic.json: HBM bytes per launch,
+    scaled by the same counters on a 1 GiB streaming kernel (--only calib)."""
+    csv_of = lambda tag, ctr: os.path.join(pmc_dir, f"{tag}_{ctr}", "run_counter_collection.csv")
+    cal_f, _ = _pmc_mean(csv_of("calib", "FETCH_SIZE"), "MulFunctor", "FETCH_SIZE")
+    cal_w, _ = _pmc_mean(csv_of("calib", "WRITE_SIZE"), "MulFunctor", "WRITE_SIZE")
+    kib = CALIB_BYTES / 1024
+    out = {"calibration": {
+        "kernel": "torch.mul(a, 1.0, out=b) over 1 GiB fp32 (reads 1 GiB, writes 1 GiB)",
+        "FETCH_SIZE_KiB": cal_f, "WRITE_SIZE_KiB": cal_w,
+        "fetch_factor": kib / cal_f, "write_factor": kib / cal_w}}
+    for path, (frag, src, alg) in PMC_PATHS.items():
+        tag = PMC_DIRS[path]
+        f, nf = _pmc_mean(csv_of(tag, "FETCH_SIZE"), frag, "FETCH_SIZE")
+        w, nw = _pmc_mean(csv_of(tag, "WRITE_SIZE"), frag, "WRITE_SIZE")
+        if f is None or w is None:
+            continue
+        rd = f * 1024 * out["calibration"]["fetch_factor"]
+        wr = w * 1024 * out["calibration"]["write_factor"]
+        out[path] = {"kernel": frag, "source": src, "source_sha256_16": source_hash(src),
+                     "dispatches": [nf, nw], "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
+                     "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                     "algorithmic_bytes": alg(), "traffic_over_algorithmic": (rd + wr) / alg()}
+    dst = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(dst, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-pmc":
+        print(json.dumps(summarize_pmc(sys.argv[2]), indent=1))
+        return 0
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -269,6 +329,16 @@ def main():
 
     paths = {}
     only = args.only
+    if only == "calib":
+        # a plain streaming kernel of known size: reads 1 GiB, writes 1 GiB;
+        # its FETCH_SIZE / WRITE_SIZE readings calibrate the HBM counters
+        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_bytes": CALIB_BYTES}))
+        return 0
     d4 = None
     if only in (None, "finch"):
         print("finch forward ...", file=sys.stderr, flush=True)
