@@ -48,20 +48,25 @@ def _run(cmds, verbose):
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source and link librwkv_wkv.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY,
+          objdir: str = OBJDIR, sources=None) -> str:
+    """Compile every HIP source and link librwkv_wkv.so; returns its path.
+
+    ``extra_flags``, ``output``, ``objdir`` and ``sources`` (a map from the
+    default source name to another file) build variants for comparison."""
+    os.makedirs(objdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        path = (sources or {}).get(src, os.path.join(CSRC, src))
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", path, "-o", obj])
     _run(cmds, verbose)
-    tmp = LIBRARY + ".tmp"
+    tmp = output + ".tmp"
     _run([[HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, output)
+    return output
 
 
 if __name__ == "__main__":

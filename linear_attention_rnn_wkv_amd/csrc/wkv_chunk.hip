@@ -7,37 +7,54 @@
 //   w_t = exp(-exp(x_t)).
 // Time-parallel evaluation (RWKV paper summary, section "Transformer-like
 // parallelization"): the sequence is cut into chunks of L = 64 tokens.  With
-// Lam_t = sum_{m<=t} log w_m (chunk-relative, fp32, kept in log2 units) and
-// S the state entering the chunk, unrolling the recurrence gives
-//   o_t = (r_t . e^{Lam_{t-1}}) S
-//       + sum_{s<t} [sum_i r_t[i] k_s[i] e^{Lam_{t-1}[i] - Lam_s[i]}] v_s
-//       + (sum_i r_t[i] u[i] k_t[i]) v_t
-//   S'  = diag(e^{Lam_L}) S + sum_s (k_s . e^{Lam_L - Lam_s})^T v_s.
-// The bracket factorises as r~_t . k~_s with r~ = r e^{Lam_{t-1} - c} and
-// k~ = k e^{c - Lam_s} around the mid-chunk reference c = Lam_{L/2}, so each
-// chunk is four 64x64x64 products on the matrix cores:
-//   P1  A^T = K~ R~^T, masked causally, bonus on the diagonal
-//   P2  O^T = V^T A^T + S^T Q^T            (Q = r . e^{Lam_{t-1}})
-//   P3  S'  = diag(e^{Lam_L}) S + Kh^T V   (Kh = k . e^{Lam_L - Lam_s}, split
-//       into bf16 hi + lo so the carried fp32 state loses no precision)
-// Every factor except r~, k~ is at most 1.  r~ and k~ stay finite while the
-// chunk's total log-decay stays above kSafeLog2 for every channel; a chunk
-// that decays faster is applied token by token instead (exact at any decay).
+// Lam_t = sum_{m<=t} log w_m (chunk-relative, fp32, kept in log2 units),
+// Lam_L its value at the chunk end and S the state entering the chunk,
+// unrolling the recurrence gives
+//   o_t = sum_{s<t} [sum_i r~_t[i] k^_s[i]] v_s + (sum_i r_t[i] u[i] k_t[i]) v_t
+//         + r~_t (diag(e^{Lam_L}) S)
+//   S'  = diag(e^{Lam_L}) S + K^^T V
+// with r~_t = r_t e^{Lam_{t-1} - Lam_L} (>= |r|) and k^_s = k_s e^{Lam_L - Lam_s}
+// (<= |k|): the factorisation is anchored at the chunk end, so the decayed
+// state diag(e^{Lam_L}) S that the update needs is also the operand of the
+// output term.  Each chunk is three products on the matrix cores:
+//   P1  A^T = K^ R~^T, masked causally, bonus on the diagonal
+//   P2  O^T = V^T A^T + (diag(e^{Lam_L}) S)^T R~^T
+//   P3  S'  = diag(e^{Lam_L}) S + (K^_hi + K^_lo)^T V   (K^ split into bf16
+//       hi + lo so the carried fp32 state loses no precision)
+// r~ and k^ stay inside the fp32 / bf16 range while the chunk's total
+// log2-decay of every channel is above kSafeLog2; a chunk that decays faster
+// is applied token by token instead (exact at any decay).
 //
-// Work split: one workgroup of four wave64s per (sequence, head).  Wave p
-// owns tokens [16p, 16p+16) of each chunk for P1 and P2, and value columns
-// [16p, 16p+16) of the fp32 state for P3, which therefore never leaves its
-// registers.  The chunk's operands are staged in LDS as bf16 tiles with a
-// padded row pitch; the state is staged as a transposed bf16 tile, double
-// buffered across chunks.  The next chunk's r, k, v, x are fetched into
-// registers while the current chunk computes.  HBM traffic is the
-// algorithmic minimum: r, k, v, o (and x for Finch) once, the state twice.
+// Work split: one workgroup of NW = 4 or 8 wave64s per (sequence, head);
+// with NH = NW / 4 and TP = 8 / NH tokens per staging thread:
+//   staging   thread t: channels 4 (t%16) + {0..3}, tokens TP (t/16) + {0..TP-1};
+//             v: tokens t/8 + 64/NH j, channels 8 (t%8) + {0..7}
+//   P1, P2    wave w: tokens [16 (w%4), +16), value columns [64/NH (w/4), +64/NH)
+//   P3        wave w: value columns [16 (w%4), +16), key rows [64/NH (w/4), +64/NH)
+// so the fp32 state never leaves registers (except in the fast-decay path).
+// Eight waves give two waves per SIMD to one head; four waves let two heads
+// share a CU.  The launcher picks eight while the heads fit on the CUs.
+// Operands are staged in LDS as row-major ([token][channel]) bf16 64x64
+// tiles with a padded pitch; operands that contract over tokens are read
+// with the transposing LDS load (ds_read_b64_tr_b16), so no tile is ever
+// written transposed.
+//
+// Pipeline: chunk c's operand reads and matrix products are issued before
+// the barrier that publishes chunk c+1's decay totals, and their results are
+// only consumed after it, so the matrix cores run while the VALU stages
+// chunk c+1 (decay scan, factors, tiles).  Two barriers per chunk; the next
+// chunk's r, k, v, x are fetched while chunk c's products run.  HBM traffic is the
+// algorithmic minimum: r, k, v, o (and x for Finch) once, the state once
+// each way.
 //
 // MFMA operand convention (v_mfma_f32_16x16x32_bf16): lane l = c + 16 g holds
 // row c of the A operand and column c of the B operand, with eight k-slots
 // indexed by (g, slot); both operands use the same (g, slot) -> k map, so
 // any consistent map is valid.  The result lane l holds rows 4 g + e
-// (e = 0..3) of column c.
+// (e = 0..3) of column c.  P1's accumulators are therefore P2's B operand
+// without leaving registers.  The transposing load: in each group of 16
+// lanes, lane j supplies the address of 4 consecutive elements of row j/4 of
+// a 4 x 16 block and receives column j of that block (rows 0..3).
 #include "launchers.h"
 #include "wkv_device.h"
 
@@ -49,14 +66,23 @@ constexpr int kL = 64;     // chunk length
 constexpr int kP = 72;     // LDS row pitch (bf16 elements) of the 64x64 tiles
 constexpr int kTile = kN * kP;
 // Smallest chunk log2-decay (per channel) handled by the factorised form:
-// its factors stay below 2^110 and above 2^-110, far from fp32 / bf16 limits.
+// r~ <= |r| 2^110 and k^ >= |k| 2^-110 stay far from fp32 / bf16 limits.
 constexpr float kSafeLog2 = -110.0f;
 
-enum { T_RT = 0, T_KT, T_Q, T_KHH, T_KHL, T_VT, T_ST0, T_ST1, T_COUNT };
+// LDS tiles, all row-major: r~, k^_hi, k^_lo, v as [token][channel]; the
+// decayed state as [j][i].
+enum { T_RS = 0, T_KRH, T_KRL, T_VR, T_ST, T_COUNT };
 
-struct Raw {       // one thread's share of a chunk: 4 tokens x 4 channels
-    u32x2 r[4], k[4], v[4];  // bf16 pairs
-    f32x4 x[4];              // Finch decay logits
+template <int NW>
+struct Raw {                           // one thread's share of a chunk
+    static constexpr int TP = 16 / NW; // tokens per staging thread
+    static constexpr int NV = 8 / NW;  // v rows per thread
+    // 16 channel quads x (64 NW / 16) token groups x TP tokens cover the chunk
+    static_assert(TP * (64 * NW / 16) == kL, "staging threads must cover the chunk");
+    static_assert(NV * 8 * NW * 8 == kL * 8, "v loaders must cover the chunk");
+    u32x2 r[TP], k[TP];                // TP tokens x 4 channels, bf16
+    f32x4 x[TP];                       // Finch decay logits
+    u32x4 v[NV];                       // NV tokens x 8 channels, bf16
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -65,8 +91,26 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 __device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
     return *(const bf16x8 *)p;
 }
-__device__ __forceinline__ bf16x8 lds4x2(const uint16_t *lo, const uint16_t *hi) {
-    const u32x2 a = *(const u32x2 *)lo, b = *(const u32x2 *)hi;
+// transposing 8-byte LDS load (see the file comment)
+__device__ __forceinline__ u32x2 lds_tr(const uint16_t *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 *lds_v4i16;
+    const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)p);
+    return __builtin_bit_cast(u32x2, t);
+}
+// column (n0 + c) of rows k0..k0+7 of a row-major tile, for lane c of its
+// 16-lane group: the operand of a product that contracts over rows
+__device__ __forceinline__ bf16x8 lds_col8(const uint16_t *tile, int k0, int n0, int c) {
+    const uint16_t *p = tile + (k0 + (c >> 2)) * kP + n0 + 4 * (c & 3);
+    const u32x2 a = lds_tr(p), b = lds_tr(p + 4 * kP);
+    const u32x4 m = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, m);
+}
+// rows k0..k0+3 and k1..k1+3 of column (n0 + c)
+__device__ __forceinline__ bf16x8 lds_col4x2(const uint16_t *tile, int k0, int k1, int n0,
+                                             int c) {
+    const int off = (c >> 2) * kP + n0 + 4 * (c & 3);
+    const u32x2 a = lds_tr(tile + k0 * kP + off), b = lds_tr(tile + k1 * kP + off);
     const u32x4 m = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, m);
 }
@@ -80,219 +124,263 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4 &lo, const f32x4 &hi) {
     return __builtin_bit_cast(bf16x8, m);
 }
 
-template <bool PT>
-__device__ __forceinline__ void load_raw(Raw &d, int c0, int tq, int cq, int T,
-                                         size_t seq_base, size_t tok_stride,
+struct Ctx {
+    int T, tq, cq, vt, vo;
+    size_t seq_base, tok_stride;
+};
+
+template <bool PT, int NW>
+__device__ __forceinline__ void load_raw(Raw<NW> &d, int c0, const Ctx &cx,
                                          const uint16_t *r, const uint16_t *k,
                                          const uint16_t *v, const float *x) {
+    constexpr int TP = Raw<NW>::TP;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int t = c0 + 4 * tq + e;
-        if (t < T) {
-            const size_t off = seq_base + (size_t)t * tok_stride + 4 * cq;
+    for (int e = 0; e < TP; ++e) {
+        const int t = c0 + TP * cx.tq + e;
+        if (t < cx.T) {
+            const size_t off = cx.seq_base + (size_t)t * cx.tok_stride + 4 * cx.cq;
             d.r[e] = *(const u32x2 *)(r + off);
             d.k[e] = *(const u32x2 *)(k + off);
-            d.v[e] = *(const u32x2 *)(v + off);
             if (PT) d.x[e] = *(const f32x4 *)(x + off);
         } else {
             d.r[e] = u32x2{0u, 0u};
             d.k[e] = u32x2{0u, 0u};
-            d.v[e] = u32x2{0u, 0u};
             if (PT) d.x[e] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-}
-
-// S_acc[m][e] = S[16 m + 4 g + e][16 w + c]  ->  st[j][i] (transposed bf16 tile)
-__device__ __forceinline__ void stage_state(uint16_t *st, const f32x4 (&S)[4], int w, int g,
-                                            int c) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        *(u32x2 *)(st + (16 * w + c) * kP + 16 * m + 4 * g) =
-            pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
+    for (int j = 0; j < Raw<NW>::NV; ++j) {
+        const int t = c0 + cx.vt + 8 * NW * j;
+        d.v[j] = (t < cx.T)
+            ? *(const u32x4 *)(v + cx.seq_base + (size_t)t * cx.tok_stride + 8 * cx.vo)
+            : u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
-template <bool PT>
-__global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(
+template <bool PT, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x,
     const float *__restrict__ u, const float *state_in, float *state_out,
     uint16_t *__restrict__ o) {
+    constexpr int NH = NW / 4;        // value / key halves split across waves
+    constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
+    constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
     __shared__ __align__(16) uint16_t sm[T_COUNT][kTile];
-    __shared__ __align__(16) float sWave[4][kN];
+    __shared__ __align__(16) float sWave[NW][kN];   // per-wave log2-decay totals
+    __shared__ __align__(16) float sDecay[NW][kN];  // e^{Lam_L}, one copy per wave
     __shared__ __align__(16) float sBonus[kL];
-    __shared__ __align__(16) float sDecay[kN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int cq = c;        // channel quad of the staging role
-    const int tq = tid >> 4; // token quad of the staging role (= 4 w + g)
+    const int p = w & 3;   // P1/P2 token tile, P3 value tile
+    const int hf = w >> 2; // P2 value part, P3 key part
 
     const int bh = blockIdx.x;
     const int b = bh / H;
     const int h = bh % H;
-    const size_t tok_stride = (size_t)H * kN;
-    const size_t seq_base = (size_t)b * T * tok_stride + (size_t)h * kN;
+    Ctx cx;
+    cx.T = T;
+    cx.cq = tid & 15;      // == c
+    cx.tq = tid >> 4;      // token group (= 4 w + g)
+    cx.vt = tid >> 3;
+    cx.vo = tid & 7;
+    cx.tok_stride = (size_t)H * kN;
+    cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
 
-    const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cq);
-    f32x4 a2_static = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
+    f32x4 a2s = {0.f, 0.f, 0.f, 0.f};
     if (!PT) {
-        const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * cq);
+        const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * cx.cq);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a2_static[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
+        for (int q = 0; q < 4; ++q) a2s[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
     }
 
+    // state tiles of this wave: S[mi][e] = S[16 (NT hf + mi) + 4 g + e][16 p + c]
     const size_t st_base = (size_t)bh * kN * kN;
-    f32x4 S[4];
+    f32x4 S[NT], SD[NT];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int mi = 0; mi < NT; ++mi)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            S[m][e] = state_in ? state_in[st_base + (size_t)(16 * m + 4 * g + e) * kN + 16 * w + c]
-                               : 0.0f;
-    stage_state(sm[T_ST0], S, w, g, c);
+            S[mi][e] = state_in
+                ? state_in[st_base + (size_t)(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c]
+                : 0.0f;
 
     const int nchunks = (T + kL - 1) / kL;
-    Raw cur, nxt;
-    load_raw<PT>(cur, 0, tq, cq, T, seq_base, tok_stride, r, k, v, x);
 
-    for (int ch = 0; ch < nchunks; ++ch) {
+    // ---- stage A: log2 decays and the in-wave part of their scan ----------
+    float a2[TP][4], lower[4];
+    auto stageA = [&](int ch, const Raw<NW> &d) {
         const int c0 = ch * kL;
-        if (ch + 1 < nchunks)
-            load_raw<PT>(nxt, c0 + kL, tq, cq, T, seq_base, tok_stride, r, k, v, x);
-
-        // ---- log2 decays of my 4 tokens x 4 channels (0 on padding) --------
-        float a2[4][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool valid = c0 + 4 * tq + e < T;
+        for (int e = 0; e < TP; ++e) {
+            const bool valid = c0 + TP * cx.tq + e < T;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float val = PT ? -exp2_fast(cur.x[e][q] * kLog2e) * kLog2e : a2_static[q];
+                const float val = PT ? -exp2_fast(d.x[e][q] * kLog2e) * kLog2e : a2s[q];
                 a2[e][q] = valid ? val : 0.0f;
             }
         }
-        // chunk-relative cumulative sums: thread, then wave (over g), then block
-        float pre[4];
+        f32x4 wt;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float tot = (a2[0][q] + a2[1][q]) + (a2[2][q] + a2[3][q]);
-            float s = tot;
+            float s = a2[0][q];
+#pragma unroll
+            for (int e = 1; e < TP; ++e) s += a2[e][q];
             const float s1 = __shfl_up(s, 16, 64);
             if (g >= 1) s += s1;
             const float s2 = __shfl_up(s, 32, 64);
             if (g >= 2) s += s2;
             const float ex = __shfl_up(s, 16, 64);
-            pre[q] = (g == 0) ? 0.0f : ex;
-            if (g == 3) sWave[w][4 * cq + q] = s;
+            lower[q] = (g == 0) ? 0.0f : ex;
+            wt[q] = s;
         }
-        __syncthreads();  // (1) wave totals visible; previous chunk fully consumed
+        if (g == 3) *(f32x4 *)&sWave[w][4 * cx.cq] = wt;
+    };
 
-        float LL[4], cmid[4];
+    // ---- stage B: prefix, factors and the operand tiles of a chunk --------
+    // (needs stage A of every wave, i.e. a barrier in between)
+    auto stageB = [&](const Raw<NW> &d) -> bool {
+        f32x4 tw[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) tw[j] = *(const f32x4 *)&sWave[j][4 * cx.cq];
+        f32x4 LL;
+        if (NW == 8)
+            LL = ((tw[0] + tw[1]) + (tw[2] + tw[3])) + ((tw[4 % NW] + tw[5 % NW]) +
+                                                       (tw[6 % NW] + tw[7 % NW]));
+        else
+            LL = (tw[0] + tw[1]) + (tw[2 % NW] + tw[3 % NW]);
+        f32x4 before = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+            if (j < w) before += tw[j];
         bool bad = false;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float t0 = sWave[0][4 * cq + q], t1 = sWave[1][4 * cq + q];
-            const float t2 = sWave[2][4 * cq + q], t3 = sWave[3][4 * cq + q];
-            const float before = (w == 0) ? 0.0f : (w == 1) ? t0 : (w == 2) ? (t0 + t1)
-                                                                           : ((t0 + t1) + t2);
-            pre[q] += before;
-            cmid[q] = t0 + t1;
-            LL[q] = ((t0 + t1) + t2) + t3;
-            bad |= LL[q] < kSafeLog2;
-        }
-
-        // ---- stage the chunk's operands in LDS -------------------------------
-        f32x4 er, ek;
+        for (int q = 0; q < 4; ++q) bad |= LL[q] < kSafeLog2;
+        if (g == 0) {
+            f32x4 dd;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            er[q] = exp2_fast(-cmid[q]);
-            ek[q] = exp2_fast(cmid[q] - LL[q]);
+            for (int q = 0; q < 4; ++q) dd[q] = exp2_fast(LL[q]);
+            *(f32x4 *)&sDecay[w][4 * cx.cq] = dd;
         }
-        float khh[4][4], khl[4][4], vv[4][4];
-        f32x4 bsum;
-        float run[4] = {pre[0], pre[1], pre[2], pre[3]};
+        float run[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tau = 4 * tq + e;
-            const float rr[4] = {bf16_lo(cur.r[e].x), bf16_hi(cur.r[e].x), bf16_lo(cur.r[e].y),
-                                 bf16_hi(cur.r[e].y)};
-            const float kk[4] = {bf16_lo(cur.k[e].x), bf16_hi(cur.k[e].x), bf16_lo(cur.k[e].y),
-                                 bf16_hi(cur.k[e].y)};
-            vv[e][0] = bf16_lo(cur.v[e].x);
-            vv[e][1] = bf16_hi(cur.v[e].x);
-            vv[e][2] = bf16_lo(cur.v[e].y);
-            vv[e][3] = bf16_hi(cur.v[e].y);
-            float qv[4], rt[4], kt[4];
-            float bs = 0.0f;
+        for (int q = 0; q < 4; ++q) run[q] = before[q] + lower[q];
+        float bs[TP];
+#pragma unroll
+        for (int e = 0; e < TP; ++e) {
+            const int tau = TP * cx.tq + e;
+            const float rr[4] = {bf16_lo(d.r[e].x), bf16_hi(d.r[e].x), bf16_lo(d.r[e].y),
+                                 bf16_hi(d.r[e].y)};
+            const float kk[4] = {bf16_lo(d.k[e].x), bf16_hi(d.k[e].x), bf16_lo(d.k[e].y),
+                                 bf16_hi(d.k[e].y)};
+            float rt[4], kh[4], khl[4];
+            float s = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float lex = run[q];
-                const float lin = run[q] + a2[e][q];
+                const float lin = lex + a2[e][q];
                 run[q] = lin;
-                const float fq = exp2_fast(lex);
-                const float fk = exp2_fast(LL[q] - lin);
-                qv[q] = rr[q] * fq;
-                rt[q] = qv[q] * er[q];
-                const float kh = kk[q] * fk;
-                kt[q] = kh * ek[q];
-                khh[e][q] = round_bf16(kh);
-                khl[e][q] = kh - khh[e][q];
-                bs = fmaf(rr[q] * uq[q], kk[q], bs);
+                rt[q] = rr[q] * exp2_fast(lex - LL[q]);
+                kh[q] = kk[q] * exp2_fast(LL[q] - lin);
+                s = fmaf(rr[q] * uq[q], kk[q], s);
             }
-            bsum[e] = bs;
-            *(u32x2 *)(sm[T_RT] + tau * kP + 4 * cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
-            *(u32x2 *)(sm[T_KT] + tau * kP + 4 * cq) = pack4(kt[0], kt[1], kt[2], kt[3]);
-            *(u32x2 *)(sm[T_Q] + tau * kP + 4 * cq) = pack4(qv[0], qv[1], qv[2], qv[3]);
+            const u32x2 hi = pack4(kh[0], kh[1], kh[2], kh[3]);
+            khl[0] = kh[0] - bf16_lo(hi.x);
+            khl[1] = kh[1] - bf16_hi(hi.x);
+            khl[2] = kh[2] - bf16_lo(hi.y);
+            khl[3] = kh[3] - bf16_hi(hi.y);
+            *(u32x2 *)(sm[T_RS] + tau * kP + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
+            *(u32x2 *)(sm[T_KRH] + tau * kP + 4 * cx.cq) = hi;
+            *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
+            bs[e] = s;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = (4 * cq + q) * kP + 4 * tq;
-            *(u32x2 *)(sm[T_KHH] + row) = pack4(khh[0][q], khh[1][q], khh[2][q], khh[3][q]);
-            *(u32x2 *)(sm[T_KHL] + row) = pack4(khl[0][q], khl[1][q], khl[2][q], khl[3][q]);
-            *(u32x2 *)(sm[T_VT] + row) = pack4(vv[0][q], vv[1][q], vv[2][q], vv[3][q]);
-        }
-        // bonus r_t diag(u) k_t^T: reduce over the 16 lanes sharing a token quad
+        for (int j = 0; j < Raw<NW>::NV; ++j)
+            *(u32x4 *)(sm[T_VR] + (cx.vt + 8 * NW * j) * kP + 8 * cx.vo) = d.v[j];
+        // bonus r_t diag(u) k_t^T: reduce over the 16 lanes sharing a token group
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float s = bsum[e];
+        for (int e = 0; e < TP; ++e) {
+            float s = bs[e];
             s += __shfl_xor(s, 1, 64);
             s += __shfl_xor(s, 2, 64);
             s += __shfl_xor(s, 4, 64);
             s += __shfl_xor(s, 8, 64);
-            bsum[e] = s;
+            bs[e] = s;
         }
-        if (c == 0) *(f32x4 *)(sBonus + 4 * tq) = bsum;
-        if (tq == 0) {
-            f32x4 d;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) d[q] = exp2_fast(LL[q]);
-            *(f32x4 *)(sDecay + 4 * cq) = d;
+        if (c == 0) {
+            if (TP == 4)
+                *(f32x4 *)&sBonus[TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
+            else
+                *(f32x2 *)&sBonus[TP * cx.tq] = f32x2{bs[0], bs[1 % TP]};
         }
-        const bool unsafe = __syncthreads_or(bad);  // (2) operands staged
+        return bad;
+    };
 
-        uint16_t *st_cur = sm[T_ST0 + (ch & 1)];
-        uint16_t *st_nxt = sm[T_ST0 + ((ch & 1) ^ 1)];
-        if (!unsafe) {
-            const int p = w;
-            // P1: A^T tiles (sigma-tile q, tau-tile p), q <= p
-            f32x4 at[4];
+    // decayed state of the next chunk, staged transposed as bf16
+    auto stage_state = [&]() {
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi) {
+            const f32x4 dd = *(const f32x4 *)&sDecay[w][16 * (NT * hf + mi) + 4 * g];
+            SD[mi] = S[mi] * dd;
+            *(u32x2 *)(sm[T_ST] + (16 * p + c) * kP + 16 * (NT * hf + mi) + 4 * g) =
+                pack4(SD[mi][0], SD[mi][1], SD[mi][2], SD[mi][3]);
+        }
+    };
+
+    // ---- matrix phase of a chunk (fast path) -------------------------------
+    f32x4 ot[NT];
+    auto matrix = [&]() {
+        f32x4 at[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // P1: A^T tiles (sigma-tile q, tau-tile p)
+            at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (q <= p) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * kP + 32 * kb + 8 * g);
+                    const bf16x8 B = lds8(sm[T_RS] + (16 * p + c) * kP + 32 * kb + 8 * g);
+                    at[q] = mfma(A, B, at[q]);
+                }
+            }
+        }
+        // P3: S' = diag(decay) S + (K^_hi + K^_lo)^T V (independent of P1)
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi) {
+            const int m = NT * hf + mi;
+            if (NW == 4) __builtin_amdgcn_sched_barrier(0);  // bound operands in flight
+            f32x4 acc = SD[mi];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int k0 = 32 * kb + 8 * g;
+                const bf16x8 Bv = lds_col8(sm[T_VR], k0, 16 * p, c);
+                acc = mfma(lds_col8(sm[T_KRH], k0, 16 * m, c), Bv, acc);
+                acc = mfma(lds_col8(sm[T_KRL], k0, 16 * m, c), Bv, acc);
+            }
+            S[mi] = acc;
+        }
+        // P2 part 2: (decayed S)^T R~^T
+        if (NW == 4) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 Br = lds8(sm[T_RS] + (16 * p + c) * kP + 32 * kb + 8 * g);
+#pragma unroll
+            for (int ni = 0; ni < NT; ++ni)
+                ot[ni] = mfma(lds8(sm[T_ST] + (16 * (NT * hf + ni) + c) * kP + 32 * kb + 8 * g),
+                              Br, ot[ni]);
+        }
+        // causal mask, bonus on the diagonal
+        {
+            const float bon = sBonus[16 * p + c];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (q <= p) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const bf16x8 A = lds8(sm[T_KT] + (16 * q + c) * kP + 32 * kb + 8 * g);
-                        const bf16x8 B = lds8(sm[T_RT] + (16 * p + c) * kP + 32 * kb + 8 * g);
-                        at[q] = mfma(A, B, at[q]);
-                    }
-                }
-                if (q == p) {  // causal mask, bonus on the diagonal
-                    const float bon = sBonus[16 * p + c];
+                if (q == p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int sl = 4 * g + e;
@@ -300,102 +388,178 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(
                     }
                 }
             }
-            // P2: O^T = V^T A^T + S^T Q^T for tau-tile p, all value tiles n
-            f32x4 ot[4];
+        }
+        // P2 part 1: V^T A^T over the causal sigma blocks
 #pragma unroll
-            for (int n = 0; n < 4; ++n) ot[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int bk = 0; bk < 2; ++bk) {
+            if (2 * bk <= p) {
+                const bf16x8 Bop = pack8(at[2 * bk], at[2 * bk + 1]);
 #pragma unroll
-            for (int bk = 0; bk < 2; ++bk) {
-                if (2 * bk <= p) {
-                    const bf16x8 Bop = pack8(at[2 * bk], at[2 * bk + 1]);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) {
-                        const uint16_t *row = sm[T_VT] + (16 * n + c) * kP + 32 * bk + 4 * g;
-                        ot[n] = mfma(lds4x2(row, row + 16), Bop, ot[n]);
-                    }
-                }
+                for (int ni = 0; ni < NT; ++ni)
+                    ot[ni] = mfma(lds_col4x2(sm[T_VR], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g,
+                                             16 * (NT * hf + ni), c),
+                                  Bop, ot[ni]);
             }
+        }
+    };
+
+    auto store_out = [&](int ch) {
+        const int t = ch * kL + 16 * p + c;
+        if (t < T) {
+            uint16_t *op = o + cx.seq_base + (size_t)t * cx.tok_stride + 16 * NT * hf + 4 * g;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 Bq = lds8(sm[T_Q] + (16 * p + c) * kP + 32 * kb + 8 * g);
+            for (int ni = 0; ni < NT; ++ni)
+                *(u32x2 *)(op + 16 * ni) = pack4(ot[ni][0], ot[ni][1], ot[ni][2], ot[ni][3]);
+        }
+    };
+
+    // ---- fast-decay chunk: its tokens one at a time with fp32 VALU ---------
+    // Waves 0..3 take the state as 16-column slabs through LDS; r, k (bf16)
+    // and w = 2^{a2} (fp32) are re-read and staged in the operand tiles.
+    auto token_by_token = [&](int ch) {
+        const int c0 = ch * kL;
+        float *sS = (float *)sm[T_RS];  // 64 x 64 fp32 spans the r~ and k^_hi tiles
 #pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    ot[n] = mfma(lds8(st_cur + (16 * n + c) * kP + 32 * kb + 8 * g), Bq, ot[n]);
+        for (int mi = 0; mi < NT; ++mi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sS[(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] = S[mi][e];
+        __syncthreads();
+        f32x4 Sc[4];
+        if (w < 4) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Sc[m][e] = sS[(16 * m + 4 * g + e) * kN + 16 * w + c];
+        }
+        __syncthreads();
+        // re-read r, k, x of the chunk one token row at a time (few registers)
+#pragma unroll 1
+        for (int e = 0; e < TP; ++e) {
+            const int tau = TP * cx.tq + e;
+            const bool valid = c0 + tau < T;
+            u32x2 rv = {0u, 0u}, kv = {0u, 0u};
+            f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+            if (valid) {
+                const size_t off = cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 4 * cx.cq;
+                rv = *(const u32x2 *)(r + off);
+                kv = *(const u32x2 *)(k + off);
+                if (PT) xv = *(const f32x4 *)(x + off);
             }
-            // P3: S' = diag(decay) S + (Kh_hi + Kh_lo)^T V for value tile w
+            f32x4 wv;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const f32x4 d = *(const f32x4 *)(sDecay + 16 * m + 4 * g);
-                S[m] *= d;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 Bv = lds8(sm[T_VT] + (16 * w + c) * kP + 32 * kb + 8 * g);
-                    S[m] = mfma(lds8(sm[T_KHH] + (16 * m + c) * kP + 32 * kb + 8 * g), Bv, S[m]);
-                    S[m] = mfma(lds8(sm[T_KHL] + (16 * m + c) * kP + 32 * kb + 8 * g), Bv, S[m]);
-                }
+            for (int q = 0; q < 4; ++q) {
+                const float a = PT ? -exp2_fast(xv[q] * kLog2e) * kLog2e : a2s[q];
+                wv[q] = valid ? exp2_fast(a) : 1.0f;
             }
-            stage_state(st_nxt, S, w, g, c);
-            // outputs: lane holds O[tau = 16 p + c][16 n + 4 g + e]
-            const int t = c0 + 16 * p + c;
-            if (t < T) {
-                uint16_t *op = o + seq_base + (size_t)t * tok_stride + 4 * g;
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-                    *(u32x2 *)(op + 16 * n) = pack4(ot[n][0], ot[n][1], ot[n][2], ot[n][3]);
-            }
-        } else {
-            // Fast-decay chunk: apply its tokens one at a time.  Raw r, k
-            // (bf16) replace the factorised tiles; w = 2^{a2} (fp32) spans
-            // the Q and Kh_hi tiles.
-            float *sw = (float *)sm[T_Q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tau = 4 * tq + e;
-                *(u32x2 *)(sm[T_RT] + tau * kP + 4 * cq) = cur.r[e];
-                *(u32x2 *)(sm[T_KT] + tau * kP + 4 * cq) = cur.k[e];
-                f32x4 wv;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) wv[q] = exp2_fast(a2[e][q]);
-                *(f32x4 *)(sw + tau * kN + 4 * cq) = wv;
-            }
-            __syncthreads();  // (3) uniform: every thread took this branch
+            *(f32x4 *)(sS + tau * kN + 4 * cx.cq) = wv;
+            *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = rv;
+            *(u32x2 *)(sm[T_ST] + tau * kP + 4 * cx.cq) = kv;
+        }
+        __syncthreads();
+        if (w < 4) {
             const int nvalid = min(kL, T - c0);
             for (int tau = 0; tau < nvalid; ++tau) {
-                const float vj = bf16_to_f32(sm[T_VT][(16 * w + c) * kP + tau]);
+                const float vj = bf16_to_f32(sm[T_VR][tau * kP + 16 * w + c]);
                 float acc = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const u32x2 rp = *(const u32x2 *)(sm[T_RT] + tau * kP + 16 * m + 4 * g);
-                    const u32x2 kp = *(const u32x2 *)(sm[T_KT] + tau * kP + 16 * m + 4 * g);
-                    const f32x4 wv = *(const f32x4 *)(sw + tau * kN + 16 * m + 4 * g);
-                    const float r4[4] = {bf16_lo(rp.x), bf16_hi(rp.x), bf16_lo(rp.y), bf16_hi(rp.y)};
-                    const float k4[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y), bf16_hi(kp.y)};
+                    const u32x2 rp = *(const u32x2 *)(sm[T_KRL] + tau * kP + 16 * m + 4 * g);
+                    const u32x2 kp = *(const u32x2 *)(sm[T_ST] + tau * kP + 16 * m + 4 * g);
+                    const f32x4 wv = *(const f32x4 *)(sS + tau * kN + 16 * m + 4 * g);
+                    const float r4[4] = {bf16_lo(rp.x), bf16_hi(rp.x), bf16_lo(rp.y),
+                                         bf16_hi(rp.y)};
+                    const float k4[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y),
+                                         bf16_hi(kp.y)};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        acc = fmaf(r4[e], S[m][e], acc);
-                        S[m][e] = fmaf(wv[e], S[m][e], k4[e] * vj);
+                        acc = fmaf(r4[e], Sc[m][e], acc);
+                        Sc[m][e] = fmaf(wv[e], Sc[m][e], k4[e] * vj);
                     }
                 }
                 acc += __shfl_xor(acc, 16, 64);
                 acc += __shfl_xor(acc, 32, 64);
                 if (g == 0) {
                     const float ov = fmaf(sBonus[tau], vj, acc);
-                    o[seq_base + (size_t)(c0 + tau) * tok_stride + 16 * w + c] =
+                    o[cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 16 * w + c] =
                         (uint16_t)pack_bf16x2(ov, 0.0f);
                 }
             }
-            stage_state(st_nxt, S, w, g, c);
         }
-        cur = nxt;
-    }
+        __syncthreads();
+        if (w < 4) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sS[(16 * m + 4 * g + e) * kN + 16 * w + c] = Sc[m][e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mi = 0; mi < NT; ++mi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[mi][e] = sS[(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c];
+    };
+
+    // ---- one pipelined step: matrix phase of chunk ch, staging of ch + 1 --
+    // buf holds chunk ch + 1's inputs: staging of ch consumed it last step.
+    Raw<NW> buf;
+    auto step = [&](int ch, bool unsafe) -> bool {
+        const bool more = ch + 1 < nchunks;
+        if (more) load_raw<PT, NW>(buf, (ch + 1) * kL, cx, r, k, v, x);
+        if (!unsafe) matrix();
+        else token_by_token(ch);
+        if (more) stageA(ch + 1, buf);
+        __syncthreads();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
+        bool bad = false;
+        if (more) bad = stageB(buf);
+        if (!unsafe) store_out(ch);
+        if (more) stage_state();
+        return __syncthreads_or(bad);  // (Y) operands of ch + 1 staged
+    };
+
+    load_raw<PT, NW>(buf, 0, cx, r, k, v, x);
+    stageA(0, buf);
+    __syncthreads();
+    const bool bad0 = stageB(buf);
+    stage_state();
+    bool unsafe = __syncthreads_or(bad0);
+    for (int ch = 0; ch < nchunks; ++ch) unsafe = step(ch, unsafe);
 
     if (state_out != nullptr) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int mi = 0; mi < NT; ++mi)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                state_out[st_base + (size_t)(16 * m + 4 * g + e) * kN + 16 * w + c] = S[m][e];
+                state_out[st_base + (size_t)(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] =
+                    S[mi][e];
     }
+}
+
+// Compute units of the current device, read once per device.
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <bool PT, int NW>
+void launch(int B, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
+            const float *x, const float *u, const float *state_in, float *state_out,
+            uint16_t *o, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((int64_t)B * H);
+    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW>), dim3(blocks), dim3(64 * NW), 0, stream, T, H,
+                       r, k, v, x, u, state_in, state_out, o);
 }
 
 }  // namespace
@@ -404,13 +568,16 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
                               const uint16_t *k, const uint16_t *v, const float *x,
                               const float *u, const float *state_in, float *state_out,
                               uint16_t *o, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((int64_t)B * H);
-    if (per_token_decay)
-        hipLaunchKernelGGL(wkv_chunk_kernel<true>, dim3(blocks), dim3(256), 0, stream, T, H, r,
-                           k, v, x, u, state_in, state_out, o);
-    else
-        hipLaunchKernelGGL(wkv_chunk_kernel<false>, dim3(blocks), dim3(256), 0, stream, T, H, r,
-                           k, v, x, u, state_in, state_out, o);
+    // eight waves per head while every head has a CU of its own, else four
+    // waves so that two heads share a CU
+    const bool wide = (int64_t)B * H <= device_cus();
+    if (per_token_decay) {
+        if (wide) launch<true, 8>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+        else launch<true, 4>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+    } else {
+        if (wide) launch<false, 8>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+        else launch<false, 4>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+    }
     return hipGetLastError();
 }
 
