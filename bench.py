@@ -88,7 +88,10 @@ class Timer:
 
 
 def flush(torch, buf):
-    buf.zero_()
+    # Read, not write, a buffer larger than the last-level caches: the inputs
+    # are evicted without leaving dirty lines whose write-back would land in
+    # the timed launch.
+    buf.sum()
 
 
 def time_launches(torch, launch, steps, warmup, flush_buf=None):

@@ -87,8 +87,8 @@ const char *rwkv_wkv_strerror(int status);
  *              state_in exactly (in-place update) but not partially overlap.
  *   y          [B][T][C] fp32 output
  *
- * Pointers need 4-byte alignment.  One sequence must span fewer than 2^31
- * elements: (T + 64) * C <= INT32_MAX, else RWKV_E_UNSUPPORTED.
+ * Pointers need 4-byte alignment.  C = H*N must be at most 2^20 and
+ * B * C below 2^36, else RWKV_E_UNSUPPORTED.
  */
 int rwkv4_wkv_fwd(int B, int T, int H, int N,
                   const float *k, const float *v,
@@ -109,7 +109,8 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N,
  *              state_in exactly, but not partially overlap it.
  *   o          [B][T][H][N] bf16 output
  *
- * All pointers need 16-byte alignment.
+ * All pointers need 16-byte alignment.  H must be at most 65536, else
+ * RWKV_E_UNSUPPORTED.
  */
 int rwkv5_wkv_fwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,

@@ -6,6 +6,9 @@
 
 namespace wkv {
 
+// Compute units of the current device (read once per device).
+int device_cus();
+
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,

@@ -12,17 +12,18 @@
 //
 // Parallel form (section "Transformer-like parallelization": wkv_t is a
 // serial scan).  The scan over time is associative: a block of n tokens
-// acts on the state as X -> e^{-n w} X + (block summary).  One workgroup of
-// 1024 lanes owns CB channels of one sequence and splits time into
-// 1024/CB segments of SEG tokens each:
-//   1. every lane loads its segment's k, v (kept in registers) and folds
-//      them into a summary from the empty state;
+// acts on the state as X -> e^{-n w} X + (block summary).  A workgroup of
+// 512 lanes owns 32 channels (one 128-byte row of k, v, y per token) of one
+// sequence and walks the sequence in passes of 16 segments x 16 tokens:
+//   1. every lane folds its segment's k, v (held in registers) into a
+//      summary from the empty state;
 //   2. summaries are scanned: inside a wave with cross-lane shuffles,
-//      across waves through LDS, starting from the incoming state;
+//      across waves through LDS, starting from the state entering the pass;
 //   3. every lane replays its segment from its carry-in state, writing y.
-// k and v are read from HBM once and y written once (12 bytes per
-// token-channel), which is what bounds this kernel.  Longer sequences loop
-// over passes of 1024/CB * SEG tokens with the state carried in LDS.
+// The next pass's k and v are in flight while a pass computes.  k and v are
+// read from HBM once and y written once (12 bytes per token-channel).
+#include <type_traits>
+
 #include "launchers.h"
 #include "wkv_device.h"
 
@@ -30,6 +31,7 @@ namespace wkv {
 namespace {
 
 constexpr float kEmptyP = -1e38f;  // exponent of the empty history
+
 
 struct St {
     float a, b, p;
@@ -98,16 +100,21 @@ __device__ __forceinline__ St shfl_up_st(const St &s, int delta) {
     return r;
 }
 
-template <int CB, int SEG>
-__global__ __launch_bounds__(1024) void rwkv4_scan_kernel(
+template <int SEG>
+struct Seg {  // one lane's tokens of a pass
+    float k[SEG], v[SEG];
+};
+
+template <int NT, int CB, int SEG>
+__global__ __launch_bounds__(NT) void rwkv4_scan_kernel(
     int T, int C, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ w, const float *__restrict__ u,
     const float *state_in, float *state_out, float *__restrict__ y) {
-    constexpr int kThreads = 1024;
-    constexpr int kWaves = kThreads / 64;
-    constexpr int kSegs = kThreads / CB;  // segments per pass
-    constexpr int kPass = kSegs * SEG;    // tokens per pass
+    constexpr int kWaves = NT / 64;
+    constexpr int kSegs = NT / CB;     // segments per pass
+    constexpr int kPass = kSegs * SEG; // tokens per pass
     static_assert(64 % CB == 0, "a wave must hold whole segment groups");
+
 
     __shared__ St s_tot[kWaves][CB];
     __shared__ float s_totnw[kWaves][CB];
@@ -120,7 +127,8 @@ __global__ __launch_bounds__(1024) void rwkv4_scan_kernel(
     const int cl = tid % CB;
     const int seg = tid / CB;
     const int nblk = (C + CB - 1) / CB;
-    const int c = (blockIdx.x % nblk) * CB + cl;
+    const int c0 = (blockIdx.x % nblk) * CB;
+    const int c = c0 + cl;
     const int b = blockIdx.x / nblk;
     const bool active = c < C;
 
@@ -139,31 +147,43 @@ __global__ __launch_bounds__(1024) void rwkv4_scan_kernel(
         carry.p = kEmptyP;
     }
 
-    // Sequence base (uniform per workgroup) plus 32-bit per-lane offsets: one
-    // sequence spans fewer than 2^31 elements (checked by the launcher).
+    // Each pass addresses its rows through a raw buffer resource (uniform,
+    // 64-bit base) with 32-bit per-lane byte offsets.  Rows past T and lanes
+    // past C fall outside the resource: their loads return zero and their
+    // stores are dropped, so loads and stores need no branches and the next
+    // pass's loads stay in flight while a pass computes.
     const size_t seq = (size_t)b * T * C;
-    const float *kseq = k + seq;
-    const float *vseq = v + seq;
-    float *yseq = y + seq;
-    for (int t0 = 0; t0 < T; t0 += kPass) {
-        const int ts = t0 + seg * SEG;
-        const int n = min(max(T - ts, 0), SEG);
+    const uint32_t row_bytes = (uint32_t)C * 4u;
+    const uint32_t lane_off = active ? (uint32_t)(seg * SEG) * row_bytes + (uint32_t)c * 4u
+                                     : 0x80000000u;
+    auto rsrc = [&](const float *base, int t0) {
+        const uint32_t rows = (uint32_t)min(kPass, T - t0);
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(base + seq + (size_t)t0 * C), (short)0,
+                                                 (int)(rows * row_bytes), 0x00020000);
+    };
 
-        float kk[SEG], vv[SEG];
-        int off = ts * C + c;
+    auto load = [&](Seg<SEG> &d, int t0) {
+        const auto rk = rsrc(k, t0), rv = rsrc(v, t0);
 #pragma unroll
         for (int i = 0; i < SEG; ++i) {
-            const bool ld = active && i < n;
-            kk[i] = ld ? kseq[off] : 0.0f;
-            vv[i] = ld ? vseq[off] : 0.0f;
-            off += C;
+            d.k[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rk, lane_off + i * row_bytes, 0, 0));
+            d.v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rv, lane_off + i * row_bytes, 0, 0));
         }
+    };
+
+    // FULL: every row of the pass exists (uniform over the workgroup)
+    auto pass_impl = [&](int t0, const Seg<SEG> &d, auto full_tag) {
+        constexpr bool full = decltype(full_tag)::value;
+        const int ts = t0 + seg * SEG;
+        const int n = full ? SEG : min(max(T - ts, 0), SEG);
 
         // 1. segment summary from the empty state
         Walk wk = walk_from(St{0.0f, 0.0f, kEmptyP});
 #pragma unroll
         for (int i = 0; i < SEG; ++i)
-            if (i < n) fold(wk, wc, kk[i], vv[i]);
+            if (full || i < n) fold(wk, wc, d.k[i], d.v[i]);
         const St sum = walk_state(wk, wc);
         const float nw = (float)n * wc;
 
@@ -197,6 +217,7 @@ __global__ __launch_bounds__(1024) void rwkv4_scan_kernel(
         // 2b. scan of the wave totals, seeded with the incoming state
         if (tid < CB) {
             St run = carry;
+#pragma unroll
             for (int wv = 0; wv < kWaves; ++wv) {
                 s_pre[wv][tid] = run;
                 run = combine(run, s_totnw[wv][tid], s_tot[wv][tid]);
@@ -207,18 +228,34 @@ __global__ __launch_bounds__(1024) void rwkv4_scan_kernel(
 
         // 3. replay the segment from its carry-in state
         Walk s = walk_from(combine(s_pre[wave][cl], excnw, exc));
-        off = ts * C + c;
+        const auto ry = rsrc(y, t0);
 #pragma unroll
         for (int i = 0; i < SEG; ++i) {
-            if (i < n) {
-                const float yi = emit(s, wc, uc, kk[i], vv[i]);
-                fold(s, wc, kk[i], vv[i]);
-                if (active) yseq[off] = yi;
+            if (full || i < n) {
+                const float yi = emit(s, wc, uc, d.k[i], d.v[i]);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, yi), ry,
+                                                      lane_off + i * row_bytes, 0, 0);
+                fold(s, wc, d.k[i], d.v[i]);
             }
-            off += C;
         }
         carry = s_carry[cl];
         __syncthreads();  // s_pre / s_carry are rewritten by the next pass
+    };
+    auto pass = [&](int t0, const Seg<SEG> &d) {
+        if (t0 + kPass <= T) pass_impl(t0, d, std::true_type{});
+        else pass_impl(t0, d, std::false_type{});
+    };
+
+    // passes, the next one's k and v in flight while the current one computes
+    Seg<SEG> bufA, bufB;
+    if (T > 0) load(bufA, 0);
+    for (int t0 = 0; t0 < T; t0 += 2 * kPass) {
+        if (t0 + kPass < T) load(bufB, t0 + kPass);
+        pass(t0, bufA);
+        if (t0 + kPass < T) {
+            if (t0 + 2 * kPass < T) load(bufA, t0 + 2 * kPass);
+            pass(t0 + kPass, bufB);
+        }
     }
 
     if (state_out != nullptr && active && tid < CB) {
@@ -245,10 +282,11 @@ __global__ void fill_kernel(float *dst, int64_t n, float value) {
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,
                         float *state_out, float *y, hipStream_t stream) {
-    constexpr int CB = 16, SEG = 16;
-    dim3 grid((unsigned)(((C + CB - 1) / CB) * (int64_t)B));
-    hipLaunchKernelGGL((rwkv4_scan_kernel<CB, SEG>), grid, dim3(1024), 0, stream,
-                       T, C, k, v, w, u, state_in, state_out, y);
+    // 32 channels (128-byte rows) x 16 segments of 16 tokens per workgroup
+    constexpr int NT = 512, CB = 32, SEG = 16;
+    const int64_t blocks = (int64_t)B * ((C + CB - 1) / CB);
+    hipLaunchKernelGGL((rwkv4_scan_kernel<NT, CB, SEG>), dim3((unsigned)blocks), dim3(NT), 0,
+                       stream, T, C, k, v, w, u, state_in, state_out, y);
     return hipGetLastError();
 }
 

@@ -79,12 +79,17 @@ int check_matrix(int B, int T, int H, int N, const void *r, const void *k, const
     return check_outputs({so, sso}, {sr, sk, sv, sx, su, ssi}, s_out, s_in);
 }
 
+constexpr int kMaxChunkedHeads = 65536;
+constexpr int64_t kMaxRwkv4Channels = 1 << 20;
+
 int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
     const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
     int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
     if (st != RWKV_OK) return st;
+    // a chunk's rows are addressed with 32-bit byte offsets
+    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     if (T == 0) {
         if (state_out == nullptr || state_out == state_in) return RWKV_OK;
@@ -123,8 +128,10 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
     const int64_t tok = checked_mul({B, T, H, N});
     const int64_t st = checked_mul({B, 3, H, N});
     if (C < 0 || tok < 0 || st < 0 || C > INT32_MAX / 2) return RWKV_E_DIM;
-    // the scan addresses one sequence with 32-bit element offsets
-    if (((int64_t)T + 64) * C > INT32_MAX) return RWKV_E_UNSUPPORTED;
+    // a pass of the scan addresses its rows with 32-bit byte offsets
+    if (C > kMaxRwkv4Channels) return RWKV_E_UNSUPPORTED;
+    // one workgroup per batch entry and block of 32 channels
+    if ((int64_t)B * ((C + 31) / 32) > INT32_MAX) return RWKV_E_UNSUPPORTED;
     if (T > 0 && (k == nullptr || v == nullptr || w == nullptr || u == nullptr ||
                   y == nullptr))
         return RWKV_E_NULL;
@@ -173,3 +180,21 @@ int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf
 }
 
 }  // extern "C"
+
+namespace wkv {
+
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+}  // namespace wkv

@@ -55,6 +55,8 @@
 // without leaving registers.  The transposing load: in each group of 16
 // lanes, lane j supplies the address of 4 consecutive elements of row j/4 of
 // a 4 x 16 block and receives column j of that block (rows 0..3).
+#include <type_traits>
+
 #include "launchers.h"
 #include "wkv_device.h"
 
@@ -114,6 +116,18 @@ __device__ __forceinline__ bf16x8 lds_col4x2(const uint16_t *tile, int k0, int k
     const u32x4 m = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, m);
 }
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xf, 0xf, true));
+}
+// sum over the 16 lanes of a DPP row (every lane receives the total)
+__device__ __forceinline__ float row_sum16(float s) {
+    s += dpp<0x128>(s);  // row_ror:8
+    s += dpp<0x124>(s);  // row_ror:4
+    s += dpp<0x4e>(s);   // quad_perm [2,3,0,1]
+    s += dpp<0xb1>(s);   // quad_perm [1,0,3,2]
+    return s;
+}
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     const u32x2 r = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
     return r;
@@ -124,37 +138,48 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4 &lo, const f32x4 &hi) {
     return __builtin_bit_cast(bf16x8, m);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 layout: no
+// stride, no swizzle, 32-bit data format): a load past the end returns zero
+// and a store past the end is dropped, which is how a ragged last chunk is
+// masked without branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
 struct Ctx {
     int T, tq, cq, vt, vo;
-    size_t seq_base, tok_stride;
+    size_t seq_base, tok_stride;  // elements
+    uint32_t tokb;                // bytes of one bf16 token row (H N 2)
+    uint32_t off_rk, off_v;       // byte offsets of this thread's first r/k and v rows
+    // bf16 bytes of chunk c0's rows up to its last valid token, and the
+    // element offset of the chunk
+    __device__ uint32_t span(int c0) const { return (uint32_t)(min(kL, T - c0) - 1) * tokb + 2 * kN; }
+    __device__ size_t base(int c0) const { return seq_base + (size_t)c0 * tok_stride; }
 };
 
+// one thread's share of chunk c0 (rows past T read as zero)
 template <bool PT, int NW>
 __device__ __forceinline__ void load_raw(Raw<NW> &d, int c0, const Ctx &cx,
                                          const uint16_t *r, const uint16_t *k,
                                          const uint16_t *v, const float *x) {
     constexpr int TP = Raw<NW>::TP;
+    const size_t cb = cx.base(c0);
+    const uint32_t span = cx.span(c0);
+    const Rsrc rr = rsrc(r + cb, span), rk = rsrc(k + cb, span), rv = rsrc(v + cb, span);
 #pragma unroll
     for (int e = 0; e < TP; ++e) {
-        const int t = c0 + TP * cx.tq + e;
-        if (t < cx.T) {
-            const size_t off = cx.seq_base + (size_t)t * cx.tok_stride + 4 * cx.cq;
-            d.r[e] = *(const u32x2 *)(r + off);
-            d.k[e] = *(const u32x2 *)(k + off);
-            if (PT) d.x[e] = *(const f32x4 *)(x + off);
-        } else {
-            d.r[e] = u32x2{0u, 0u};
-            d.k[e] = u32x2{0u, 0u};
-            if (PT) d.x[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t off = cx.off_rk + e * cx.tokb;
+        d.r[e] = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
+        d.k[e] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+        if (PT) {
+            const Rsrc rx = rsrc(x + cb, 2 * span);
+            d.x[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * off, 0, 0));
         }
     }
 #pragma unroll
-    for (int j = 0; j < Raw<NW>::NV; ++j) {
-        const int t = c0 + cx.vt + 8 * NW * j;
-        d.v[j] = (t < cx.T)
-            ? *(const u32x4 *)(v + cx.seq_base + (size_t)t * cx.tok_stride + 8 * cx.vo)
-            : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < Raw<NW>::NV; ++j)
+        d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0, 0);
 }
 
 template <bool PT, int NW>
@@ -190,6 +215,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     cx.vo = tid & 7;
     cx.tok_stride = (size_t)H * kN;
     cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
+    cx.tokb = (uint32_t)H * kN * 2;
+    cx.off_rk = (uint32_t)(TP * cx.tq) * cx.tokb + 8 * cx.cq;
+    cx.off_v = (uint32_t)cx.vt * cx.tokb + 16 * cx.vo;
 
     const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
     f32x4 a2s = {0.f, 0.f, 0.f, 0.f};
@@ -212,18 +240,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     const int nchunks = (T + kL - 1) / kL;
 
-    // ---- stage A: log2 decays and the in-wave part of their scan ----------
+    // Eagle: the log2-decay is a per-channel constant, so the factors of a
+    // full chunk do not change from chunk to chunk: their bases are computed
+    // once, and each token's factor follows by one multiply.
+    f32x4 wq = {1.f, 1.f, 1.f, 1.f};  // 2^{a2} per channel (Eagle)
+    f32x4 eLL = {0.f, 0.f, 0.f, 0.f}, eF1 = wq, eF2 = wq;
+    if (!PT) {
+        const float t0 = (float)(TP * cx.tq);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wq[q] = exp2_fast(a2s[q]);
+            eLL[q] = (float)kL * a2s[q];
+            eF1[q] = exp2_fast(t0 * a2s[q] - eLL[q]);
+            eF2[q] = exp2_fast(eLL[q] - (t0 + TP) * a2s[q]);
+        }
+    }
+
+    // ---- stage A (Finch): log2 decays and the in-wave part of their scan --
     float a2[TP][4], lower[4];
     auto stageA = [&](int ch, const Raw<NW> &d) {
+        if (!PT) return;
         const int c0 = ch * kL;
 #pragma unroll
         for (int e = 0; e < TP; ++e) {
             const bool valid = c0 + TP * cx.tq + e < T;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float val = PT ? -exp2_fast(d.x[e][q] * kLog2e) * kLog2e : a2s[q];
-                a2[e][q] = valid ? val : 0.0f;
-            }
+            for (int q = 0; q < 4; ++q)
+                a2[e][q] = valid ? -exp2_fast(d.x[e][q] * kLog2e) * kLog2e : 0.0f;
         }
         f32x4 wt;
 #pragma unroll
@@ -243,21 +286,59 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     };
 
     // ---- stage B: prefix, factors and the operand tiles of a chunk --------
-    // (needs stage A of every wave, i.e. a barrier in between)
-    auto stageB = [&](const Raw<NW> &d) -> bool {
-        f32x4 tw[NW];
+    // (Finch needs stage A of every wave, i.e. a barrier in between)
+    auto stageB = [&](int ch, const Raw<NW> &d) -> bool {
+        const int c0 = ch * kL;
+        f32x4 LL, F1, F2;     // chunk total; 2^{lex_first - LL}; 2^{LL - lin_last}
+        float wv[TP][4];      // per-token decay factors 2^{a2}
+        if (PT) {
+            // partial sums over the waves in a fixed order: every thread of a
+            // channel obtains the same bits for the chunk total
+            f32x4 part = *(const f32x4 *)&sWave[0][4 * cx.cq];
+            f32x4 before = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NW; ++j) tw[j] = *(const f32x4 *)&sWave[j][4 * cx.cq];
-        f32x4 LL;
-        if (NW == 8)
-            LL = ((tw[0] + tw[1]) + (tw[2] + tw[3])) + ((tw[4 % NW] + tw[5 % NW]) +
-                                                       (tw[6 % NW] + tw[7 % NW]));
-        else
-            LL = (tw[0] + tw[1]) + (tw[2 % NW] + tw[3 % NW]);
-        f32x4 before = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 1; j < NW; ++j) {
+                if (j == w) before = part;
+                part += *(const f32x4 *)&sWave[j][4 * cx.cq];
+            }
+            LL = part;
+            f32x4 pre, lin;
 #pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-            if (j < w) before += tw[j];
+            for (int q = 0; q < 4; ++q) {
+                pre[q] = before[q] + lower[q];
+                float run = pre[q];
+#pragma unroll
+                for (int e = 0; e < TP; ++e) {
+                    run += a2[e][q];
+                    wv[e][q] = exp2_fast(a2[e][q]);
+                }
+                lin[q] = run;
+                F1[q] = exp2_fast(pre[q] - LL[q]);
+                F2[q] = exp2_fast(LL[q] - lin[q]);
+            }
+        } else {
+            const int nvalid = min(kL, T - c0);
+            if (nvalid == kL) {
+                LL = eLL;
+                F1 = eF1;
+                F2 = eF2;
+            } else {  // ragged last chunk: tokens past T do not decay
+                const float t0 = (float)min(TP * cx.tq, nvalid);
+                const float t1 = (float)min(TP * cx.tq + TP, nvalid);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    LL[q] = (float)nvalid * a2s[q];
+                    F1[q] = exp2_fast(t0 * a2s[q] - LL[q]);
+                    F2[q] = exp2_fast(LL[q] - t1 * a2s[q]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < TP; ++e) {
+                const bool valid = c0 + TP * cx.tq + e < T;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wv[e][q] = valid ? wq[q] : 1.0f;
+            }
+        }
         bool bad = false;
 #pragma unroll
         for (int q = 0; q < 4; ++q) bad |= LL[q] < kSafeLog2;
@@ -267,9 +348,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int q = 0; q < 4; ++q) dd[q] = exp2_fast(LL[q]);
             *(f32x4 *)&sDecay[w][4 * cx.cq] = dd;
         }
-        float run[4];
+        // k^ factors run backwards from the last token, r~ factors forwards
+        float f2[TP][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) run[q] = before[q] + lower[q];
+        for (int q = 0; q < 4; ++q) {
+            f2[TP - 1][q] = F2[q];
+#pragma unroll
+            for (int e = TP - 2; e >= 0; --e) f2[e][q] = f2[e + 1][q] * wv[e + 1][q];
+        }
+        f32x4 f1 = F1;
         float bs[TP];
 #pragma unroll
         for (int e = 0; e < TP; ++e) {
@@ -279,15 +366,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             const float kk[4] = {bf16_lo(d.k[e].x), bf16_hi(d.k[e].x), bf16_lo(d.k[e].y),
                                  bf16_hi(d.k[e].y)};
             float rt[4], kh[4], khl[4];
-            float s = 0.0f;
+            float sb = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float lex = run[q];
-                const float lin = lex + a2[e][q];
-                run[q] = lin;
-                rt[q] = rr[q] * exp2_fast(lex - LL[q]);
-                kh[q] = kk[q] * exp2_fast(LL[q] - lin);
-                s = fmaf(rr[q] * uq[q], kk[q], s);
+                rt[q] = rr[q] * f1[q];
+                f1[q] *= wv[e][q];
+                kh[q] = kk[q] * f2[e][q];
+                sb = fmaf(rr[q] * uq[q], kk[q], sb);
             }
             const u32x2 hi = pack4(kh[0], kh[1], kh[2], kh[3]);
             khl[0] = kh[0] - bf16_lo(hi.x);
@@ -297,21 +382,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             *(u32x2 *)(sm[T_RS] + tau * kP + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
             *(u32x2 *)(sm[T_KRH] + tau * kP + 4 * cx.cq) = hi;
             *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
-            bs[e] = s;
+            bs[e] = row_sum16(sb);  // bonus r_t diag(u) k_t^T over the token's 64 channels
         }
 #pragma unroll
         for (int j = 0; j < Raw<NW>::NV; ++j)
             *(u32x4 *)(sm[T_VR] + (cx.vt + 8 * NW * j) * kP + 8 * cx.vo) = d.v[j];
-        // bonus r_t diag(u) k_t^T: reduce over the 16 lanes sharing a token group
-#pragma unroll
-        for (int e = 0; e < TP; ++e) {
-            float s = bs[e];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 4, 64);
-            s += __shfl_xor(s, 8, 64);
-            bs[e] = s;
-        }
         if (c == 0) {
             if (TP == 4)
                 *(f32x4 *)&sBonus[TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
@@ -332,85 +407,85 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
     };
 
-    // ---- matrix phase of a chunk (fast path) -------------------------------
+    // ---- matrix phase of a chunk (fast path), specialised on the token tile
     f32x4 ot[NT];
-    auto matrix = [&]() {
-        f32x4 at[4];
+    auto matrix_p = [&](auto tile) {
+        constexpr int P = decltype(tile)::value;
+        f32x4 at[P + 1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // P1: A^T tiles (sigma-tile q, tau-tile p)
+        for (int q = 0; q <= P; ++q) {  // P1: A^T tiles (sigma-tile q, tau-tile P)
             at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (q <= p) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * kP + 32 * kb + 8 * g);
-                    const bf16x8 B = lds8(sm[T_RS] + (16 * p + c) * kP + 32 * kb + 8 * g);
-                    at[q] = mfma(A, B, at[q]);
-                }
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * kP + 32 * kb + 8 * g);
+                const bf16x8 B = lds8(sm[T_RS] + (16 * P + c) * kP + 32 * kb + 8 * g);
+                at[q] = mfma(A, B, at[q]);
             }
         }
         // P3: S' = diag(decay) S + (K^_hi + K^_lo)^T V (independent of P1)
 #pragma unroll
         for (int mi = 0; mi < NT; ++mi) {
             const int m = NT * hf + mi;
-            if (NW == 4) __builtin_amdgcn_sched_barrier(0);  // bound operands in flight
             f32x4 acc = SD[mi];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int k0 = 32 * kb + 8 * g;
-                const bf16x8 Bv = lds_col8(sm[T_VR], k0, 16 * p, c);
+                const bf16x8 Bv = lds_col8(sm[T_VR], k0, 16 * P, c);
                 acc = mfma(lds_col8(sm[T_KRH], k0, 16 * m, c), Bv, acc);
                 acc = mfma(lds_col8(sm[T_KRL], k0, 16 * m, c), Bv, acc);
             }
             S[mi] = acc;
         }
         // P2 part 2: (decayed S)^T R~^T
-        if (NW == 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 Br = lds8(sm[T_RS] + (16 * p + c) * kP + 32 * kb + 8 * g);
+            const bf16x8 Br = lds8(sm[T_RS] + (16 * P + c) * kP + 32 * kb + 8 * g);
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
                 ot[ni] = mfma(lds8(sm[T_ST] + (16 * (NT * hf + ni) + c) * kP + 32 * kb + 8 * g),
                               Br, ot[ni]);
         }
-        // causal mask, bonus on the diagonal
+        // causal mask of the diagonal tile, bonus on its diagonal
         {
-            const float bon = sBonus[16 * p + c];
+            const float bon = sBonus[16 * P + c];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q == p) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int sl = 4 * g + e;
-                        at[q][e] = sl < c ? at[q][e] : (sl == c ? bon : 0.0f);
-                    }
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * g + e;
+                at[P][e] = sl < c ? at[P][e] : (sl == c ? bon : 0.0f);
             }
         }
         // P2 part 1: V^T A^T over the causal sigma blocks
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk) {
-            if (2 * bk <= p) {
-                const bf16x8 Bop = pack8(at[2 * bk], at[2 * bk + 1]);
+        for (int bk = 0; 2 * bk <= P; ++bk) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const bf16x8 Bop = pack8(at[2 * bk], (2 * bk + 1 <= P) ? at[(2 * bk + 1) % (P + 1)]
+                                                                   : zero);
 #pragma unroll
-                for (int ni = 0; ni < NT; ++ni)
-                    ot[ni] = mfma(lds_col4x2(sm[T_VR], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g,
-                                             16 * (NT * hf + ni), c),
-                                  Bop, ot[ni]);
-            }
+            for (int ni = 0; ni < NT; ++ni)
+                ot[ni] = mfma(lds_col4x2(sm[T_VR], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g,
+                                         16 * (NT * hf + ni), c),
+                              Bop, ot[ni]);
+        }
+    };
+    auto matrix = [&]() {
+        switch (p) {  // wave-uniform
+            case 0: matrix_p(std::integral_constant<int, 0>{}); break;
+            case 1: matrix_p(std::integral_constant<int, 1>{}); break;
+            case 2: matrix_p(std::integral_constant<int, 2>{}); break;
+            default: matrix_p(std::integral_constant<int, 3>{}); break;
         }
     };
 
     auto store_out = [&](int ch) {
-        const int t = ch * kL + 16 * p + c;
-        if (t < T) {
-            uint16_t *op = o + cx.seq_base + (size_t)t * cx.tok_stride + 16 * NT * hf + 4 * g;
+        const int c0 = ch * kL;
+        const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
+        const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
 #pragma unroll
-            for (int ni = 0; ni < NT; ++ni)
-                *(u32x2 *)(op + 16 * ni) = pack4(ot[ni][0], ot[ni][1], ot[ni][2], ot[ni][3]);
-        }
+        for (int ni = 0; ni < NT; ++ni)
+            __builtin_amdgcn_raw_buffer_store_b64(pack4(ot[ni][0], ot[ni][1], ot[ni][2], ot[ni][3]),
+                                                  ro, off + 32 * ni, 0, 0);
     };
 
     // ---- fast-decay chunk: its tokens one at a time with fp32 VALU ---------
@@ -514,7 +589,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (more) stageA(ch + 1, buf);
         __syncthreads();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
-        if (more) bad = stageB(buf);
+        if (more) bad = stageB(ch + 1, buf);
         if (!unsafe) store_out(ch);
         if (more) stage_state();
         return __syncthreads_or(bad);  // (Y) operands of ch + 1 staged
@@ -523,7 +598,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     load_raw<PT, NW>(buf, 0, cx, r, k, v, x);
     stageA(0, buf);
     __syncthreads();
-    const bool bad0 = stageB(buf);
+    const bool bad0 = stageB(0, buf);
     stage_state();
     bool unsafe = __syncthreads_or(bad0);
     for (int ch = 0; ch < nchunks; ++ch) unsafe = step(ch, unsafe);
@@ -536,21 +611,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 state_out[st_base + (size_t)(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] =
                     S[mi][e];
     }
-}
-
-// Compute units of the current device, read once per device.
-int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
 }
 
 template <bool PT, int NW>

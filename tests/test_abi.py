@@ -83,8 +83,8 @@ def test_rwkv4_bad_dims(L, dims):
     assert rwkv4(L, B=B, T=T, H=H, N=N) == E_DIM
 
 
-def test_rwkv4_too_long_sequence(L):
-    assert rwkv4(L, B=1, T=1 << 21, H=1, N=1 << 10) == E_UNSUP
+def test_rwkv4_too_many_channels(L):
+    assert rwkv4(L, B=1, T=1, H=1, N=(1 << 20) + 4) == E_UNSUP
 
 
 @pytest.mark.parametrize("missing", ["k", "v", "w", "u", "y"])
@@ -123,6 +123,12 @@ def test_rwkv4_state_partial_overlap(L):
 def test_matrix_head_size_must_be_64(L, fn):
     assert matrix(L, fn, N=32) == E_UNSUP
     assert matrix(L, fn, N=128) == E_UNSUP
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+def test_matrix_head_count_limit(L, fn):
+    # chunk rows are addressed with 32-bit byte offsets: at most 65536 heads
+    assert matrix(L, fn, B=1, T=1, H=65537, si=None, so=None) == E_UNSUP
 
 
 @pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
