@@ -42,8 +42,9 @@
 // Pipeline: chunk c's operand reads and matrix products are issued before
 // the barrier that publishes chunk c+1's decay totals, and their results are
 // only consumed after it, so the matrix cores run while the VALU stages
-// chunk c+1 (decay scan, factors, tiles).  Two barriers per chunk; the next
-// chunk's r, k, v, x are fetched while chunk c's products run.  HBM traffic is the
+// chunk c+1 (decay scan, factors, tiles).  Two barriers per chunk.  Chunk
+// c+1's r, k, v are fetched while chunk c's products run; Finch's decay
+// logits (the first operand a chunk's staging needs) one step ahead of that.  HBM traffic is the
 // algorithmic minimum: r, k, v, o (and x for Finch) once, the state once
 // each way.
 //
@@ -116,6 +117,17 @@ __device__ __forceinline__ bf16x8 lds_col4x2(const uint16_t *tile, int k0, int k
     const u32x4 m = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, m);
 }
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have
+// completed (lgkmcnt(0)) before it arrives.  Unlike __syncthreads() it does
+// not order global memory, which no thread here reads after another wrote
+// it; the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
 template <int Ctrl>
 __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xf, 0xf, true));
@@ -158,11 +170,11 @@ struct Ctx {
     __device__ size_t base(int c0) const { return seq_base + (size_t)c0 * tok_stride; }
 };
 
-// one thread's share of chunk c0 (rows past T read as zero)
-template <bool PT, int NW>
-__device__ __forceinline__ void load_raw(Raw<NW> &d, int c0, const Ctx &cx,
+// one thread's r, k, v of chunk c0 (rows past T read as zero)
+template <int NW>
+__device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
                                          const uint16_t *r, const uint16_t *k,
-                                         const uint16_t *v, const float *x) {
+                                         const uint16_t *v) {
     constexpr int TP = Raw<NW>::TP;
     const size_t cb = cx.base(c0);
     const uint32_t span = cx.span(c0);
@@ -172,14 +184,21 @@ __device__ __forceinline__ void load_raw(Raw<NW> &d, int c0, const Ctx &cx,
         const uint32_t off = cx.off_rk + e * cx.tokb;
         d.r[e] = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
         d.k[e] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
-        if (PT) {
-            const Rsrc rx = rsrc(x + cb, 2 * span);
-            d.x[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * off, 0, 0));
-        }
     }
 #pragma unroll
     for (int j = 0; j < Raw<NW>::NV; ++j)
         d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0, 0);
+}
+
+// one thread's Finch decay logits of chunk c0 (rows past T read as zero)
+template <int NW>
+__device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const float *x) {
+    constexpr int TP = Raw<NW>::TP;
+    const Rsrc rx = rsrc(x + cx.base(c0), 2 * cx.span(c0));
+#pragma unroll
+    for (int e = 0; e < TP; ++e)
+        d.x[e] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (cx.off_rk + e * cx.tokb), 0, 0));
 }
 
 template <bool PT, int NW>
@@ -195,6 +214,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     __shared__ __align__(16) float sWave[NW][kN];   // per-wave log2-decay totals
     __shared__ __align__(16) float sDecay[NW][kN];  // e^{Lam_L}, one copy per wave
     __shared__ __align__(16) float sBonus[kL];
+    __shared__ int sBad[NW];  // per wave: a channel of the next chunk decays too fast
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -499,7 +519,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sS[(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] = S[mi][e];
-        __syncthreads();
+        lds_barrier();
         f32x4 Sc[4];
         if (w < 4) {
 #pragma unroll
@@ -508,7 +528,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 for (int e = 0; e < 4; ++e)
                     Sc[m][e] = sS[(16 * m + 4 * g + e) * kN + 16 * w + c];
         }
-        __syncthreads();
+        lds_barrier();
         // re-read r, k, x of the chunk one token row at a time (few registers)
 #pragma unroll 1
         for (int e = 0; e < TP; ++e) {
@@ -532,7 +552,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = rv;
             *(u32x2 *)(sm[T_ST] + tau * kP + 4 * cx.cq) = kv;
         }
-        __syncthreads();
+        lds_barrier();
         if (w < 4) {
             const int nvalid = min(kL, T - c0);
             for (int tau = 0; tau < nvalid; ++tau) {
@@ -562,7 +582,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (w < 4) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -570,7 +590,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 for (int e = 0; e < 4; ++e)
                     sS[(16 * m + 4 * g + e) * kN + 16 * w + c] = Sc[m][e];
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int mi = 0; mi < NT; ++mi)
 #pragma unroll
@@ -580,27 +600,45 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- one pipelined step: matrix phase of chunk ch, staging of ch + 1 --
     // buf holds chunk ch + 1's inputs: staging of ch consumed it last step.
+    // LDS barrier that also ORs a flag over the workgroup.  sBad[w] is
+    // written again only after the next barrier (X), when every wave has
+    // read it.
+    auto barrier_or = [&](bool flag) -> bool {
+        const bool any = __builtin_amdgcn_ballot_w64(flag) != 0;
+        if (lane == 0) sBad[w] = any ? 1 : 0;
+        lds_barrier();
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) r |= sBad[j];
+        return r != 0;
+    };
+    // buf holds chunk ch + 1's inputs when step ch starts: its r, k, v were
+    // requested at the start of the step, its x (Finch) right after the
+    // previous step's stage A had read the registers, a whole step earlier.
     Raw<NW> buf;
     auto step = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < nchunks;
-        if (more) load_raw<PT, NW>(buf, (ch + 1) * kL, cx, r, k, v, x);
+        if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
         if (!unsafe) matrix();
         else token_by_token(ch);
         if (more) stageA(ch + 1, buf);
-        __syncthreads();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
+        if (PT && ch + 2 < nchunks) load_x<NW>(buf, (ch + 2) * kL, cx, x);
+        lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf);
         if (!unsafe) store_out(ch);
         if (more) stage_state();
-        return __syncthreads_or(bad);  // (Y) operands of ch + 1 staged
+        return barrier_or(bad);  // (Y) operands of ch + 1 staged
     };
 
-    load_raw<PT, NW>(buf, 0, cx, r, k, v, x);
+    if (PT) load_x<NW>(buf, 0, cx, x);
+    load_rkv<NW>(buf, 0, cx, r, k, v);
     stageA(0, buf);
-    __syncthreads();
+    if (PT && nchunks > 1) load_x<NW>(buf, kL, cx, x);
+    lds_barrier();
     const bool bad0 = stageB(0, buf);
     stage_state();
-    bool unsafe = __syncthreads_or(bad0);
+    bool unsafe = barrier_or(bad0);
     for (int ch = 0; ch < nchunks; ++ch) unsafe = step(ch, unsafe);
 
     if (state_out != nullptr) {
