@@ -66,8 +66,14 @@ namespace {
 
 constexpr int kN = 64;     // head size
 constexpr int kL = 64;     // chunk length
-constexpr int kP = 72;     // LDS row pitch (bf16 elements) of the 64x64 tiles
-constexpr int kTile = kN * kP;
+// LDS row pitches (bf16 elements) of the 64x64 tiles.  Rows read whole by
+// 16-byte loads (r~, the decayed state) are 72 elements apart: 8 lanes reading
+// rows c..c+7 hit 32 distinct banks.  Tiles read down their columns by the
+// transposing load (k^_hi, k^_lo, v) are 80 apart: the 4 rows x 4 column
+// groups that 16 lanes address then also cover 32 distinct banks.
+constexpr int kPR = 72;
+constexpr int kPC = 80;
+constexpr int kTile = kN * kPC;
 // Smallest chunk log2-decay (per channel) handled by the factorised form:
 // r~ <= |r| 2^110 and k^ >= |k| 2^-110 stay far from fp32 / bf16 limits.
 constexpr float kSafeLog2 = -110.0f;
@@ -75,6 +81,7 @@ constexpr float kSafeLog2 = -110.0f;
 // LDS tiles, all row-major: r~, k^_hi, k^_lo, v as [token][channel]; the
 // decayed state as [j][i].
 enum { T_RS = 0, T_KRH, T_KRL, T_VR, T_ST, T_COUNT };
+__device__ constexpr int pitch(int t) { return (t == T_RS || t == T_ST) ? kPR : kPC; }
 
 template <int NW>
 struct Raw {                           // one thread's share of a chunk
@@ -104,16 +111,16 @@ __device__ __forceinline__ u32x2 lds_tr(const uint16_t *p) {
 // column (n0 + c) of rows k0..k0+7 of a row-major tile, for lane c of its
 // 16-lane group: the operand of a product that contracts over rows
 __device__ __forceinline__ bf16x8 lds_col8(const uint16_t *tile, int k0, int n0, int c) {
-    const uint16_t *p = tile + (k0 + (c >> 2)) * kP + n0 + 4 * (c & 3);
-    const u32x2 a = lds_tr(p), b = lds_tr(p + 4 * kP);
+    const uint16_t *p = tile + (k0 + (c >> 2)) * kPC + n0 + 4 * (c & 3);
+    const u32x2 a = lds_tr(p), b = lds_tr(p + 4 * kPC);
     const u32x4 m = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, m);
 }
 // rows k0..k0+3 and k1..k1+3 of column (n0 + c)
 __device__ __forceinline__ bf16x8 lds_col4x2(const uint16_t *tile, int k0, int k1, int n0,
                                              int c) {
-    const int off = (c >> 2) * kP + n0 + 4 * (c & 3);
-    const u32x2 a = lds_tr(tile + k0 * kP + off), b = lds_tr(tile + k1 * kP + off);
+    const int off = (c >> 2) * kPC + n0 + 4 * (c & 3);
+    const u32x2 a = lds_tr(tile + k0 * kPC + off), b = lds_tr(tile + k1 * kPC + off);
     const u32x4 m = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, m);
 }
@@ -399,14 +406,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             khl[1] = kh[1] - bf16_hi(hi.x);
             khl[2] = kh[2] - bf16_lo(hi.y);
             khl[3] = kh[3] - bf16_hi(hi.y);
-            *(u32x2 *)(sm[T_RS] + tau * kP + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
-            *(u32x2 *)(sm[T_KRH] + tau * kP + 4 * cx.cq) = hi;
-            *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
+            *(u32x2 *)(sm[T_RS] + tau * pitch(T_RS) + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
+            *(u32x2 *)(sm[T_KRH] + tau * pitch(T_KRH) + 4 * cx.cq) = hi;
+            *(u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
             bs[e] = row_sum16(sb);  // bonus r_t diag(u) k_t^T over the token's 64 channels
         }
 #pragma unroll
         for (int j = 0; j < Raw<NW>::NV; ++j)
-            *(u32x4 *)(sm[T_VR] + (cx.vt + 8 * NW * j) * kP + 8 * cx.vo) = d.v[j];
+            *(u32x4 *)(sm[T_VR] + (cx.vt + 8 * NW * j) * pitch(T_VR) + 8 * cx.vo) = d.v[j];
         if (c == 0) {
             if (TP == 4)
                 *(f32x4 *)&sBonus[TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int mi = 0; mi < NT; ++mi) {
             const f32x4 dd = *(const f32x4 *)&sDecay[w][16 * (NT * hf + mi) + 4 * g];
             SD[mi] = S[mi] * dd;
-            *(u32x2 *)(sm[T_ST] + (16 * p + c) * kP + 16 * (NT * hf + mi) + 4 * g) =
+            *(u32x2 *)(sm[T_ST] + (16 * p + c) * pitch(T_ST) + 16 * (NT * hf + mi) + 4 * g) =
                 pack4(SD[mi][0], SD[mi][1], SD[mi][2], SD[mi][3]);
         }
     };
@@ -437,8 +444,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * kP + 32 * kb + 8 * g);
-                const bf16x8 B = lds8(sm[T_RS] + (16 * P + c) * kP + 32 * kb + 8 * g);
+                const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * pitch(T_KRH) + 32 * kb + 8 * g);
+                const bf16x8 B = lds8(sm[T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
                 at[q] = mfma(A, B, at[q]);
             }
         }
@@ -461,10 +468,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 Br = lds8(sm[T_RS] + (16 * P + c) * kP + 32 * kb + 8 * g);
+            const bf16x8 Br = lds8(sm[T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
-                ot[ni] = mfma(lds8(sm[T_ST] + (16 * (NT * hf + ni) + c) * kP + 32 * kb + 8 * g),
+                ot[ni] = mfma(lds8(sm[T_ST] + (16 * (NT * hf + ni) + c) * pitch(T_ST) + 32 * kb + 8 * g),
                               Br, ot[ni]);
         }
         // causal mask of the diagonal tile, bonus on its diagonal
@@ -549,19 +556,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 wv[q] = valid ? exp2_fast(a) : 1.0f;
             }
             *(f32x4 *)(sS + tau * kN + 4 * cx.cq) = wv;
-            *(u32x2 *)(sm[T_KRL] + tau * kP + 4 * cx.cq) = rv;
-            *(u32x2 *)(sm[T_ST] + tau * kP + 4 * cx.cq) = kv;
+            *(u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = rv;
+            *(u32x2 *)(sm[T_ST] + tau * pitch(T_ST) + 4 * cx.cq) = kv;
         }
         lds_barrier();
         if (w < 4) {
             const int nvalid = min(kL, T - c0);
             for (int tau = 0; tau < nvalid; ++tau) {
-                const float vj = bf16_to_f32(sm[T_VR][tau * kP + 16 * w + c]);
+                const float vj = bf16_to_f32(sm[T_VR][tau * pitch(T_VR) + 16 * w + c]);
                 float acc = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const u32x2 rp = *(const u32x2 *)(sm[T_KRL] + tau * kP + 16 * m + 4 * g);
-                    const u32x2 kp = *(const u32x2 *)(sm[T_ST] + tau * kP + 16 * m + 4 * g);
+                    const u32x2 rp = *(const u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 16 * m + 4 * g);
+                    const u32x2 kp = *(const u32x2 *)(sm[T_ST] + tau * pitch(T_ST) + 16 * m + 4 * g);
                     const f32x4 wv = *(const f32x4 *)(sS + tau * kN + 16 * m + 4 * g);
                     const float r4[4] = {bf16_lo(rp.x), bf16_hi(rp.x), bf16_lo(rp.y),
                                          bf16_hi(rp.y)};
