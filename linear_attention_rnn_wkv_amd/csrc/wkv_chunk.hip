@@ -26,11 +26,13 @@
 // is applied token by token instead (exact at any decay).
 //
 // Work split: one workgroup of NW = 4 or 8 wave64s per (sequence, head);
-// with NH = NW / 4 and TP = 8 / NH tokens per staging thread:
+// with NH = NW / 4 and TP = 16 / NW tokens per staging thread:
 //   staging   thread t: channels 4 (t%16) + {0..3}, tokens TP (t/16) + {0..TP-1};
-//             v: tokens t/8 + 64/NH j, channels 8 (t%8) + {0..7}
+//             v: tokens t/8 + 8 NW j, channels 8 (t%8) + {0..7}
 //   P1, P2    wave w: tokens [16 (w%4), +16), value columns [64/NH (w/4), +64/NH)
-//   P3        wave w: value columns [16 (w%4), +16), key rows [64/NH (w/4), +64/NH)
+//   P3        wave w: key rows [(128/NW) (w/2), +128/NW), value columns
+//             [32 (w%2), +32) -- a block, so each wave reads only its share
+//             of K^ and V
 // so the fp32 state never leaves registers (except in the fast-decay path).
 // Eight waves give two waves per SIMD to one head; four waves let two heads
 // share a CU.  The launcher picks eight while the heads fit on the CUs.
@@ -228,8 +230,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int p = w & 3;   // P1/P2 token tile, P3 value tile
-    const int hf = w >> 2; // P2 value part, P3 key part
+    const int p = w & 3;   // P1/P2 token tile
+    const int hf = w >> 2; // P2 value part
 
     const int bh = blockIdx.x;
     const int b = bh / H;
@@ -254,15 +256,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int q = 0; q < 4; ++q) a2s[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
     }
 
-    // state tiles of this wave: S[mi][e] = S[16 (NT hf + mi) + 4 g + e][16 p + c]
+    // State tiles of this wave (P3): a block of MI key tiles x 2 value tiles,
+    // so a wave reads a half or a quarter of K^ and half of V per chunk.
+    // S[t][e] = S[skey(t) + 4 g + e][sval(t) + c].
+    constexpr int MI = 8 / NW;
+    const int skey0 = 16 * MI * (w >> 1), sval0 = 32 * (w & 1);
+    auto skey = [&](int t) { return skey0 + 16 * (t >> 1); };
+    auto sval = [&](int t) { return sval0 + 16 * (t & 1); };
+    static_assert(2 * MI == NT, "a wave holds NT state tiles");
     const size_t st_base = (size_t)bh * kN * kN;
     f32x4 S[NT], SD[NT];
 #pragma unroll
-    for (int mi = 0; mi < NT; ++mi)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            S[mi][e] = state_in
-                ? state_in[st_base + (size_t)(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c]
+            S[t][e] = state_in
+                ? state_in[st_base + (size_t)(skey(t) + 4 * g + e) * kN + sval(t) + c]
                 : 0.0f;
 
     const int nchunks = (T + kL - 1) / kL;
@@ -426,11 +435,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // decayed state of the next chunk, staged transposed as bf16
     auto stage_state = [&]() {
 #pragma unroll
-        for (int mi = 0; mi < NT; ++mi) {
-            const f32x4 dd = *(const f32x4 *)&sDecay[w][16 * (NT * hf + mi) + 4 * g];
-            SD[mi] = S[mi] * dd;
-            *(u32x2 *)(sm[T_ST] + (16 * p + c) * pitch(T_ST) + 16 * (NT * hf + mi) + 4 * g) =
-                pack4(SD[mi][0], SD[mi][1], SD[mi][2], SD[mi][3]);
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 dd = *(const f32x4 *)&sDecay[w][skey(t) + 4 * g];
+            SD[t] = S[t] * dd;
+            *(u32x2 *)(sm[T_ST] + (sval(t) + c) * pitch(T_ST) + skey(t) + 4 * g) =
+                pack4(SD[t][0], SD[t][1], SD[t][2], SD[t][3]);
         }
     };
 
@@ -451,18 +460,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
         // P3: S' = diag(decay) S + (K^_hi + K^_lo)^T V (independent of P1)
 #pragma unroll
-        for (int mi = 0; mi < NT; ++mi) {
-            const int m = NT * hf + mi;
-            f32x4 acc = SD[mi];
+        for (int kb = 0; kb < 2; ++kb) {
+            const int k0 = 32 * kb + 8 * g;
+            bf16x8 Bv[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int k0 = 32 * kb + 8 * g;
-                const bf16x8 Bv = lds_col8(sm[T_VR], k0, 16 * P, c);
-                acc = mfma(lds_col8(sm[T_KRH], k0, 16 * m, c), Bv, acc);
-                acc = mfma(lds_col8(sm[T_KRL], k0, 16 * m, c), Bv, acc);
+            for (int vj = 0; vj < 2; ++vj) Bv[vj] = lds_col8(sm[T_VR], k0, sval0 + 16 * vj, c);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const bf16x8 Ah = lds_col8(sm[T_KRH], k0, skey0 + 16 * mi, c);
+                const bf16x8 Al = lds_col8(sm[T_KRL], k0, skey0 + 16 * mi, c);
+#pragma unroll
+                for (int vj = 0; vj < 2; ++vj) {
+                    f32x4 &acc = SD[2 * mi + vj];  // becomes the new state
+                    acc = mfma(Ah, Bv[vj], acc);
+                    acc = mfma(Al, Bv[vj], acc);
+                }
             }
-            S[mi] = acc;
         }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) S[t] = SD[t];
         // P2 part 2: (decayed S)^T R~^T
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -522,10 +538,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const int c0 = ch * kL;
         float *sS = (float *)sm[T_RS];  // 64 x 64 fp32 spans the r~ and k^_hi tiles
 #pragma unroll
-        for (int mi = 0; mi < NT; ++mi)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sS[(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] = S[mi][e];
+                sS[(skey(t) + 4 * g + e) * kN + sval(t) + c] = S[t][e];
         lds_barrier();
         f32x4 Sc[4];
         if (w < 4) {
@@ -599,10 +615,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
         lds_barrier();
 #pragma unroll
-        for (int mi = 0; mi < NT; ++mi)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S[mi][e] = sS[(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c];
+                S[t][e] = sS[(skey(t) + 4 * g + e) * kN + sval(t) + c];
     };
 
     // ---- one pipelined step: matrix phase of chunk ch, staging of ch + 1 --
@@ -650,11 +666,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     if (state_out != nullptr) {
 #pragma unroll
-        for (int mi = 0; mi < NT; ++mi)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                state_out[st_base + (size_t)(16 * (NT * hf + mi) + 4 * g + e) * kN + 16 * p + c] =
-                    S[mi][e];
+                state_out[st_base + (size_t)(skey(t) + 4 * g + e) * kN + sval(t) + c] = S[t][e];
     }
 }
 
