@@ -30,8 +30,9 @@
  * length).
  *
  * Conventions for every entry point
- *  - All tensor pointers are DEVICE pointers owned by the caller.  The
- *    library allocates nothing and keeps no state between calls.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The only
+ *    memory the library allocates is rwkv4_wkv_fwd's chain workspace (see
+ *    there); no call keeps state that changes a later call's results.
  *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
  *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
  *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
@@ -89,6 +90,14 @@ const char *rwkv_wkv_strerror(int status);
  *
  * Pointers need 4-byte alignment.  C = H*N must be at most 2^20 and
  * B * C below 2^36, else RWKV_E_UNSUPPORTED.
+ *
+ * Workspace: the 256-token passes of a sequence's channel block run in
+ * separate workgroups that hand the state on through a device workspace
+ * (about 0.8 KB per workgroup of a launch, at most 8192 workgroups per
+ * launch).  It is allocated on the first call for each (device, stream),
+ * grown when a call needs more (that call then synchronises the stream), and
+ * kept until the process ends.  Calls on one stream share it safely; the
+ * first call on a stream must not be made during graph capture.
  */
 int rwkv4_wkv_fwd(int B, int T, int H, int N,
                   const float *k, const float *v,

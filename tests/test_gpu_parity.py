@@ -76,6 +76,14 @@ def test_rwkv4_workload2_full():
     rwkv4_check(S.workload(2))
 
 
+def test_rwkv4_split_over_launches():
+    # 4100 (sequence, 32-channel block) pairs x 2 passes exceed one launch's
+    # workgroup budget: the passes run in two launches, the state carried
+    # between them through the library's workspace
+    print("rwkv4 B=4100 T=257 C=32 (two launches)", flush=True)
+    rwkv4_check(S.rwkv4_inputs(4100, 257, 32, 11, k_sigma=2.0))
+
+
 def test_rwkv4_large_keys():
     # |k| up to ~100: the unscaled numerator would overflow fp32 without the
     # running maximum exponent
