@@ -9,6 +9,14 @@ namespace wkv {
 // Compute units of the current device (read once per device).
 int device_cus();
 
+// Device workspace of one kind for (current device, stream), at least `bytes`
+// long and zero-filled when first allocated (on `stream`).  Launches on one
+// stream run in order and may share it; a kernel that uses flags in it must
+// leave them cleared.  A larger request reallocates (synchronising the
+// stream first).  Kept until the process ends.
+enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1 };
+hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out);
+
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,

@@ -27,8 +27,6 @@
 // sequences x channel blocks alone would not fill the chip.  k and v are read
 // from HBM once and y written once (12 bytes per token-channel).
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
 
 #include "launchers.h"
@@ -353,42 +351,6 @@ __global__ void fill_kernel(float *dst, int64_t n, float value) {
 
 }  // namespace
 
-namespace {
-// Chain workspace (records and flags) per device and stream: launches on one
-// stream run in order, so they may share it; the flags are cleared when it is
-// allocated and every launch leaves them cleared.  Kept until the process
-// ends.
-struct Workspace {
-    void *p = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
-hipError_t rwkv4_workspace(hipStream_t stream, size_t bytes, void **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &ws = g_ws[{dev, stream}];
-    if (ws.bytes < bytes) {
-        if (ws.p != nullptr) {
-            if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-            if ((e = hipFree(ws.p)) != hipSuccess) return e;
-            ws.p = nullptr;
-            ws.bytes = 0;
-        }
-        const size_t n = (bytes + 255) / 256 * 256;
-        if ((e = hipMalloc(&ws.p, n)) != hipSuccess) return e;
-        if ((e = launch_fill((float *)ws.p, (int64_t)(n / 4), 0.0f, stream)) != hipSuccess)
-            return e;
-        ws.bytes = n;
-    }
-    *out = ws.p;
-    return hipSuccess;
-}
-}  // namespace
-
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,
                         float *state_out, float *y, hipStream_t stream) {
@@ -409,7 +371,8 @@ hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
     const size_t rec_bytes = (size_t)links * 6 * CB * 4;
     const size_t carry_bytes = windows ? (size_t)B * 3 * C * 4 : 0;
     char *ws = nullptr;
-    hipError_t e = rwkv4_workspace(stream, flag_bytes + rec_bytes + carry_bytes, (void **)&ws);
+    hipError_t e = stream_workspace(kWsRwkv4Chain, stream, flag_bytes + rec_bytes + carry_bytes,
+                                    (void **)&ws);
     if (e != hipSuccess) return e;
     unsigned *flags = (unsigned *)ws;
     unsigned *err = flags + kMaxLinks;

@@ -5,6 +5,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include <hip/hip_runtime.h>
 
 #include "launchers.h"
@@ -182,6 +186,38 @@ int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf
 }  // extern "C"
 
 namespace wkv {
+
+namespace {
+struct Workspace {
+    void *p = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::tuple<int, int, hipStream_t>, Workspace> g_ws;
+}  // namespace
+
+hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &ws = g_ws[std::make_tuple(kind, dev, stream)];
+    if (ws.bytes < bytes) {
+        if (ws.p != nullptr) {
+            if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+            if ((e = hipFree(ws.p)) != hipSuccess) return e;
+            ws.p = nullptr;
+            ws.bytes = 0;
+        }
+        const size_t n = (bytes + 255) / 256 * 256;
+        if ((e = hipMalloc(&ws.p, n)) != hipSuccess) return e;
+        if ((e = launch_fill((float *)ws.p, (int64_t)(n / 4), 0.0f, stream)) != hipSuccess)
+            return e;
+        ws.bytes = n;
+    }
+    *out = ws.p;
+    return hipSuccess;
+}
 
 int device_cus() {
     static int cache[64] = {0};

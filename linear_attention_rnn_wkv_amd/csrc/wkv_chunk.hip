@@ -210,12 +210,20 @@ __device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const 
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (cx.off_rk + e * cx.tokb), 0, 0));
 }
 
+// Balanced split of B*H = first_extra + extra heads over first_extra
+// workgroups (see the kernel); extra == 0: one head per workgroup.
+struct Split {
+    int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    float *slots;     // [extra * (K - 1)][64][64] states between segments
+    unsigned *flags;  // [max_slots] slot flags, then an error word
+};
+
 template <bool PT, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x,
     const float *__restrict__ u, const float *state_in, float *state_out,
-    uint16_t *__restrict__ o) {
+    uint16_t *__restrict__ o, Split sp) {
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
@@ -233,9 +241,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     const int p = w & 3;   // P1/P2 token tile
     const int hf = w >> 2; // P2 value part
 
-    const int bh = blockIdx.x;
-    const int b = bh / H;
-    const int h = bh % H;
     Ctx cx;
     cx.T = T;
     cx.cq = tid & 15;      // == c
@@ -243,18 +248,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     cx.vt = tid >> 3;
     cx.vo = tid & 7;
     cx.tok_stride = (size_t)H * kN;
-    cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
     cx.tokb = (uint32_t)H * kN * 2;
     cx.off_rk = (uint32_t)(TP * cx.tq) * cx.tokb + 8 * cx.cq;
     cx.off_v = (uint32_t)cx.vt * cx.tokb + 16 * cx.vo;
-
-    const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
-    f32x4 a2s = {0.f, 0.f, 0.f, 0.f};
-    if (!PT) {
-        const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * cx.cq);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a2s[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
-    }
 
     // State tiles of this wave (P3): a block of MI key tiles x 2 value tiles,
     // so a wave reads a half or a quarter of K^ and half of V per chunk.
@@ -264,33 +260,57 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto skey = [&](int t) { return skey0 + 16 * (t >> 1); };
     auto sval = [&](int t) { return sval0 + 16 * (t & 1); };
     static_assert(2 * MI == NT, "a wave holds NT state tiles");
-    const size_t st_base = (size_t)bh * kN * kN;
+    auto sidx = [&](int t, int e) { return (skey(t) + 4 * g + e) * kN + sval(t) + c; };
     f32x4 S[NT], SD[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[t][e] = state_in
-                ? state_in[st_base + (size_t)(skey(t) + 4 * g + e) * kN + sval(t) + c]
-                : 0.0f;
 
     const int nchunks = (T + kL - 1) / kL;
 
-    // Eagle: the log2-decay is a per-channel constant, so the factors of a
-    // full chunk do not change from chunk to chunk: their bases are computed
-    // once, and each token's factor follows by one multiply.
-    f32x4 wq = {1.f, 1.f, 1.f, 1.f};  // 2^{a2} per channel (Eagle)
-    f32x4 eLL = {0.f, 0.f, 0.f, 0.f}, eF1 = wq, eF2 = wq;
-    if (!PT) {
-        const float t0 = (float)(TP * cx.tq);
+    // Per-head values, set by set_head.  Eagle: the log2-decay is a
+    // per-channel constant, so the factors of a full chunk do not change
+    // from chunk to chunk: their bases are computed once per head, and each
+    // token's factor follows by one multiply.
+    f32x4 uq, a2s, wq, eLL, eF1, eF2;
+    int bh = 0;  // (sequence, head) of the current job
+    auto set_head = [&](int head) {
+        bh = head;
+        const int b = head / H, h = head % H;
+        cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
+        uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
+        a2s = f32x4{0.f, 0.f, 0.f, 0.f};
+        wq = f32x4{1.f, 1.f, 1.f, 1.f};
+        eLL = a2s;
+        eF1 = wq;
+        eF2 = wq;
+        if (!PT) {
+            const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * cx.cq);
+            const float t0 = (float)(TP * cx.tq);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            wq[q] = exp2_fast(a2s[q]);
-            eLL[q] = (float)kL * a2s[q];
-            eF1[q] = exp2_fast(t0 * a2s[q] - eLL[q]);
-            eF2[q] = exp2_fast(eLL[q] - (t0 + TP) * a2s[q]);
+            for (int q = 0; q < 4; ++q) {
+                a2s[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
+                wq[q] = exp2_fast(a2s[q]);
+                eLL[q] = (float)kL * a2s[q];
+                eF1[q] = exp2_fast(t0 * a2s[q] - eLL[q]);
+                eF2[q] = exp2_fast(eLL[q] - (t0 + TP) * a2s[q]);
+            }
         }
-    }
+    };
+    // the current head's state from state_in (zeros without one) / to state_out
+    auto load_state = [&]() {
+        const size_t base = (size_t)bh * kN * kN;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[t][e] = state_in ? state_in[base + sidx(t, e)] : 0.0f;
+    };
+    auto save_state = [&]() {
+        if (state_out == nullptr) return;
+        const size_t base = (size_t)bh * kN * kN;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) state_out[base + sidx(t, e)] = S[t][e];
+    };
 
     // ---- stage A (Finch): log2 decays and the in-wave part of their scan --
     float a2[TP][4], lower[4];
@@ -639,13 +659,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // requested at the start of the step, its x (Finch) right after the
     // previous step's stage A had read the registers, a whole step earlier.
     Raw<NW> buf;
+    int ch_end = nchunks;  // end of the current job's chunk range
     auto step = [&](int ch, bool unsafe) -> bool {
-        const bool more = ch + 1 < nchunks;
+        const bool more = ch + 1 < ch_end;
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
         if (!unsafe) matrix();
         else token_by_token(ch);
         if (more) stageA(ch + 1, buf);
-        if (PT && ch + 2 < nchunks) load_x<NW>(buf, (ch + 2) * kL, cx, x);
+        if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf);
@@ -653,34 +674,125 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (more) stage_state();
         return barrier_or(bad);  // (Y) operands of ch + 1 staged
     };
+    // chunks [ch0, ch1) of the current head from the state in S
+    auto run_job = [&](int ch0, int ch1) {
+        if (ch0 >= ch1) return;
+        ch_end = ch1;
+        if (PT) load_x<NW>(buf, ch0 * kL, cx, x);
+        load_rkv<NW>(buf, ch0 * kL, cx, r, k, v);
+        stageA(ch0, buf);
+        if (PT && ch0 + 1 < ch1) load_x<NW>(buf, (ch0 + 1) * kL, cx, x);
+        lds_barrier();
+        const bool bad0 = stageB(ch0, buf);
+        stage_state();
+        bool unsafe = barrier_or(bad0);
+        for (int ch = ch0; ch < ch1; ++ch) unsafe = step(ch, unsafe);
+    };
 
-    if (PT) load_x<NW>(buf, 0, cx, x);
-    load_rkv<NW>(buf, 0, cx, r, k, v);
-    stageA(0, buf);
-    if (PT && nchunks > 1) load_x<NW>(buf, kL, cx, x);
-    lds_barrier();
-    const bool bad0 = stageB(0, buf);
-    stage_state();
-    bool unsafe = barrier_or(bad0);
-    for (int ch = 0; ch < nchunks; ++ch) unsafe = step(ch, unsafe);
+    if (sp.extra == 0) {  // one head per workgroup
+        set_head(blockIdx.x);
+        load_state();
+        run_job(0, nchunks);
+        save_state();
+        return;
+    }
 
-    if (state_out != nullptr) {
+    // Balanced split (eight waves, one workgroup per CU): workgroup i runs
+    // its own head i and one segment of one of the sp.extra remaining heads.
+    // The segments of an extra head run on workgroups i, i + sp.stride, ...
+    // (the same XCD, dispatched in order), and segment s starts after the
+    // workgroup's first s/K of its own head, by when segment s-1 is done:
+    //   own [0, a) -> extra segment s = [a, b) -> own [a, nchunks)
+    // The state between segments goes through the handoff workspace.
+    const int own = blockIdx.x;
+    const int xcd = own % sp.stride, local = own / sp.stride;
+    const int chain = local / sp.K, seg = local % sp.K;
+    const int ext = xcd + sp.stride * chain;  // extra head index among sp.extra
+    if (chain >= sp.chains_per_xcd || ext >= sp.extra) {
+        set_head(own);
+        load_state();
+        run_job(0, nchunks);
+        save_state();
+        return;
+    }
+    const int a = seg * nchunks / sp.K, e1 = (seg + 1) * nchunks / sp.K;
+    auto ld = [](const void *ptr) {
+        return __hip_atomic_load((unsigned *)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto st = [](void *ptr, unsigned val) {
+        __hip_atomic_store((unsigned *)ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    set_head(own);
+    load_state();
+    run_job(0, a);
+    f32x4 Sown[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) Sown[t] = S[t];
+
+    set_head(sp.first_extra + ext);
+    if (seg == 0) {
+        load_state();
+    } else {
+        // Slots and flags are touched only by agent-scope relaxed atomics,
+        // which act at the device's coherence point: the producer's stores
+        // complete before its flag store, and the state is read only after
+        // the flag was seen.  The consumer clears the flag for the next
+        // launch.  Polls are bounded (about a second): the producer has a
+        // lower workgroup index on the same XCD, so it is already running.
+        const int slot = ext * (sp.K - 1) + seg - 1;
+        const float *src = sp.slots + (size_t)slot * kN * kN;
+        if (tid == 0) {
+            int polls = 0;
+            while (ld(sp.flags + slot) == 0u) {
+                __builtin_amdgcn_s_sleep(8);
+                if (++polls > (1 << 20)) {
+                    st(sp.flags + sp.max_slots, 1u);  // error word
+                    break;
+                }
+            }
+        }
+        lds_barrier();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                state_out[st_base + (size_t)(skey(t) + 4 * g + e) * kN + sval(t) + c] = S[t][e];
+            for (int e = 0; e < 4; ++e) S[t][e] = __uint_as_float(ld(src + sidx(t, e)));
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
+        lds_barrier();
+        if (tid == 0) st(sp.flags + slot, 0u);
     }
+    run_job(a, e1);
+    if (seg + 1 == sp.K) {
+        save_state();
+    } else {
+        const int slot = ext * (sp.K - 1) + seg;
+        float *dst = sp.slots + (size_t)slot * kN * kN;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st(dst + sidx(t, e), __float_as_uint(S[t][e]));
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
+        lds_barrier();
+        if (tid == 0) st(sp.flags + slot, 1u);
+    }
+
+    set_head(own);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S[t] = Sown[t];
+    run_job(a, nchunks);
+    save_state();
 }
 
 template <bool PT, int NW>
-void launch(int B, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
+void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
             const float *x, const float *u, const float *state_in, float *state_out,
-            uint16_t *o, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((int64_t)B * H);
-    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW>), dim3(blocks), dim3(64 * NW), 0, stream, T, H,
-                       r, k, v, x, u, state_in, state_out, o);
+            uint16_t *o, const Split &sp, hipStream_t stream) {
+    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0,
+                       stream, T, H, r, k, v, x, u, state_in, state_out, o, sp);
 }
+
+// XCDs of the device: workgroups are dealt to them round-robin
+constexpr int kXcds = 8;
+constexpr int kMaxSlots = 4096;
 
 }  // namespace
 
@@ -688,15 +800,43 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
                               const uint16_t *k, const uint16_t *v, const float *x,
                               const float *u, const float *state_in, float *state_out,
                               uint16_t *o, hipStream_t stream) {
-    // eight waves per head while every head has a CU of its own, else four
-    // waves so that two heads share a CU
-    const bool wide = (int64_t)B * H <= device_cus();
+    // Eight waves per head while every head has a CU of its own.  With up to
+    // half as many heads again, eight waves and the balanced split: one
+    // workgroup per CU, each running one head plus one K-th of an extra
+    // head.  Beyond that, four waves so that two heads share a CU.
+    const int64_t heads = (int64_t)B * H;
+    const int cus = device_cus();
+    Split sp{};
+    bool wide = heads <= cus;
+    if (!wide && cus % kXcds == 0 && T >= 4 * kL) {
+        const int64_t extra = heads - cus;
+        const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
+        const int64_t K = (cus / kXcds) / chains_per_xcd;
+        if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
+            sp.extra = (int)extra;
+            sp.first_extra = cus;
+            sp.K = (int)K;
+            sp.stride = kXcds;
+            sp.chains_per_xcd = (int)chains_per_xcd;
+            sp.max_slots = kMaxSlots;
+            const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
+            const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
+            char *ws = nullptr;
+            hipError_t e = stream_workspace(kWsChunkHandoff, stream, flag_bytes + slot_bytes,
+                                            (void **)&ws);
+            if (e != hipSuccess) return e;
+            sp.flags = (unsigned *)ws;
+            sp.slots = (float *)(ws + flag_bytes);
+            wide = true;
+        }
+    }
+    const int blocks = (int)(sp.extra ? sp.first_extra : heads);
     if (per_token_decay) {
-        if (wide) launch<true, 8>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
-        else launch<true, 4>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+        if (wide) launch<true, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
+        else launch<true, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
     } else {
-        if (wide) launch<false, 8>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
-        else launch<false, 4>(B, T, H, r, k, v, x, u, state_in, state_out, o, stream);
+        if (wide) launch<false, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
+        else launch<false, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
     }
     return hipGetLastError();
 }
