@@ -252,7 +252,7 @@ def cpu_baseline(S, d4):
 PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic bytes)
     "finch_fwd": ("wkv_chunk_kernel<true,", "wkv_chunk.hip", lambda: finch_bytes(8, 4096, 40)),
     "eagle_fwd": ("wkv_chunk_kernel<false,", "wkv_chunk.hip", lambda: eagle_bytes(8, 4096, 32)),
-    "rwkv4_fwd": ("rwkv4_scan_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
+    "rwkv4_fwd": ("rwkv4_chain_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
     "finch_decode": ("wkv6_step_kernel", "wkv_step.hip", lambda: decode_bytes_per_step(256, 64)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
