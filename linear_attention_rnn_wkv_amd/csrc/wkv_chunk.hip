@@ -227,11 +227,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
-    __shared__ __align__(16) uint16_t sm[T_COUNT][kTile];
-    __shared__ __align__(16) float sWave[NW][kN];   // per-wave log2-decay totals
-    __shared__ __align__(16) float sDecay[NW][kN];  // e^{Lam_L}, one copy per wave
-    __shared__ __align__(16) float sBonus[kL];
-    __shared__ int sBad[NW];  // per wave: a channel of the next chunk decays too fast
+    // Eight waves (one workgroup per CU) double-buffer the operand tiles, the
+    // decay totals, the bonus and the range flags by chunk parity: chunk c
+    // uses set c & 1, so one barrier per chunk suffices (see the step).
+    constexpr bool DB = NW == 8;
+    constexpr int NS = DB ? 2 : 1;
+    __shared__ __align__(16) uint16_t sm[NS][T_COUNT][kTile];
+    __shared__ __align__(16) float sWave[NS][NW][kN];  // per-wave log2-decay totals
+    __shared__ __align__(16) float sDecay[NW][kN];     // e^{Lam_L}, one copy per wave
+    __shared__ __align__(16) float sBonus[NS][kL];
+    __shared__ int sBad[NS][NW];  // per wave: a channel of the next chunk decays too fast
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- stage A (Finch): log2 decays and the in-wave part of their scan --
     float a2[TP][4], lower[4];
-    auto stageA = [&](int ch, const Raw<NW> &d) {
+    auto stageA = [&](int ch, const Raw<NW> &d, int set) {
         if (!PT) return;
         const int c0 = ch * kL;
 #pragma unroll
@@ -338,24 +343,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             lower[q] = (g == 0) ? 0.0f : ex;
             wt[q] = s;
         }
-        if (g == 3) *(f32x4 *)&sWave[w][4 * cx.cq] = wt;
+        if (g == 3) *(f32x4 *)&sWave[set][w][4 * cx.cq] = wt;
     };
 
     // ---- stage B: prefix, factors and the operand tiles of a chunk --------
     // (Finch needs stage A of every wave, i.e. a barrier in between)
-    auto stageB = [&](int ch, const Raw<NW> &d) -> bool {
+    auto stageB = [&](int ch, const Raw<NW> &d, int set) -> bool {
         const int c0 = ch * kL;
         f32x4 LL, F1, F2;     // chunk total; 2^{lex_first - LL}; 2^{LL - lin_last}
         float wv[TP][4];      // per-token decay factors 2^{a2}
         if (PT) {
             // partial sums over the waves in a fixed order: every thread of a
             // channel obtains the same bits for the chunk total
-            f32x4 part = *(const f32x4 *)&sWave[0][4 * cx.cq];
+            f32x4 part = *(const f32x4 *)&sWave[set][0][4 * cx.cq];
             f32x4 before = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 1; j < NW; ++j) {
                 if (j == w) before = part;
-                part += *(const f32x4 *)&sWave[j][4 * cx.cq];
+                part += *(const f32x4 *)&sWave[set][j][4 * cx.cq];
             }
             LL = part;
             f32x4 pre, lin;
@@ -435,37 +440,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             khl[1] = kh[1] - bf16_hi(hi.x);
             khl[2] = kh[2] - bf16_lo(hi.y);
             khl[3] = kh[3] - bf16_hi(hi.y);
-            *(u32x2 *)(sm[T_RS] + tau * pitch(T_RS) + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
-            *(u32x2 *)(sm[T_KRH] + tau * pitch(T_KRH) + 4 * cx.cq) = hi;
-            *(u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
+            *(u32x2 *)(sm[set][T_RS] + tau * pitch(T_RS) + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
+            *(u32x2 *)(sm[set][T_KRH] + tau * pitch(T_KRH) + 4 * cx.cq) = hi;
+            *(u32x2 *)(sm[set][T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
             bs[e] = row_sum16(sb);  // bonus r_t diag(u) k_t^T over the token's 64 channels
         }
 #pragma unroll
         for (int j = 0; j < Raw<NW>::NV; ++j)
-            *(u32x4 *)(sm[T_VR] + (cx.vt + 8 * NW * j) * pitch(T_VR) + 8 * cx.vo) = d.v[j];
+            *(u32x4 *)(sm[set][T_VR] + (cx.vt + 8 * NW * j) * pitch(T_VR) + 8 * cx.vo) = d.v[j];
         if (c == 0) {
             if (TP == 4)
-                *(f32x4 *)&sBonus[TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
+                *(f32x4 *)&sBonus[set][TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
             else
-                *(f32x2 *)&sBonus[TP * cx.tq] = f32x2{bs[0], bs[1 % TP]};
+                *(f32x2 *)&sBonus[set][TP * cx.tq] = f32x2{bs[0], bs[1 % TP]};
         }
         return bad;
     };
 
     // decayed state of the next chunk, staged transposed as bf16
-    auto stage_state = [&]() {
+    auto stage_state = [&](int set) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const f32x4 dd = *(const f32x4 *)&sDecay[w][skey(t) + 4 * g];
             SD[t] = S[t] * dd;
-            *(u32x2 *)(sm[T_ST] + (sval(t) + c) * pitch(T_ST) + skey(t) + 4 * g) =
+            *(u32x2 *)(sm[set][T_ST] + (sval(t) + c) * pitch(T_ST) + skey(t) + 4 * g) =
                 pack4(SD[t][0], SD[t][1], SD[t][2], SD[t][3]);
         }
     };
 
     // ---- matrix phase of a chunk (fast path), specialised on the token tile
     f32x4 ot[NT];
-    auto matrix_p = [&](auto tile) {
+    auto matrix_p = [&](auto tile, int set) {
         constexpr int P = decltype(tile)::value;
         f32x4 at[P + 1];
 #pragma unroll
@@ -473,8 +478,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 A = lds8(sm[T_KRH] + (16 * q + c) * pitch(T_KRH) + 32 * kb + 8 * g);
-                const bf16x8 B = lds8(sm[T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
+                const bf16x8 A = lds8(sm[set][T_KRH] + (16 * q + c) * pitch(T_KRH) + 32 * kb + 8 * g);
+                const bf16x8 B = lds8(sm[set][T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
                 at[q] = mfma(A, B, at[q]);
             }
         }
@@ -484,11 +489,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             const int k0 = 32 * kb + 8 * g;
             bf16x8 Bv[2];
 #pragma unroll
-            for (int vj = 0; vj < 2; ++vj) Bv[vj] = lds_col8(sm[T_VR], k0, sval0 + 16 * vj, c);
+            for (int vj = 0; vj < 2; ++vj) Bv[vj] = lds_col8(sm[set][T_VR], k0, sval0 + 16 * vj, c);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const bf16x8 Ah = lds_col8(sm[T_KRH], k0, skey0 + 16 * mi, c);
-                const bf16x8 Al = lds_col8(sm[T_KRL], k0, skey0 + 16 * mi, c);
+                const bf16x8 Ah = lds_col8(sm[set][T_KRH], k0, skey0 + 16 * mi, c);
+                const bf16x8 Al = lds_col8(sm[set][T_KRL], k0, skey0 + 16 * mi, c);
 #pragma unroll
                 for (int vj = 0; vj < 2; ++vj) {
                     f32x4 &acc = SD[2 * mi + vj];  // becomes the new state
@@ -504,15 +509,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 Br = lds8(sm[T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
+            const bf16x8 Br = lds8(sm[set][T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
-                ot[ni] = mfma(lds8(sm[T_ST] + (16 * (NT * hf + ni) + c) * pitch(T_ST) + 32 * kb + 8 * g),
+                ot[ni] = mfma(lds8(sm[set][T_ST] + (16 * (NT * hf + ni) + c) * pitch(T_ST) + 32 * kb + 8 * g),
                               Br, ot[ni]);
         }
         // causal mask of the diagonal tile, bonus on its diagonal
         {
-            const float bon = sBonus[16 * P + c];
+            const float bon = sBonus[set][16 * P + c];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int sl = 4 * g + e;
@@ -527,17 +532,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                                                                    : zero);
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
-                ot[ni] = mfma(lds_col4x2(sm[T_VR], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g,
+                ot[ni] = mfma(lds_col4x2(sm[set][T_VR], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g,
                                          16 * (NT * hf + ni), c),
                               Bop, ot[ni]);
         }
     };
-    auto matrix = [&]() {
+    auto matrix = [&](int set) {
         switch (p) {  // wave-uniform
-            case 0: matrix_p(std::integral_constant<int, 0>{}); break;
-            case 1: matrix_p(std::integral_constant<int, 1>{}); break;
-            case 2: matrix_p(std::integral_constant<int, 2>{}); break;
-            default: matrix_p(std::integral_constant<int, 3>{}); break;
+            case 0: matrix_p(std::integral_constant<int, 0>{}, set); break;
+            case 1: matrix_p(std::integral_constant<int, 1>{}, set); break;
+            case 2: matrix_p(std::integral_constant<int, 2>{}, set); break;
+            default: matrix_p(std::integral_constant<int, 3>{}, set); break;
         }
     };
 
@@ -554,9 +559,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // ---- fast-decay chunk: its tokens one at a time with fp32 VALU ---------
     // Waves 0..3 take the state as 16-column slabs through LDS; r, k (bf16)
     // and w = 2^{a2} (fp32) are re-read and staged in the operand tiles.
-    auto token_by_token = [&](int ch) {
+    auto token_by_token = [&](int ch, int set) {
         const int c0 = ch * kL;
-        float *sS = (float *)sm[T_RS];  // 64 x 64 fp32 spans the r~ and k^_hi tiles
+        float *sS = (float *)sm[set][T_RS];  // 64 x 64 fp32 spans the r~ and k^_hi tiles
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -592,19 +597,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 wv[q] = valid ? exp2_fast(a) : 1.0f;
             }
             *(f32x4 *)(sS + tau * kN + 4 * cx.cq) = wv;
-            *(u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = rv;
-            *(u32x2 *)(sm[T_ST] + tau * pitch(T_ST) + 4 * cx.cq) = kv;
+            *(u32x2 *)(sm[set][T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = rv;
+            *(u32x2 *)(sm[set][T_ST] + tau * pitch(T_ST) + 4 * cx.cq) = kv;
         }
         lds_barrier();
         if (w < 4) {
             const int nvalid = min(kL, T - c0);
             for (int tau = 0; tau < nvalid; ++tau) {
-                const float vj = bf16_to_f32(sm[T_VR][tau * pitch(T_VR) + 16 * w + c]);
+                const float vj = bf16_to_f32(sm[set][T_VR][tau * pitch(T_VR) + 16 * w + c]);
                 float acc = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const u32x2 rp = *(const u32x2 *)(sm[T_KRL] + tau * pitch(T_KRL) + 16 * m + 4 * g);
-                    const u32x2 kp = *(const u32x2 *)(sm[T_ST] + tau * pitch(T_ST) + 16 * m + 4 * g);
+                    const u32x2 rp = *(const u32x2 *)(sm[set][T_KRL] + tau * pitch(T_KRL) + 16 * m + 4 * g);
+                    const u32x2 kp = *(const u32x2 *)(sm[set][T_ST] + tau * pitch(T_ST) + 16 * m + 4 * g);
                     const f32x4 wv = *(const f32x4 *)(sS + tau * kN + 16 * m + 4 * g);
                     const float r4[4] = {bf16_lo(rp.x), bf16_hi(rp.x), bf16_lo(rp.y),
                                          bf16_hi(rp.y)};
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 acc += __shfl_xor(acc, 16, 64);
                 acc += __shfl_xor(acc, 32, 64);
                 if (g == 0) {
-                    const float ov = fmaf(sBonus[tau], vj, acc);
+                    const float ov = fmaf(sBonus[set][tau], vj, acc);
                     o[cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 16 * w + c] =
                         (uint16_t)pack_bf16x2(ov, 0.0f);
                 }
@@ -643,50 +648,75 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- one pipelined step: matrix phase of chunk ch, staging of ch + 1 --
     // buf holds chunk ch + 1's inputs: staging of ch consumed it last step.
-    // LDS barrier that also ORs a flag over the workgroup.  sBad[w] is
+    // LDS barrier that also ORs a flag over the workgroup.  sBad[set][w] is
     // written again only after the next barrier (X), when every wave has
     // read it.
-    auto barrier_or = [&](bool flag) -> bool {
+    auto barrier_or = [&](bool flag, int set) -> bool {
         const bool any = __builtin_amdgcn_ballot_w64(flag) != 0;
-        if (lane == 0) sBad[w] = any ? 1 : 0;
+        if (lane == 0) sBad[set][w] = any ? 1 : 0;
         lds_barrier();
         int r = 0;
 #pragma unroll
-        for (int j = 0; j < NW; ++j) r |= sBad[j];
+        for (int j = 0; j < NW; ++j) r |= sBad[set][j];
         return r != 0;
     };
-    // buf holds chunk ch + 1's inputs when step ch starts: its r, k, v were
-    // requested at the start of the step, its x (Finch) right after the
-    // previous step's stage A had read the registers, a whole step earlier.
     Raw<NW> buf;
     int ch_end = nchunks;  // end of the current job's chunk range
-    auto step = [&](int ch, bool unsafe) -> bool {
+
+    // Four waves, one tile set, two barriers per chunk.  buf holds chunk
+    // ch + 1's inputs when step ch starts: its r, k, v were requested at the
+    // start of the step, its x (Finch) right after the previous step's stage
+    // A had read the registers, a whole step earlier.
+    auto step2 = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < ch_end;
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
-        if (!unsafe) matrix();
-        else token_by_token(ch);
-        if (more) stageA(ch + 1, buf);
+        if (!unsafe) matrix(0);
+        else token_by_token(ch, 0);
+        if (more) stageA(ch + 1, buf, 0);
         if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
-        if (more) bad = stageB(ch + 1, buf);
+        if (more) bad = stageB(ch + 1, buf, 0);
         if (!unsafe) store_out(ch);
-        if (more) stage_state();
-        return barrier_or(bad);  // (Y) operands of ch + 1 staged
+        if (more) stage_state(0);
+        return barrier_or(bad, 0);  // (Y) operands of ch + 1 staged
+    };
+    // Eight waves, chunk c in set c & 1, one barrier per chunk.  When step
+    // ch starts, chunk ch is staged in set ch & 1 and chunk ch + 1's decay
+    // totals are in sWave[(ch + 1) & 1]; the step stages chunk ch + 1 in the
+    // other set while chunk ch's products run, and scans chunk ch + 2's
+    // decays, so nothing a wave writes is read by another before the barrier.
+    auto step1 = [&](int ch, bool unsafe) -> bool {
+        const int cur = ch & 1, nxt = cur ^ 1;
+        const bool more = ch + 1 < ch_end;
+        if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
+        if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
+        if (!unsafe) matrix(cur);
+        else token_by_token(ch, cur);
+        bool bad = false;
+        if (more) bad = stageB(ch + 1, buf, nxt);
+        if (!unsafe) store_out(ch);
+        if (more) stage_state(nxt);
+        if (ch + 2 < ch_end) stageA(ch + 2, buf, cur);
+        return barrier_or(bad, cur);  // chunk ch + 1 staged, ch + 2's totals out
     };
     // chunks [ch0, ch1) of the current head from the state in S
     auto run_job = [&](int ch0, int ch1) {
         if (ch0 >= ch1) return;
         ch_end = ch1;
+        const int s0 = DB ? (ch0 & 1) : 0;
         if (PT) load_x<NW>(buf, ch0 * kL, cx, x);
         load_rkv<NW>(buf, ch0 * kL, cx, r, k, v);
-        stageA(ch0, buf);
+        stageA(ch0, buf, s0);
         if (PT && ch0 + 1 < ch1) load_x<NW>(buf, (ch0 + 1) * kL, cx, x);
         lds_barrier();
-        const bool bad0 = stageB(ch0, buf);
-        stage_state();
-        bool unsafe = barrier_or(bad0);
-        for (int ch = ch0; ch < ch1; ++ch) unsafe = step(ch, unsafe);
+        const bool bad0 = stageB(ch0, buf, s0);
+        stage_state(s0);
+        // (DB: chunk ch0 + 1's scan after stage B of ch0 has used the scan
+        // registers; the other parity's flags, next used two barriers later)
+        if (DB && ch0 + 1 < ch1) stageA(ch0 + 1, buf, s0 ^ 1);
+        bool unsafe = barrier_or(bad0, DB ? (s0 ^ 1) : 0);
+        for (int ch = ch0; ch < ch1; ++ch) unsafe = DB ? step1(ch, unsafe) : step2(ch, unsafe);
     };
 
     if (sp.extra == 0) {  // one head per workgroup
