@@ -163,9 +163,11 @@ def test_chunked_shapes(per_token, B, T, H):
 # More heads than CUs (256 on MI355X): one workgroup per CU runs a whole head
 # plus a segment of one of the remaining heads, whose state is handed from
 # segment to segment between workgroups.  320 heads: four segments; 300: five;
-# 270: sixteen segments for five chunks (empty segments pass the state on).
+# 270: sixteen segments for five chunks (empty segments pass the state on);
+# 400 heads: four-wave workgroups, two heads per CU.
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
-@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (2, 320, 135)])
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (2, 320, 135),
+                                   (4, 130, 100)])
 def test_chunked_more_heads_than_cus(per_token, B, T, H):
     print(f"chunked {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     g, o, so = chunked_check(matrix_case(B, T, H, 400 + H, per_token), per_token)
