@@ -31,8 +31,10 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The only
- *    memory the library allocates is rwkv4_wkv_fwd's chain workspace (see
- *    there); no call keeps state that changes a later call's results.
+ *    memory the library allocates is two per-stream workspaces: the chain
+ *    workspace of rwkv4_wkv_fwd and the hand-off workspace of the chunked
+ *    Eagle/Finch calls (see there); no call keeps state that changes a
+ *    later call's results.
  *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
  *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
  *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
@@ -120,6 +122,12 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N,
  *
  * All pointers need 16-byte alignment.  H must be at most 65536, else
  * RWKV_E_UNSUPPORTED.
+ *
+ * Workspace: when B*H exceeds the device's compute units (at most by half
+ * again) and T >= 256, each workgroup runs its own head plus a segment of an
+ * extra head, and the segments hand the state on through a device workspace
+ * (16 KB per hand-off, at most 4096).  It is allocated, grown and kept as
+ * rwkv4_wkv_fwd's chain workspace, with the same rules.
  */
 int rwkv5_wkv_fwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
