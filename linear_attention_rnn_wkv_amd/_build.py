@@ -16,6 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "librwkv_wkv.so")
 SOURCES = ["rwkv_wkv_abi.hip", "rwkv4_scan.hip", "wkv_step.hip", "wkv_chunk.hip"]
+# The RWKV-4 chain counts arrivals with one lane's returning atomic whose
+# result is only needed at the end of the workgroup; the atomic optimizer
+# would broadcast it at once and so wait for the round trip right there.
+SOURCE_FLAGS = {"rwkv4_scan.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -61,7 +65,8 @@ def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY,
         path = (sources or {}).get(src, os.path.join(CSRC, src))
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", path, "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c", path, "-o",
+                     obj])
     _run(cmds, verbose)
     tmp = output + ".tmp"
     _run([[HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)

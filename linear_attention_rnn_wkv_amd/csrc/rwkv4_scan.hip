@@ -110,31 +110,53 @@ struct Seg {  // one lane's tokens of a pass
     float k[SEG], v[SEG];
 };
 
-// Workspace record of one workgroup of a chain: the aggregate of its pass
-// (state after the pass from the empty state) and its inclusive state, each
-// (a, b, p) for CB channels, plus a flag: 0 nothing, 1 aggregate, 2 inclusive.
-constexpr unsigned kAgg = 1u, kIncl = 2u;
-// Bound on the polls of a predecessor's flag (about a second): predecessors
-// have lower workgroup indices and are dispatched first, so the wait always
-// ends; the bound only guarantees that the kernel terminates.
+// Workspace of the chains.  A record of one workgroup holds the aggregate of
+// its pass (state after the pass from the empty state) and its inclusive
+// state, each (a, b, p) for CB channels.  Every record word is 64 bits: the
+// value in the low half and the tag epoch + 1 in the high half, so a word
+// read with the current tag was written by this launch and needs no separate
+// flag.  Once every workgroup of a launch holds the epoch it is advanced,
+// which makes all records of the launch stale without clearing them.
+//
+// When that is: the last pass of a chain finishes its walk only after every
+// pass of the chain has published a tagged record (walks reach back to an
+// inclusive state, whose publisher walked before it, down to pass 0), i.e.
+// after each of them has read the epoch.  The last passes of the chains then
+// arrive at one of kGroups counters, and the last arrival of each group at a
+// total; the last arrival there advances the epoch.  Two levels keep any one
+// counter to a few dozen atomics (a single counter hit by every workgroup
+// serialises and stalls the memory system).
+constexpr int kGroups = 64;
+struct Ctrl {  // each word on a 128-byte line of its own
+    struct Line {
+        unsigned n, pad[31];
+    };
+    Line epoch, err, total, group[kGroups];
+};
+// Bound on the polls of a predecessor's record (about a second):
+// predecessors have lower workgroup indices and are dispatched first, so the
+// wait always ends; the bound only guarantees that the kernel terminates.
 constexpr int kSpinLimit = 1 << 20;
 
+// Registers are capped so that three 512-thread workgroups (six waves per
+// SIMD) share a CU: then every pass of the benchmark-sized launches is
+// resident at once and no chain waits for a workgroup slot.
 template <int NT, int CB, int SEG>
-__global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
+__global__ __launch_bounds__(NT, 3 * NT / 256) void rwkv4_chain_kernel(
     int T, int t_begin, int nq, int C, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ w, const float *__restrict__ u,
-    const float *state_in, float *state_out, float *__restrict__ y, float *recs,
-    unsigned *flags, unsigned *err) {
+    const float *state_in, float *state_out, float *__restrict__ y,
+    unsigned long long *recs, Ctrl *ctrl) {
     constexpr int kWaves = NT / 64;
     constexpr int kSegs = NT / CB;     // segments per pass
     constexpr int kPass = kSegs * SEG; // tokens per pass
     static_assert(64 % CB == 0, "a wave must hold whole segment groups");
+    static_assert(kWaves >= 2, "waves 0 and 1 split the chain work");
 
     __shared__ St s_tot[kWaves][CB];
     __shared__ float s_totnw[kWaves][CB];
-    __shared__ St s_pre[kWaves][CB];
-    __shared__ float s_prenw[kWaves][CB];
     __shared__ St s_excl[CB];
+    __shared__ unsigned s_epoch;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -177,47 +199,33 @@ __global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
         }
     }
 
-    // Chain records and flags are only accessed with agent-scope relaxed
-    // atomics, which read and write at the device's coherence point: they
-    // need no cache write-back or invalidation (a release/acquire pair would
-    // write back and invalidate the whole L2 on every poll and publish).
-    // Order comes from waiting for the record stores to complete before the
-    // flag is stored, and on the reading side from reading the records only
-    // after the flag load has returned.
-    auto ld = [](const void *p) {
-        return __hip_atomic_load((unsigned *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The control block and the records are only accessed with agent-scope
+    // relaxed atomics, which read and write at the device's coherence point,
+    // so they need no cache write-back or invalidation.  A record word is
+    // valid on its own (its tag), so a publisher never waits for its stores.
+    using u64 = unsigned long long;
+    auto ld32 = [](const unsigned *p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto st = [](void *p, unsigned val) {
-        __hip_atomic_store((unsigned *)p, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    auto ld64 = [](const u64 *p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    // wait until a predecessor's flag reaches `atleast`; returns the flag
-    auto wait_flag = [&](const unsigned *f, unsigned atleast) -> unsigned {
-        unsigned val;
-        int polls = 0;
-        while ((val = ld(f)) < atleast) {
-            __builtin_amdgcn_s_sleep(4);
-            if (++polls > kSpinLimit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return atleast;
-            }
-        }
-        return val;
+    auto st64 = [](u64 *p, u64 val) {
+        __hip_atomic_store(p, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto publish = [&](int link, int slot, const St &s, unsigned flag) {
-        float *rec = recs + (size_t)link * 6 * CB + slot * 3 * CB;
-        st(rec + tid, __float_as_uint(s.a));
-        st(rec + CB + tid, __float_as_uint(s.b));
-        st(rec + 2 * CB + tid, __float_as_uint(s.p));
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the records have landed
-        __asm__ volatile("" ::: "memory");
-        if (tid == 0) st(flags + link, flag);
+    // record words of channel cl: link, slot 0 aggregate / 1 inclusive
+    auto word = [&](int link, int slot, int comp) {
+        return recs + ((size_t)link * 6 + slot * 3 + comp) * CB + cl;
     };
-    auto record = [&](int link, int slot) {
-        const float *rec = recs + (size_t)link * 6 * CB + slot * 3 * CB;
-        return St{__uint_as_float(ld(rec + tid)), __uint_as_float(ld(rec + CB + tid)),
-                  __uint_as_float(ld(rec + 2 * CB + tid))};
+    auto publish = [&](int link, int slot, const St &s, unsigned tag) {
+        const u64 hi = (u64)tag << 32;
+        st64(word(link, slot, 0), hi | __float_as_uint(s.a));
+        st64(word(link, slot, 1), hi | __float_as_uint(s.b));
+        st64(word(link, slot, 2), hi | __float_as_uint(s.p));
     };
+    // the epoch is read with the operands
+    unsigned epoch = 0;
+    if (tid == 0) epoch = ld32(&ctrl->epoch.n);
 
     // FULL: every row of the pass exists (uniform over the workgroup)
     auto pass = [&](auto full_tag) {
@@ -232,6 +240,8 @@ __global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
             if (full || i < n) fold(wk, wc, d.k[i], d.v[i]);
         const St sum = walk_state(wk, wc);
         const float nw = (float)n * wc;
+        if (tid == 0) s_epoch = epoch;
+        unsigned arrived = 0;  // thread 0 of a chain's last pass: its group's count
 
         // 2a. inclusive scan over the segment groups of this wave
         St inc = sum;
@@ -260,19 +270,28 @@ __global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
         }
         __syncthreads();
 
-        // 2b. prefixes of the wave totals from the empty state, the pass's
-        // aggregate, and the state entering the pass from the chain
-        if (tid < CB) {
-            St run{0.0f, 0.0f, kEmptyP};
-            float rnw = 0.0f;
+        // 2b. every lane: the prefix of the wave totals before its wave
+        // (from the empty state) and the pass's aggregate
+        St pre{0.0f, 0.0f, kEmptyP}, run = pre;
+        float prenw = 0.0f, rnw = 0.0f;
 #pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) {
-                s_pre[wv][tid] = run;
-                s_prenw[wv][tid] = rnw;
-                run = combine(run, s_totnw[wv][tid], s_tot[wv][tid]);
-                rnw += s_totnw[wv][tid];
+        for (int wv = 0; wv < kWaves; ++wv) {
+            if (wv == wave) {
+                pre = run;
+                prenw = rnw;
             }
-            const int link = q * units + unit;
+            run = combine(run, s_totnw[wv][cl], s_tot[wv][cl]);
+            rnw += s_totnw[wv][cl];
+        }
+
+        // 2c. the state entering the pass, from the chain.  Wave 1
+        // publishes the aggregate and wave 0 walks back: stores count with
+        // loads in a wave's memory counter, so a wave that waits for its
+        // polls would also wait for its own stores to complete.
+        const int link = q * units + unit;
+        const unsigned tag = s_epoch + 1u;
+        if (wave == 1 && lane < CB && q > 0 && q + 1 < nq) publish(link, 0, run, tag);
+        if (tid < CB) {
             St excl;
             if (q == 0) {
                 excl = St{0.0f, 0.0f, kEmptyP};
@@ -281,48 +300,73 @@ __global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
                     excl = St{sp[0], sp[C], sp[2 * (size_t)C]};
                 }
             } else {
-                if (q + 1 < nq) publish(link, 0, run, kAgg);
                 // walk back: aggregates until an inclusive state (pass 0
-                // publishes only its inclusive state, so the walk ends there)
+                // publishes only its inclusive state, so the walk ends
+                // there).  Every channel reads a predecessor's inclusive
+                // state, then its aggregate; while neither is complete, lane
+                // 0 alone polls its own two words (two loads per poll).
+                auto ok = [&](u64 x) { return (unsigned)(x >> 32) == tag; };
+                auto val = [](u64 x) { return __uint_as_float((unsigned)x); };
                 St acc{0.0f, 0.0f, kEmptyP};
                 float accnw = 0.0f;
-                for (int j = q - 1;; --j) {
+                int polls = 0;
+                auto give_up = [&]() {  // cannot happen: see kSpinLimit
+                    if (++polls <= kSpinLimit) return false;
+                    __hip_atomic_fetch_or(&ctrl->err.n, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                    return true;
+                };
+                excl = acc;
+                for (int j = q - 1;;) {
                     const int lj = j * units + unit;
-                    if (wait_flag(flags + lj, kAgg) >= kIncl || j == 0) {
-                        excl = combine(record(lj, 1), accnw, acc);
-                        break;
+                    {
+                        const u64 xa = ld64(word(lj, 1, 0)), xb = ld64(word(lj, 1, 1)),
+                                  xp = ld64(word(lj, 1, 2));
+                        if (__all(ok(xa) && ok(xb) && ok(xp))) {
+                            excl = combine(St{val(xa), val(xb), val(xp)}, accnw, acc);
+                            break;
+                        }
                     }
-                    acc = combine(record(lj, 0), accnw, acc);
-                    accnw += (float)kPass * wc;  // predecessors are whole passes
+                    if (j > 0) {
+                        const u64 xa = ld64(word(lj, 0, 0)), xb = ld64(word(lj, 0, 1)),
+                                  xp = ld64(word(lj, 0, 2));
+                        if (__all(ok(xa) && ok(xb) && ok(xp))) {
+                            acc = combine(St{val(xa), val(xb), val(xp)}, accnw, acc);
+                            accnw += (float)kPass * wc;  // predecessors are whole passes
+                            --j;
+                            continue;
+                        }
+                    }
+                    bool late = false;
+                    for (;;) {
+                        __builtin_amdgcn_s_sleep(2);
+                        int shown = 0;
+                        if (tid == 0)
+                            shown = ok(ld64(word(lj, 1, 2))) || (j > 0 && ok(ld64(word(lj, 0, 2))));
+                        if (__shfl(shown, 0, 64) || (late = give_up())) break;
+                    }
+                    if (late) break;
                 }
             }
             const St incl = combine(excl, rnw, run);
             if (q + 1 < nq) {
-                publish(link, 1, incl, kIncl);
-            } else {
-                if (state_out != nullptr && active) {
-                    float *sp = state_out + (size_t)b * 3 * C + c;
-                    sp[0] = incl.a;
-                    sp[C] = incl.b;
-                    sp[2 * (size_t)C] = incl.p;
-                }
-                // A workgroup publishes its inclusive state only after its
-                // walk, so once every flag of the chain is inclusive no walk
-                // reads them any more: only then clear them for the next
-                // launch (clearing one while a later walk may still pass it
-                // would strand that walk).
-                if (tid == 0) {
-                    for (int j = 0; j + 1 < nq; ++j) wait_flag(flags + j * units + unit, kIncl);
-                    for (int j = 0; j + 1 < nq; ++j) st(flags + j * units + unit, 0u);
-                }
+                publish(link, 1, incl, tag);
+            } else if (state_out != nullptr && active) {
+                float *sp = state_out + (size_t)b * 3 * C + c;
+                sp[0] = incl.a;
+                sp[C] = incl.b;
+                sp[2 * (size_t)C] = incl.p;
             }
             s_excl[tid] = excl;
+            // after the walk (see Ctrl); the count is only read at the end
+            if (tid == 0 && q > 0 && q + 1 == nq)
+                arrived = __hip_atomic_fetch_add(&ctrl->group[unit % kGroups].n, 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
 
         // 3. replay the segment from its carry-in state
-        Walk s = walk_from(combine(s_excl[cl], s_prenw[wave][cl] + excnw,
-                                   combine(s_pre[wave][cl], excnw, exc)));
+        Walk s = walk_from(combine(s_excl[cl], prenw + excnw, combine(pre, excnw, exc)));
         const auto ry = rsrc(y);
 #pragma unroll
         for (int i = 0; i < SEG; ++i) {
@@ -331,6 +375,25 @@ __global__ __launch_bounds__(NT) void rwkv4_chain_kernel(
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, yi), ry,
                                                       lane_off + i * row_bytes, 0, 0);
                 fold(s, wc, d.k[i], d.v[i]);
+            }
+        }
+
+        // the last arrival of a group counts at the total, and the last
+        // arrival there advances the epoch (tag 0 stays unused)
+        if (tid == 0 && q > 0 && q + 1 == nq) {
+            const int g = unit % kGroups;
+            if (arrived == (unsigned)((units - 1 - g) / kGroups)) {
+                __hip_atomic_store(&ctrl->group[g].n, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned t = __hip_atomic_fetch_add(&ctrl->total.n, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (t + 1 == (unsigned)min(units, kGroups)) {
+                    __hip_atomic_store(&ctrl->total.n, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned next = s_epoch + 1u == 0xffffffffu ? 0u : s_epoch + 1u;
+                    __hip_atomic_store(&ctrl->epoch.n, next, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
     };
@@ -364,27 +427,25 @@ hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
     constexpr int64_t kMaxLinks = 8192;
     const int64_t per_launch = std::max<int64_t>(1, std::min<int64_t>(passes, kMaxLinks / units));
     const bool windows = per_launch < passes;
-    // layout: flags (a fixed region, so the cleared flags of one launch are
-    // the cleared flags of the next whatever its shape), records, carry
+    // layout: control block, records, carry
     const int64_t links = per_launch * units;
-    const size_t flag_bytes = (size_t)kMaxLinks * 4 + 256;
-    const size_t rec_bytes = (size_t)links * 6 * CB * 4;
+    const size_t ctrl_bytes = (sizeof(Ctrl) + 255) / 256 * 256;
+    const size_t rec_bytes = (size_t)links * 6 * CB * 8;
     const size_t carry_bytes = windows ? (size_t)B * 3 * C * 4 : 0;
     char *ws = nullptr;
-    hipError_t e = stream_workspace(kWsRwkv4Chain, stream, flag_bytes + rec_bytes + carry_bytes,
+    hipError_t e = stream_workspace(kWsRwkv4Chain, stream, ctrl_bytes + rec_bytes + carry_bytes,
                                     (void **)&ws);
     if (e != hipSuccess) return e;
-    unsigned *flags = (unsigned *)ws;
-    unsigned *err = flags + kMaxLinks;
-    float *recs = (float *)(ws + flag_bytes);
-    float *carry = (float *)(ws + flag_bytes + rec_bytes);
+    Ctrl *ctrl = (Ctrl *)ws;
+    unsigned long long *recs = (unsigned long long *)(ws + ctrl_bytes);
+    float *carry = (float *)(ws + ctrl_bytes + rec_bytes);
     for (int64_t q0 = 0; q0 < passes; q0 += per_launch) {
         const int64_t nq = std::min(per_launch, passes - q0);
         const float *si = q0 == 0 ? state_in : carry;
         float *so = q0 + nq == passes ? state_out : carry;
         hipLaunchKernelGGL((rwkv4_chain_kernel<NT, CB, SEG>), dim3((unsigned)(nq * units)),
                            dim3(NT), 0, stream, T, (int)(q0 * kPass), (int)nq, C, k, v, w, u,
-                           si, so, y, recs, flags, err);
+                           si, so, y, recs, ctrl);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
