@@ -40,6 +40,11 @@ def rwkv4_check(d, state_in=None, H=1):
     si = None if state_in is None else to_dev(state_in)
     y, so = W.rwkv4_wkv_fwd(k, v, w, u, state_in=si, H=H)
     sync()
+    rwkv4_assert(d, y, so, state_in)
+    return y, so, None
+
+
+def rwkv4_assert(d, y, so, state_in=None):
     num_in = den_in = None
     if state_in is not None:
         num_in = state_in[:, 0].astype(np.float64) * np.exp(state_in[:, 2].astype(np.float64))
@@ -56,7 +61,6 @@ def rwkv4_check(d, state_in=None, H=1):
         vmax = np.maximum(vmax, np.abs(num_in) / np.maximum(den_in, 1e-300))
     assert np.max(np.abs(den - ref["den"]) / ref["den"]) <= RWKV4_TOL
     assert np.max(np.abs(num - ref["num"]) / (ref["den"] * vmax)) <= RWKV4_TOL
-    return y, so, ref
 
 
 def test_rwkv4_workload1():
@@ -82,6 +86,47 @@ def test_rwkv4_split_over_launches():
     # between them through the library's workspace
     print("rwkv4 B=4100 T=257 C=32 (two launches)", flush=True)
     rwkv4_check(S.rwkv4_inputs(4100, 257, 32, 11, k_sigma=2.0))
+
+
+def test_rwkv4_repeated_calls_take_fresh_records():
+    # the same four-pass shape with new data on every call: the chain records
+    # an earlier call left in the workspace must never be taken for this
+    # call's (they would give the earlier call's carries)
+    for seed in (21, 22, 23):
+        print(f"rwkv4 B=2 T=1024 C=64 seed {seed}", flush=True)
+        rwkv4_check(S.rwkv4_inputs(2, 1024, 64, seed, k_sigma=2.0))
+
+
+def capture(fn):
+    """fn() captured into a HIP graph on a side stream, after one eager call
+    on that stream (which allocates the stream's workspace)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    return g
+
+
+def test_rwkv4_graph_replays():
+    # every state a chain keeps between launches lives on the device, so
+    # replays of a captured launch take fresh records each time
+    print("rwkv4 graph B=2 T=1024 C=64", flush=True)
+    ds = [S.rwkv4_inputs(2, 1024, 64, 31 + i, k_sigma=2.0) for i in range(3)]
+    k, v, w, u = (to_dev(ds[0][n]) for n in ("k", "v", "w", "u"))
+    y = torch.empty_like(k)
+    so = torch.empty((2, 3, 64), device="cuda")
+    g = capture(lambda: W.rwkv4_wkv_fwd(k, v, w, u, y=y, state_out=so))
+    for d in ds + ds:
+        for t, n in ((k, "k"), (v, "v"), (w, "w"), (u, "u")):
+            t.copy_(to_dev(d[n]))
+        sync()
+        g.replay()
+        sync()
+        rwkv4_assert(d, y, so)
 
 
 def test_rwkv4_large_keys():
@@ -174,6 +219,29 @@ def test_chunked_more_heads_than_cus(per_token, B, T, H):
     o2, s2 = run_chunked(g, per_token)  # the handoff flags were left cleared
     sync()
     assert torch.equal(o, o2) and torch.equal(so, s2)
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_chunked_graph_replays(per_token):
+    # 300 heads: the segments of the extra heads hand their states on through
+    # the stream's workspace, whose flags every launch leaves cleared
+    print(f"chunked {'finch' if per_token else 'eagle'} graph B=1 T=300 H=300", flush=True)
+    ds = [matrix_case(1, 300, 300, 500 + i, per_token) for i in range(2)]
+    g0 = matrix_inputs_dev(ds[0])
+    o = torch.empty_like(g0["r"])
+    so = torch.empty_like(g0["s0"])
+    fn = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    graph = capture(lambda: fn(g0["r"], g0["k"], g0["v"], g0["x"], g0["u"], state_in=g0["s0"],
+                               state_out=so, o=o))
+    for d in ds + ds:
+        for n, t in matrix_inputs_dev(d).items():
+            g0[n].copy_(t)
+        sync()
+        graph.replay()
+        sync()
+        o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
+        assert_matrix_close(bf16_host(o), o_ref, "o")
+        assert_matrix_close(f64_host(so), s_ref, "state")
 
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
