@@ -95,11 +95,16 @@ const char *rwkv_wkv_strerror(int status);
  *
  * Workspace: the 256-token passes of a sequence's channel block run in
  * separate workgroups that hand the state on through a device workspace
- * (about 0.8 KB per workgroup of a launch, at most 8192 workgroups per
- * launch).  It is allocated on the first call for each (device, stream),
- * grown when a call needs more (that call then synchronises the stream), and
- * kept until the process ends.  Calls on one stream share it safely; the
- * first call on a stream must not be made during graph capture.
+ * (1.5 KB per workgroup of a launch, at most 8192 workgroups per launch,
+ * plus 8.5 KB of counters).  It is allocated on the first call for each
+ * (device, stream), grown when a call needs more (that call then
+ * synchronises the stream), and kept until the process ends.  Calls on one
+ * stream share it safely, also as replays of a captured graph (the kernels
+ * keep every piece of their bookkeeping on the device); the first call on a
+ * stream must not be made during graph capture.  Outputs of sequences longer
+ * than one pass may differ from run to run in the last bits: how far back a
+ * pass finds a finished predecessor depends on timing, and so does the order
+ * in which the carried state is combined.
  */
 int rwkv4_wkv_fwd(int B, int T, int H, int N,
                   const float *k, const float *v,
