@@ -7,7 +7,8 @@ bf16 r/k/v, fp32 per-token decay logits and fp32 state, inputs resident in
 HBM.  The JSON line reports tokens*channels/s of the timed steps, the
 roofline of the chunked kernel (algorithmic bytes / average kernel time vs
 8 TB/s), the fp64 oracle timed on the host cores, and the other operators on
-their own workloads under "paths" (RWKV-4 scan, Eagle chunked, Finch decode).
+their own workloads under "paths" (RWKV-4 scan, Eagle chunked, and the
+single-token decode steps of Finch, Eagle and RWKV-4).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-paths]
                        [--skip-cpu] [--only PATH]
@@ -40,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
-    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "calib"],
+    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
+                                       "rwkv4_decode", "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -137,6 +139,15 @@ def decode_bytes_per_step(B, H, N=64):
     return 2 * B * H * N * N * 4 + tok * (2 * 3 + 4 + 2) + H * N * 4
 
 
+def eagle_decode_bytes_per_step(B, H, N=64):
+    tok = B * H * N
+    return 2 * B * H * N * N * 4 + tok * (2 * 3 + 2) + 2 * H * N * 4
+
+
+def rwkv4_decode_bytes_per_step(B, C):
+    return B * C * 12 + 2 * B * 3 * C * 4 + 2 * C * 4
+
+
 def chunk_mfma_flops(B, T, H, N=64, L=64):
     # per chunk and head, as executed: A^T (lower-triangular 16x16 tiles,
     # K = N), A V (causal K-blocks), Q S, Kh_hi V + Kh_lo V, all bf16 MFMA
@@ -192,23 +203,46 @@ def run_rwkv4(torch, W, S, H2D, args, flush_buf):
     return res
 
 
-def run_decode(torch, W, S, H2D, args):
-    spec = S.WORKLOADS[5]
+def run_decode(torch, W, S, H2D, args, cfg=5):
+    """Back-to-back single-token steps: Finch (workload 5) over distinct
+    per-step inputs; Eagle (6) and RWKV-4 (7) cycle through 64 distinct
+    steps' inputs (the bytes each step moves are the same)."""
+    spec = S.WORKLOADS[cfg]
     steps = args.decode_steps
-    d = S.workload(5, steps=steps)
+    distinct = steps if cfg == 5 else min(steps, 64)
+    d = S.workload(cfg, steps=distinct)
     g = H2D(d)
-    st = g["s0"].clone()
-    o = torch.empty_like(g["r"])
-    views = [(g["r"][s].unsqueeze(1), g["k"][s].unsqueeze(1), g["v"][s].unsqueeze(1),
-              g["x"][s].unsqueeze(1), o[s].unsqueeze(1)) for s in range(steps)]
+    if cfg == 7:
+        st = torch.zeros((spec["B"], 3, spec["C"]), device="cuda")
+        st[:, 2] = -1e38
+        s0 = st.clone()
+        y = torch.empty_like(g["k"])
+        views = [(g["k"][s].unsqueeze(1), g["v"][s].unsqueeze(1), y[s].unsqueeze(1))
+                 for s in range(distinct)]
 
-    def one(s):
-        r, k, v, x, os_ = views[s]
-        W.rwkv6_wkv_step(r, k, v, x, g["u"], st, o=os_)
+        def one(s):
+            k, v, ys = views[s % distinct]
+            W.rwkv4_wkv_step(k, v, g["w"], g["u"], st, y=ys)
+        nbytes = rwkv4_decode_bytes_per_step(spec["B"], spec["C"])
+    else:
+        st = g["s0"].clone()
+        s0 = g["s0"]
+        o = torch.empty_like(g["r"])
+        per_token = cfg == 5
+        views = [(g["r"][s].unsqueeze(1), g["k"][s].unsqueeze(1), g["v"][s].unsqueeze(1),
+                  g["x"][s].unsqueeze(1) if per_token else g["x"], o[s].unsqueeze(1))
+                 for s in range(distinct)]
+        step = W.rwkv6_wkv_step if per_token else W.rwkv5_wkv_step
+
+        def one(s):
+            r, k, v, x, os_ = views[s % distinct]
+            step(r, k, v, x, g["u"], st, o=os_)
+        nbytes = (decode_bytes_per_step(spec["B"], spec["H"]) if per_token
+                  else eagle_decode_bytes_per_step(spec["B"], spec["H"]))
 
     for s in range(min(8, steps)):  # warm-up on a scratch copy of the state
         one(s)
-    st.copy_(g["s0"])
+    st.copy_(s0)
     torch.cuda.synchronize()
     timer = Timer(torch)
     t0 = time.perf_counter()
@@ -224,8 +258,7 @@ def run_decode(torch, W, S, H2D, args):
     total_ms = start.elapsed_time(end)
     ms = timer.ms()
     per = sum(ms) / len(ms)
-    nbytes = decode_bytes_per_step(spec["B"], spec["H"])
-    return {"workload": S.WORKLOAD_NAMES[5], "steps": steps,
+    return {"workload": S.WORKLOAD_NAMES[cfg], "steps": steps, "distinct_steps": distinct,
             "steps_per_s": steps / (total_ms / 1e3), "interval_ms": total_ms,
             "kernel_ms_mean": per, "wall_s": wall,
             "algorithmic_bytes_per_step": nbytes,
@@ -261,10 +294,16 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
     "finch_fwd": ("wkv_chunk_kernel<true,", "wkv_chunk.hip", lambda: finch_bytes(8, 4096, 40)),
     "eagle_fwd": ("wkv_chunk_kernel<false,", "wkv_chunk.hip", lambda: eagle_bytes(8, 4096, 32)),
     "rwkv4_fwd": ("rwkv4_chain_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
-    "finch_decode": ("wkv6_step_kernel", "wkv_step.hip", lambda: decode_bytes_per_step(256, 64)),
+    "finch_decode": ("wkv_step_kernel<true>", "wkv_step.hip",
+                     lambda: decode_bytes_per_step(256, 64)),
+    "eagle_decode": ("wkv_step_kernel<false>", "wkv_step.hip",
+                     lambda: eagle_decode_bytes_per_step(256, 64)),
+    "rwkv4_decode": ("rwkv4_step_kernel", "rwkv4_step.hip",
+                     lambda: rwkv4_decode_bytes_per_step(256, 4096)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
-            "finch_decode": "decode"}
+            "finch_decode": "decode", "eagle_decode": "eagle_decode",
+            "rwkv4_decode": "rwkv4_decode"}
 
 
 def _pmc_mean(csv_path, fragment, counter):
@@ -367,6 +406,12 @@ def main():
     if not args.skip_paths and only in (None, "decode"):
         print("finch decode ...", file=sys.stderr, flush=True)
         paths["finch_decode"] = run_decode(torch, W, S, H2D, args)
+    if not args.skip_paths and only in (None, "eagle_decode"):
+        print("eagle decode ...", file=sys.stderr, flush=True)
+        paths["eagle_decode"] = run_decode(torch, W, S, H2D, args, cfg=6)
+    if not args.skip_paths and only in (None, "rwkv4_decode"):
+        print("rwkv4 decode ...", file=sys.stderr, flush=True)
+        paths["rwkv4_decode"] = run_decode(torch, W, S, H2D, args, cfg=7)
     torch.cuda.synchronize()
 
     if "finch_fwd" not in paths:

@@ -113,6 +113,27 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N,
                   float *y, void *stream);
 
 /*
+ * RWKV-4 WKV, serial (RNN) mode (RWKV paper summary, section "RNN-like
+ * sequential decoding": an output needs only the latest state).  Tokens are
+ * applied one at a time; decoding calls it with T == 1.  Arguments as
+ * rwkv4_wkv_fwd, except:
+ *
+ *   state      [B][3][C] fp32 (a, b, p), read as the history and overwritten
+ *              with the state after token T (required, never NULL; it must
+ *              not overlap any other argument).
+ *
+ * Within a call the running exponent p is recomputed from the key that last
+ * set it and the steps since, so its rounding does not build up over the
+ * call's tokens; the stored p is rounded once per call.  Splitting a
+ * sequence therefore changes results in the last bits only.  B * C must be
+ * at most 2^38, else RWKV_E_UNSUPPORTED.
+ */
+int rwkv4_wkv_step(int B, int T, int H, int N,
+                   const float *k, const float *v,
+                   const float *w, const float *u,
+                   float *state, float *y, void *stream);
+
+/*
  * Eagle (RWKV-5) WKV forward, time-parallel (chunked) mode.  N must be 64.
  *
  *   r, k, v    [B][T][H][N] bf16 receptance, key, value
@@ -166,6 +187,16 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N,
  * bit-identical outputs and state.
  */
 int rwkv6_wkv_step(int B, int T, int H, int N,
+                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                   const float *x, const float *u,
+                   float *state, rwkv_bf16 *o, void *stream);
+
+/*
+ * Eagle (RWKV-5) WKV, serial (RNN) mode.  As rwkv6_wkv_step, except that x
+ * is the static decay logit omega, [H][N] fp32, shared by all tokens and
+ * sequences (as in rwkv5_wkv_fwd).
+ */
+int rwkv5_wkv_step(int B, int T, int H, int N,
                    const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                    const float *x, const float *u,
                    float *state, rwkv_bf16 *o, void *stream);

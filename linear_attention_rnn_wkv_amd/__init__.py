@@ -8,8 +8,10 @@ other implementation to fall back to, and calling any operator without the
 built library raises.
 
 Operators (names as in the C ABI):
-  rwkv4_wkv_fwd   RWKV-4 per-channel WKV, fp32
+  rwkv4_wkv_fwd   RWKV-4 per-channel WKV, fp32, time-parallel
+  rwkv4_wkv_step  RWKV-4 per-channel WKV, fp32, serial (decode)
   rwkv5_wkv_fwd   Eagle matrix-state WKV, time-parallel (chunked)
+  rwkv5_wkv_step  Eagle matrix-state WKV, serial (decode)
   rwkv6_wkv_fwd   Finch matrix-state WKV, time-parallel (chunked)
   rwkv6_wkv_step  Finch matrix-state WKV, serial (decode)
 """
@@ -23,8 +25,8 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librwkv_wkv.
 RWKV_OK = 0
 STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPORTED",
           -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP"}
-EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv5_wkv_fwd", "rwkv6_wkv_fwd",
-           "rwkv6_wkv_step")
+EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
+           "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step")
 
 _lib = None
 
@@ -52,8 +54,12 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P]
-        L.rwkv6_wkv_step.restype = I
-        L.rwkv6_wkv_step.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
+        L.rwkv4_wkv_step.restype = I
+        L.rwkv4_wkv_step.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+        for name in ("rwkv5_wkv_step", "rwkv6_wkv_step"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -115,6 +121,28 @@ def rwkv4_wkv_fwd(k, v, w, u, state_in=None, state_out=None, y=None, H=1,
     return y, state_out
 
 
+def rwkv4_wkv_step(k, v, w, u, state, y=None, H=1, stream=None):
+    """RWKV-4 WKV, serial: k, v: [B, T, C] fp32 (T = 1 to decode); w, u: [C];
+    state: [B, 3, C] fp32 (a, b, p), updated in place.  Returns y."""
+    import torch
+    B, T, C = k.shape
+    if C % H:
+        raise ValueError("C must be divisible by H")
+    f32 = torch.float32
+    _expect("k", k, (B, T, C), f32)
+    _expect("v", v, (B, T, C), f32)
+    _expect("w", w, (C,), f32)
+    _expect("u", u, (C,), f32)
+    _expect("state", state, (B, 3, C), f32)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=f32, device=k.device)
+    _expect("y", y, (B, T, C), f32)
+    _check("rwkv4_wkv_step", lib().rwkv4_wkv_step(
+        B, T, H, C // H, _ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(state), _ptr(y),
+        _stream(stream)))
+    return y
+
+
 def _matrix_args(r, k, v, x, u, per_token):
     import torch
     B, T, H, N = r.shape
@@ -161,17 +189,26 @@ def rwkv6_wkv_fwd(r, k, v, x, u, state_in=None, state_out=None, o=None,
                        return_state, stream)
 
 
-def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):
-    """Finch WKV, serial: r, k, v: [B, T, H, 64] bf16 (T = 1 to decode);
-    x: [B, T, H, 64] fp32; u: [H, 64]; state: [B, H, 64, 64] fp32, updated in
-    place.  Returns o."""
+def _matrix_step(name, per_token, r, k, v, x, u, state, o, stream):
     import torch
-    B, T, H, N = _matrix_args(r, k, v, x, u, True)
+    B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
     _expect("state", state, (B, H, N, N), torch.float32)
     if o is None:
         o = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=r.device)
     _expect("o", o, (B, T, H, N), torch.bfloat16)
-    _check("rwkv6_wkv_step", lib().rwkv6_wkv_step(
+    _check(name, getattr(lib(), name)(
         B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state), _ptr(o),
         _stream(stream)))
     return o
+
+
+def rwkv5_wkv_step(r, k, v, x, u, state, o=None, stream=None):
+    """Eagle WKV, serial: as rwkv6_wkv_step but x (decay logit omega): [H, 64]."""
+    return _matrix_step("rwkv5_wkv_step", False, r, k, v, x, u, state, o, stream)
+
+
+def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):
+    """Finch WKV, serial: r, k, v: [B, T, H, 64] bf16 (T = 1 to decode);
+    x: [B, T, H, 64] fp32; u: [H, 64]; state: [B, H, 64, 64] fp32, updated in
+    place.  Returns o."""
+    return _matrix_step("rwkv6_wkv_step", True, r, k, v, x, u, state, o, stream)

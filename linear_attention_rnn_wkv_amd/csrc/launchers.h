@@ -22,11 +22,16 @@ hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,
                         float *state_out, float *y, hipStream_t stream);
 
-// Finch serial (RNN-mode) path, N = 64, state updated in place.
-hipError_t launch_wkv6_step(int B, int T, int H, const uint16_t *r,
-                            const uint16_t *k, const uint16_t *v, const float *x,
-                            const float *u, float *state, uint16_t *o,
-                            hipStream_t stream);
+// RWKV-4 serial (RNN-mode) path, (a, b, p) state updated in place.
+hipError_t launch_rwkv4_step(int B, int T, int C, const float *k, const float *v,
+                             const float *w, const float *u, float *state, float *y,
+                             hipStream_t stream);
+
+// Eagle (per_token_decay = false) / Finch serial (RNN-mode) path, N = 64,
+// state updated in place.
+hipError_t launch_wkv_step(bool per_token_decay, int B, int T, int H, const uint16_t *r,
+                           const uint16_t *k, const uint16_t *v, const float *x,
+                           const float *u, float *state, uint16_t *o, hipStream_t stream);
 
 // Eagle / Finch chunked (time-parallel) path, N = 64.
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,

@@ -106,6 +106,17 @@ int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                                               state_in, state_out, o, s));
 }
 
+int matrix_step(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
+                const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
+                float *state, rwkv_bf16 *o, void *stream) {
+    const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
+    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state, state, true, o);
+    if (st != RWKV_OK) return st;
+    if (T == 0) return RWKV_OK;
+    return hip_status(wkv::launch_wkv_step(per_token, B, T, H, r, k, v, x, u, state, o,
+                                           (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +171,32 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
         wkv::launch_rwkv4(B, T, (int)C, k, v, w, u, state_in, state_out, y, s));
 }
 
+int rwkv4_wkv_step(int B, int T, int H, int N, const float *k, const float *v,
+                   const float *w, const float *u, float *state, float *y, void *stream) {
+    if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
+    const int64_t C = checked_mul({H, N});
+    const int64_t tok = checked_mul({B, T, H, N});
+    const int64_t st = checked_mul({B, 3, H, N});
+    if (C < 0 || tok < 0 || st < 0 || C > INT32_MAX / 2) return RWKV_E_DIM;
+    // one thread per (sequence, channel)
+    if ((int64_t)B * C > ((int64_t)1 << 38)) return RWKV_E_UNSUPPORTED;
+    if (state == nullptr) return RWKV_E_NULL;
+    if (T > 0 && (k == nullptr || v == nullptr || w == nullptr || u == nullptr ||
+                  y == nullptr))
+        return RWKV_E_NULL;
+    for (const void *p : {(const void *)k, (const void *)v, (const void *)w,
+                          (const void *)u, (const void *)state, (const void *)y})
+        if (p != nullptr && !aligned(p, 4)) return RWKV_E_ALIGN;
+    const Span sk{k, tok * 4}, sv{v, tok * 4}, sw{w, C * 4}, su{u, C * 4}, ss{state, st * 4},
+        sy{y, tok * 4};
+    if (T == 0) return RWKV_OK;
+    // state is read and written in place: it must not overlap the inputs or y
+    const int chk = check_outputs({sy, ss}, {sk, sv, sw, su});
+    if (chk != RWKV_OK) return chk;
+    return hip_status(wkv::launch_rwkv4_step(B, T, (int)C, k, v, w, u, state, y,
+                                             (hipStream_t)stream));
+}
+
 int rwkv5_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                   const rwkv_bf16 *v, const float *x, const float *u,
                   const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
@@ -172,15 +209,16 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
     return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
 }
 
+int rwkv5_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                   const rwkv_bf16 *v, const float *x, const float *u, float *state,
+                   rwkv_bf16 *o, void *stream) {
+    return matrix_step(false, B, T, H, N, r, k, v, x, u, state, o, stream);
+}
+
 int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                    const rwkv_bf16 *v, const float *x, const float *u, float *state,
                    rwkv_bf16 *o, void *stream) {
-    const int64_t x_elems = checked_mul({B, T, H, N});
-    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state, state, true, o);
-    if (st != RWKV_OK) return st;
-    if (T == 0) return RWKV_OK;
-    return hip_status(
-        wkv::launch_wkv6_step(B, T, H, r, k, v, x, u, state, o, (hipStream_t)stream));
+    return matrix_step(true, B, T, H, N, r, k, v, x, u, state, o, stream);
 }
 
 }  // extern "C"

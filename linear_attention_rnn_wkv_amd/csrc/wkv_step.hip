@@ -1,10 +1,13 @@
-// wkv_step.hip -- Finch (RWKV-6) WKV in serial (RNN) mode on gfx950.
+// wkv_step.hip -- Eagle (RWKV-5) and Finch (RWKV-6) WKV in serial (RNN) mode
+// on gfx950.
 //
 // Operation, per head (RWKV-5/6 summary, blob.wenxiaobai.com, 4.1.2 "Eagle
 // time mixing" and 4.2.2 "Finch time mixing"; RWKV paper summary, section
 // "RNN-like sequential decoding"):
 //   o_t[j] = sum_i r_t[i] S[i][j] + (sum_i r_t[i] u[i] k_t[i]) v_t[j]
 //   S[i][j] <- w_t[i] S[i][j] + k_t[i] v_t[j],   w_t = exp(-exp(x_t))
+// Finch reads a decay logit x_t per token; Eagle's x is one per channel of a
+// head, shared by every token and sequence (so its decay is computed once).
 //
 // One wave64 owns one (sequence, head): its 64x64 fp32 state (16 KiB) is
 // loaded once into registers, every token of the call is applied to it,
@@ -31,7 +34,8 @@ __device__ __forceinline__ float wave_sum(float s) {
     return s;
 }
 
-__global__ __launch_bounds__(256) void wkv6_step_kernel(
+template <bool PT>
+__global__ __launch_bounds__(256) void wkv_step_kernel(
     int BH, int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x, const float *__restrict__ u,
     float *state, uint16_t *__restrict__ o) {
@@ -49,14 +53,14 @@ __global__ __launch_bounds__(256) void wkv6_step_kernel(
     for (int m = 0; m < 16; ++m) S[m] = *(const f32x4 *)(sp + m * 4 * kN);
 
     const float uu = u[h * kN + lane];
+    const float w_head = PT ? 0.0f : exp_fast(-exp_fast(x[h * kN + lane]));
     for (int t = 0; t < T; ++t) {
         const size_t base = (((size_t)b * T + t) * H + h) * kN;
         const float ri = bf16_to_f32(r[base + lane]);
         const float ki = bf16_to_f32(k[base + lane]);
-        const float xi = x[base + lane];
         const u32x2 vp = *(const u32x2 *)(v + base + 4 * c4);
         const float vj[4] = {bf16_lo(vp.x), bf16_hi(vp.x), bf16_lo(vp.y), bf16_hi(vp.y)};
-        const float wi = exp_fast(-exp_fast(xi));
+        const float wi = PT ? exp_fast(-exp_fast(x[base + lane])) : w_head;
         const float bonus = wave_sum(ri * uu * ki);
 
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -91,13 +95,17 @@ __global__ __launch_bounds__(256) void wkv6_step_kernel(
 
 }  // namespace
 
-hipError_t launch_wkv6_step(int B, int T, int H, const uint16_t *r, const uint16_t *k,
-                            const uint16_t *v, const float *x, const float *u,
-                            float *state, uint16_t *o, hipStream_t stream) {
+hipError_t launch_wkv_step(bool per_token_decay, int B, int T, int H, const uint16_t *r,
+                           const uint16_t *k, const uint16_t *v, const float *x,
+                           const float *u, float *state, uint16_t *o, hipStream_t stream) {
     const int64_t BH = (int64_t)B * H;
     const int64_t blocks = (BH + kHeadsPerBlock - 1) / kHeadsPerBlock;
-    hipLaunchKernelGGL(wkv6_step_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (int)BH, T, H, r, k, v, x, u, state, o);
+    if (per_token_decay)
+        hipLaunchKernelGGL(wkv_step_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (int)BH, T, H, r, k, v, x, u, state, o);
+    else
+        hipLaunchKernelGGL(wkv_step_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                           stream, (int)BH, T, H, r, k, v, x, u, state, o);
     return hipGetLastError();
 }
 

@@ -69,11 +69,18 @@ def matrix(L, fn, B=2, T=8, H=2, N=64, r=1, k=2, v=3, x=4, u=5, si=6, so=7, o=8,
                           a["so"], a["o"], None)
 
 
-def step(L, B=2, T=1, H=2, N=64, r=1, k=2, v=3, x=4, u=5, s=6, o=7, **mis):
+def step(L, B=2, T=1, H=2, N=64, r=1, k=2, v=3, x=4, u=5, s=6, o=7, fn="rwkv6_wkv_step",
+         **mis):
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
          for n, i in dict(r=r, k=k, v=v, x=x, u=u, s=s, o=o).items()}
-    return L.rwkv6_wkv_step(B, T, H, N, a["r"], a["k"], a["v"], a["x"], a["u"], a["s"],
-                            a["o"], None)
+    return getattr(L, fn)(B, T, H, N, a["r"], a["k"], a["v"], a["x"], a["u"], a["s"],
+                          a["o"], None)
+
+
+def rwkv4_step(L, B=2, T=1, H=1, N=16, k=1, v=2, w=3, u=4, s=5, y=6, **mis):
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
+         for n, i in dict(k=k, v=v, w=w, u=u, s=s, y=y).items()}
+    return L.rwkv4_wkv_step(B, T, H, N, a["k"], a["v"], a["w"], a["u"], a["s"], a["y"], None)
 
 
 @pytest.mark.parametrize("dims", [(0, 8, 1, 16), (2, -1, 1, 16), (2, 8, 0, 16),
@@ -161,13 +168,60 @@ def test_matrix_aliasing(L, fn):
     assert matrix(L, fn, so=8) == E_ALIAS   # state_out == o
 
 
-def test_step_requires_state(L):
-    assert step(L, s=None) == E_NULL
+STEPS = ["rwkv5_wkv_step", "rwkv6_wkv_step"]
 
 
-def test_step_rejects_output_on_state(L):
-    assert step(L, o=6) == E_ALIAS
+@pytest.mark.parametrize("fn", STEPS)
+def test_step_requires_state(L, fn):
+    assert step(L, s=None, fn=fn) == E_NULL
 
 
-def test_step_head_size(L):
-    assert step(L, N=16) == E_UNSUP
+@pytest.mark.parametrize("fn", STEPS)
+def test_step_rejects_output_on_state(L, fn):
+    assert step(L, o=6, fn=fn) == E_ALIAS
+
+
+@pytest.mark.parametrize("fn", STEPS)
+def test_step_head_size(L, fn):
+    assert step(L, N=16, fn=fn) == E_UNSUP
+
+
+@pytest.mark.parametrize("fn", STEPS)
+@pytest.mark.parametrize("missing", ["r", "k", "v", "x", "u", "o"])
+def test_step_null(L, fn, missing):
+    assert step(L, fn=fn, **{missing: None}) == E_NULL
+
+
+def test_rwkv4_step_requires_state(L):
+    assert rwkv4_step(L, s=None) == E_NULL
+
+
+@pytest.mark.parametrize("missing", ["k", "v", "w", "u", "y"])
+def test_rwkv4_step_null(L, missing):
+    assert rwkv4_step(L, **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("dims", [(0, 1, 1, 16), (2, -1, 1, 16), (2, 1, 0, 16)])
+def test_rwkv4_step_bad_dims(L, dims):
+    B, T, H, N = dims
+    assert rwkv4_step(L, B=B, T=T, H=H, N=N) == E_DIM
+
+
+def test_rwkv4_step_aliasing(L):
+    assert rwkv4_step(L, y=5) == E_ALIAS   # y on the state
+    assert rwkv4_step(L, s=1) == E_ALIAS   # state on k
+    assert rwkv4_step(L, y=2) == E_ALIAS   # y on v
+
+
+@pytest.mark.parametrize("which", ["k", "s", "y"])
+def test_rwkv4_step_misaligned(L, which):
+    kw = dict(k=1, v=2, w=3, u=4, s=5, y=6)
+    a = {n: addr(i, 2 if n == which else 0) for n, i in kw.items()}
+    st = L.rwkv4_wkv_step(2, 1, 1, 16, a["k"], a["v"], a["w"], a["u"], a["s"], a["y"], None)
+    assert st == E_ALIGN
+
+
+def test_rwkv4_step_size_limit(L):
+    # one thread per (sequence, channel): B * C up to 2^38
+    # (the state, 3 * B * C floats, stays within the per-tensor element limit)
+    assert rwkv4_step(L, B=1 << 20, T=1, H=286102, N=1) == E_UNSUP

@@ -352,17 +352,19 @@ def test_chunked_t0():
 # ---------------------------------------------------------------------------
 # Finch, serial mode
 
-def run_step(g, state):
-    return W.rwkv6_wkv_step(g["r"], g["k"], g["v"], g["x"], g["u"], state)
+def run_step(g, state, per_token=True):
+    fn = W.rwkv6_wkv_step if per_token else W.rwkv5_wkv_step
+    return fn(g["r"], g["k"], g["v"], g["x"], g["u"], state)
 
 
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 5, 3), (1, 64, 1), (3, 130, 2)])
-def test_step_vs_oracle(B, T, H):
-    print(f"step B={B} T={T} H={H}", flush=True)
-    d = matrix_case(B, T, H, 300 + T, True)
+def test_step_vs_oracle(per_token, B, T, H):
+    print(f"step {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    d = matrix_case(B, T, H, 300 + T, per_token)
     g = matrix_inputs_dev(d)
     st = g["s0"].clone()
-    o = run_step(g, st)
+    o = run_step(g, st, per_token)
     sync()
     o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
     assert_matrix_close(bf16_host(o), o_ref, "o")
@@ -370,33 +372,96 @@ def test_step_vs_oracle(B, T, H):
     assert rms < 1e-5 and mx < 1e-4, (rms, mx)  # the serial state is fp32-accurate
 
 
-def test_step_split_anywhere_is_bitwise():
-    d = matrix_case(2, 37, 2, 16, True)
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_step_split_anywhere_is_bitwise(per_token):
+    d = matrix_case(2, 37, 2, 16, per_token)
     g = matrix_inputs_dev(d)
     st = g["s0"].clone()
-    o = run_step(g, st)
+    o = run_step(g, st, per_token)
+    timed = ("r", "k", "v", "x") if per_token else ("r", "k", "v")
     for cuts in ([1], [17], [5, 6, 30]):
         s2 = g["s0"].clone()
         outs = []
         edges = [0] + cuts + [37]
         for a, b in zip(edges[:-1], edges[1:]):
-            part = {n: (g[n][:, a:b].contiguous() if n in ("r", "k", "v", "x") else g[n])
-                    for n in g}
-            outs.append(run_step(part, s2))
+            part = {n: (g[n][:, a:b].contiguous() if n in timed else g[n]) for n in g}
+            outs.append(run_step(part, s2, per_token))
         sync()
         assert torch.equal(torch.cat(outs, 1), o) and torch.equal(s2, st)
 
 
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 @pytest.mark.parametrize("T", [64, 200])
-def test_step_and_chunked_agree(T):
-    d = matrix_case(2, T, 3, 17 + T, True)
+def test_step_and_chunked_agree(per_token, T):
+    d = matrix_case(2, T, 3, 17 + T, per_token)
     g = matrix_inputs_dev(d)
-    o_c, s_c = run_chunked(g, True)
+    o_c, s_c = run_chunked(g, per_token)
     st = g["s0"].clone()
-    o_s = run_step(g, st)
+    o_s = run_step(g, st, per_token)
     sync()
     assert_matrix_close(bf16_host(o_c), bf16_host(o_s), "chunked vs step o")
     assert_matrix_close(f64_host(s_c), f64_host(st), "chunked vs step state")
+
+
+# ---------------------------------------------------------------------------
+# RWKV-4, serial
+
+def empty_rwkv4_state(B, C):
+    st = torch.zeros((B, 3, C), device="cuda")
+    st[:, 2] = -1e38
+    return st
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 5, 33), (1, 64, 64), (3, 130, 17),
+                                   (2, 1000, 96)])
+def test_rwkv4_step_vs_oracle(B, T, C):
+    # the first half from the empty history, the rest from the state it left
+    print(f"rwkv4 step B={B} T={T} C={C}", flush=True)
+    d = S.rwkv4_inputs(B, T, C, 600 + T + C, k_sigma=2.0)
+    w, u = to_dev(d["w"]), to_dev(d["u"])
+    st = empty_rwkv4_state(B, C)
+    t1 = T // 2
+    part = lambda a, b: {n: (d[n][:, a:b] if n in "kv" else d[n]) for n in d}
+    if t1 > 0:
+        head = part(0, t1)
+        y1 = W.rwkv4_wkv_step(to_dev(head["k"]), to_dev(head["v"]), w, u, st)
+        sync()
+        rwkv4_assert(head, y1, st)
+    mid = st.cpu().numpy()
+    tail = part(t1, T)
+    y2 = W.rwkv4_wkv_step(to_dev(tail["k"]), to_dev(tail["v"]), w, u, st)
+    sync()
+    rwkv4_assert(tail, y2, st, state_in=mid if t1 > 0 else None)
+
+
+def test_rwkv4_long_decode():
+    """1024 single-token steps on 8 sequences x 4096 channels: the stored
+    exponent is rounded once per step, and the state still meets the
+    tolerance against the oracle."""
+    print("rwkv4 decode B=8 C=4096 steps=1024", flush=True)
+    d = S.rwkv4_inputs(1024, 8, 4096, 71, k_sigma=2.0)  # [steps, B, C]
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    st = empty_rwkv4_state(8, 4096)
+    y = torch.empty_like(k)
+    for s in range(1024):
+        W.rwkv4_wkv_step(k[s].unsqueeze(1), v[s].unsqueeze(1), w, u, st, y=y[s].unsqueeze(1))
+    sync()
+    seq = {"k": np.ascontiguousarray(d["k"].transpose(1, 0, 2)),
+           "v": np.ascontiguousarray(d["v"].transpose(1, 0, 2)), "w": d["w"], "u": d["u"]}
+    rwkv4_assert(seq, y.transpose(0, 1), st)
+
+
+def test_rwkv4_step_and_fwd_agree():
+    d = S.rwkv4_inputs(3, 700, 64, 23, k_sigma=2.0)
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    y_f, s_f = W.rwkv4_wkv_fwd(k, v, w, u)
+    st = empty_rwkv4_state(3, 64)
+    y_s = W.rwkv4_wkv_step(k, v, w, u, st)
+    sync()
+    ref = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"])
+    diff = np.abs(f64_host(y_f) - f64_host(y_s)) / np.maximum(np.abs(ref["y"]), ref["scale"])
+    assert np.max(diff) <= 2 * RWKV4_TOL
+    rwkv4_assert(d, y_s, st)
 
 
 def gpu_rel_errors(got, ref):
@@ -409,35 +474,60 @@ def gpu_rel_errors(got, ref):
             float(torch.max(diff / torch.maximum(ref.abs(), rms))))
 
 
-def test_decode_workload5_full():
-    """256 sequences x 64 heads x 1024 decode steps, against the oracle on
-    sampled heads and against the chunked forward over the same tokens."""
-    spec = S.WORKLOADS[5]
-    B, steps, H = spec["B"], spec["steps"], spec["H"]
-    print(f"decode workload 5: B={B} H={H} steps={steps}", flush=True)
-    d = S.workload(5)
-    g = matrix_inputs_dev(d)  # r, k, v, x: [steps, B, H, 64]
+@pytest.mark.parametrize("cfg", [5, 6], ids=["finch", "eagle"])
+def test_decode_workload_full(cfg):
+    """256 sequences x 64 heads of decode steps (1024 for Finch, 64 for
+    Eagle), against the oracle on sampled heads and against the chunked
+    forward over the same tokens."""
+    per_token = cfg == 5
+    spec = S.WORKLOADS[cfg]
+    B, H = spec["B"], spec["H"]
+    steps = spec["steps"] if per_token else 64
+    print(f"decode workload {cfg}: B={B} H={H} steps={steps}", flush=True)
+    d = S.workload(cfg, steps=steps)
+    g = matrix_inputs_dev(d)  # r, k, v (Finch: x): [steps, B, H, 64]
     st = g["s0"].clone()
     o = torch.empty((steps, B, H, 64), dtype=torch.bfloat16, device="cuda")
+    one = lambda t, s: t[s].unsqueeze(1)
     for s in range(steps):
-        W.rwkv6_wkv_step(g["r"][s].unsqueeze(1), g["k"][s].unsqueeze(1),
-                         g["v"][s].unsqueeze(1), g["x"][s].unsqueeze(1), g["u"], st,
-                         o=o[s].unsqueeze(1))
+        x = one(g["x"], s) if per_token else g["x"]
+        step = W.rwkv6_wkv_step if per_token else W.rwkv5_wkv_step
+        step(one(g["r"], s), one(g["k"], s), one(g["v"], s), x, g["u"], st, o=one(o, s))
     sync()
     print("decode done; oracle on sampled heads", flush=True)
     for b, h in sample_heads(B, H):
         sl = lambda a: np.ascontiguousarray(a[:, b, h])[None, :, None]
+        x = sl(d["x"]) if per_token else d["x"][h:h + 1]
         o_ref, s_ref = oracle.wkv_matrix(
             S.bf16_to_f32(sl(d["r"])), S.bf16_to_f32(sl(d["k"])), S.bf16_to_f32(sl(d["v"])),
-            sl(d["x"]), d["u"][h:h + 1], d["s0"][b:b + 1, h:h + 1])
+            x, d["u"][h:h + 1], d["s0"][b:b + 1, h:h + 1])
         assert_matrix_close(bf16_host(o[:, b, h]), o_ref[0, :, 0], f"o head {(b, h)}")
         assert_matrix_close(f64_host(st[b, h]), s_ref[0, 0], f"state head {(b, h)}")
     print("chunked forward over the same tokens", flush=True)
     perm = lambda t: t.transpose(0, 1).contiguous()
-    o_c, s_c = W.rwkv6_wkv_fwd(perm(g["r"]), perm(g["k"]), perm(g["v"]), perm(g["x"]),
-                               g["u"], state_in=g["s0"])
+    fwd = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    o_c, s_c = fwd(perm(g["r"]), perm(g["k"]), perm(g["v"]),
+                   perm(g["x"]) if per_token else g["x"], g["u"], state_in=g["s0"])
     sync()
     rms, mx = gpu_rel_errors(perm(o), o_c)
     assert rms <= 5e-3 and mx <= 3e-2, (rms, mx)
     rms, mx = gpu_rel_errors(st, s_c)
     assert rms <= 5e-3 and mx <= 3e-2, (rms, mx)
+
+
+def test_rwkv4_decode_workload7():
+    """256 sequences x 4096 channels, 64 decode steps from the empty history,
+    against the oracle on every channel."""
+    spec = S.WORKLOADS[7]
+    B, C, steps = spec["B"], spec["C"], 64
+    print(f"rwkv4 decode workload 7: B={B} C={C} steps={steps}", flush=True)
+    d = S.workload(7, steps=steps)  # k, v: [steps, B, C]
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    st = empty_rwkv4_state(B, C)
+    y = torch.empty((steps, B, C), device="cuda")
+    for s in range(steps):
+        W.rwkv4_wkv_step(k[s].unsqueeze(1), v[s].unsqueeze(1), w, u, st, y=y[s].unsqueeze(1))
+    sync()
+    seq = {"k": np.ascontiguousarray(d["k"].transpose(1, 0, 2)),
+           "v": np.ascontiguousarray(d["v"].transpose(1, 0, 2)), "w": d["w"], "u": d["u"]}
+    rwkv4_assert(seq, y.transpose(0, 1), st)

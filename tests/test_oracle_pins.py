@@ -305,16 +305,31 @@ def test_matrix_split_invariance_bitwise(oracle_lib, cut):
     assert np.array_equal(s2, sT)
 
 
-def test_matrix_stepwise_equals_sequence_bitwise(oracle_lib):
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_matrix_stepwise_equals_sequence_bitwise(oracle_lib, per_token):
     # decoding one token per call with the state handed over equals one call
-    r, k, v, x, u, s0 = small_matrix_case(1, 12, 2, 8, 36, True)
+    r, k, v, x, u, s0 = small_matrix_case(1, 12, 2, 8, 36, per_token)
     o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=oracle_lib)
     s = s0.astype(np.float64)
     for t in range(12):
-        ot, s = oracle.wkv_matrix(r[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1],
-                                  x[:, t:t + 1], u, s, lib=oracle_lib)
+        xt = x[:, t:t + 1] if per_token else x
+        ot, s = oracle.wkv_matrix(r[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], xt, u, s,
+                                  lib=oracle_lib)
         assert np.array_equal(ot[:, 0], o[:, t])
     assert np.array_equal(s, sT)
+
+
+def test_rwkv4_stepwise_equals_sequence_bitwise(oracle_lib):
+    # RWKV-4 decoding: one token per call, the (Num, Den) history handed over
+    d = S.rwkv4_inputs(2, 12, 8, 37, k_sigma=2.0)
+    full = oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], lib=oracle_lib)
+    num = den = None
+    for t in range(12):
+        out = oracle.rwkv4_fwd(d["k"][:, t:t + 1], d["v"][:, t:t + 1], d["w"], d["u"],
+                               num, den, lib=oracle_lib)
+        assert np.array_equal(out["y"][:, 0], full["y"][:, t])
+        num, den = out["num"], out["den"]
+    assert np.array_equal(num, full["num"]) and np.array_equal(den, full["den"])
 
 
 def test_matrix_scaling_exact(oracle_lib):

@@ -131,11 +131,11 @@ def wkv_inputs(B, T, H, N, cfg, per_token, s0_sigma=0.0, rkv_sigma=0.125,
 
 
 def decode_inputs(B, steps, H, N, cfg, s0_sigma=0.1, rkv_sigma=0.125,
-                  omega=(-6.0, -0.5), delta_sigma=0.5, u_sigma=0.5):
-    """Finch decode: per-step r, k, v (bf16 bits) and x (fp32) laid out
-    [steps][B][H][N] so that each step's slice is one contiguous [B,1,H,N]
-    operand; u [H,N]; s0 [B,H,N,N]."""
-    d = wkv_inputs(steps, B, H, N, cfg, True, 0.0, rkv_sigma, omega,
+                  omega=(-6.0, -0.5), delta_sigma=0.5, u_sigma=0.5, per_token=True):
+    """Finch (Eagle: per_token=False) decode: per-step r, k, v (bf16 bits) and
+    Finch's x (fp32) laid out [steps][B][H][N] so that each step's slice is one
+    contiguous [B,1,H,N] operand; Eagle's x [H,N]; u [H,N]; s0 [B,H,N,N]."""
+    d = wkv_inputs(steps, B, H, N, cfg, per_token, 0.0, rkv_sigma, omega,
                    delta_sigma, u_sigma)
     d["s0"] = (normal((B, H, N, N), s0_sigma, cfg, T_S0) if s0_sigma > 0
                else np.zeros((B, H, N, N), np.float32))
@@ -151,6 +151,9 @@ WORKLOADS = {
     3: dict(kind="eagle", B=8, T=4096, H=32, N=64, s0_sigma=0.0),
     4: dict(kind="finch", B=8, T=4096, H=40, N=64, s0_sigma=0.1),
     5: dict(kind="decode", B=256, steps=1024, H=64, N=64, s0_sigma=0.1),
+    # serial mode of the other two generations at the same 7B-class width
+    6: dict(kind="eagle_decode", B=256, steps=1024, H=64, N=64, s0_sigma=0.1),
+    7: dict(kind="rwkv4_decode", B=256, steps=1024, C=4096, k_sigma=2.0),
 }
 
 WORKLOAD_NAMES = {
@@ -159,11 +162,13 @@ WORKLOAD_NAMES = {
     3: "eagle_fwd_B8_T4096_D2048_H32_N64_bf16",
     4: "finch_fwd_B8_T4096_D2560_H40_N64_bf16",
     5: "finch_decode_B256_D4096_H64_N64_x1024",
+    6: "eagle_decode_B256_D4096_H64_N64_x1024",
+    7: "rwkv4_decode_B256_C4096_x1024",
 }
 
 
 def workload(cfg, **override):
-    """Inputs of workload ``cfg`` (1..5); keyword overrides change sizes."""
+    """Inputs of workload ``cfg`` (1..7); keyword overrides change sizes."""
     spec = dict(WORKLOADS[cfg])
     spec.update(override)
     kind = spec.pop("kind")
@@ -175,7 +180,10 @@ def workload(cfg, **override):
     if kind == "finch":
         return wkv_inputs(spec["B"], spec["T"], spec["H"], spec["N"], cfg, True,
                           spec["s0_sigma"])
-    if kind == "decode":
+    if kind in ("decode", "eagle_decode"):
         return decode_inputs(spec["B"], spec["steps"], spec["H"], spec["N"], cfg,
-                             spec["s0_sigma"])
+                             spec["s0_sigma"], per_token=kind == "decode")
+    if kind == "rwkv4_decode":
+        # k, v [steps][B][C]: each step's slice is one contiguous [B,1,C] operand
+        return rwkv4_inputs(spec["steps"], spec["B"], spec["C"], cfg, spec["k_sigma"])
     raise ValueError(kind)
