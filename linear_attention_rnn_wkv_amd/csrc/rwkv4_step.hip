@@ -19,8 +19,11 @@
 //
 // One thread per (sequence, channel); consecutive threads take consecutive
 // channels, so every load and store of a wave covers 256 contiguous bytes.
-// Decoding (T == 1) moves 36 bytes per channel: k, v, y and the state read
-// and written.  Longer calls fetch the operands of kBlock tokens at once.
+// Longer calls fetch the operands of kBlock tokens at once.  Decoding
+// (T == 1) moves 36 bytes per channel: k, v, y and the state read and
+// written; when C is a multiple of 4 and every pointer is 16-byte aligned a
+// thread takes 4 channels with 16-byte accesses (a quarter of the
+// instructions and of the waves).
 #include "launchers.h"
 #include "wkv_device.h"
 
@@ -28,6 +31,47 @@ namespace wkv {
 namespace {
 
 constexpr int kBlock = 8;
+
+// Running state of a channel: Num = a e^p, Den = b e^p, p = kp - m w.
+struct Run {
+    float a, b, kp, m;
+};
+
+// output of token (k, v), then the update
+__device__ __forceinline__ float token(Run &s, float w, float u, float k, float v) {
+    const float p = fmaf(-s.m, w, s.kp);
+    const float uk = u + k;
+    const bool hist = p > uk;
+    const float e = exp_fast(-fabsf(p - uk));
+    const float eh = hist ? 1.0f : e, ec = hist ? e : 1.0f;
+    const float y = fmaf(eh, s.a, ec * v) * __builtin_amdgcn_rcpf(fmaf(eh, s.b, ec));
+    const float pw = fmaf(-(s.m + 1.0f), w, s.kp);
+    const bool old = pw > k;
+    const float f = exp_fast(-fabsf(pw - k));
+    const float fo = old ? 1.0f : f, fn = old ? f : 1.0f;
+    s.a = fmaf(fo, s.a, fn * v);
+    s.b = fmaf(fo, s.b, fn);
+    s.kp = old ? s.kp : k;
+    s.m = old ? s.m + 1.0f : 0.0f;
+    return y;
+}
+
+// The state to store: p = kp - m w rounded, and r = (kp - m w) - p exactly
+// (up to a rounding of r itself; the product's error by a fused multiply-add,
+// the difference's by the two-sum, with explicit roundings so that nothing is
+// fused) folded into a and b as e^r = 1 + r.
+__device__ __forceinline__ void store_state(const Run &s, float w, float &a, float &b,
+                                            float &p) {
+    const float mw = __fmul_rn(s.m, w);
+    const float mw_err = fmaf(s.m, w, -mw);
+    const float ps = __fsub_rn(s.kp, mw);
+    const float bb = __fsub_rn(ps, s.kp);
+    const float s_err = __fadd_rn(__fsub_rn(s.kp, __fsub_rn(ps, bb)), __fsub_rn(-mw, bb));
+    const float r = __fsub_rn(s_err, mw_err);
+    a = fmaf(s.a, r, s.a);
+    b = fmaf(s.b, r, s.b);
+    p = ps;
+}
 
 __global__ __launch_bounds__(256) void rwkv4_step_kernel(
     int B, int T, int C, const float *__restrict__ k, const float *__restrict__ v,
@@ -38,7 +82,7 @@ __global__ __launch_bounds__(256) void rwkv4_step_kernel(
     const int64_t b = i / C;
     const int c = (int)(i - b * C);
     float *sp = state + b * 3 * C + c;
-    float sa = sp[0], sb = sp[C], kp = sp[2 * (int64_t)C], m = 0.0f;
+    Run st{sp[0], sp[C], sp[2 * (int64_t)C], 0.0f};
     const float wc = w[c], uc = u[c];
     const float *kptr = k + b * (int64_t)T * C + c;
     const float *vptr = v + b * (int64_t)T * C + c;
@@ -54,38 +98,39 @@ __global__ __launch_bounds__(256) void rwkv4_step_kernel(
 #pragma unroll
         for (int j = 0; j < kBlock; ++j) {
             if (t0 + j >= T) break;
-            const float kt = kk[j], vt = vv[j];
-            // output
-            const float p = fmaf(-m, wc, kp);
-            const float uk = uc + kt;
-            const bool hist = p > uk;
-            const float e = exp_fast(-fabsf(p - uk));
-            const float eh = hist ? 1.0f : e, ec = hist ? e : 1.0f;
-            yptr[(int64_t)(t0 + j) * C] =
-                fmaf(eh, sa, ec * vt) * __builtin_amdgcn_rcpf(fmaf(eh, sb, ec));
-            // update
-            const float pw = fmaf(-(m + 1.0f), wc, kp);
-            const bool old = pw > kt;
-            const float f = exp_fast(-fabsf(pw - kt));
-            const float fo = old ? 1.0f : f, fn = old ? f : 1.0f;
-            sa = fmaf(fo, sa, fn * vt);
-            sb = fmaf(fo, sb, fn);
-            kp = old ? kp : kt;
-            m = old ? m + 1.0f : 0.0f;
+            yptr[(int64_t)(t0 + j) * C] = token(st, wc, uc, kk[j], vv[j]);
         }
     }
-    // p = kp - m w rounded, and r = (kp - m w) - p exactly (up to a rounding
-    // of r itself): the product's error by a fused multiply-add, the
-    // difference's by the two-sum; explicit roundings keep them unfused
-    const float mw = __fmul_rn(m, wc);
-    const float mw_err = fmaf(m, wc, -mw);
-    const float ps = __fsub_rn(kp, mw);
-    const float bb = __fsub_rn(ps, kp);
-    const float s_err = __fadd_rn(__fsub_rn(kp, __fsub_rn(ps, bb)), __fsub_rn(-mw, bb));
-    const float r = __fsub_rn(s_err, mw_err);
-    sp[0] = fmaf(sa, r, sa);
-    sp[C] = fmaf(sb, r, sb);
-    sp[2 * (int64_t)C] = ps;
+    store_state(st, wc, sp[0], sp[C], sp[2 * (int64_t)C]);
+}
+
+// One token, four channels per thread (C % 4 == 0, 16-byte aligned).
+__global__ __launch_bounds__(256) void rwkv4_decode4_kernel(
+    int B, int C4, const f32x4 *__restrict__ k, const f32x4 *__restrict__ v,
+    const f32x4 *__restrict__ w, const f32x4 *__restrict__ u, f32x4 *state,
+    f32x4 *__restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)B * C4) return;  // no barriers in this kernel
+    const int64_t b = i / C4;
+    const int c = (int)(i - b * C4);
+    f32x4 *sp = state + b * 3 * C4 + c;
+    const f32x4 sa = sp[0], sb = sp[C4], sq = sp[2 * (int64_t)C4];
+    const f32x4 kk = k[i], vv = v[i], ww = w[c], uu = u[c];
+    f32x4 yo, na, nb, np;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        Run st{sa[j], sb[j], sq[j], 0.0f};
+        yo[j] = token(st, ww[j], uu[j], kk[j], vv[j]);
+        float a_, b_, p_;
+        store_state(st, ww[j], a_, b_, p_);
+        na[j] = a_;
+        nb[j] = b_;
+        np[j] = p_;
+    }
+    y[i] = yo;
+    sp[0] = na;
+    sp[C4] = nb;
+    sp[2 * (int64_t)C4] = np;
 }
 
 }  // namespace
@@ -93,6 +138,15 @@ __global__ __launch_bounds__(256) void rwkv4_step_kernel(
 hipError_t launch_rwkv4_step(int B, int T, int C, const float *k, const float *v,
                              const float *w, const float *u, float *state, float *y,
                              hipStream_t stream) {
+    auto a16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (T == 1 && C % 4 == 0 && a16(k) && a16(v) && a16(w) && a16(u) && a16(state) &&
+        a16(y)) {
+        const int64_t n4 = (int64_t)B * (C / 4);
+        hipLaunchKernelGGL(rwkv4_decode4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
+                           0, stream, B, C / 4, (const f32x4 *)k, (const f32x4 *)v,
+                           (const f32x4 *)w, (const f32x4 *)u, (f32x4 *)state, (f32x4 *)y);
+        return hipGetLastError();
+    }
     const int64_t n = (int64_t)B * C;
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(rwkv4_step_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, B, T,

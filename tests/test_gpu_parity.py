@@ -451,6 +451,30 @@ def test_rwkv4_long_decode():
     rwkv4_assert(seq, y.transpose(0, 1), st)
 
 
+def test_rwkv4_decode_vector_path_matches_scalar():
+    # one token with C % 4 == 0 and 16-byte aligned tensors takes four
+    # channels per thread; the same step on 4-byte aligned views takes the
+    # per-channel kernel: both apply the same operations
+    B, C = 3, 1000
+    d = S.rwkv4_inputs(B, 1, C, 29, k_sigma=2.0)
+    st0 = empty_rwkv4_state(B, C)
+    W.rwkv4_wkv_step(to_dev(d["k"]), to_dev(d["v"]), to_dev(d["w"]), to_dev(d["u"]), st0)
+    outs = []
+    for off in (0, 1):  # 16-byte aligned, then shifted by one float
+        buf = lambda a: torch.empty(a.size + 4, device="cuda")[off:off + a.size].view(a.shape)
+        k, v, w, u = (buf(d[n]) for n in ("k", "v", "w", "u"))
+        for t, n in ((k, "k"), (v, "v"), (w, "w"), (u, "u")):
+            t.copy_(to_dev(d[n]))
+        st = torch.empty(st0.numel() + 4, device="cuda")[off:off + st0.numel()].view(st0.shape)
+        st.copy_(st0)
+        y = buf(d["k"])
+        W.rwkv4_wkv_step(k, v, w, u, st, y=y)
+        sync()
+        outs.append((y.clone(), st.clone()))
+    assert outs[0][0].data_ptr() % 16 == 0
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_rwkv4_step_and_fwd_agree():
     d = S.rwkv4_inputs(3, 700, 64, 23, k_sigma=2.0)
     k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
