@@ -323,7 +323,7 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
                      lambda: decode_bytes_per_step(256, 64)),
     "eagle_decode": ("wkv_step_kernel<false>", "wkv_step.hip",
                      lambda: eagle_decode_bytes_per_step(256, 64)),
-    "rwkv4_decode": ("rwkv4_step_kernel", "rwkv4_step.hip",
+    "rwkv4_decode": ("rwkv4_decode4_kernel", "rwkv4_step.hip",
                      lambda: rwkv4_decode_bytes_per_step(256, 4096)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
