@@ -443,6 +443,9 @@ def main():
         print(json.dumps({"paths": paths}))
         return 0
 
+    for key, rec in paths.items():  # counter-measured HBM bytes, while current
+        if key in PMC_PATHS:
+            rec["traffic_bytes"] = measured_traffic(PMC_PATHS[key][1], key)
     finch = paths["finch_fwd"]
     spec = S.WORKLOADS[4]
     ms = finch["wall_s"] / args.steps * 1e3
