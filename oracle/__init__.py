@@ -43,6 +43,9 @@ def _bind(lib):
     lib.oracle_wkv_matrix.restype = ctypes.c_int
     lib.oracle_wkv_matrix.argtypes = [L, L, L, L, f, f, f, f, ctypes.c_int, f,
                                       d, d, d, ctypes.c_int]
+    lib.oracle_wkv_matrix_bwd.restype = ctypes.c_int
+    lib.oracle_wkv_matrix_bwd.argtypes = [L, L, L, L, f, f, f, f, ctypes.c_int, f,
+                                          d, d, d, d, d, d, d, d, d, ctypes.c_int]
     return lib
 
 
@@ -147,3 +150,51 @@ def wkv_matrix(r, k, v, x, u, s_in=None, nthreads=None, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_wkv_matrix failed ({rc})")
     return o, s_out
+
+
+def wkv_matrix_bwd(r, k, v, x, u, d_o, s_in=None, d_sT=None, nthreads=None, lib=None):
+    """Eagle / Finch WKV backward in fp64 (reverse-mode of the serial
+    recurrence).
+
+    Forward inputs as in wkv_matrix; d_o: [B, T, H, N] gradient of the output;
+    d_sT: [B, H, N, N] gradient of the final state (None = zero).
+    Returns a dict of float64 arrays: dr, dk, dv ([B, T, H, N]), dx
+    ([B, T, H, N] for Finch, [H, N] summed over b and t for Eagle), du ([H, N],
+    summed over b and t) and ds0 ([B, H, N, N]).
+    """
+    lib = lib or load()
+    r, rp = _f32(r)
+    k, kp = _f32(k)
+    v, vp = _f32(v)
+    x, xp = _f32(x)
+    u, up = _f32(u)
+    B, T, H, N = r.shape
+    assert k.shape == r.shape and v.shape == r.shape and u.shape == (H, N)
+    per_token = 0 if x.shape == (H, N) else 1
+    if per_token:
+        assert x.shape == r.shape, x.shape
+    keep = []
+    if s_in is None:
+        sp = _null_d()
+    else:
+        s_in, sp = _f64(s_in)
+        assert s_in.shape == (B, H, N, N)
+    d_o, dop = _f64(d_o)
+    assert d_o.shape == r.shape
+    if d_sT is None:
+        dsp = _null_d()
+    else:
+        d_sT, dsp = _f64(d_sT)
+        assert d_sT.shape == (B, H, N, N)
+    out = {n: np.empty(r.shape, np.float64) for n in ("dr", "dk", "dv")}
+    out["dx"] = np.empty(r.shape if per_token else (H, N), np.float64)
+    out["du"] = np.empty((H, N), np.float64)
+    out["ds0"] = np.empty((B, H, N, N), np.float64)
+    rc = lib.oracle_wkv_matrix_bwd(B, T, H, N, rp, kp, vp, xp, per_token, up, sp, dop, dsp,
+                                   _f64(out["dr"])[1], _f64(out["dk"])[1], _f64(out["dv"])[1],
+                                   _f64(out["dx"])[1], _f64(out["du"])[1],
+                                   _f64(out["ds0"])[1], int(nthreads or default_threads()))
+    del keep
+    if rc != 0:
+        raise RuntimeError(f"oracle_wkv_matrix_bwd failed ({rc})")
+    return out

@@ -156,3 +156,144 @@ int oracle_wkv_matrix(long B, long T, long H, long N,
     }
     return bad ? ORACLE_BAD_ARG : ORACLE_OK;
 }
+
+/*
+ * Eagle / Finch backward: the gradients of a loss L through the forward
+ * above, given dL/do and dL/dS_T.  This is reverse-mode differentiation of
+ * the serial recurrence, one token at a time from the last to the first
+ * (no chunking, no closed forms).  With S the state before token t (the one
+ * o_t reads), beta = sum_i r_i u_i k_i and dbeta = sum_j do_j v_j:
+ *     dr_i = sum_j do_j S_ij + u_i k_i dbeta
+ *     dk_i = sum_j dS'_ij v_j + u_i r_i dbeta      (dS' = dL/dS after token t)
+ *     dv_j = sum_i dS'_ij k_i + beta do_j
+ *     dw_i = sum_j dS'_ij S_ij,   dx_i = dw_i w_i (-exp(x_i))
+ *     du_i += r_i k_i dbeta
+ *     dS_ij = w_i dS'_ij + r_i do_j                 (dL/dS before token t)
+ * The forward states are needed in reverse order: every CK-th state is kept
+ * and the states of one segment are recomputed from it.
+ *   r, k, v, x, x_per_token, u, s_in   as in oracle_wkv_matrix
+ *   d_o       [B][T][H][N]
+ *   d_sT      [B][H][N][N], or NULL for zero
+ *   d_r, d_k, d_v   [B][T][H][N]
+ *   d_x       [B][T][H][N] (Finch), or [H][N] summed over b and t (Eagle)
+ *   d_u       [H][N], summed over b and t
+ *   d_s0      [B][H][N][N], or NULL
+ * Sums over sequences are taken in sequence order after the parallel loop,
+ * so results do not depend on the thread count.
+ */
+#define CK 64
+int oracle_wkv_matrix_bwd(long B, long T, long H, long N,
+                          const float *r, const float *k, const float *v,
+                          const float *x, int x_per_token, const float *u,
+                          const double *s_in, const double *d_o, const double *d_sT,
+                          double *d_r, double *d_k, double *d_v, double *d_x,
+                          double *d_u, double *d_s0, int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || N < 1 || nthreads < 1) return ORACLE_BAD_ARG;
+    long units = B * H, NN = N * N, nseg = (T + CK - 1) / CK;
+    /* per-unit partial sums of d_u (and of Eagle's d_x) */
+    double *pu = (double *)calloc((size_t)(units * N), sizeof(double));
+    double *px = x_per_token ? NULL : (double *)calloc((size_t)(units * N), sizeof(double));
+    if (!pu || (!x_per_token && !px)) {
+        free(pu); free(px);
+        return ORACLE_BAD_ARG;
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long b = unit / H, h = unit % H;
+        double *ck = (double *)malloc(sizeof(double) * (size_t)((nseg + 1) * NN));
+        double *seg = (double *)malloc(sizeof(double) * (size_t)(CK * NN));
+        double *dS = (double *)malloc(sizeof(double) * (size_t)NN);
+        double *wt = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!ck || !seg || !dS || !wt) {
+            free(ck); free(seg); free(dS); free(wt);
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        const float *uh = u + h * N;
+        /* forward, in dS as the running state: keep the state before tokens
+           0, CK, 2 CK, ... */
+        double *S = dS;
+        for (long i = 0; i < NN; ++i) S[i] = s_in ? s_in[(b * H + h) * NN + i] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            long base = ((b * T + t) * H + h) * N;
+            const float *xt = x_per_token ? x + base : x + h * N;
+            if (t % CK == 0)
+                for (long i = 0; i < NN; ++i) ck[(t / CK) * NN + i] = S[i];
+            for (long i = 0; i < N; ++i) wt[i] = exp(-exp((double)xt[i]));
+            for (long i = 0; i < N; ++i)
+                for (long j = 0; j < N; ++j)
+                    S[i * N + j] = wt[i] * S[i * N + j] + (double)k[base + i] * (double)v[base + j];
+        }
+        /* reverse */
+        for (long i = 0; i < NN; ++i) dS[i] = d_sT ? d_sT[(b * H + h) * NN + i] : 0.0;
+        for (long sg = nseg - 1; sg >= 0; --sg) {
+            long t0 = sg * CK, t1 = t0 + CK < T ? t0 + CK : T;
+            /* states before tokens t0 .. t1-1 */
+            for (long i = 0; i < NN; ++i) seg[i] = ck[sg * NN + i];
+            for (long t = t0; t + 1 < t1; ++t) {
+                long base = ((b * T + t) * H + h) * N;
+                const float *xt = x_per_token ? x + base : x + h * N;
+                const double *Sp = seg + (t - t0) * NN;
+                double *Sn = seg + (t - t0 + 1) * NN;
+                for (long i = 0; i < N; ++i) wt[i] = exp(-exp((double)xt[i]));
+                for (long i = 0; i < N; ++i)
+                    for (long j = 0; j < N; ++j)
+                        Sn[i * N + j] = wt[i] * Sp[i * N + j] +
+                                        (double)k[base + i] * (double)v[base + j];
+            }
+            for (long t = t1 - 1; t >= t0; --t) {
+                long base = ((b * T + t) * H + h) * N;
+                const float *rt = r + base, *kt = k + base, *vt = v + base;
+                const float *xt = x_per_token ? x + base : x + h * N;
+                const double *dot = d_o + base;
+                const double *Sp = seg + (t - t0) * NN;
+                for (long i = 0; i < N; ++i) wt[i] = exp(-exp((double)xt[i]));
+                double beta = 0.0, dbeta = 0.0;
+                for (long i = 0; i < N; ++i) beta += (double)rt[i] * (double)uh[i] * (double)kt[i];
+                for (long j = 0; j < N; ++j) dbeta += dot[j] * (double)vt[j];
+                for (long i = 0; i < N; ++i) {
+                    double ar = 0.0, ak = 0.0, aw = 0.0;
+                    for (long j = 0; j < N; ++j) {
+                        ar += dot[j] * Sp[i * N + j];
+                        ak += dS[i * N + j] * (double)vt[j];
+                        aw += dS[i * N + j] * Sp[i * N + j];
+                    }
+                    d_r[base + i] = ar + (double)uh[i] * (double)kt[i] * dbeta;
+                    d_k[base + i] = ak + (double)uh[i] * (double)rt[i] * dbeta;
+                    double dx = aw * wt[i] * (-exp((double)xt[i]));
+                    if (x_per_token) d_x[base + i] = dx;
+                    else px[unit * N + i] += dx;
+                    pu[unit * N + i] += (double)rt[i] * (double)kt[i] * dbeta;
+                }
+                for (long j = 0; j < N; ++j) {
+                    double av = 0.0;
+                    for (long i = 0; i < N; ++i) av += dS[i * N + j] * (double)kt[i];
+                    d_v[base + j] = av + beta * dot[j];
+                }
+                for (long i = 0; i < N; ++i)
+                    for (long j = 0; j < N; ++j)
+                        dS[i * N + j] = wt[i] * dS[i * N + j] + (double)rt[i] * dot[j];
+            }
+        }
+        if (d_s0)
+            for (long i = 0; i < NN; ++i) d_s0[(b * H + h) * NN + i] = dS[i];
+        free(ck); free(seg); free(dS); free(wt);
+    }
+    if (!bad) {
+        for (long h = 0; h < H; ++h)
+            for (long i = 0; i < N; ++i) {
+                double su = 0.0, sx = 0.0;
+                for (long b = 0; b < B; ++b) {
+                    su += pu[(b * H + h) * N + i];
+                    if (!x_per_token) sx += px[(b * H + h) * N + i];
+                }
+                d_u[h * N + i] = su;
+                if (!x_per_token) d_x[h * N + i] = sx;
+            }
+    }
+    free(pu); free(px);
+    return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+}

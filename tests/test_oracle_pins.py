@@ -371,3 +371,99 @@ def test_thread_count_does_not_change_results(oracle_lib):
     a = oracle.wkv_matrix(r, k, v, x, u, s0, nthreads=1, lib=oracle_lib)
     b = oracle.wkv_matrix(r, k, v, x, u, s0, nthreads=5, lib=oracle_lib)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Eagle / Finch backward
+
+def _loss(r, k, v, x, u, s0, G, Hs, lib):
+    o, sT = oracle.wkv_matrix(r, k, v, x, u, s0, lib=lib)
+    return float(np.sum(o * G) + np.sum(sT * Hs))
+
+
+def _bwd_case(T, per_token, seed, N=4, H=1, B=1):
+    r, k, v, x, u, s0 = small_matrix_case(B, T, H, N, seed, per_token)
+    g = np.random.default_rng(seed)
+    G = g.standard_normal((B, T, H, N))
+    Hs = g.standard_normal((B, H, N, N))
+    return r, k, v, x, u, s0, G, Hs
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("T", [5, 70])
+def test_matrix_bwd_finite_differences(oracle_lib, per_token, T):
+    # Every gradient entry against central differences of the forward oracle:
+    # the step 2^-12 is exact on these fp32 inputs (|value| < 2^11), so the
+    # difference quotient is the fp64 derivative up to O(h^2).  T = 70 crosses
+    # the backward's 64-token recomputation segment.
+    r, k, v, x, u, s0, G, Hs = _bwd_case(T, per_token, 40 + T)
+    got = oracle.wkv_matrix_bwd(r, k, v, x, u, G, s0, Hs, lib=oracle_lib)
+    h = 2.0 ** -12
+    args = dict(r=r, k=k, v=v, x=x, u=u)
+    names = {"r": "dr", "k": "dk", "v": "dv", "x": "dx", "u": "du"}
+    for name, a in args.items():
+        fd = np.zeros(a.shape)
+        for idx in np.ndindex(a.shape):
+            lo, hi = (dict(args), dict(args))
+            for sgn, dct in ((-1, lo), (1, hi)):
+                p = a.copy()
+                p[idx] = np.float32(p[idx] + sgn * h)
+                assert p[idx] == a[idx] + sgn * h
+                dct[name] = p
+            fd[idx] = (_loss(hi["r"], hi["k"], hi["v"], hi["x"], hi["u"], s0, G, Hs,
+                             oracle_lib) -
+                       _loss(lo["r"], lo["k"], lo["v"], lo["x"], lo["u"], s0, G, Hs,
+                             oracle_lib)) / (2 * h)
+        ref = got[names[name]]
+        scale = max(np.max(np.abs(fd)), 1e-12)
+        assert np.max(np.abs(ref - fd)) <= 2e-6 * scale, (name, np.max(np.abs(ref - fd)), scale)
+    # the initial state (fp64 input): a smaller step, all entries
+    fd = np.zeros(s0.shape)
+    hs = 1e-6
+    for idx in np.ndindex(s0.shape):
+        p, m = s0.astype(np.float64), s0.astype(np.float64)
+        p[idx] += hs
+        m[idx] -= hs
+        fd[idx] = (_loss(r, k, v, x, u, p, G, Hs, oracle_lib) -
+                   _loss(r, k, v, x, u, m, G, Hs, oracle_lib)) / (2 * hs)
+    assert np.max(np.abs(got["ds0"] - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1e-12)
+
+
+def test_matrix_bwd_no_decay_is_linear_attention_backward(oracle_lib):
+    # x = -200 makes w = 1 in fp64: the forward is causal linear attention
+    # O = tril(R K^T, -1) V + diag(R diag(u) K^T) V + R S0, S_T = S0 + K^T V,
+    # whose gradients are plain matrix products (numpy)
+    T, N = 40, 8
+    r, k, v, x, u, s0, G, Hs = _bwd_case(T, True, 77, N=N)
+    x = np.full_like(x, -200.0)
+    got = oracle.wkv_matrix_bwd(r, k, v, x, u, G, s0, Hs, lib=oracle_lib)
+    R, K, V = (a[0, :, 0].astype(np.float64) for a in (r, k, v))
+    uu, S0, dO, dST = u[0].astype(np.float64), s0[0, 0], G[0, :, 0], Hs[0, 0]
+    dM = dO @ V.T
+    dMl = np.tril(dM, -1)
+    dd = np.diag(dM)
+    beta = np.sum(R * uu * K, axis=1)
+    M = np.tril(R @ K.T, -1) + np.diag(beta)
+    dR = dMl @ K + (uu * K) * dd[:, None] + dO @ S0.T
+    dK = dMl.T @ R + (uu * R) * dd[:, None] + V @ dST.T
+    dV = M.T @ dO + K @ dST
+    dS0 = R.T @ dO + dST
+    du = np.sum(R * K * dd[:, None], axis=0)
+    for name, want in (("dr", dR), ("dk", dK), ("dv", dV)):
+        assert np.allclose(got[name][0, :, 0], want, rtol=1e-12, atol=1e-12), name
+    assert np.allclose(got["ds0"][0, 0], dS0, rtol=1e-12, atol=1e-12)
+    assert np.allclose(got["du"][0], du, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(got["dx"])) < 1e-80  # dw/dx = -w e^x, e^-200 ~ 1e-87
+
+
+def test_matrix_bwd_eagle_decay_gradient_is_finch_summed(oracle_lib):
+    # Eagle's x is Finch's x repeated over sequences and tokens, so its
+    # gradient is the sum of Finch's per-token gradients
+    B, T, H, N = 2, 30, 2, 8
+    r, k, v, x, u, s0, G, Hs = _bwd_case(T, False, 78, N=N, H=H, B=B)
+    xf = np.broadcast_to(x, (B, T, H, N)).copy()
+    e = oracle.wkv_matrix_bwd(r, k, v, x, u, G, s0, Hs, lib=oracle_lib)
+    f = oracle.wkv_matrix_bwd(r, k, v, xf, u, G, s0, Hs, lib=oracle_lib)
+    assert np.allclose(e["dx"], f["dx"].sum(axis=(0, 1)), rtol=1e-12, atol=1e-14)
+    for n in ("dr", "dk", "dv", "du", "ds0"):
+        assert np.array_equal(e[n], f[n]), n
