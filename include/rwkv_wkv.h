@@ -55,6 +55,7 @@
 #define RWKV_WKV_H
 
 #include <stdint.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -200,6 +201,53 @@ int rwkv5_wkv_step(int B, int T, int H, int N,
                    const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                    const float *x, const float *u,
                    float *state, rwkv_bf16 *o, void *stream);
+
+/*
+ * Eagle / Finch backward of the time-parallel forward (rwkv5_wkv_fwd,
+ * rwkv6_wkv_fwd): the gradients of a loss L with respect to every input,
+ * given dL/do and dL/dS_T.  Reverse-mode differentiation of the recurrence
+ * in the RWKV-5/6 summary, 4.1.2 "Eagle time mixing" and 4.2.2 "Finch time
+ * mixing"; RWKV paper summary, "Transformer-like parallelization" (the
+ * training pass runs time-parallel).  N must be 64.
+ *
+ *   r, k, v, x, u, state_in   the forward's inputs, as in rwkv6_wkv_fwd
+ *              (rwkv5_wkv_bwd: x is [H][N]); state_in may be NULL (zeros)
+ *   d_o        [B][T][H][N] bf16, dL/do
+ *   d_state_out  [B][H][N][N] fp32 dL/dS_T, or NULL for zero
+ *   d_r, d_k, d_v  [B][T][H][N] bf16 outputs
+ *   d_x        fp32 output: [B][T][H][N] (rwkv6), or [H][N] summed over
+ *              sequences and tokens (rwkv5)
+ *   d_u        [H][N] fp32 output, summed over sequences and tokens
+ *   d_state_in [B][H][N][N] fp32 output dL/dS_0, or NULL; it may equal
+ *              d_state_out exactly (in place)
+ *   workspace  device memory of at least rwkv_wkv_bwd_workspace_bytes(B, T,
+ *              H, N) bytes, 16-byte aligned, owned by the caller and not
+ *              overlapping any other argument (RWKV_E_DIM if too small).  It
+ *              holds the state entering every 64-token chunk, recomputed by
+ *              the forward: 16 KiB per chunk and head.
+ *
+ * All pointers need 16-byte alignment; outputs may not overlap inputs or
+ * each other.  H must be at most 65536.  T = 0 sets d_u (and rwkv5's d_x)
+ * to zero and d_state_in to d_state_out.  Sums over sequences are taken in
+ * a fixed order (results do not depend on scheduling).
+ */
+size_t rwkv_wkv_bwd_workspace_bytes(int B, int T, int H, int N);
+
+int rwkv5_wkv_bwd(int B, int T, int H, int N,
+                  const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                  const float *x, const float *u, const float *state_in,
+                  const rwkv_bf16 *d_o, const float *d_state_out,
+                  rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
+                  float *d_x, float *d_u, float *d_state_in,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+int rwkv6_wkv_bwd(int B, int T, int H, int N,
+                  const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                  const float *x, const float *u, const float *state_in,
+                  const rwkv_bf16 *d_o, const float *d_state_out,
+                  rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
+                  float *d_x, float *d_u, float *d_state_in,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

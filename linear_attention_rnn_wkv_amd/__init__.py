@@ -14,6 +14,9 @@ Operators (names as in the C ABI):
   rwkv5_wkv_step  Eagle matrix-state WKV, serial (decode)
   rwkv6_wkv_fwd   Finch matrix-state WKV, time-parallel (chunked)
   rwkv6_wkv_step  Finch matrix-state WKV, serial (decode)
+  rwkv5_wkv_bwd   Eagle backward of the chunked forward
+  rwkv6_wkv_bwd   Finch backward of the chunked forward
+  rwkv_wkv_bwd_workspace_bytes  workspace size of the backward
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ RWKV_OK = 0
 STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPORTED",
           -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP"}
 EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
-           "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step")
+           "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step", "rwkv5_wkv_bwd",
+           "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes")
 
 _lib = None
 
@@ -60,6 +64,12 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
+        L.rwkv_wkv_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.rwkv_wkv_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        for name in ("rwkv5_wkv_bwd", "rwkv6_wkv_bwd"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I] + [P] * 15 + [ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -212,3 +222,66 @@ def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):
     x: [B, T, H, 64] fp32; u: [H, 64]; state: [B, H, 64, 64] fp32, updated in
     place.  Returns o."""
     return _matrix_step("rwkv6_wkv_step", True, r, k, v, x, u, state, o, stream)
+
+
+def _matrix_bwd(name, per_token, r, k, v, x, u, d_o, state_in, d_state_out, grads,
+                workspace, stream):
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect("d_o", d_o, (B, T, H, N), bf)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), f32)
+    if d_state_out is not None:
+        _expect("d_state_out", d_state_out, (B, H, N, N), f32)
+    g = dict(grads or {})
+    dev = r.device
+    g.setdefault("d_r", torch.empty((B, T, H, N), dtype=bf, device=dev))
+    g.setdefault("d_k", torch.empty((B, T, H, N), dtype=bf, device=dev))
+    g.setdefault("d_v", torch.empty((B, T, H, N), dtype=bf, device=dev))
+    g.setdefault("d_x", torch.empty((B, T, H, N) if per_token else (H, N), dtype=f32,
+                                    device=dev))
+    g.setdefault("d_u", torch.empty((H, N), dtype=f32, device=dev))
+    g.setdefault("d_state_in", torch.empty((B, H, N, N), dtype=f32, device=dev))
+    for n, shape, dt in (("d_r", (B, T, H, N), bf), ("d_k", (B, T, H, N), bf),
+                         ("d_v", (B, T, H, N), bf),
+                         ("d_x", (B, T, H, N) if per_token else (H, N), f32),
+                         ("d_u", (H, N), f32)):
+        _expect(n, g[n], shape, dt)
+    if g["d_state_in"] is not None:
+        _expect("d_state_in", g["d_state_in"], (B, H, N, N), f32)
+    need = lib().rwkv_wkv_bwd_workspace_bytes(B, max(T, 1), H, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    _check(name, getattr(lib(), name)(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in), _ptr(d_o),
+        _ptr(d_state_out), _ptr(g["d_r"]), _ptr(g["d_k"]), _ptr(g["d_v"]), _ptr(g["d_x"]),
+        _ptr(g["d_u"]), _ptr(g["d_state_in"]), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return g
+
+
+def rwkv5_wkv_bwd(r, k, v, x, u, d_o, state_in=None, d_state_out=None, grads=None,
+                  workspace=None, stream=None):
+    """Eagle backward.  Forward inputs as in rwkv5_wkv_fwd; d_o: [B, T, H, 64]
+    bf16; d_state_out: [B, H, 64, 64] fp32 or None.  Returns a dict d_r, d_k,
+    d_v (bf16), d_x ([H, 64], summed), d_u ([H, 64]), d_state_in.  ``grads``
+    may supply any of the output tensors; ``workspace`` a uint8 tensor of at
+    least rwkv_wkv_bwd_workspace_bytes bytes."""
+    return _matrix_bwd("rwkv5_wkv_bwd", False, r, k, v, x, u, d_o, state_in, d_state_out,
+                       grads, workspace, stream)
+
+
+def rwkv6_wkv_bwd(r, k, v, x, u, d_o, state_in=None, d_state_out=None, grads=None,
+                  workspace=None, stream=None):
+    """Finch backward: as rwkv5_wkv_bwd, with d_x [B, T, H, 64]."""
+    return _matrix_bwd("rwkv6_wkv_bwd", True, r, k, v, x, u, d_o, state_in, d_state_out,
+                       grads, workspace, stream)
+
+
+def workspace_bytes(B, T, H, N=64):
+    """Bytes of device workspace the backward needs."""
+    return int(lib().rwkv_wkv_bwd_workspace_bytes(B, T, H, N))

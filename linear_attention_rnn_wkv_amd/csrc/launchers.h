@@ -33,12 +33,24 @@ hipError_t launch_wkv_step(bool per_token_decay, int B, int T, int H, const uint
                            const uint16_t *k, const uint16_t *v, const float *x,
                            const float *u, float *state, uint16_t *o, hipStream_t stream);
 
-// Eagle / Finch chunked (time-parallel) path, N = 64.
+// Eagle / Finch chunked (time-parallel) path, N = 64.  With chunk_states
+// non-NULL it writes, instead of o and state_out, the state entering every
+// chunk and the final state: [B H][ceil(T/64) + 1][64][64] fp32.
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
                               const uint16_t *r, const uint16_t *k,
                               const uint16_t *v, const float *x, const float *u,
                               const float *state_in, float *state_out,
-                              uint16_t *o, hipStream_t stream);
+                              uint16_t *o, hipStream_t stream,
+                              float *chunk_states = nullptr);
+
+// Eagle / Finch chunked backward, N = 64: workspace size and launch (the
+// forward's state recomputation, the reverse sweep, the sums over sequences).
+size_t wkv_bwd_workspace_bytes(int B, int T, int H);
+hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint16_t *r,
+                          const uint16_t *k, const uint16_t *v, const float *x, const float *u,
+                          const float *state_in, const uint16_t *d_o, const float *d_sT,
+                          uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
+                          float *d_s0, void *workspace, hipStream_t stream);
 
 // Fill n floats with `value` (used for empty / zero states when T == 0).
 hipError_t launch_fill(float *dst, int64_t n, float value, hipStream_t stream);

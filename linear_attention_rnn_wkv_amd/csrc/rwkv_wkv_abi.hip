@@ -117,6 +117,54 @@ int matrix_step(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                                            (hipStream_t)stream));
 }
 
+int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
+               const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
+               const float *state_in, const rwkv_bf16 *d_o, const float *d_state_out,
+               rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
+               float *d_state_in, void *workspace, size_t workspace_bytes, void *stream) {
+    if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
+    const int64_t tok = checked_mul({B, T, H, N});
+    const int64_t st = checked_mul({B, H, N, N});
+    const int64_t hn = checked_mul({H, N});
+    if (tok < 0 || st < 0 || hn < 0) return RWKV_E_DIM;
+    if (N != 64) return RWKV_E_UNSUPPORTED;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
+    const int64_t x_elems = per_token ? tok : hn;
+    const int64_t dx_elems = per_token ? tok : hn;
+    if (x == nullptr || u == nullptr || d_x == nullptr || d_u == nullptr) return RWKV_E_NULL;
+    if (T > 0 && (r == nullptr || k == nullptr || v == nullptr || d_o == nullptr ||
+                  d_r == nullptr || d_k == nullptr || d_v == nullptr || workspace == nullptr))
+        return RWKV_E_NULL;
+    for (const void *p : {(const void *)r, (const void *)k, (const void *)v, (const void *)x,
+                          (const void *)u, (const void *)state_in, (const void *)d_o,
+                          (const void *)d_state_out, (const void *)d_r, (const void *)d_k,
+                          (const void *)d_v, (const void *)d_x, (const void *)d_u,
+                          (const void *)d_state_in, (const void *)workspace})
+        if (p != nullptr && !aligned(p, 16)) return RWKV_E_ALIGN;
+    const size_t need = T > 0 ? wkv::wkv_bwd_workspace_bytes(B, T, H) : 0;
+    if (T > 0 && workspace_bytes < need) return RWKV_E_DIM;
+    const Span sr{r, tok * 2}, sk{k, tok * 2}, sv{v, tok * 2}, sx{x, x_elems * 4},
+        su{u, hn * 4}, ssi{state_in, st * 4}, sdo{d_o, tok * 2}, sdso{d_state_out, st * 4},
+        sdr{d_r, tok * 2}, sdk{d_k, tok * 2}, sdv{d_v, tok * 2}, sdx{d_x, dx_elems * 4},
+        sdu{d_u, hn * 4}, sdsi{d_state_in, st * 4}, sws{workspace, (int64_t)need};
+    const int chk = check_outputs({sdr, sdk, sdv, sdx, sdu, sdsi, sws},
+                                  {sr, sk, sv, sx, su, ssi, sdo, sdso}, d_state_in, d_state_out);
+    if (chk != RWKV_OK) return chk;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {  // no tokens: dS_0 = dS_T; the parameter gradients are zero
+        hipError_t e = wkv::launch_fill(d_u, hn, 0.0f, s);
+        if (e == hipSuccess && !per_token) e = wkv::launch_fill(d_x, hn, 0.0f, s);
+        if (e == hipSuccess && d_state_in != nullptr)
+            e = d_state_out ? hipMemcpyAsync(d_state_in, d_state_out, st * 4,
+                                             hipMemcpyDeviceToDevice, s)
+                            : wkv::launch_fill(d_state_in, st, 0.0f, s);
+        return hip_status(e);
+    }
+    return hip_status(wkv::launch_wkv_bwd(per_token, B, T, H, r, k, v, x, u, state_in, d_o,
+                                          d_state_out, d_r, d_k, d_v, d_x, d_u, d_state_in,
+                                          workspace, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +255,29 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
                   const rwkv_bf16 *v, const float *x, const float *u,
                   const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
     return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+}
+
+size_t rwkv_wkv_bwd_workspace_bytes(int B, int T, int H, int N) {
+    if (B < 1 || T < 1 || H < 1 || N != 64) return 0;
+    return wkv::wkv_bwd_workspace_bytes(B, T, H);
+}
+
+int rwkv5_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                  const rwkv_bf16 *v, const float *x, const float *u, const float *state_in,
+                  const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
+                  rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u, float *d_state_in,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    return matrix_bwd(false, B, T, H, N, r, k, v, x, u, state_in, d_o, d_state_out, d_r, d_k,
+                      d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream);
+}
+
+int rwkv6_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                  const rwkv_bf16 *v, const float *x, const float *u, const float *state_in,
+                  const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
+                  rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u, float *d_state_in,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    return matrix_bwd(true, B, T, H, N, r, k, v, x, u, state_in, d_o, d_state_out, d_r, d_k,
+                      d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream);
 }
 
 int rwkv5_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,

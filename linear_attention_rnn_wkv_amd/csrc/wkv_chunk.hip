@@ -62,153 +62,17 @@
 
 #include "launchers.h"
 #include "wkv_device.h"
+#include "wkv_tiles.h"
 
 namespace wkv {
 namespace {
 
-constexpr int kN = 64;     // head size
-constexpr int kL = 64;     // chunk length
-// LDS row pitches (bf16 elements) of the 64x64 tiles.  Rows read whole by
-// 16-byte loads (r~, the decayed state) are 72 elements apart: 8 lanes reading
-// rows c..c+7 hit 32 distinct banks.  Tiles read down their columns by the
-// transposing load (k^_hi, k^_lo, v) are 80 apart: the 4 rows x 4 column
-// groups that 16 lanes address then also cover 32 distinct banks.
-constexpr int kPR = 72;
-constexpr int kPC = 80;
-constexpr int kTile = kN * kPC;
-// Smallest chunk log2-decay (per channel) handled by the factorised form:
-// r~ <= |r| 2^110 and k^ >= |k| 2^-110 stay far from fp32 / bf16 limits.
-constexpr float kSafeLog2 = -110.0f;
+using namespace tiles;
 
 // LDS tiles, all row-major: r~, k^_hi, k^_lo, v as [token][channel]; the
 // decayed state as [j][i].
 enum { T_RS = 0, T_KRH, T_KRL, T_VR, T_ST, T_COUNT };
 __device__ constexpr int pitch(int t) { return (t == T_RS || t == T_ST) ? kPR : kPC; }
-
-template <int NW>
-struct Raw {                           // one thread's share of a chunk
-    static constexpr int TP = 16 / NW; // tokens per staging thread
-    static constexpr int NV = 8 / NW;  // v rows per thread
-    // 16 channel quads x (64 NW / 16) token groups x TP tokens cover the chunk
-    static_assert(TP * (64 * NW / 16) == kL, "staging threads must cover the chunk");
-    static_assert(NV * 8 * NW * 8 == kL * 8, "v loaders must cover the chunk");
-    u32x2 r[TP], k[TP];                // TP tokens x 4 channels, bf16
-    f32x4 x[TP];                       // Finch decay logits
-    u32x4 v[NV];                       // NV tokens x 8 channels, bf16
-};
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
-    return *(const bf16x8 *)p;
-}
-// transposing 8-byte LDS load (see the file comment)
-__device__ __forceinline__ u32x2 lds_tr(const uint16_t *p) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4i16 *lds_v4i16;
-    const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)p);
-    return __builtin_bit_cast(u32x2, t);
-}
-// column (n0 + c) of rows k0..k0+7 of a row-major tile, for lane c of its
-// 16-lane group: the operand of a product that contracts over rows
-__device__ __forceinline__ bf16x8 lds_col8(const uint16_t *tile, int k0, int n0, int c) {
-    const uint16_t *p = tile + (k0 + (c >> 2)) * kPC + n0 + 4 * (c & 3);
-    const u32x2 a = lds_tr(p), b = lds_tr(p + 4 * kPC);
-    const u32x4 m = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, m);
-}
-// rows k0..k0+3 and k1..k1+3 of column (n0 + c)
-__device__ __forceinline__ bf16x8 lds_col4x2(const uint16_t *tile, int k0, int k1, int n0,
-                                             int c) {
-    const int off = (c >> 2) * kPC + n0 + 4 * (c & 3);
-    const u32x2 a = lds_tr(tile + k0 * kPC + off), b = lds_tr(tile + k1 * kPC + off);
-    const u32x4 m = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, m);
-}
-// Workgroup barrier for LDS traffic only: this wave's LDS operations have
-// completed (lgkmcnt(0)) before it arrives.  Unlike __syncthreads() it does
-// not order global memory, which no thread here reads after another wrote
-// it; the empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xf, 0xf, true));
-}
-// sum over the 16 lanes of a DPP row (every lane receives the total)
-__device__ __forceinline__ float row_sum16(float s) {
-    s += dpp<0x128>(s);  // row_ror:8
-    s += dpp<0x124>(s);  // row_ror:4
-    s += dpp<0x4e>(s);   // quad_perm [2,3,0,1]
-    s += dpp<0xb1>(s);   // quad_perm [1,0,3,2]
-    return s;
-}
-__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
-    const u32x2 r = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
-    return r;
-}
-__device__ __forceinline__ bf16x8 pack8(const f32x4 &lo, const f32x4 &hi) {
-    const u32x4 m = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                     pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-    return __builtin_bit_cast(bf16x8, m);
-}
-
-// Raw buffer resource over `bytes` bytes from `base` (gfx9 layout: no
-// stride, no swizzle, 32-bit data format): a load past the end returns zero
-// and a store past the end is dropped, which is how a ragged last chunk is
-// masked without branches.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
-}
-
-struct Ctx {
-    int T, tq, cq, vt, vo;
-    size_t seq_base, tok_stride;  // elements
-    uint32_t tokb;                // bytes of one bf16 token row (H N 2)
-    uint32_t off_rk, off_v;       // byte offsets of this thread's first r/k and v rows
-    // bf16 bytes of chunk c0's rows up to its last valid token, and the
-    // element offset of the chunk
-    __device__ uint32_t span(int c0) const { return (uint32_t)(min(kL, T - c0) - 1) * tokb + 2 * kN; }
-    __device__ size_t base(int c0) const { return seq_base + (size_t)c0 * tok_stride; }
-};
-
-// one thread's r, k, v of chunk c0 (rows past T read as zero)
-template <int NW>
-__device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
-                                         const uint16_t *r, const uint16_t *k,
-                                         const uint16_t *v) {
-    constexpr int TP = Raw<NW>::TP;
-    const size_t cb = cx.base(c0);
-    const uint32_t span = cx.span(c0);
-    const Rsrc rr = rsrc(r + cb, span), rk = rsrc(k + cb, span), rv = rsrc(v + cb, span);
-#pragma unroll
-    for (int e = 0; e < TP; ++e) {
-        const uint32_t off = cx.off_rk + e * cx.tokb;
-        d.r[e] = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
-        d.k[e] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < Raw<NW>::NV; ++j)
-        d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0, 0);
-}
-
-// one thread's Finch decay logits of chunk c0 (rows past T read as zero)
-template <int NW>
-__device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const float *x) {
-    constexpr int TP = Raw<NW>::TP;
-    const Rsrc rx = rsrc(x + cx.base(c0), 2 * cx.span(c0));
-#pragma unroll
-    for (int e = 0; e < TP; ++e)
-        d.x[e] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (cx.off_rk + e * cx.tokb), 0, 0));
-}
 
 // Balanced split of B*H = first_extra + extra heads over first_extra
 // workgroups (see the kernel); extra == 0: one head per workgroup.
@@ -218,12 +82,15 @@ struct Split {
     unsigned *flags;  // [max_slots] slot flags, then an error word
 };
 
-template <bool PT, int NW>
+// SAVE: instead of the outputs and the final state, store the state entering
+// every chunk and the final state, [B H][nchunks + 1][64][64] fp32 key-major,
+// for the backward pass.
+template <bool PT, int NW, bool SAVE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x,
     const float *__restrict__ u, const float *state_in, float *state_out,
-    uint16_t *__restrict__ o, Split sp) {
+    uint16_t *__restrict__ o, Split sp, float *chunk_states) {
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
@@ -308,7 +175,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int e = 0; e < 4; ++e)
                 S[t][e] = state_in ? state_in[base + sidx(t, e)] : 0.0f;
     };
+    // the state entering chunk ch of the current head (SAVE)
+    auto save_chunk = [&](int ch) {
+        const size_t base = ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) chunk_states[base + sidx(t, e)] = S[t][e];
+    };
     auto save_state = [&]() {
+        if (SAVE) {
+            save_chunk(nchunks);
+            return;
+        }
         if (state_out == nullptr) return;
         const size_t base = (size_t)bh * kN * kN;
 #pragma unroll
@@ -547,6 +426,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     };
 
     auto store_out = [&](int ch) {
+        if (SAVE) return;
         const int c0 = ch * kL;
         const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
@@ -623,7 +503,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 }
                 acc += __shfl_xor(acc, 16, 64);
                 acc += __shfl_xor(acc, 32, 64);
-                if (g == 0) {
+                if (g == 0 && !SAVE) {
                     const float ov = fmaf(sBonus[set][tau], vj, acc);
                     o[cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 16 * w + c] =
                         (uint16_t)pack_bf16x2(ov, 0.0f);
@@ -670,6 +550,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto step2 = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < ch_end;
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
+        if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(0);
         else token_by_token(ch, 0);
         if (more) stageA(ch + 1, buf, 0);
@@ -691,6 +572,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const bool more = ch + 1 < ch_end;
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
         if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
+        if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(cur);
         else token_by_token(ch, cur);
         bool bad = false;
@@ -812,12 +694,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     save_state();
 }
 
-template <bool PT, int NW>
+template <bool PT, int NW, bool SAVE = false>
 void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
             const float *x, const float *u, const float *state_in, float *state_out,
-            uint16_t *o, const Split &sp, hipStream_t stream) {
-    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0,
-                       stream, T, H, r, k, v, x, u, state_in, state_out, o, sp);
+            uint16_t *o, const Split &sp, hipStream_t stream, float *chunk_states = nullptr) {
+    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW, SAVE>), dim3((unsigned)blocks), dim3(64 * NW),
+                       0, stream, T, H, r, k, v, x, u, state_in, state_out, o, sp,
+                       chunk_states);
 }
 
 // XCDs of the device: workgroups are dealt to them round-robin
@@ -829,7 +712,7 @@ constexpr int kMaxSlots = 4096;
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const uint16_t *r,
                               const uint16_t *k, const uint16_t *v, const float *x,
                               const float *u, const float *state_in, float *state_out,
-                              uint16_t *o, hipStream_t stream) {
+                              uint16_t *o, hipStream_t stream, float *chunk_states) {
     // Eight waves per head while every head has a CU of its own.  With up to
     // half as many heads again, eight waves and the balanced split: one
     // workgroup per CU, each running one head plus one K-th of an extra
@@ -861,6 +744,16 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         }
     }
     const int blocks = (int)(sp.extra ? sp.first_extra : heads);
+    if (chunk_states != nullptr) {  // the backward's state recomputation
+        if (per_token_decay) {
+            if (wide) launch<true, 8, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+            else launch<true, 4, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+        } else {
+            if (wide) launch<false, 8, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+            else launch<false, 4, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+        }
+        return hipGetLastError();
+    }
     if (per_token_decay) {
         if (wide) launch<true, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
         else launch<true, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);

@@ -1,0 +1,749 @@
+// wkv_chunk_bwd.hip -- Eagle (RWKV-5) / Finch (RWKV-6) WKV backward in
+// time-parallel (chunked) mode on gfx950, bf16 MFMA with fp32 accumulation.
+//
+// The forward (RWKV-5/6 summary, blob.wenxiaobai.com, section 4 notation;
+// 4.1.2 "Eagle time mixing"; 4.2.2 "Finch time mixing"), per head:
+//   o_t = r_t S_{t-1} + (r_t diag(u) k_t^T) v_t,  S_t = diag(w_t) S_{t-1} + k_t^T v_t,
+//   w_t = exp(-exp(x_t)) = e^{g_t}.
+// Given dL/do and dL/dS_T, the gradients are, with S_c the state entering a
+// chunk of L = 64 tokens, dS_end the gradient of the state leaving it, Lam
+// the chunk-relative cumulative log-decay (log2 units), r~ = r e^{Lam_{t-1} -
+// Lam_L}, k^ = k e^{Lam_L - Lam_s}, A[t][s] = r~_t . k^_s and dA[t][s] =
+// do_t . v_s for s < t (strictly causal), beta_t = r_t diag(u) k_t^T and
+// dbeta_t = do_t . v_t:
+//   dr_t = e^{Lam_{t-1}-Lam_L} [sum_s dA[t][s] k^_s + do_t (diag(e^{Lam_L}) S_c)^T]
+//          + u k_t dbeta_t
+//   dk_s = e^{Lam_L-Lam_s} [sum_t dA[t][s] r~_t + v_s dS_end^T] + u r_s dbeta_s
+//   dv_s = sum_t A[t][s] do_t + k^_s dS_end + beta_s do_s
+//   dS_c = diag(e^{Lam_L}) (dS_end + R~^T dO),   du = sum_t r_t k_t dbeta_t.
+// The decay gradient needs no state: writing dr^a, dk^a for dr, dk without
+// their bonus terms, every (query t, key s) pair with s < m < t carries the
+// decay of token m, and summing over pairs gives
+//   dg_m = sum_{t > m} r_t dr^a_t - sum_{s >= m} k_s dk^a_s + sum_j (dS_T o S_T)[.][j],
+// the last term being the final state seen as a query after the last token.
+// It is a suffix sum over the sequence, carried across chunks as the sweep
+// runs backwards; dx = dg g (g = -e^x).
+//
+// Passes: the forward kernel first stores the state entering every chunk
+// (and the final state) in the workspace; this kernel then runs one
+// workgroup of four waves per (sequence, head) over the chunks from last to
+// first, carrying dS in registers.  Per chunk, products on the matrix cores
+// (wave w owns token tile w):
+//   dA^T (s <= t tiles), dA and A (t >= s tiles);
+//   dr~^T = K^^T dA^T + S_c dO^T (scaled by e^{Lam_L} per row),
+//   dk^^T = R~^T dA + dS_end V^T,  dv^T = dO^T A + dS_end^T K^^T,
+//   dS   += (R~_hi + R~_lo)^T dO (then scaled by e^{Lam_L} per row).
+// dr~ and dk^ go through LDS in fp32 to the staging threads, which apply the
+// factors and the bonus terms and run the decay-gradient scan.  A chunk
+// whose decay falls below the factorised range (as in the forward) is taken
+// token by token on the VALU, with the states inside it recomputed from S_c.
+#include <type_traits>
+
+#include "launchers.h"
+#include "wkv_device.h"
+#include "wkv_tiles.h"
+
+namespace wkv {
+namespace {
+
+using namespace tiles;
+
+constexpr int NW = 4;            // waves per workgroup
+constexpr int TP = 4;            // tokens per staging thread
+constexpr int kPF = 68;          // pitch (floats) of the fp32 gradient tiles
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// bf16 operand tiles, row-major with pitch kPC: r~ and k^ (hi, lo), v, do
+// as [token][channel]; S_c (hi, lo) as [i][j]; dS_end (hi, lo) transposed,
+// [j][i].  Every operand of the products that form dr~ and dk^ is split
+// into bf16 hi + lo (and so are dA^T, dA): the decay gradient is a
+// difference of suffix sums of r dr and k dk, which amplifies their
+// relative error, and plain bf16 operands (2^-9) would leave it at ~1e-2.
+enum { B_R = 0, B_RL, B_K, B_KL, B_V, B_DO, B_SC, B_SCL, B_DST, B_DSTL, B_COUNT };
+
+// a = hi + lo with hi, lo bf16: the two halves of a product operand
+__device__ __forceinline__ void split8(const f32x4 &a, const f32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+    hi = pack8(a, b);
+    const u32x4 hb = __builtin_bit_cast(u32x4, hi);
+    const f32x4 ra = {a[0] - bf16_lo(hb.x), a[1] - bf16_hi(hb.x), a[2] - bf16_lo(hb.y),
+                      a[3] - bf16_hi(hb.y)};
+    const f32x4 rb = {b[0] - bf16_lo(hb.z), b[1] - bf16_hi(hb.z), b[2] - bf16_lo(hb.w),
+                      b[3] - bf16_hi(hb.w)};
+    lo = pack8(ra, rb);
+}
+__device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
+    return pack4(a[0] - bf16_lo(hi.x), a[1] - bf16_hi(hi.x), a[2] - bf16_lo(hi.y),
+                 a[3] - bf16_hi(hi.y));
+}
+
+template <bool PT>
+__global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
+    int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ x, const float *__restrict__ u,
+    const uint16_t *__restrict__ d_o, const float *__restrict__ d_sT,
+    const float *__restrict__ chunk_states, uint16_t *__restrict__ d_r,
+    uint16_t *__restrict__ d_k, uint16_t *__restrict__ d_v, float *__restrict__ d_x,
+    float *__restrict__ du_part, float *__restrict__ dx_part, float *__restrict__ d_s0) {
+    __shared__ __align__(16) uint16_t sm[B_COUNT][kTile];
+    __shared__ __align__(16) float sDR[kL * kPF];   // dr~ [token][channel]
+    __shared__ __align__(16) float sDK[kL * kPF];   // dk^ [token][channel]
+    __shared__ __align__(16) float sWave[NW][kN];   // per-wave log2-decay totals
+    __shared__ __align__(16) float sDecay[kN];      // e^{Lam_L}
+    __shared__ __align__(16) float sBonus[kL];      // beta_t
+    __shared__ __align__(16) float sDBeta[kL];      // dbeta_t
+    __shared__ __align__(16) float sScan[NW][kN];   // per-wave totals of the dg scan
+    __shared__ __align__(16) float sCF[NW][kN];     // partial rows of sum_j dS_T S_T
+    __shared__ int sBad[NW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H;
+    const int nchunks = (T + kL - 1) / kL;
+
+    Ctx cx;
+    cx.T = T;
+    cx.cq = c;
+    cx.tq = tid >> 4;  // = 4 w + g
+    cx.vt = tid >> 3;
+    cx.vo = tid & 7;
+    cx.tok_stride = (size_t)H * kN;
+    cx.tokb = (uint32_t)H * kN * 2;
+    cx.off_rk = (uint32_t)(TP * cx.tq) * cx.tokb + 8 * cx.cq;
+    cx.off_v = (uint32_t)cx.vt * cx.tokb + 16 * cx.vo;
+    cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
+
+    // dS block of this wave (as the forward's state): key rows
+    // [32 (w/2), +32) x value columns [32 (w%2), +32), four 16x16 tiles;
+    // dS[t][e] = dS[skey(t) + 4 g + e][sval(t) + c]
+    const int skey0 = 32 * (w >> 1), sval0 = 32 * (w & 1);
+    auto skey = [&](int t) { return skey0 + 16 * (t >> 1); };
+    auto sval = [&](int t) { return sval0 + 16 * (t & 1); };
+    auto sidx = [&](int t, int e) { return (skey(t) + 4 * g + e) * kN + sval(t) + c; };
+    f32x4 dS[4];
+
+    const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * c);
+    f32x4 a2e = {0.f, 0.f, 0.f, 0.f};  // Eagle: log2-decay per channel
+    if (!PT) {
+        const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a2e[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
+    }
+
+    // ---- initial dS = dL/dS_T and the final-state term of dg ---------------
+    {
+        const size_t sbase = (size_t)bh * kN * kN;
+        const float *ST = chunk_states + ((size_t)bh * (nchunks + 1) + nchunks) * kN * kN;
+        f32x4 part[2];  // rows skey0 + 16 mi + 4 g + e: sum over this wave's columns
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) part[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dS[t][e] = d_sT ? d_sT[sbase + sidx(t, e)] : 0.0f;
+                part[t >> 1][e] += dS[t][e] * ST[sidx(t, e)];
+            }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[mi][e] = row_sum16(part[mi][e]);
+        if (c == 0)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                *(f32x4 *)&sCF[w][skey0 + 16 * mi + 4 * g] = part[mi];
+    }
+    lds_barrier();
+    // carry of the dg suffix sum for this thread's channels 4 c .. 4 c + 3:
+    // the final-state term, then the totals of the chunks already done
+    f32x4 carry;
+    {
+        const int wa = (4 * c) / 32 * 2;  // the two waves holding these key rows
+        carry = *(const f32x4 *)&sCF[wa][4 * c] + *(const f32x4 *)&sCF[wa + 1][4 * c];
+    }
+    f32x4 du_acc = {0.f, 0.f, 0.f, 0.f}, dx_acc = {0.f, 0.f, 0.f, 0.f};
+    float fb_dx = 0.0f;  // threads < 64: Eagle dx of channel tid from fast-decay chunks
+
+    // fixed thread mapping of the chunk-state tile: row tid/4, 16 columns
+    const int sc_row = tid >> 2, sc_col = 16 * (tid & 3);
+
+    for (int ch = nchunks - 1; ch >= 0; --ch) {
+        const int c0 = ch * kL;
+        // ---- operands of the chunk ----------------------------------------
+        Raw<NW> d;
+        if (PT) load_x<NW>(d, c0, cx, x);
+        load_rkv<NW>(d, c0, cx, r, k, v);
+        u32x4 dov[Raw<NW>::NV];
+        {
+            const Rsrc rd = rsrc(d_o + cx.base(c0), cx.span(c0));
+#pragma unroll
+            for (int j = 0; j < Raw<NW>::NV; ++j)
+                dov[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, cx.off_v + j * 8 * NW * cx.tokb,
+                                                               0, 0);
+        }
+        f32x4 scv[4];
+        {
+            const float *Sc = chunk_states + ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) scv[q] = *(const f32x4 *)(Sc + sc_row * kN + sc_col + 4 * q);
+        }
+
+        // ---- stage A: log2 decays and their in-wave scan -------------------
+        float a2[TP][4], lower[4];
+#pragma unroll
+        for (int e = 0; e < TP; ++e) {
+            const bool valid = c0 + TP * cx.tq + e < T;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                a2[e][q] = !valid ? 0.0f : PT ? -exp2_fast(d.x[e][q] * kLog2e) * kLog2e : a2e[q];
+        }
+        {
+            f32x4 wt;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float s = a2[0][q];
+#pragma unroll
+                for (int e = 1; e < TP; ++e) s += a2[e][q];
+                const float s1 = __shfl_up(s, 16, 64);
+                if (g >= 1) s += s1;
+                const float s2 = __shfl_up(s, 32, 64);
+                if (g >= 2) s += s2;
+                const float ex = __shfl_up(s, 16, 64);
+                lower[q] = (g == 0) ? 0.0f : ex;
+                wt[q] = s;
+            }
+            if (g == 3) *(f32x4 *)&sWave[w][4 * c] = wt;
+        }
+        lds_barrier();  // (1) decay totals
+
+        // ---- stage B: factors, operand tiles, bonus ------------------------
+        f32x4 LL, before = {0.f, 0.f, 0.f, 0.f};
+        {
+            f32x4 part = *(const f32x4 *)&sWave[0][4 * c];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) {
+                if (j == w) before = part;
+                part += *(const f32x4 *)&sWave[j][4 * c];
+            }
+            LL = part;
+        }
+        bool bad = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bad |= LL[q] < kSafeLog2;
+        if (w == 0 && g == 0) {
+            f32x4 dd;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dd[q] = exp2_fast(LL[q]);
+            *(f32x4 *)&sDecay[4 * c] = dd;
+        }
+        float fr[TP][4], fk[TP][4];  // e^{Lam_{t-1} - Lam_L}, e^{Lam_L - Lam_t}
+        {
+            float wv[TP][4], f1[4], f2[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float pre = before[q] + lower[q];
+                float run = pre;
+#pragma unroll
+                for (int e = 0; e < TP; ++e) {
+                    run += a2[e][q];
+                    wv[e][q] = exp2_fast(a2[e][q]);
+                }
+                f1[q] = exp2_fast(pre - LL[q]);
+                f2[q] = exp2_fast(LL[q] - run);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                fk[TP - 1][q] = f2[q];
+#pragma unroll
+                for (int e = TP - 2; e >= 0; --e) fk[e][q] = fk[e + 1][q] * wv[e + 1][q];
+#pragma unroll
+                for (int e = 0; e < TP; ++e) {
+                    fr[e][q] = f1[q];
+                    f1[q] *= wv[e][q];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < TP; ++e) {
+            const int tau = TP * cx.tq + e;
+            const float rr[4] = {bf16_lo(d.r[e].x), bf16_hi(d.r[e].x), bf16_lo(d.r[e].y),
+                                 bf16_hi(d.r[e].y)};
+            const float kk[4] = {bf16_lo(d.k[e].x), bf16_hi(d.k[e].x), bf16_lo(d.k[e].y),
+                                 bf16_hi(d.k[e].y)};
+            float rt[4], rl[4], kh[4], sb = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                rt[q] = rr[q] * fr[e][q];
+                kh[q] = kk[q] * fk[e][q];
+                sb = fmaf(rr[q] * uq[q], kk[q], sb);
+            }
+            const u32x2 hi = pack4(rt[0], rt[1], rt[2], rt[3]);
+            rl[0] = rt[0] - bf16_lo(hi.x);
+            rl[1] = rt[1] - bf16_hi(hi.x);
+            rl[2] = rt[2] - bf16_lo(hi.y);
+            rl[3] = rt[3] - bf16_hi(hi.y);
+            *(u32x2 *)(sm[B_R] + tau * kPC + 4 * c) = hi;
+            *(u32x2 *)(sm[B_RL] + tau * kPC + 4 * c) = pack4(rl[0], rl[1], rl[2], rl[3]);
+            const u32x2 khi = pack4(kh[0], kh[1], kh[2], kh[3]);
+            *(u32x2 *)(sm[B_K] + tau * kPC + 4 * c) = khi;
+            *(u32x2 *)(sm[B_KL] + tau * kPC + 4 * c) = lo4(f32x4{kh[0], kh[1], kh[2], kh[3]}, khi);
+            const float bs = row_sum16(sb);
+            if (c == 0) sBonus[tau] = bs;
+        }
+#pragma unroll
+        for (int j = 0; j < Raw<NW>::NV; ++j) {
+            *(u32x4 *)(sm[B_V] + (cx.vt + 8 * NW * j) * kPC + 8 * cx.vo) = d.v[j];
+            *(u32x4 *)(sm[B_DO] + (cx.vt + 8 * NW * j) * kPC + 8 * cx.vo) = dov[j];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 hi = pack4(scv[q][0], scv[q][1], scv[q][2], scv[q][3]);
+            *(u32x2 *)(sm[B_SC] + sc_row * kPC + sc_col + 4 * q) = hi;
+            *(u32x2 *)(sm[B_SCL] + sc_row * kPC + sc_col + 4 * q) = lo4(scv[q], hi);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const u32x2 hi = pack4(dS[t][0], dS[t][1], dS[t][2], dS[t][3]);
+            *(u32x2 *)(sm[B_DST] + (sval(t) + c) * kPC + skey(t) + 4 * g) = hi;
+            *(u32x2 *)(sm[B_DSTL] + (sval(t) + c) * kPC + skey(t) + 4 * g) = lo4(dS[t], hi);
+        }
+        // (2) operands staged; the range flag is uniform over the workgroup
+        const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) sBad[w] = any ? 1 : 0;
+        lds_barrier();
+        const bool unsafe = (sBad[0] | sBad[1] | sBad[2] | sBad[3]) != 0;
+        if (unsafe) {
+            // ---- fast-decay chunk: its tokens one at a time, backwards -----
+            // Raw r, k (bf16) and w (fp32) are staged in the factor tiles,
+            // whose products this chunk does not run.  Wave w holds columns
+            // [16 w, +16) of dS and of the recomputed state:
+            // X[m][e] = X[16 m + 4 g + e][16 w + c].  For each token the state
+            // before it is recomputed from S_c (quadratic in the chunk length,
+            // exact at any decay); the row sums over the columns are formed
+            // per wave and added over the waves through LDS.
+            uint16_t *tr = sm[B_R], *tk = sm[B_RL];
+            float *tw = (float *)sm[B_SC];       // [64][64] fp32 over B_SC, B_DST
+            float *red = (float *)sm[B_K];       // [2][3][NW][64] partial row sums
+            float *xfer = sDR;                   // layout changes of dS
+#pragma unroll
+            for (int e = 0; e < TP; ++e) {
+                const int tau = TP * cx.tq + e;
+                *(u32x2 *)(tr + tau * kPC + 4 * c) = d.r[e];
+                *(u32x2 *)(tk + tau * kPC + 4 * c) = d.k[e];
+                f32x4 wv;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wv[q] = exp2_fast(a2[e][q]);
+                *(f32x4 *)(tw + tau * kN + 4 * c) = wv;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xfer[(skey(t) + 4 * g + e) * kPF + sval(t) + c] = dS[t][e];
+            if (tid < kL) {  // dbeta of every token of the chunk
+                float db = 0.0f;
+                for (int j = 0; j < kN; ++j)
+                    db = fmaf(bf16_to_f32(sm[B_DO][tid * kPC + j]), bf16_to_f32(sm[B_V][tid * kPC + j]), db);
+                sDBeta[tid] = db;
+            }
+            lds_barrier();
+            f32x4 dSc[4], Sc0[4];
+            const float *Sg = chunk_states + ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dSc[m][e] = xfer[(16 * m + 4 * g + e) * kPF + 16 * w + c];
+                    Sc0[m][e] = Sg[(16 * m + 4 * g + e) * kN + 16 * w + c];
+                }
+            lds_barrier();  // xfer (sDR) is free again
+            const int nvalid = min(kL, T - c0);
+            const int j = 16 * w + c;
+            for (int tau = nvalid - 1; tau >= 0; --tau) {
+                f32x4 Sw[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Sw[m] = Sc0[m];
+                for (int t2 = 0; t2 < tau; ++t2) {
+                    const float vj = bf16_to_f32(sm[B_V][t2 * kPC + j]);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const f32x4 wv = *(const f32x4 *)(tw + t2 * kN + 16 * m + 4 * g);
+                        const u32x2 kp = *(const u32x2 *)(tk + t2 * kPC + 16 * m + 4 * g);
+                        const float k4[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y), bf16_hi(kp.y)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Sw[m][e] = fmaf(wv[e], Sw[m][e], k4[e] * vj);
+                    }
+                }
+                const float vj = bf16_to_f32(sm[B_V][tau * kPC + j]);
+                const float doj = bf16_to_f32(sm[B_DO][tau * kPC + j]);
+                float* rb = red + (tau & 1) * 3 * NW * kN;
+                float dvj = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const u32x2 kp = *(const u32x2 *)(tk + tau * kPC + 16 * m + 4 * g);
+                    const u32x2 rp = *(const u32x2 *)(tr + tau * kPC + 16 * m + 4 * g);
+                    const f32x4 wv = *(const f32x4 *)(tw + tau * kN + 16 * m + 4 * g);
+                    const float k4[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y), bf16_hi(kp.y)};
+                    const float r4[4] = {bf16_lo(rp.x), bf16_hi(rp.x), bf16_lo(rp.y), bf16_hi(rp.y)};
+                    f32x4 pr, pk, pw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pr[e] = row_sum16(doj * Sw[m][e]);        // dr^a: do . S row
+                        pk[e] = row_sum16(dSc[m][e] * vj);        // dk^a: dS' row . v
+                        pw[e] = row_sum16(dSc[m][e] * Sw[m][e]);  // dw
+                        dvj = fmaf(dSc[m][e], k4[e], dvj);
+                        dSc[m][e] = fmaf(wv[e], dSc[m][e], r4[e] * doj);
+                    }
+                    if (c == 0) {
+                        *(f32x4 *)(rb + (0 * NW + w) * kN + 16 * m + 4 * g) = pr;
+                        *(f32x4 *)(rb + (1 * NW + w) * kN + 16 * m + 4 * g) = pk;
+                        *(f32x4 *)(rb + (2 * NW + w) * kN + 16 * m + 4 * g) = pw;
+                    }
+                }
+                dvj += __shfl_xor(dvj, 16, 64);
+                dvj += __shfl_xor(dvj, 32, 64);
+                if (g == 0)
+                    d_v[cx.base(c0) + (size_t)tau * cx.tok_stride + j] =
+                        (uint16_t)pack_bf16x2(fmaf(sBonus[tau], doj, dvj), 0.0f);
+                lds_barrier();
+                if (tid < kN) {
+                    float a = 0.0f, bsum = 0.0f, dw = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NW; ++q) {
+                        a += rb[(0 * NW + q) * kN + tid];
+                        bsum += rb[(1 * NW + q) * kN + tid];
+                        dw += rb[(2 * NW + q) * kN + tid];
+                    }
+                    sDR[tau * kPF + tid] = a;
+                    sDK[tau * kPF + tid] = bsum;
+                    // dL/dg = dw w, dL/dx = dL/dg g with g = ln w = log2(w) ln 2
+                    const float wt = tw[tau * kN + tid];
+                    const float xg = PT ? x[cx.base(c0) + (size_t)tau * cx.tok_stride + tid]
+                                        : x[(size_t)h * kN + tid];
+                    const float gnat = -exp2_fast(xg * kLog2e);
+                    const float dxv = dw * wt * gnat;
+                    if (PT) d_x[cx.base(c0) + (size_t)tau * cx.tok_stride + tid] = dxv;
+                    else fb_dx += dxv;
+                }
+            }
+            // dS back to the block layout (after the last reads of w)
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tw[(16 * m + 4 * g + e) * kN + 16 * w + c] = dSc[m][e];
+            lds_barrier();
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dS[t][e] = tw[(skey(t) + 4 * g + e) * kN + sval(t) + c];
+        }
+        // ---- products -----------------------------------------------------
+        const Rsrc rdv = rsrc(d_v + cx.base(c0), cx.span(c0));
+        auto products = [&](auto tile) {
+            constexpr int P = decltype(tile)::value;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            // dA^T[s][t] = v_s . do_t: s-tiles q <= P, t-tile P
+            f32x4 dat[P + 1];
+#pragma unroll
+            for (int q = 0; q <= P; ++q) {
+                dat[q] = zero;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    dat[q] = mfma(lds8(sm[B_V] + (16 * q + c) * kPC + 32 * kb + 8 * g),
+                                  lds8(sm[B_DO] + (16 * P + c) * kPC + 32 * kb + 8 * g), dat[q]);
+            }
+            // diagonal: dbeta_t, then the strict causal mask (s < t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * g + e;
+                if (sl == c) sDBeta[16 * P + c] = dat[P][e];
+                dat[P][e] = sl < c ? dat[P][e] : 0.0f;
+            }
+            // dA[t][s] and A[t][s]: t-tiles q >= P, s-tile P
+            f32x4 da[4 - P], aa[4 - P];
+#pragma unroll
+            for (int q = P; q < 4; ++q) {
+                da[q - P] = zero;
+                aa[q - P] = zero;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    da[q - P] = mfma(lds8(sm[B_DO] + (16 * q + c) * kPC + 32 * kb + 8 * g),
+                                     lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g), da[q - P]);
+                    aa[q - P] = mfma(lds8(sm[B_R] + (16 * q + c) * kPC + 32 * kb + 8 * g),
+                                     lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g), aa[q - P]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {  // diagonal tile: keep t > s
+                const int tl = 4 * g + e;
+                da[0][e] = tl > c ? da[0][e] : 0.0f;
+                aa[0][e] = tl > c ? aa[0][e] : 0.0f;
+            }
+            // dr~^T[i][t] (t = 16 P + c): K^^T dA^T + diag(e^{Lam_L}) S_c dO^T
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                f32x4 acc = zero, st = zero;
+#pragma unroll
+                for (int bk = 0; 2 * bk <= P; ++bk) {
+                    bf16x8 Bh, Bl;
+                    split8(dat[2 * bk], (2 * bk + 1 <= P) ? dat[(2 * bk + 1) % (P + 1)] : zero, Bh, Bl);
+                    const bf16x8 Ah = lds_col4x2(sm[B_K], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g, 16 * ii, c);
+                    const bf16x8 Al = lds_col4x2(sm[B_KL], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g, 16 * ii, c);
+                    acc = mfma(Ah, Bh, acc);
+                    acc = mfma(Ah, Bl, acc);
+                    acc = mfma(Al, Bh, acc);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 Bd = lds8(sm[B_DO] + (16 * P + c) * kPC + 32 * kb + 8 * g);
+                    st = mfma(lds8(sm[B_SC] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bd, st);
+                    st = mfma(lds8(sm[B_SCL] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bd, st);
+                }
+                const f32x4 dd = *(const f32x4 *)&sDecay[16 * ii + 4 * g];
+                acc += st * dd;
+                *(f32x4 *)&sDR[(16 * P + c) * kPF + 16 * ii + 4 * g] = acc;
+            }
+            // dk^^T[i][s] (s = 16 P + c): R~^T dA + dS_end V^T
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                f32x4 acc = zero;
+#pragma unroll
+                for (int bk = P / 2; bk < 2; ++bk) {
+                    const f32x4 t0 = (2 * bk >= P) ? da[2 * bk >= P ? 2 * bk - P : 0] : zero;
+                    const f32x4 t1 = (2 * bk + 1 >= P) ? da[2 * bk + 1 >= P ? 2 * bk + 1 - P : 0] : zero;
+                    bf16x8 Bh, Bl;
+                    split8(t0, t1, Bh, Bl);
+                    const bf16x8 Ah = lds_col4x2(sm[B_R], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g, 16 * ii, c);
+                    const bf16x8 Al = lds_col4x2(sm[B_RL], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g, 16 * ii, c);
+                    acc = mfma(Ah, Bh, acc);
+                    acc = mfma(Ah, Bl, acc);
+                    acc = mfma(Al, Bh, acc);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 Bv = lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g);
+                    acc = mfma(lds_col8(sm[B_DST], 32 * kb + 8 * g, 16 * ii, c), Bv, acc);
+                    acc = mfma(lds_col8(sm[B_DSTL], 32 * kb + 8 * g, 16 * ii, c), Bv, acc);
+                }
+                *(f32x4 *)&sDK[(16 * P + c) * kPF + 16 * ii + 4 * g] = acc;
+            }
+            // dv^T[j][s] (s = 16 P + c): dO^T A + dS_end^T K^^T, plus beta_s do_s
+            const float bon = sBonus[16 * P + c];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 acc = zero;
+#pragma unroll
+                for (int bk = P / 2; bk < 2; ++bk) {
+                    const f32x4 t0 = (2 * bk >= P) ? aa[2 * bk >= P ? 2 * bk - P : 0] : zero;
+                    const f32x4 t1 = (2 * bk + 1 >= P) ? aa[2 * bk + 1 >= P ? 2 * bk + 1 - P : 0] : zero;
+                    acc = mfma(lds_col4x2(sm[B_DO], 32 * bk + 4 * g, 32 * bk + 16 + 4 * g, 16 * jj, c),
+                               pack8(t0, t1), acc);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    acc = mfma(lds8(sm[B_DST] + (16 * jj + c) * kPC + 32 * kb + 8 * g),
+                               lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g), acc);
+                const u32x2 dop = *(const u32x2 *)(sm[B_DO] + (16 * P + c) * kPC + 16 * jj + 4 * g);
+                acc[0] = fmaf(bon, bf16_lo(dop.x), acc[0]);
+                acc[1] = fmaf(bon, bf16_hi(dop.x), acc[1]);
+                acc[2] = fmaf(bon, bf16_lo(dop.y), acc[2]);
+                acc[3] = fmaf(bon, bf16_hi(dop.y), acc[3]);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    pack4(acc[0], acc[1], acc[2], acc[3]), rdv,
+                    (uint32_t)(16 * P + c) * cx.tokb + 2 * (16 * jj + 4 * g), 0, 0);
+            }
+            // dS_c = diag(e^{Lam_L}) (dS_end + (R~_hi + R~_lo)^T dO)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int k0 = 32 * kb + 8 * g;
+                bf16x8 Bd[2];
+#pragma unroll
+                for (int vj = 0; vj < 2; ++vj) Bd[vj] = lds_col8(sm[B_DO], k0, sval0 + 16 * vj, c);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) {
+                    const bf16x8 Ah = lds_col8(sm[B_R], k0, skey0 + 16 * mi, c);
+                    const bf16x8 Al = lds_col8(sm[B_RL], k0, skey0 + 16 * mi, c);
+#pragma unroll
+                    for (int vj = 0; vj < 2; ++vj) {
+                        dS[2 * mi + vj] = mfma(Ah, Bd[vj], dS[2 * mi + vj]);
+                        dS[2 * mi + vj] = mfma(Al, Bd[vj], dS[2 * mi + vj]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dS[t] *= *(const f32x4 *)&sDecay[skey(t) + 4 * g];
+        };
+        if (!unsafe) {
+            switch (w) {  // wave-uniform
+                case 0: products(std::integral_constant<int, 0>{}); break;
+                case 1: products(std::integral_constant<int, 1>{}); break;
+                case 2: products(std::integral_constant<int, 2>{}); break;
+                default: products(std::integral_constant<int, 3>{}); break;
+            }
+        }
+        lds_barrier();  // (3) dr~, dk^, dbeta in LDS
+
+        // ---- dr, dk, du and the decay-gradient scan -------------------------
+        f32x4 Dsum;       // this thread's D = r dr^a - k dk^a summed over its tokens
+        float Dv[TP][4], rdr[TP][4];
+        {
+            const Rsrc rr_ = rsrc(d_r + cx.base(c0), cx.span(c0));
+            const Rsrc rk_ = rsrc(d_k + cx.base(c0), cx.span(c0));
+#pragma unroll
+            for (int e = 0; e < TP; ++e) {
+                const int tau = TP * cx.tq + e;
+                const f32x4 dr4 = *(const f32x4 *)&sDR[tau * kPF + 4 * c];
+                const f32x4 dk4 = *(const f32x4 *)&sDK[tau * kPF + 4 * c];
+                const float db = sDBeta[tau];
+                const float rr[4] = {bf16_lo(d.r[e].x), bf16_hi(d.r[e].x), bf16_lo(d.r[e].y),
+                                     bf16_hi(d.r[e].y)};
+                const float kk[4] = {bf16_lo(d.k[e].x), bf16_hi(d.k[e].x), bf16_lo(d.k[e].y),
+                                     bf16_hi(d.k[e].y)};
+                float drv[4], dkv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float dra = unsafe ? dr4[q] : dr4[q] * fr[e][q];
+                    const float dka = unsafe ? dk4[q] : dk4[q] * fk[e][q];
+                    drv[q] = fmaf(uq[q] * kk[q], db, dra);
+                    dkv[q] = fmaf(uq[q] * rr[q], db, dka);
+                    rdr[e][q] = rr[q] * dra;
+                    Dv[e][q] = rdr[e][q] - kk[q] * dka;
+                    du_acc[q] = fmaf(rr[q] * kk[q], db, du_acc[q]);
+                }
+                const uint32_t off = cx.off_rk + e * cx.tokb;
+                __builtin_amdgcn_raw_buffer_store_b64(pack4(drv[0], drv[1], drv[2], drv[3]), rr_, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(pack4(dkv[0], dkv[1], dkv[2], dkv[3]), rk_, off, 0, 0);
+            }
+            // suffix sums: within the thread, then over the later token groups
+            // of the wave (lanes 16 and 32 above), then over the later waves
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int e = TP - 2; e >= 0; --e) Dv[e][q] += Dv[e + 1][q];
+                float s = Dv[0][q];
+                const float s1 = __shfl_down(s, 16, 64);
+                if (g <= 2) s += s1;
+                const float s2 = __shfl_down(s, 32, 64);
+                if (g <= 1) s += s2;
+                Dsum[q] = s - Dv[0][q];  // exclusive: later groups of this wave
+                if (g == 0) sScan[w][4 * c + q] = s;
+            }
+        }
+        lds_barrier();  // (4) wave totals of the scan
+        {
+            f32x4 later = {0.f, 0.f, 0.f, 0.f}, total = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = NW - 1; j >= 0; --j) {
+                const f32x4 t = *(const f32x4 *)&sScan[j][4 * c];
+                if (j > w) later += t;
+                total += t;
+            }
+            f32x4 dxv[TP];
+#pragma unroll
+            for (int e = 0; e < TP; ++e)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // suffix over the tokens from this one on, minus its own r dr^a
+                    const float dg = carry[q] + later[q] + Dsum[q] + Dv[e][q] - rdr[e][q];
+                    dxv[e][q] = dg * a2[e][q] * kLn2;
+                    if (!unsafe) dx_acc[q] += dxv[e][q];
+                }
+            // (a fast-decay chunk wrote its decay gradient from dw directly)
+            if (PT && !unsafe) {
+                const Rsrc rx = rsrc(d_x + cx.base(c0), 2 * cx.span(c0));
+#pragma unroll
+                for (int e = 0; e < TP; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dxv[e]), rx,
+                                                           2 * (cx.off_rk + e * cx.tokb), 0, 0);
+            }
+            carry += total;
+        }
+    }
+
+    // ---- gradient of the initial state, partial du (and Eagle dx) ----------
+    if (d_s0 != nullptr) {
+        const size_t sbase = (size_t)bh * kN * kN;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d_s0[sbase + sidx(t, e)] = dS[t][e];
+    }
+    // sum over the 16 token groups: lanes 16 and 32 apart, then the waves
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        du_acc[q] += __shfl_xor(du_acc[q], 16, 64);
+        du_acc[q] += __shfl_xor(du_acc[q], 32, 64);
+        dx_acc[q] += __shfl_xor(dx_acc[q], 16, 64);
+        dx_acc[q] += __shfl_xor(dx_acc[q], 32, 64);
+    }
+    lds_barrier();
+    if (g == 0) {
+        *(f32x4 *)&sScan[w][4 * c] = du_acc;
+        *(f32x4 *)&sCF[w][4 * c] = dx_acc;
+    }
+    lds_barrier();
+    if (tid < kN) {
+        float su = 0.0f, sx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            su += sScan[j][tid];
+            sx += sCF[j][tid];
+        }
+        du_part[(size_t)bh * kN + tid] = su;
+        if (!PT) dx_part[(size_t)bh * kN + tid] = sx + fb_dx;
+    }
+}
+
+// out[h][i] = sum over b of part[b][h][i], in sequence order
+__global__ void sum_over_batch_kernel(int B, int HN, const float *part, float *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= HN) return;
+    float s = 0.0f;
+    for (int b = 0; b < B; ++b) s += part[(size_t)b * HN + i];
+    out[i] = s;
+}
+
+}  // namespace
+
+size_t wkv_bwd_workspace_bytes(int B, int T, int H) {
+    const size_t nchunks = (size_t)(T + kL - 1) / kL;
+    return (size_t)B * H * (nchunks + 1) * kN * kN * 4 + 2 * (size_t)B * H * kN * 4;
+}
+
+hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint16_t *r,
+                          const uint16_t *k, const uint16_t *v, const float *x, const float *u,
+                          const float *state_in, const uint16_t *d_o, const float *d_sT,
+                          uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
+                          float *d_s0, void *workspace, hipStream_t stream) {
+    const size_t nchunks = (size_t)(T + kL - 1) / kL;
+    float *chunk_states = (float *)workspace;
+    float *du_part = chunk_states + (size_t)B * H * (nchunks + 1) * kN * kN;
+    float *dx_part = du_part + (size_t)B * H * kN;
+    hipError_t e = launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in,
+                                      nullptr, nullptr, stream, chunk_states);
+    if (e != hipSuccess) return e;
+    if (per_token_decay)
+        hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)(B * H)), dim3(256), 0, stream, T,
+                           H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
+                           dx_part, d_s0);
+    else
+        hipLaunchKernelGGL(wkv_bwd_kernel<false>, dim3((unsigned)(B * H)), dim3(256), 0, stream, T,
+                           H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
+                           dx_part, d_s0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int HN = H * kN;
+    hipLaunchKernelGGL(sum_over_batch_kernel, dim3((unsigned)((HN + 255) / 256)), dim3(256), 0,
+                       stream, B, HN, du_part, d_u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!per_token_decay) {
+        hipLaunchKernelGGL(sum_over_batch_kernel, dim3((unsigned)((HN + 255) / 256)), dim3(256), 0,
+                           stream, B, HN, dx_part, d_x);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace wkv

@@ -225,3 +225,72 @@ def test_rwkv4_step_size_limit(L):
     # one thread per (sequence, channel): B * C up to 2^38
     # (the state, 3 * B * C floats, stays within the per-tensor element limit)
     assert rwkv4_step(L, B=1 << 20, T=1, H=286102, N=1) == E_UNSUP
+
+
+# ---------------------------------------------------------------------------
+# backward
+
+BWD_NAMES = ("r", "k", "v", "x", "u", "si", "do", "dso", "dr", "dk", "dv", "dx", "du", "dsi",
+             "ws")
+
+
+def bwd(L, fn="rwkv6_wkv_bwd", B=2, T=8, H=2, N=64, ws_bytes=None, **over):
+    idx = {n: i + 1 for i, n in enumerate(BWD_NAMES)}
+    idx.update({n: v for n, v in over.items() if n in idx})
+    mis = over.get("mis", {})
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
+    if ws_bytes is None:
+        ws_bytes = L.rwkv_wkv_bwd_workspace_bytes(B, max(T, 1), H, N) if N == 64 else 1 << 20
+    return getattr(L, fn)(B, T, H, N, *(a[n] for n in BWD_NAMES[:-1]), a["ws"], ws_bytes, None)
+
+
+BWDS = ["rwkv5_wkv_bwd", "rwkv6_wkv_bwd"]
+
+
+def test_bwd_workspace_size(L):
+    # the state entering each 64-token chunk plus the final state, per head,
+    # and two per-head partial sums
+    assert L.rwkv_wkv_bwd_workspace_bytes(2, 130, 3, 64) == 2 * 3 * 4 * 64 * 64 * 4 + 2 * 2 * 3 * 64 * 4
+    assert L.rwkv_wkv_bwd_workspace_bytes(2, 130, 3, 32) == 0
+
+
+@pytest.mark.parametrize("fn", BWDS)
+@pytest.mark.parametrize("missing", ["r", "k", "v", "x", "u", "do", "dr", "dk", "dv", "dx", "du",
+                                     "ws"])
+def test_bwd_null(L, fn, missing):
+    assert bwd(L, fn, **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("fn", BWDS)
+def test_bwd_optional_pointers(L, fn):
+    # state_in, d_state_out and d_state_in may be NULL; validation then passes
+    # and only the launch (on fake addresses) is left, which these tests skip
+    # by asking for a too-small workspace
+    assert bwd(L, fn, si=None, dso=None, dsi=None, ws_bytes=16) == E_DIM
+
+
+@pytest.mark.parametrize("fn", BWDS)
+def test_bwd_small_workspace(L, fn):
+    need = L.rwkv_wkv_bwd_workspace_bytes(2, 8, 2, 64)
+    assert bwd(L, fn, ws_bytes=need - 1) == E_DIM
+
+
+@pytest.mark.parametrize("fn", BWDS)
+def test_bwd_head_size_and_dims(L, fn):
+    assert bwd(L, fn, N=32) == E_UNSUP
+    assert bwd(L, fn, B=0) == E_DIM
+    assert bwd(L, fn, T=-1) == E_DIM
+
+
+@pytest.mark.parametrize("fn", BWDS)
+@pytest.mark.parametrize("which", ["r", "do", "dx", "ws", "dsi"])
+def test_bwd_misaligned(L, fn, which):
+    assert bwd(L, fn, mis={which: 8}) == E_ALIGN
+
+
+@pytest.mark.parametrize("fn", BWDS)
+def test_bwd_aliasing(L, fn):
+    assert bwd(L, fn, dr=1) == E_ALIAS    # d_r on r
+    assert bwd(L, fn, dx=9) == E_ALIAS    # d_x on d_r
+    assert bwd(L, fn, ws=7) == E_ALIAS    # workspace on d_o
+    assert bwd(L, fn, mis={"dsi": 16}, dsi=8) == E_ALIAS  # d_state_in partly on d_state_out

@@ -555,3 +555,144 @@ def test_rwkv4_decode_workload7():
     seq = {"k": np.ascontiguousarray(d["k"].transpose(1, 0, 2)),
            "v": np.ascontiguousarray(d["v"].transpose(1, 0, 2)), "w": d["w"], "u": d["u"]}
     rwkv4_assert(seq, y.transpose(0, 1), st)
+
+
+# ---------------------------------------------------------------------------
+# Eagle / Finch backward
+
+def bwd_case(B, T, H, seed, per_token, dst_sigma=0.1, **kw):
+    d = matrix_case(B, T, H, seed, per_token, **kw)
+    d.update(S.grad_inputs(B, T, H, 64, seed, dst_sigma=dst_sigma))
+    return d
+
+
+def bwd_run(d, per_token, ws=None):
+    g = matrix_inputs_dev(d)
+    dO = to_dev(d["d_o"], True)
+    dST = to_dev(d["d_sT"])
+    fn = W.rwkv6_wkv_bwd if per_token else W.rwkv5_wkv_bwd
+    out = fn(g["r"], g["k"], g["v"], g["x"], g["u"], dO, state_in=g["s0"], d_state_out=dST,
+             workspace=ws)
+    sync()
+    return out
+
+
+def bwd_ref(d):
+    r, k, v, x, u, s0 = matrix_inputs_f32(d)
+    return oracle.wkv_matrix_bwd(r, k, v, x, u, S.bf16_to_f32(d["d_o"]), s0, d["d_sT"])
+
+
+def assert_f32_close(got, ref, what):
+    # an fp32 output against the oracle rounded to fp32: where the exact value
+    # underflows fp32 (decay gradients at w = 1 are ~e^-200), zero is exact
+    ref32 = ref.astype(np.float32).astype(np.float64)
+    if not np.any(ref32):
+        assert not np.any(got), f"{what}: expected exact zeros"
+        return
+    assert_matrix_close(got, ref32, what)
+
+
+def bwd_check(d, per_token, what=""):
+    got = bwd_run(d, per_token)
+    ref = bwd_ref(d)
+    for n, key in (("d_r", "dr"), ("d_k", "dk"), ("d_v", "dv")):
+        assert_matrix_close(bf16_host(got[n]), ref[key], f"{what} {n}")
+    assert_f32_close(f64_host(got["d_x"]), ref["dx"], f"{what} d_x")
+    assert_matrix_close(f64_host(got["d_u"]), ref["du"], f"{what} d_u")
+    assert_matrix_close(f64_host(got["d_state_in"]), ref["ds0"], f"{what} d_state_in")
+    return got, ref
+
+
+BWD_SHAPES = [(1, 1, 1), (1, 63, 1), (1, 64, 1), (1, 65, 2), (2, 130, 3), (1, 300, 2),
+              (2, 257, 1)]
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", BWD_SHAPES)
+def test_bwd_vs_oracle(per_token, B, T, H):
+    print(f"bwd {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    bwd_check(bwd_case(B, T, H, 700 + T + H, per_token), per_token)
+
+
+@pytest.mark.parametrize("logit", [-200.0, 10.0, "mixed"])
+def test_bwd_extreme_decays(logit):
+    # x = 10 gives w = 0 (a chunk of such decays runs token by token),
+    # x = -200 gives w = 1; "mixed" puts both in one chunk, across channels
+    print(f"bwd extreme decay {logit}", flush=True)
+    d = bwd_case(2, 150, 2, 31, True)
+    if logit == "mixed":
+        x = d["x"].copy()
+        x[..., ::3] = 10.0
+        x[:, 70:90, :, 1::3] = -200.0
+        d["x"] = x
+    else:
+        d["x"] = np.full_like(d["x"], logit)
+    bwd_check(d, True, f"x={logit}")
+
+
+def test_bwd_zero_state_gradients_and_no_initial_state():
+    d = bwd_case(1, 100, 2, 33, True, dst_sigma=0.0)
+    d["s0"] = np.zeros_like(d["s0"])
+    bwd_check(d, True)
+
+
+def test_bwd_state_gradient_in_place():
+    # d_state_in may be the d_state_out buffer itself
+    d = bwd_case(2, 100, 2, 35, True)
+    ref = bwd_run(d, True)
+    g = matrix_inputs_dev(d)
+    ds = to_dev(d["d_sT"])
+    out = W.rwkv6_wkv_bwd(g["r"], g["k"], g["v"], g["x"], g["u"], to_dev(d["d_o"], True),
+                          state_in=g["s0"], d_state_out=ds, grads={"d_state_in": ds})
+    sync()
+    assert out["d_state_in"] is ds
+    for n in ref:
+        assert torch.equal(ref[n], out[n]), n
+
+
+def test_bwd_deterministic_and_workspace_reuse():
+    d = bwd_case(2, 200, 3, 34, True)
+    ws = torch.empty(W.workspace_bytes(2, 200, 3), dtype=torch.uint8, device="cuda")
+    a = bwd_run(d, True, ws)
+    b = bwd_run(d, True, ws)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_bwd_full_workload_sampled_heads(per_token):
+    """Backward at the full prefill workloads (Eagle B8 T4096 H32, Finch B8
+    T4096 H40) in the launch configuration the bench times, against the oracle
+    on sampled heads."""
+    cfg = 4 if per_token else 3
+    spec = S.WORKLOADS[cfg]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    print(f"bwd workload {cfg}: B={B} T={T} H={H}", flush=True)
+    d = S.workload(cfg)
+    d.update(S.grad_inputs(B, T, H, 64, cfg))
+    got = bwd_run(d, per_token)
+    print("bwd done; oracle on sampled heads", flush=True)
+    for b, h in sample_heads(B, H, n=4):
+        sub = {n: d[n][b:b + 1, :, h:h + 1] for n in ("r", "k", "v", "d_o")}
+        sub["x"] = d["x"][b:b + 1, :, h:h + 1] if per_token else d["x"][h:h + 1]
+        sub["u"] = d["u"][h:h + 1]
+        sub["s0"] = d["s0"][b:b + 1, h:h + 1]
+        sub["d_sT"] = d["d_sT"][b:b + 1, h:h + 1]
+        ref = bwd_ref(sub)
+        for n, key in (("d_r", "dr"), ("d_k", "dk"), ("d_v", "dv")):
+            assert_matrix_close(bf16_host(got[n][b:b + 1, :, h:h + 1]), ref[key], f"{n} {(b, h)}")
+        if per_token:
+            assert_matrix_close(f64_host(got["d_x"][b:b + 1, :, h:h + 1]), ref["dx"], f"d_x {(b, h)}")
+        assert_matrix_close(f64_host(got["d_state_in"][b:b + 1, h:h + 1]), ref["ds0"],
+                            f"d_state_in {(b, h)}")
+    # the sums over sequences, against the oracle on all sequences of one head
+    h = 1
+    sub = {n: np.ascontiguousarray(d[n][:, :, h:h + 1]) for n in ("r", "k", "v", "d_o")}
+    sub["x"] = np.ascontiguousarray(d["x"][:, :, h:h + 1]) if per_token else d["x"][h:h + 1]
+    sub["u"] = d["u"][h:h + 1]
+    sub["s0"] = np.ascontiguousarray(d["s0"][:, h:h + 1])
+    sub["d_sT"] = np.ascontiguousarray(d["d_sT"][:, h:h + 1])
+    ref = bwd_ref(sub)
+    assert_matrix_close(f64_host(got["d_u"][h:h + 1]), ref["du"], "d_u")
+    if not per_token:
+        assert_matrix_close(f64_host(got["d_x"][h:h + 1]), ref["dx"], "d_x")

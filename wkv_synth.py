@@ -24,6 +24,7 @@ BLOCK = 1 << 20
 
 # tensor ids (stable: changing one changes every stored expectation)
 T_R, T_K, T_V, T_OMEGA, T_DELTA, T_U, T_S0, T_W = 1, 2, 3, 4, 5, 6, 7, 4
+T_DO, T_DST = 8, 9  # gradients arriving at the backward
 
 
 def _threads():
@@ -127,6 +128,15 @@ def wkv_inputs(B, T, H, N, cfg, per_token, s0_sigma=0.0, rkv_sigma=0.125,
         d["s0"] = normal((B, H, N, N), s0_sigma, cfg, T_S0)
     else:
         d["s0"] = np.zeros((B, H, N, N), np.float32)
+    return d
+
+
+def grad_inputs(B, T, H, N, cfg, do_sigma=0.125, dst_sigma=0.1):
+    """Gradients arriving at the backward: d_o bf16 bits [B,T,H,N] ~
+    N(0, do_sigma); d_sT fp32 [B,H,N,N] ~ N(0, dst_sigma) (zeros when 0)."""
+    d = {"d_o": to_bf16(normal((B, T, H, N), do_sigma, cfg, T_DO))}
+    d["d_sT"] = (normal((B, H, N, N), dst_sigma, cfg, T_DST) if dst_sigma > 0
+                 else np.zeros((B, H, N, N), np.float32))
     return d
 
 
