@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
     ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
-                                       "rwkv4_decode", "calib"],
+                                       "rwkv4_decode", "finch_bwd", "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -148,6 +148,13 @@ def rwkv4_decode_bytes_per_step(B, C):
     return B * C * 12 + 2 * B * 3 * C * 4 + 2 * C * 4
 
 
+def finch_bwd_bytes(B, T, H, N=64):
+    # read r, k, v, d_o (bf16) and x (fp32); write d_r, d_k, d_v (bf16) and d_x
+    # (fp32); the states in and out and their gradients; u and d_u
+    tok = B * T * H * N
+    return tok * (2 * 4 + 4 + 2 * 3 + 4) + 4 * B * H * N * N * 4 + 2 * H * N * 4
+
+
 def chunk_mfma_flops(B, T, H, N=64, L=64):
     # per chunk and head, as executed: A^T (lower-triangular 16x16 tiles,
     # K = N), A V (causal K-blocks), Q S, Kh_hi V + Kh_lo V, all bf16 MFMA
@@ -181,6 +188,36 @@ def run_finch(torch, W, S, H2D, args, cfg=4):
         "mfma_frac": chunk_mfma_flops(B, T, H) / sec / 1e12 / MFMA_BF16_PEAK_TFS,
     })
     return res, d
+
+
+def run_finch_bwd(torch, W, S, H2D, args, d4=None):
+    """Backward of the Finch workload: the state recomputation (a forward
+    pass that stores the state entering every chunk), the reverse sweep and
+    the sums over sequences, timed together as one call."""
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    d = dict(d4) if d4 is not None else S.workload(4)
+    d.update(S.grad_inputs(B, T, H, 64, 4))
+    g = H2D(d)
+    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    grads = {"d_r": torch.empty_like(g["r"]), "d_k": torch.empty_like(g["r"]),
+             "d_v": torch.empty_like(g["r"]), "d_x": torch.empty_like(g["x"]),
+             "d_u": torch.empty_like(g["u"]), "d_state_in": torch.empty_like(g["s0"])}
+
+    def launch():
+        W.rwkv6_wkv_bwd(g["r"], g["k"], g["v"], g["x"], g["u"], g["d_o"], state_in=g["s0"],
+                        d_state_out=g["d_sT"], grads=grads, workspace=ws)
+
+    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2))
+    nbytes = finch_bwd_bytes(B, T, H)
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({"workload": "finch_bwd_B8_T4096_D2560_H40_N64_bf16",
+                "tokens_channels_per_s": B * T * H * 64 / sec,
+                "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                "workspace_bytes": ws.numel(),
+                "note": "one call = state recomputation + reverse sweep + sums"})
+    return res
 
 
 def run_rwkv4(torch, W, S, H2D, args, flush_buf):
@@ -428,6 +465,9 @@ def main():
         flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         paths["rwkv4_fwd"] = run_rwkv4(torch, W, S, H2D, args, flush_buf)
         del flush_buf
+    if not args.skip_paths and only in (None, "finch_bwd"):
+        print("finch backward ...", file=sys.stderr, flush=True)
+        paths["finch_bwd"] = run_finch_bwd(torch, W, S, H2D, args, d4)
     if not args.skip_paths and only in (None, "decode"):
         print("finch decode ...", file=sys.stderr, flush=True)
         paths["finch_decode"] = run_decode(torch, W, S, H2D, args)
