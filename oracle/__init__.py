@@ -43,6 +43,8 @@ def _bind(lib):
     lib.oracle_wkv_matrix.restype = ctypes.c_int
     lib.oracle_wkv_matrix.argtypes = [L, L, L, L, f, f, f, f, ctypes.c_int, f,
                                       d, d, d, ctypes.c_int]
+    lib.oracle_norm_gate.restype = ctypes.c_int
+    lib.oracle_norm_gate.argtypes = [L, L, L, d, f, f, f, ctypes.c_double, d, ctypes.c_int]
     lib.oracle_wkv_matrix_bwd.restype = ctypes.c_int
     lib.oracle_wkv_matrix_bwd.argtypes = [L, L, L, L, f, f, f, f, ctypes.c_int, f,
                                           d, d, d, d, d, d, d, d, d, ctypes.c_int]
@@ -198,3 +200,23 @@ def wkv_matrix_bwd(r, k, v, x, u, d_o, s_in=None, d_sT=None, nthreads=None, lib=
     if rc != 0:
         raise RuntimeError(f"oracle_wkv_matrix_bwd failed ({rc})")
     return out
+
+
+def norm_gate(o, g, ln_w, ln_b, eps, nthreads=None, lib=None):
+    """Eagle / Finch output epilogue in fp64: per head and token, LayerNorm of
+    o over the head's channels (eps added to the biased variance), times ln_w
+    plus ln_b, times silu(g).  o, g: [..., H, N]; ln_w, ln_b: [H, N]."""
+    lib = lib or load()
+    o, op = _f64(o)
+    g, gp = _f32(g)
+    ln_w, wp = _f32(ln_w)
+    ln_b, bp = _f32(ln_b)
+    H, N = o.shape[-2:]
+    assert g.shape == o.shape and ln_w.shape == (H, N) and ln_b.shape == (H, N)
+    rows = o.size // (H * N)
+    y = np.empty(o.shape, np.float64)
+    rc = lib.oracle_norm_gate(rows, H, N, op, gp, wp, bp, float(eps), _f64(y)[1],
+                              int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_norm_gate failed ({rc})")
+    return y

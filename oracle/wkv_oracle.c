@@ -297,3 +297,40 @@ int oracle_wkv_matrix_bwd(long B, long T, long H, long N,
     free(pu); free(px);
     return bad ? ORACLE_BAD_ARG : ORACLE_OK;
 }
+
+/*
+ * Output epilogue of Eagle / Finch time mixing (RWKV-5/6 summary, 4.1.2
+ * "Eagle time mixing": a LayerNorm on each of the h heads separately, i.e. a
+ * GroupNorm over h groups, and a SiLU gate on the attention output, before
+ * the output weights):
+ *     y = (LayerNorm_head(o) * ln_w + ln_b) * silu(g),   silu(g) = g / (1 + e^-g),
+ * with the mean and the (biased) variance over the N channels of one head
+ * of one token, and eps added to the variance.
+ *   o, g      [rows][H][N]   (rows = B * T)
+ *   ln_w, ln_b  [H][N]
+ *   y         [rows][H][N]
+ */
+int oracle_norm_gate(long rows, long H, long N, const double *o, const float *g,
+                     const float *ln_w, const float *ln_b, double eps, double *y,
+                     int nthreads)
+{
+    if (rows < 0 || H < 1 || N < 1 || nthreads < 1) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long unit = 0; unit < rows * H; ++unit) {
+        long h = unit % H;
+        const double *ou = o + unit * N;
+        double mean = 0.0, var = 0.0;
+        for (long i = 0; i < N; ++i) mean += ou[i];
+        mean /= (double)N;
+        for (long i = 0; i < N; ++i) var += (ou[i] - mean) * (ou[i] - mean);
+        var /= (double)N;
+        double rstd = 1.0 / sqrt(var + eps);
+        for (long i = 0; i < N; ++i) {
+            double gi = (double)g[unit * N + i];
+            double silu = gi / (1.0 + exp(-gi));
+            double n = (ou[i] - mean) * rstd * (double)ln_w[h * N + i] + (double)ln_b[h * N + i];
+            y[unit * N + i] = n * silu;
+        }
+    }
+    return ORACLE_OK;
+}

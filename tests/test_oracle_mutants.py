@@ -69,6 +69,11 @@ MUTANTS = {
     "bwd_du_drops_r": ("pu[unit * N + i] += (double)rt[i] * (double)kt[i] * dbeta;",
                        "pu[unit * N + i] += (double)kt[i] * dbeta;"),
     "bwd_checkpoint_only_first": ("if (t % CK == 0)\n", "if (t == 0)\n"),
+    "ng_unbiased_variance": ("var /= (double)N;", "var /= (double)(N - 1);"),
+    "ng_drops_eps": ("double rstd = 1.0 / sqrt(var + eps);", "double rstd = 1.0 / sqrt(var);"),
+    "ng_sigmoid_gate": ("double silu = gi / (1.0 + exp(-gi));", "double silu = 1.0 / (1.0 + exp(-gi));"),
+    "ng_no_centering": ("double n = (ou[i] - mean) * rstd", "double n = ou[i] * rstd"),
+    "ng_bias_wrong_head": ("(double)ln_b[h * N + i];", "(double)ln_b[((h + 1) % H) * N + i];"),
     "bwd_ignores_final_state_gradient": (
         "dS[i] = d_sT ? d_sT[(b * H + h) * NN + i] : 0.0;", "dS[i] = 0.0;"),
 }
@@ -90,6 +95,9 @@ PINS = [
     (P.test_matrix_bwd_finite_differences, {"per_token": True, "T": 70}),
     (P.test_matrix_bwd_no_decay_is_linear_attention_backward, {}),
     (P.test_matrix_bwd_eagle_decay_gradient_is_finch_summed, {}),
+    (P.test_norm_gate_is_group_norm_times_silu, {}),
+    (P.test_norm_gate_normalises_each_head, {}),
+    (P.test_norm_gate_affine_and_gate_structure, {}),
 ]
 
 

@@ -467,3 +467,52 @@ def test_matrix_bwd_eagle_decay_gradient_is_finch_summed(oracle_lib):
     assert np.allclose(e["dx"], f["dx"].sum(axis=(0, 1)), rtol=1e-12, atol=1e-14)
     for n in ("dr", "dk", "dv", "du", "ds0"):
         assert np.array_equal(e[n], f[n]), n
+
+
+# ---------------------------------------------------------------------------
+# output epilogue: LayerNorm per head (GroupNorm over heads), SiLU gate
+
+def _ng_case(seed, rows=6, H=3, N=8):
+    g = np.random.default_rng(seed)
+    o = g.standard_normal((rows, H, N)) * 3 + 1
+    gate = g.standard_normal((rows, H, N)).astype(np.float32)
+    w = (g.standard_normal((H, N)) * 0.5 + 1).astype(np.float32)
+    b = (g.standard_normal((H, N)) * 0.2).astype(np.float32)
+    return o, gate, w, b
+
+
+def test_norm_gate_is_group_norm_times_silu(oracle_lib):
+    # against torch's group_norm (float64, CPU) and silu: one group per head
+    torch = pytest.importorskip("torch")
+    o, gate, w, b = _ng_case(1)
+    rows, H, N = o.shape
+    got = oracle.norm_gate(o, gate, w, b, 1e-5, lib=oracle_lib)
+    t = torch.from_numpy(o.reshape(rows, H * N))
+    gn = torch.nn.functional.group_norm(t, H, torch.from_numpy(w.reshape(-1)).double(),
+                                        torch.from_numpy(b.reshape(-1)).double(), eps=1e-5)
+    want = gn.numpy().reshape(o.shape) * torch.nn.functional.silu(
+        torch.from_numpy(gate).double()).numpy()
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_norm_gate_normalises_each_head(oracle_lib):
+    # unit weight, zero bias, a gate large enough that silu(g) = g to fp64:
+    # y / g has zero mean and (for eps = 0) unit variance per head and token
+    o, gate, w, b = _ng_case(2)
+    gate = np.full_like(gate, 40.0)
+    y = oracle.norm_gate(o, gate, np.ones_like(w), np.zeros_like(b), 0.0, lib=oracle_lib) / 40.0
+    assert np.allclose(y.mean(axis=-1), 0.0, atol=1e-12)
+    assert np.allclose((y ** 2).mean(axis=-1), 1.0, rtol=1e-12)
+
+
+def test_norm_gate_affine_and_gate_structure(oracle_lib):
+    o, gate, w, b = _ng_case(3)
+    base = oracle.norm_gate(o, np.full_like(gate, 40.0), np.ones_like(w), np.zeros_like(b),
+                            1e-3, lib=oracle_lib) / 40.0
+    y = oracle.norm_gate(o, gate, w, b, 1e-3, lib=oracle_lib)
+    silu = gate / (1.0 + np.exp(-gate.astype(np.float64)))
+    assert np.allclose(y, (base * w + b) * silu, rtol=1e-12, atol=1e-13)
+    # a zero gate closes the output; shifting o by a constant per head changes nothing
+    assert not np.any(oracle.norm_gate(o, np.zeros_like(gate), w, b, 1e-3, lib=oracle_lib))
+    shifted = oracle.norm_gate(o + 7.0, gate, w, b, 1e-3, lib=oracle_lib)
+    assert np.allclose(shifted, y, rtol=1e-10, atol=1e-12)
