@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
     ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
-                                       "rwkv4_decode", "finch_bwd", "calib"],
+                                       "rwkv4_decode", "finch_bwd", "finch_gated", "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -188,6 +188,31 @@ def run_finch(torch, W, S, H2D, args, cfg=4):
         "mfma_frac": chunk_mfma_flops(B, T, H) / sec / 1e12 / MFMA_BF16_PEAK_TFS,
     })
     return res, d
+
+
+def run_finch_gated(torch, W, S, H2D, args, d4=None):
+    """The Finch forward with the output epilogue (LayerNorm per head, SiLU
+    gate) fused into the output write."""
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    d = dict(d4) if d4 is not None else S.workload(4)
+    d.update(S.epilogue_inputs(B, T, H, 64, 4))
+    g = H2D(d)
+    y = torch.empty_like(g["r"])
+    so = torch.empty_like(g["s0"])
+
+    def launch():
+        W.rwkv6_wkv_fwd_gated(g["r"], g["k"], g["v"], g["x"], g["u"], g["g"], g["ln_w"],
+                              g["ln_b"], 1e-5, state_in=g["s0"], state_out=so, y=y)
+
+    res = time_launches(torch, launch, args.steps, args.warmup)
+    nbytes = finch_bytes(B, T, H) + B * T * H * 64 * 2 + 2 * H * 64 * 4  # + gate, norm params
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({"workload": "finch_fwd_gated_B8_T4096_D2560_H40_N64_bf16",
+                "tokens_channels_per_s": B * T * H * 64 / sec,
+                "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+    return res
 
 
 def run_finch_bwd(torch, W, S, H2D, args, d4=None):
@@ -465,6 +490,9 @@ def main():
         flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
         paths["rwkv4_fwd"] = run_rwkv4(torch, W, S, H2D, args, flush_buf)
         del flush_buf
+    if not args.skip_paths and only in (None, "finch_gated"):
+        print("finch forward with the epilogue ...", file=sys.stderr, flush=True)
+        paths["finch_fwd_gated"] = run_finch_gated(torch, W, S, H2D, args, d4)
     if not args.skip_paths and only in (None, "finch_bwd"):
         print("finch backward ...", file=sys.stderr, flush=True)
         paths["finch_bwd"] = run_finch_bwd(torch, W, S, H2D, args, d4)

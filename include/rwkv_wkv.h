@@ -203,6 +203,39 @@ int rwkv5_wkv_step(int B, int T, int H, int N,
                    float *state, rwkv_bf16 *o, void *stream);
 
 /*
+ * Eagle / Finch time-parallel forward with the time-mixing epilogue fused
+ * into the output write (RWKV-5/6 summary, 4.1.2 "Eagle time mixing": a
+ * LayerNorm on each of the h heads, equivalently a GroupNorm over h groups,
+ * and a SiLU gate on the attention output before the output weights):
+ *
+ *   y = ((o - mean) / sqrt(var + eps) * ln_w + ln_b) * g / (1 + e^-g)
+ *
+ * with o the output of rwkv5/6_wkv_fwd for the same arguments, and the mean
+ * and biased variance over the N = 64 channels of one head of one token
+ * (taken from the fp32 accumulators, before rounding).
+ *
+ *   g          [B][T][H][N] bf16 gate
+ *   ln_w, ln_b [H][N] fp32 per-channel weight and bias of the norm
+ *   eps        added to the variance; finite and >= 0, else RWKV_E_DIM
+ *   y          [B][T][H][N] bf16 output (in place of o)
+ * Other arguments, the state and the error codes as rwkv6_wkv_fwd (rwkv5:
+ * x is [H][N]).  All pointers need 16-byte alignment.
+ */
+int rwkv5_wkv_fwd_gated(int B, int T, int H, int N,
+                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                        const float *x, const float *u,
+                        const float *state_in, float *state_out,
+                        const rwkv_bf16 *g, const float *ln_w, const float *ln_b,
+                        float eps, rwkv_bf16 *y, void *stream);
+
+int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
+                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                        const float *x, const float *u,
+                        const float *state_in, float *state_out,
+                        const rwkv_bf16 *g, const float *ln_w, const float *ln_b,
+                        float eps, rwkv_bf16 *y, void *stream);
+
+/*
  * Eagle / Finch backward of the time-parallel forward (rwkv5_wkv_fwd,
  * rwkv6_wkv_fwd): the gradients of a loss L with respect to every input,
  * given dL/do and dL/dS_T.  Reverse-mode differentiation of the recurrence

@@ -14,6 +14,9 @@ Operators (names as in the C ABI):
   rwkv5_wkv_step  Eagle matrix-state WKV, serial (decode)
   rwkv6_wkv_fwd   Finch matrix-state WKV, time-parallel (chunked)
   rwkv6_wkv_step  Finch matrix-state WKV, serial (decode)
+  rwkv5_wkv_fwd_gated, rwkv6_wkv_fwd_gated
+                  the chunked forward with the LayerNorm-per-head and SiLU-gate
+                  epilogue fused into the output
   rwkv5_wkv_bwd   Eagle backward of the chunked forward
   rwkv6_wkv_bwd   Finch backward of the chunked forward
   rwkv_wkv_bwd_workspace_bytes  workspace size of the backward
@@ -30,7 +33,8 @@ STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPO
           -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP"}
 EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
            "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step", "rwkv5_wkv_bwd",
-           "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes")
+           "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes", "rwkv5_wkv_fwd_gated",
+           "rwkv6_wkv_fwd_gated")
 
 _lib = None
 
@@ -64,6 +68,10 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
+        for name in ("rwkv5_wkv_fwd_gated", "rwkv6_wkv_fwd_gated"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I] + [P] * 10 + [ctypes.c_float, P, P]
         L.rwkv_wkv_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.rwkv_wkv_bwd_workspace_bytes.argtypes = [I, I, I, I]
         for name in ("rwkv5_wkv_bwd", "rwkv6_wkv_bwd"):
@@ -215,6 +223,46 @@ def _matrix_step(name, per_token, r, k, v, x, u, state, o, stream):
 def rwkv5_wkv_step(r, k, v, x, u, state, o=None, stream=None):
     """Eagle WKV, serial: as rwkv6_wkv_step but x (decay logit omega): [H, 64]."""
     return _matrix_step("rwkv5_wkv_step", False, r, k, v, x, u, state, o, stream)
+
+
+def _matrix_fwd_gated(name, per_token, r, k, v, x, u, g, ln_w, ln_b, eps, state_in,
+                      state_out, y, return_state, stream):
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect("g", g, (B, T, H, N), bf)
+    _expect("ln_w", ln_w, (H, N), f32)
+    _expect("ln_b", ln_b, (H, N), f32)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), f32)
+    if y is None:
+        y = torch.empty((B, T, H, N), dtype=bf, device=r.device)
+    _expect("y", y, (B, T, H, N), bf)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, N, N), dtype=f32, device=r.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, H, N, N), f32)
+    _check(name, getattr(lib(), name)(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in),
+        _ptr(state_out), _ptr(g), _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(y),
+        _stream(stream)))
+    return y, state_out
+
+
+def rwkv5_wkv_fwd_gated(r, k, v, x, u, g, ln_w, ln_b, eps=1e-5, state_in=None,
+                        state_out=None, y=None, return_state=True, stream=None):
+    """Eagle forward with the epilogue: y = (LayerNorm per head of o, times
+    ln_w plus ln_b) * silu(g).  g: [B, T, H, 64] bf16; ln_w, ln_b: [H, 64]
+    fp32.  Returns (y, state_out)."""
+    return _matrix_fwd_gated("rwkv5_wkv_fwd_gated", False, r, k, v, x, u, g, ln_w, ln_b, eps,
+                             state_in, state_out, y, return_state, stream)
+
+
+def rwkv6_wkv_fwd_gated(r, k, v, x, u, g, ln_w, ln_b, eps=1e-5, state_in=None,
+                        state_out=None, y=None, return_state=True, stream=None):
+    """Finch forward with the epilogue (as rwkv5_wkv_fwd_gated, x per token)."""
+    return _matrix_fwd_gated("rwkv6_wkv_fwd_gated", True, r, k, v, x, u, g, ln_w, ln_b, eps,
+                             state_in, state_out, y, return_state, stream)
 
 
 def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):

@@ -43,6 +43,15 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
                               uint16_t *o, hipStream_t stream,
                               float *chunk_states = nullptr);
 
+// Eagle / Finch chunked forward with the time-mixing epilogue (LayerNorm per
+// head, affine, SiLU gate) applied to the output: y instead of o.
+hipError_t launch_wkv_chunked_gated(bool per_token_decay, int B, int T, int H,
+                                    const uint16_t *r, const uint16_t *k, const uint16_t *v,
+                                    const float *x, const float *u, const float *state_in,
+                                    float *state_out, const uint16_t *gate, const float *ln_w,
+                                    const float *ln_b, float eps, uint16_t *y,
+                                    hipStream_t stream);
+
 // Eagle / Finch chunked backward, N = 64: workspace size and launch (the
 // forward's state recomputation, the reverse sweep, the sums over sequences).
 size_t wkv_bwd_workspace_bytes(int B, int T, int H);

@@ -106,6 +106,31 @@ int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                                               state_in, state_out, o, s));
 }
 
+int matrix_fwd_gated(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
+                     const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
+                     const float *state_in, float *state_out, const rwkv_bf16 *gate,
+                     const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
+                     void *stream) {
+    const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
+    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, y);
+    if (st != RWKV_OK) return st;
+    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
+    if (!(eps >= 0.0f) || eps > 1e30f) return RWKV_E_DIM;  // also rejects NaN
+    if (T > 0 && (gate == nullptr || ln_w == nullptr || ln_b == nullptr)) return RWKV_E_NULL;
+    for (const void *p : {(const void *)gate, (const void *)ln_w, (const void *)ln_b})
+        if (p != nullptr && !aligned(p, 16)) return RWKV_E_ALIGN;
+    const int64_t tok = checked_mul({B, T, H, N}), st_el = checked_mul({B, H, N, N});
+    const Span sy{y, tok * 2}, sso{state_out, st_el * 4}, sg{gate, tok * 2},
+        sw{ln_w, (int64_t)H * N * 4}, sb{ln_b, (int64_t)H * N * 4};
+    if (T > 0 && check_outputs({sy, sso}, {sg, sw, sb}) != RWKV_OK) return RWKV_E_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) return matrix_fwd(per_token, B, T, H, N, r, k, v, x, u, state_in, state_out,
+                                  y, stream);
+    return hip_status(wkv::launch_wkv_chunked_gated(per_token, B, T, H, r, k, v, x, u,
+                                                    state_in, state_out, gate, ln_w, ln_b,
+                                                    eps, y, s));
+}
+
 int matrix_step(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                 const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                 float *state, rwkv_bf16 *o, void *stream) {
@@ -255,6 +280,24 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
                   const rwkv_bf16 *v, const float *x, const float *u,
                   const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
     return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+}
+
+int rwkv5_wkv_fwd_gated(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                        const rwkv_bf16 *v, const float *x, const float *u,
+                        const float *state_in, float *state_out, const rwkv_bf16 *gate,
+                        const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
+                        void *stream) {
+    return matrix_fwd_gated(false, B, T, H, N, r, k, v, x, u, state_in, state_out, gate, ln_w,
+                            ln_b, eps, y, stream);
+}
+
+int rwkv6_wkv_fwd_gated(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                        const rwkv_bf16 *v, const float *x, const float *u,
+                        const float *state_in, float *state_out, const rwkv_bf16 *gate,
+                        const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
+                        void *stream) {
+    return matrix_fwd_gated(true, B, T, H, N, r, k, v, x, u, state_in, state_out, gate, ln_w,
+                            ln_b, eps, y, stream);
 }
 
 size_t rwkv_wkv_bwd_workspace_bytes(int B, int T, int H, int N) {

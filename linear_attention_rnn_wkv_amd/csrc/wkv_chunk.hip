@@ -85,12 +85,21 @@ struct Split {
 // SAVE: instead of the outputs and the final state, store the state entering
 // every chunk and the final state, [B H][nchunks + 1][64][64] fp32 key-major,
 // for the backward pass.
-template <bool PT, int NW, bool SAVE>
+// EPI (four waves): write, instead of o, the output after the time-mixing
+// epilogue (RWKV-5/6 summary, 4.1.2: a LayerNorm on each head, i.e. a
+// GroupNorm over the heads, and a SiLU gate):
+//   y = ((o - mean) / sqrt(var + eps) * ln_w + ln_b) * g / (1 + e^-g),
+// mean and (biased) variance over the 64 channels of one head and token,
+// taken from the fp32 accumulators before any rounding.
+template <bool PT, int NW, bool SAVE, bool EPI = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x,
     const float *__restrict__ u, const float *state_in, float *state_out,
-    uint16_t *__restrict__ o, Split sp, float *chunk_states) {
+    uint16_t *__restrict__ o, Split sp, float *chunk_states,
+    const uint16_t *__restrict__ gate, const float *__restrict__ ln_w,
+    const float *__restrict__ ln_b, float eps) {
+    static_assert(!EPI || NW == 4, "the epilogue needs a head's channels in one wave");
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
@@ -104,6 +113,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     __shared__ __align__(16) float sDecay[NW][kN];     // e^{Lam_L}, one copy per wave
     __shared__ __align__(16) float sBonus[NS][kL];
     __shared__ int sBad[NS][NW];  // per wave: a channel of the next chunk decays too fast
+    // EPI: outputs of a fast-decay chunk before the epilogue, [token][channel]
+    __shared__ __align__(16) float sO[EPI ? kL * kN : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -425,11 +436,59 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
     };
 
+    // EPI: this lane's gate values (token 16 p + c, channels 16 ni + 4 g + e)
+    // of a chunk, requested at the start of its step
+    u32x2 gq[EPI ? NT : 1];
+    auto load_gate = [&](int ch) {
+        const int c0 = ch * kL;
+        const Rsrc rg = rsrc(gate + cx.base(c0), cx.span(c0));
+        const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (4 * g);
+#pragma unroll
+        for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
+            gq[ni] = __builtin_amdgcn_raw_buffer_load_b64(rg, off + 32 * ni, 0, 0);
+    };
+    auto silu = [](float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_fast(-z)); };
+
     auto store_out = [&](int ch) {
         if (SAVE) return;
         const int c0 = ch * kL;
         const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
+        if (EPI) {
+            // the 64 channels of token 16 p + c: 16 in this lane, the rest in
+            // lanes 16 and 32 apart; mean, then the squared deviations
+            float s = 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += ot[ni][e];
+            s += __shfl_xor(s, 16, 64);
+            s += __shfl_xor(s, 32, 64);
+            const float mean = s * (1.0f / kN);
+            float q = 0.0f;
+#pragma unroll
+            for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q = fmaf(ot[ni][e] - mean, ot[ni][e] - mean, q);
+            q += __shfl_xor(q, 16, 64);
+            q += __shfl_xor(q, 32, 64);
+            const float rstd = __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps);
+            const int h = bh % H;
+#pragma unroll
+            for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
+                const f32x4 lw = *(const f32x4 *)(ln_w + (size_t)h * kN + 16 * ni + 4 * g);
+                const f32x4 lb = *(const f32x4 *)(ln_b + (size_t)h * kN + 16 * ni + 4 * g);
+                const float gv[4] = {bf16_lo(gq[ni].x), bf16_hi(gq[ni].x), bf16_lo(gq[ni].y),
+                                     bf16_hi(gq[ni].y)};
+                f32x4 yv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    yv[e] = fmaf((ot[ni][e] - mean) * rstd, lw[e], lb[e]) * silu(gv[e]);
+                __builtin_amdgcn_raw_buffer_store_b64(pack4(yv[0], yv[1], yv[2], yv[3]), ro,
+                                                      off + 32 * ni, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni)
             __builtin_amdgcn_raw_buffer_store_b64(pack4(ot[ni][0], ot[ni][1], ot[ni][2], ot[ni][3]),
@@ -505,8 +564,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 acc += __shfl_xor(acc, 32, 64);
                 if (g == 0 && !SAVE) {
                     const float ov = fmaf(sBonus[set][tau], vj, acc);
-                    o[cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 16 * w + c] =
-                        (uint16_t)pack_bf16x2(ov, 0.0f);
+                    if (EPI)
+                        sO[tau * kN + 16 * w + c] = ov;
+                    else
+                        o[cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 16 * w + c] =
+                            (uint16_t)pack_bf16x2(ov, 0.0f);
                 }
             }
         }
@@ -524,6 +586,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 S[t][e] = sS[(skey(t) + 4 * g + e) * kN + sval(t) + c];
+        if (EPI) {
+            // the epilogue of the chunk from sO: four threads per token, 16
+            // channels each (written before the barrier above)
+            const int tok = tid >> 2, q4 = tid & 3;
+            float ov[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ov[i] = sO[tok * kN + 16 * q4 + i];
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s += ov[i];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            const float mean = s * (1.0f / kN);
+            float q = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q = fmaf(ov[i] - mean, ov[i] - mean, q);
+            q += __shfl_xor(q, 1, 64);
+            q += __shfl_xor(q, 2, 64);
+            const float rstd = __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps);
+            const int h = bh % H;
+            const Rsrc rg = rsrc(gate + cx.base(c0), cx.span(c0));
+            const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
+            const uint32_t off = (uint32_t)tok * cx.tokb + 2 * (16 * q4);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16 * hh, 0, 0);
+                const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+                u32x4 out;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i0 = 8 * hh + 2 * m, ch0 = 16 * q4 + i0;
+                    const float y0 = fmaf((ov[i0] - mean) * rstd, ln_w[(size_t)h * kN + ch0],
+                                          ln_b[(size_t)h * kN + ch0]) * silu(bf16_lo(gw[m]));
+                    const float y1 = fmaf((ov[i0 + 1] - mean) * rstd, ln_w[(size_t)h * kN + ch0 + 1],
+                                          ln_b[(size_t)h * kN + ch0 + 1]) * silu(bf16_hi(gw[m]));
+                    const uint32_t pk = pack_bf16x2(y0, y1);
+                    if (m == 0) out.x = pk;
+                    else if (m == 1) out.y = pk;
+                    else if (m == 2) out.z = pk;
+                    else out.w = pk;
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(out, ro, off + 16 * hh, 0, 0);
+            }
+        }
     };
 
     // ---- one pipelined step: matrix phase of chunk ch, staging of ch + 1 --
@@ -550,6 +656,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto step2 = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < ch_end;
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
+        if (EPI && !unsafe) load_gate(ch);
         if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(0);
         else token_by_token(ch, 0);
@@ -694,13 +801,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     save_state();
 }
 
-template <bool PT, int NW, bool SAVE = false>
+template <bool PT, int NW, bool SAVE = false, bool EPI = false>
 void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
             const float *x, const float *u, const float *state_in, float *state_out,
-            uint16_t *o, const Split &sp, hipStream_t stream, float *chunk_states = nullptr) {
-    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW, SAVE>), dim3((unsigned)blocks), dim3(64 * NW),
-                       0, stream, T, H, r, k, v, x, u, state_in, state_out, o, sp,
-                       chunk_states);
+            uint16_t *o, const Split &sp, hipStream_t stream, float *chunk_states = nullptr,
+            const uint16_t *gate = nullptr, const float *ln_w = nullptr,
+            const float *ln_b = nullptr, float eps = 0.0f) {
+    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW, SAVE, EPI>), dim3((unsigned)blocks),
+                       dim3(64 * NW), 0, stream, T, H, r, k, v, x, u, state_in, state_out, o,
+                       sp, chunk_states, gate, ln_w, ln_b, eps);
 }
 
 // XCDs of the device: workgroups are dealt to them round-robin
@@ -761,6 +870,25 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         if (wide) launch<false, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
         else launch<false, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_wkv_chunked_gated(bool per_token_decay, int B, int T, int H,
+                                    const uint16_t *r, const uint16_t *k, const uint16_t *v,
+                                    const float *x, const float *u, const float *state_in,
+                                    float *state_out, const uint16_t *gate, const float *ln_w,
+                                    const float *ln_b, float eps, uint16_t *y,
+                                    hipStream_t stream) {
+    // four waves per head (a head's 64 output channels of a token in one
+    // wave), two heads per CU
+    const int blocks = B * H;
+    const Split sp{};
+    if (per_token_decay)
+        launch<true, 4, false, true>(blocks, T, H, r, k, v, x, u, state_in, state_out, y, sp,
+                                     stream, nullptr, gate, ln_w, ln_b, eps);
+    else
+        launch<false, 4, false, true>(blocks, T, H, r, k, v, x, u, state_in, state_out, y, sp,
+                                      stream, nullptr, gate, ln_w, ln_b, eps);
     return hipGetLastError();
 }
 

@@ -294,3 +294,34 @@ def test_bwd_aliasing(L, fn):
     assert bwd(L, fn, dx=9) == E_ALIAS    # d_x on d_r
     assert bwd(L, fn, ws=7) == E_ALIAS    # workspace on d_o
     assert bwd(L, fn, mis={"dsi": 16}, dsi=8) == E_ALIAS  # d_state_in partly on d_state_out
+
+
+# ---------------------------------------------------------------------------
+# forward with the output epilogue
+
+def gated(L, fn="rwkv6_wkv_fwd_gated", B=2, T=8, H=2, N=64, eps=1e-5, **over):
+    names = ("r", "k", "v", "x", "u", "si", "so", "g", "w", "b", "y")
+    idx = {n: i + 1 for i, n in enumerate(names)}
+    idx.update({n: val for n, val in over.items() if n in idx})
+    mis = over.get("mis", {})
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
+    return getattr(L, fn)(B, T, H, N, *(a[n] for n in names[:10]), eps, a["y"], None)
+
+
+GATED = ["rwkv5_wkv_fwd_gated", "rwkv6_wkv_fwd_gated"]
+
+
+@pytest.mark.parametrize("fn", GATED)
+@pytest.mark.parametrize("missing", ["r", "x", "u", "g", "w", "b", "y"])
+def test_gated_null(L, fn, missing):
+    assert gated(L, fn, **{missing: None}) == E_NULL
+
+
+@pytest.mark.parametrize("fn", GATED)
+def test_gated_checks(L, fn):
+    assert gated(L, fn, N=32) == E_UNSUP
+    assert gated(L, fn, eps=-1.0) == E_DIM
+    assert gated(L, fn, eps=float("nan")) == E_DIM
+    assert gated(L, fn, mis={"g": 8}) == E_ALIGN
+    assert gated(L, fn, y=8) == E_ALIAS   # y on the gate
+    assert gated(L, fn, y=1) == E_ALIAS   # y on r

@@ -696,3 +696,96 @@ def test_bwd_full_workload_sampled_heads(per_token):
     assert_matrix_close(f64_host(got["d_u"][h:h + 1]), ref["du"], "d_u")
     if not per_token:
         assert_matrix_close(f64_host(got["d_x"][h:h + 1]), ref["dx"], "d_x")
+
+
+# ---------------------------------------------------------------------------
+# time-parallel forward with the output epilogue (LayerNorm per head, SiLU gate)
+
+EPS = 1e-5
+
+
+def gated_case(B, T, H, seed, per_token, **kw):
+    d = matrix_case(B, T, H, seed, per_token, **kw)
+    d.update(S.epilogue_inputs(B, T, H, 64, seed))
+    return d
+
+
+def gated_run(d, per_token):
+    g = matrix_inputs_dev(d)
+    fn = W.rwkv6_wkv_fwd_gated if per_token else W.rwkv5_wkv_fwd_gated
+    y, so = fn(g["r"], g["k"], g["v"], g["x"], g["u"], to_dev(d["g"], True), to_dev(d["ln_w"]),
+               to_dev(d["ln_b"]), EPS, state_in=g["s0"])
+    sync()
+    return y, so
+
+
+def gated_ref(d):
+    """y from the oracle, and the normalised value before the gate (the
+    oracle's epilogue with a gate of 40, where silu(40) = 40 in fp64)."""
+    o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
+    gate = S.bf16_to_f32(d["g"])
+    y_ref = oracle.norm_gate(o_ref, gate, d["ln_w"], d["ln_b"], EPS)
+    n_ref = oracle.norm_gate(o_ref, np.full_like(gate, 40.0), d["ln_w"], d["ln_b"], EPS) / 40.0
+    return y_ref, n_ref, gate, s_ref
+
+
+def assert_gated_close(y, y_ref, n_ref, gate, what):
+    """The gate multiplies exactly, so y carries the normalised value's error
+    times |silu(g)| plus its own bf16 rounding: the forward's bounds apply to
+    the normalised value (RMS 5e-3 of y as a whole; per element 3e-2 of
+    max(|n|, rms(n)), scaled by |silu(g)|)."""
+    rms, _ = rel_errors(y, y_ref)
+    assert rms <= 5e-3, f"{what}: rms_rel {rms:.3e}"
+    sg = np.abs(gate / (1.0 + np.exp(-gate.astype(np.float64))))
+    scale = np.maximum(np.abs(n_ref), np.sqrt(np.mean(n_ref ** 2))) * sg + np.abs(y_ref) * 2.0 ** -8
+    mx = np.max(np.abs(y - y_ref) / np.maximum(scale, 1e-30))
+    assert mx <= 3e-2, f"{what}: max error {mx:.3e} of the gated scale"
+
+
+def gated_check(d, per_token):
+    y, so = gated_run(d, per_token)
+    y_ref, n_ref, gate, s_ref = gated_ref(d)
+    assert_gated_close(bf16_host(y), y_ref, n_ref, gate, "y")
+    assert_matrix_close(f64_host(so), s_ref, "state")
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 63, 1), (1, 65, 2), (2, 130, 3), (1, 300, 2)])
+def test_gated_vs_oracle(per_token, B, T, H):
+    print(f"gated {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    gated_check(gated_case(B, T, H, 900 + T + H, per_token), per_token)
+
+
+@pytest.mark.parametrize("logit", [-200.0, 10.0, "mixed"])
+def test_gated_extreme_decays(logit):
+    # x = 10 makes the chunks run token by token: the epilogue then reads the
+    # chunk's outputs back from LDS
+    print(f"gated extreme decay {logit}", flush=True)
+    d = gated_case(2, 150, 2, 37, True)
+    if logit == "mixed":
+        x = d["x"].copy()
+        x[..., ::3] = 10.0
+        x[:, 70:90, :, 1::3] = -200.0
+        d["x"] = x
+    else:
+        d["x"] = np.full_like(d["x"], logit)
+    gated_check(d, True)
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_gated_full_workload_sampled_heads(per_token):
+    cfg = 4 if per_token else 3
+    spec = S.WORKLOADS[cfg]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    print(f"gated workload {cfg}: B={B} T={T} H={H}", flush=True)
+    d = S.workload(cfg)
+    d.update(S.epilogue_inputs(B, T, H, 64, cfg))
+    y, so = gated_run(d, per_token)
+    for b, h in sample_heads(B, H, n=4):
+        sub = {n: d[n][b:b + 1, :, h:h + 1] for n in ("r", "k", "v", "g")}
+        sub["x"] = d["x"][b:b + 1, :, h:h + 1] if per_token else d["x"][h:h + 1]
+        sub["u"], sub["s0"] = d["u"][h:h + 1], d["s0"][b:b + 1, h:h + 1]
+        sub["ln_w"], sub["ln_b"] = d["ln_w"][h:h + 1], d["ln_b"][h:h + 1]
+        y_ref, n_ref, gate, s_ref = gated_ref(sub)
+        assert_gated_close(bf16_host(y[b:b + 1, :, h:h + 1]), y_ref, n_ref, gate, f"y {(b, h)}")
+        assert_matrix_close(f64_host(so[b:b + 1, h:h + 1]), s_ref, f"state {(b, h)}")

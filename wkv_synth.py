@@ -25,6 +25,7 @@ BLOCK = 1 << 20
 # tensor ids (stable: changing one changes every stored expectation)
 T_R, T_K, T_V, T_OMEGA, T_DELTA, T_U, T_S0, T_W = 1, 2, 3, 4, 5, 6, 7, 4
 T_DO, T_DST = 8, 9  # gradients arriving at the backward
+T_G, T_LNW, T_LNB = 10, 11, 12  # gate and norm parameters of the output epilogue
 
 
 def _threads():
@@ -138,6 +139,14 @@ def grad_inputs(B, T, H, N, cfg, do_sigma=0.125, dst_sigma=0.1):
     d["d_sT"] = (normal((B, H, N, N), dst_sigma, cfg, T_DST) if dst_sigma > 0
                  else np.zeros((B, H, N, N), np.float32))
     return d
+
+
+def epilogue_inputs(B, T, H, N, cfg, g_sigma=1.0, w_sigma=0.1, b_sigma=0.1):
+    """Output epilogue: gate g bf16 bits [B,T,H,N] ~ N(0, g_sigma); norm
+    weight ln_w ~ 1 + N(0, w_sigma) and bias ln_b ~ N(0, b_sigma), fp32 [H,N]."""
+    return {"g": to_bf16(normal((B, T, H, N), g_sigma, cfg, T_G)),
+            "ln_w": normal((H, N), w_sigma, cfg, T_LNW, mean=1.0),
+            "ln_b": normal((H, N), b_sigma, cfg, T_LNB)}
 
 
 def decode_inputs(B, steps, H, N, cfg, s0_sigma=0.1, rkv_sigma=0.125,
