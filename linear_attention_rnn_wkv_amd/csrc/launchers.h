@@ -41,7 +41,9 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
                               const uint16_t *v, const float *x, const float *u,
                               const float *state_in, float *state_out,
                               uint16_t *o, hipStream_t stream,
-                              float *chunk_states = nullptr);
+                              float *chunk_states = nullptr, const uint16_t *gate = nullptr,
+                              const float *ln_w = nullptr, const float *ln_b = nullptr,
+                              float eps = 0.0f);
 
 // Eagle / Finch chunked forward with the time-mixing epilogue (LayerNorm per
 // head, affine, SiLU gate) applied to the output: y instead of o.

@@ -85,12 +85,16 @@ struct Split {
 // SAVE: instead of the outputs and the final state, store the state entering
 // every chunk and the final state, [B H][nchunks + 1][64][64] fp32 key-major,
 // for the backward pass.
-// EPI (four waves): write, instead of o, the output after the time-mixing
+// EPI: write, instead of o, the output after the time-mixing
 // epilogue (RWKV-5/6 summary, 4.1.2: a LayerNorm on each head, i.e. a
 // GroupNorm over the heads, and a SiLU gate):
 //   y = ((o - mean) / sqrt(var + eps) * ln_w + ln_b) * g / (1 + e^-g),
 // mean and (biased) variance over the 64 channels of one head and token,
-// taken from the fp32 accumulators before any rounding.
+// taken from the fp32 accumulators before any rounding.  With eight waves a
+// token's channels are split over two waves: each forms the mean and the sum
+// of squared deviations of its half, the halves are merged through LDS
+// after the step's barrier, and the chunk's outputs are written at the start
+// of the next step (before its products overwrite the accumulators).
 template <bool PT, int NW, bool SAVE, bool EPI = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
@@ -99,7 +103,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     uint16_t *__restrict__ o, Split sp, float *chunk_states,
     const uint16_t *__restrict__ gate, const float *__restrict__ ln_w,
     const float *__restrict__ ln_b, float eps) {
-    static_assert(!EPI || NW == 4, "the epilogue needs a head's channels in one wave");
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
@@ -115,6 +118,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     __shared__ int sBad[NS][NW];  // per wave: a channel of the next chunk decays too fast
     // EPI: outputs of a fast-decay chunk before the epilogue, [token][channel]
     __shared__ __align__(16) float sO[EPI ? kL * kN : 1];
+    // EPI, eight waves: (mean, sum of squared deviations) of each half-token
+    __shared__ __align__(16) f32x2 sStat[EPI ? NS : 1][NW][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,12 +158,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // from chunk to chunk: their bases are computed once per head, and each
     // token's factor follows by one multiply.
     f32x4 uq, a2s, wq, eLL, eF1, eF2;
+    f32x4 lnw[EPI ? NT : 1], lnb[EPI ? NT : 1];  // EPI: this lane's norm weight and bias
     int bh = 0;  // (sequence, head) of the current job
     auto set_head = [&](int head) {
         bh = head;
         const int b = head / H, h = head % H;
         cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
         uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
+        if (EPI) {
+#pragma unroll
+            for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
+                const int ch0 = 16 * (NT * hf + ni) + 4 * g;
+                lnw[ni] = *(const f32x4 *)(ln_w + (size_t)h * kN + ch0);
+                lnb[ni] = *(const f32x4 *)(ln_b + (size_t)h * kN + ch0);
+            }
+        }
         a2s = f32x4{0.f, 0.f, 0.f, 0.f};
         wq = f32x4{1.f, 1.f, 1.f, 1.f};
         eLL = a2s;
@@ -442,21 +456,63 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto load_gate = [&](int ch) {
         const int c0 = ch * kL;
         const Rsrc rg = rsrc(gate + cx.base(c0), cx.span(c0));
-        const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (4 * g);
+        const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
 #pragma unroll
         for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
             gq[ni] = __builtin_amdgcn_raw_buffer_load_b64(rg, off + 32 * ni, 0, 0);
     };
     auto silu = [](float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_fast(-z)); };
 
-    auto store_out = [&](int ch) {
+    // EPI: y of this lane's outputs from the token's mean and 1 / sqrt(var +
+    // eps), packed in yq; stored by epi_flush once the step's loads have been
+    // consumed (stores share the in-order memory counter with loads, so a
+    // store ahead of a load that is waited for is waited for too)
+    u32x2 yq[EPI ? NT : 1];
+    int yq_ch = -1;
+    auto epi_compute = [&](float mean, float rstd) {
+#pragma unroll
+        for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
+            const float gv[4] = {bf16_lo(gq[ni].x), bf16_hi(gq[ni].x), bf16_lo(gq[ni].y),
+                                 bf16_hi(gq[ni].y)};
+            f32x4 yv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                yv[e] = fmaf((ot[ni][e] - mean) * rstd, lnw[ni][e], lnb[ni][e]) * silu(gv[e]);
+            yq[ni] = pack4(yv[0], yv[1], yv[2], yv[3]);
+        }
+    };
+    auto epi_flush = [&]() {
+        if (!EPI || yq_ch < 0) return;
+        const int c0 = yq_ch * kL;
+        const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
+        const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
+#pragma unroll
+        for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
+            __builtin_amdgcn_raw_buffer_store_b64(yq[ni], ro, off + 32 * ni, 0, 0);
+        yq_ch = -1;
+    };
+    int epi_ch = -1, epi_set = 0;  // eight waves: a chunk whose outputs wait for the merge
+    auto epi_finish = [&]() {
+        if (!EPI || epi_ch < 0) return;
+        const f32x2 a = sStat[epi_set][w][c], b = sStat[epi_set][w ^ 4][c];
+        // two halves of 32 channels: n_a n_b / (n_a + n_b) = 16
+        const float d = a[0] - b[0];
+        const float mean = 0.5f * (a[0] + b[0]);
+        const float m2 = a[1] + b[1] + 16.0f * d * d;
+        epi_compute(mean, __builtin_amdgcn_rsqf(m2 * (1.0f / kN) + eps));
+        yq_ch = epi_ch;
+        epi_ch = -1;
+    };
+
+    auto store_out = [&](int ch, int set) {
         if (SAVE) return;
         const int c0 = ch * kL;
         const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
         if (EPI) {
-            // the 64 channels of token 16 p + c: 16 in this lane, the rest in
-            // lanes 16 and 32 apart; mean, then the squared deviations
+            // this wave's channels of token 16 p + c: 4 NT in this lane, the
+            // rest in lanes 16 and 32 apart; mean, then squared deviations
+            constexpr float inv = 1.0f / (4 * NT * 4);
             float s = 0.0f;
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
@@ -464,7 +520,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 for (int e = 0; e < 4; ++e) s += ot[ni][e];
             s += __shfl_xor(s, 16, 64);
             s += __shfl_xor(s, 32, 64);
-            const float mean = s * (1.0f / kN);
+            const float mean = s * inv;
             float q = 0.0f;
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni)
@@ -472,20 +528,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 for (int e = 0; e < 4; ++e) q = fmaf(ot[ni][e] - mean, ot[ni][e] - mean, q);
             q += __shfl_xor(q, 16, 64);
             q += __shfl_xor(q, 32, 64);
-            const float rstd = __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps);
-            const int h = bh % H;
-#pragma unroll
-            for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
-                const f32x4 lw = *(const f32x4 *)(ln_w + (size_t)h * kN + 16 * ni + 4 * g);
-                const f32x4 lb = *(const f32x4 *)(ln_b + (size_t)h * kN + 16 * ni + 4 * g);
-                const float gv[4] = {bf16_lo(gq[ni].x), bf16_hi(gq[ni].x), bf16_lo(gq[ni].y),
-                                     bf16_hi(gq[ni].y)};
-                f32x4 yv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    yv[e] = fmaf((ot[ni][e] - mean) * rstd, lw[e], lb[e]) * silu(gv[e]);
-                __builtin_amdgcn_raw_buffer_store_b64(pack4(yv[0], yv[1], yv[2], yv[3]), ro,
-                                                      off + 32 * ni, 0, 0);
+            if (NH == 1) {  // the whole token is in this wave
+                epi_compute(mean, __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps));
+                yq_ch = ch;
+                epi_flush();
+            } else {
+                if (g == 0) sStat[set][w][c] = f32x2{mean, q};
+                epi_ch = ch;
+                epi_set = set;
             }
             return;
         }
@@ -587,36 +637,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int e = 0; e < 4; ++e)
                 S[t][e] = sS[(skey(t) + 4 * g + e) * kN + sval(t) + c];
         if (EPI) {
-            // the epilogue of the chunk from sO: four threads per token, 16
-            // channels each (written before the barrier above)
-            const int tok = tid >> 2, q4 = tid & 3;
-            float ov[16];
+            // the epilogue of the chunk from sO (written before the barrier
+            // above): LPT threads per token, CPT channels each
+            constexpr int CPT = kL * kN / (64 * NW), LPT = kN / CPT;
+            const int tok = tid / LPT, qq = tid % LPT;
+            float ov[CPT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ov[i] = sO[tok * kN + 16 * q4 + i];
+            for (int i = 0; i < CPT; ++i) ov[i] = sO[tok * kN + CPT * qq + i];
             float s = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s += ov[i];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
+            for (int i = 0; i < CPT; ++i) s += ov[i];
+#pragma unroll
+            for (int m = 1; m < LPT; m <<= 1) s += __shfl_xor(s, m, 64);
             const float mean = s * (1.0f / kN);
             float q = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) q = fmaf(ov[i] - mean, ov[i] - mean, q);
-            q += __shfl_xor(q, 1, 64);
-            q += __shfl_xor(q, 2, 64);
+            for (int i = 0; i < CPT; ++i) q = fmaf(ov[i] - mean, ov[i] - mean, q);
+#pragma unroll
+            for (int m = 1; m < LPT; m <<= 1) q += __shfl_xor(q, m, 64);
             const float rstd = __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps);
             const int h = bh % H;
             const Rsrc rg = rsrc(gate + cx.base(c0), cx.span(c0));
             const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
-            const uint32_t off = (uint32_t)tok * cx.tokb + 2 * (16 * q4);
+            const uint32_t off = (uint32_t)tok * cx.tokb + 2 * (CPT * qq);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < CPT / 8; ++hh) {
                 const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16 * hh, 0, 0);
                 const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
                 u32x4 out;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int i0 = 8 * hh + 2 * m, ch0 = 16 * q4 + i0;
+                    const int i0 = 8 * hh + 2 * m, ch0 = CPT * qq + i0;
                     const float y0 = fmaf((ov[i0] - mean) * rstd, ln_w[(size_t)h * kN + ch0],
                                           ln_b[(size_t)h * kN + ch0]) * silu(bf16_lo(gw[m]));
                     const float y1 = fmaf((ov[i0 + 1] - mean) * rstd, ln_w[(size_t)h * kN + ch0 + 1],
@@ -665,7 +716,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, 0);
-        if (!unsafe) store_out(ch);
+        if (!unsafe) store_out(ch, 0);
         if (more) stage_state(0);
         return barrier_or(bad, 0);  // (Y) operands of ch + 1 staged
     };
@@ -677,6 +728,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto step1 = [&](int ch, bool unsafe) -> bool {
         const int cur = ch & 1, nxt = cur ^ 1;
         const bool more = ch + 1 < ch_end;
+        epi_finish();  // the previous chunk's outputs, merged after its barrier
+        if (EPI && !unsafe) load_gate(ch);
         if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
         if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
         if (SAVE) save_chunk(ch);
@@ -684,7 +737,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         else token_by_token(ch, cur);
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, nxt);
-        if (!unsafe) store_out(ch);
+        epi_flush();  // the previous chunk's y, after this step's loads were consumed
+        if (!unsafe) store_out(ch, cur);
         if (more) stage_state(nxt);
         if (ch + 2 < ch_end) stageA(ch + 2, buf, cur);
         return barrier_or(bad, cur);  // chunk ch + 1 staged, ch + 2's totals out
@@ -706,6 +760,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (DB && ch0 + 1 < ch1) stageA(ch0 + 1, buf, s0 ^ 1);
         bool unsafe = barrier_or(bad0, DB ? (s0 ^ 1) : 0);
         for (int ch = ch0; ch < ch1; ++ch) unsafe = DB ? step1(ch, unsafe) : step2(ch, unsafe);
+        epi_finish();
+        epi_flush();
     };
 
     if (sp.extra == 0) {  // one head per workgroup
@@ -821,7 +877,9 @@ constexpr int kMaxSlots = 4096;
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const uint16_t *r,
                               const uint16_t *k, const uint16_t *v, const float *x,
                               const float *u, const float *state_in, float *state_out,
-                              uint16_t *o, hipStream_t stream, float *chunk_states) {
+                              uint16_t *o, hipStream_t stream, float *chunk_states,
+                              const uint16_t *gate, const float *ln_w, const float *ln_b,
+                              float eps) {
     // Eight waves per head while every head has a CU of its own.  With up to
     // half as many heads again, eight waves and the balanced split: one
     // workgroup per CU, each running one head plus one K-th of an extra
@@ -853,23 +911,23 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         }
     }
     const int blocks = (int)(sp.extra ? sp.first_extra : heads);
-    if (chunk_states != nullptr) {  // the backward's state recomputation
+    // plain forward; the backward's state recomputation (SAVE); the forward
+    // with the output epilogue (EPI)
+    auto go = [&](auto save_tag, auto epi_tag) {
+        constexpr bool SV = decltype(save_tag)::value, EP = decltype(epi_tag)::value;
+        float *so = SV ? nullptr : state_out;
+        uint16_t *out = SV ? nullptr : o;
         if (per_token_decay) {
-            if (wide) launch<true, 8, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
-            else launch<true, 4, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+            if (wide) launch<true, 8, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
+            else launch<true, 4, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
         } else {
-            if (wide) launch<false, 8, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
-            else launch<false, 4, true>(blocks, T, H, r, k, v, x, u, state_in, nullptr, nullptr, sp, stream, chunk_states);
+            if (wide) launch<false, 8, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
+            else launch<false, 4, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
         }
-        return hipGetLastError();
-    }
-    if (per_token_decay) {
-        if (wide) launch<true, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
-        else launch<true, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
-    } else {
-        if (wide) launch<false, 8>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
-        else launch<false, 4>(blocks, T, H, r, k, v, x, u, state_in, state_out, o, sp, stream);
-    }
+    };
+    if (chunk_states != nullptr) go(std::true_type{}, std::false_type{});
+    else if (gate != nullptr) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
     return hipGetLastError();
 }
 
@@ -879,17 +937,8 @@ hipError_t launch_wkv_chunked_gated(bool per_token_decay, int B, int T, int H,
                                     float *state_out, const uint16_t *gate, const float *ln_w,
                                     const float *ln_b, float eps, uint16_t *y,
                                     hipStream_t stream) {
-    // four waves per head (a head's 64 output channels of a token in one
-    // wave), two heads per CU
-    const int blocks = B * H;
-    const Split sp{};
-    if (per_token_decay)
-        launch<true, 4, false, true>(blocks, T, H, r, k, v, x, u, state_in, state_out, y, sp,
-                                     stream, nullptr, gate, ln_w, ln_b, eps);
-    else
-        launch<false, 4, false, true>(blocks, T, H, r, k, v, x, u, state_in, state_out, y, sp,
-                                      stream, nullptr, gate, ln_w, ln_b, eps);
-    return hipGetLastError();
+    return launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in, state_out, y,
+                              stream, nullptr, gate, ln_w, ln_b, eps);
 }
 
 }  // namespace wkv
