@@ -120,6 +120,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     __shared__ __align__(16) float sO[EPI ? kL * kN : 1];
     // EPI, eight waves: (mean, sum of squared deviations) of each half-token
     __shared__ __align__(16) f32x2 sStat[EPI ? NS : 1][NW][16];
+    // EPI, eight waves: the chunk's gate, [token][channel] bf16, staged with
+    // its operands (four waves, short of registers, load it per lane)
+    constexpr bool GST = EPI && NW == 8;
+    __shared__ __align__(16) uint16_t sG[GST ? NS : 1][GST ? kL * kPR : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -158,19 +162,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // from chunk to chunk: their bases are computed once per head, and each
     // token's factor follows by one multiply.
     f32x4 uq, a2s, wq, eLL, eF1, eF2;
-    f32x4 lnw[EPI ? NT : 1], lnb[EPI ? NT : 1];  // EPI: this lane's norm weight and bias
+    // EPI on eight waves: this lane's norm weight and bias, held per head (on
+    // four waves, where registers are short, read when they are used)
+    constexpr bool LNREG = EPI && NW == 8;
+    f32x4 lnw[LNREG ? NT : 1], lnb[LNREG ? NT : 1];
     int bh = 0;  // (sequence, head) of the current job
+    auto ln_at = [&](int ni, const float *base) -> f32x4 {
+        return *(const f32x4 *)(base + (size_t)(bh % H) * kN + 16 * (NT * hf + ni) + 4 * g);
+    };
     auto set_head = [&](int head) {
         bh = head;
         const int b = head / H, h = head % H;
         cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
         uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
-        if (EPI) {
+        if (LNREG) {
 #pragma unroll
-            for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
-                const int ch0 = 16 * (NT * hf + ni) + 4 * g;
-                lnw[ni] = *(const f32x4 *)(ln_w + (size_t)h * kN + ch0);
-                lnb[ni] = *(const f32x4 *)(ln_b + (size_t)h * kN + ch0);
+            for (int ni = 0; ni < (LNREG ? NT : 1); ++ni) {
+                lnw[ni] = ln_at(ni, ln_w);
+                lnb[ni] = ln_at(ni, ln_b);
             }
         }
         a2s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -252,6 +261,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- stage B: prefix, factors and the operand tiles of a chunk --------
     // (Finch needs stage A of every wave, i.e. a barrier in between)
+    // a chunk's inputs in registers between their load and their staging
+    // (EPI: the gate of the chunk, loaded in v's layout)
+    Raw<NW> buf;
+    u32x4 graw[GST ? Raw<NW>::NV : 1];
+    int ch_end = nchunks;  // end of the current job's chunk range
     auto stageB = [&](int ch, const Raw<NW> &d, int set) -> bool {
         const int c0 = ch * kL;
         f32x4 LL, F1, F2;     // chunk total; 2^{lex_first - LL}; 2^{LL - lin_last}
@@ -352,6 +366,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 #pragma unroll
         for (int j = 0; j < Raw<NW>::NV; ++j)
             *(u32x4 *)(sm[set][T_VR] + (cx.vt + 8 * NW * j) * pitch(T_VR) + 8 * cx.vo) = d.v[j];
+        if (GST) {
+#pragma unroll
+            for (int j = 0; j < (GST ? Raw<NW>::NV : 1); ++j)
+                *(u32x4 *)(sG[set] + (cx.vt + 8 * NW * j) * kPR + 8 * cx.vo) = graw[j];
+        }
         if (c == 0) {
             if (TP == 4)
                 *(f32x4 *)&sBonus[set][TP * cx.tq] = f32x4{bs[0], bs[1 % TP], bs[2 % TP], bs[3 % TP]};
@@ -450,12 +469,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
     };
 
-    // EPI: this lane's gate values (token 16 p + c, channels 16 ni + 4 g + e)
-    // of a chunk, requested at the start of its step
+    // EPI: gq, this lane's gate values (token 16 p + c, channels 16 (NT hf +
+    // ni) + 4 g + e) of a chunk.  Eight waves: the gate is loaded with the
+    // chunk's r, k, v in v's coalesced layout (NV rows of 8 channels per
+    // thread), written to sG by stage B and read from there after the
+    // chunk's products.  Four waves: loaded into gq at the start of the step.
     u32x2 gq[EPI ? NT : 1];
-    auto load_gate = [&](int ch) {
+    auto load_in = [&](int ch) {  // (past the job's chunks: issued, empty)
+        const bool ok = ch < ch_end;
+        load_rkv<NW>(buf, ch * kL, cx, r, k, v, ok);
+        if (GST) {
+            const int c0 = ch * kL;
+            const Rsrc rg = rsrc(gate + cx.base(ok ? c0 : 0), ok ? cx.span(c0) : 0u);
+#pragma unroll
+            for (int j = 0; j < (GST ? Raw<NW>::NV : 1); ++j)
+                graw[j] = __builtin_amdgcn_raw_buffer_load_b128(rg, cx.off_v + j * 8 * NW * cx.tokb,
+                                                                0, 0);
+        }
+    };
+    auto gate_lds = [&](int set) {
+#pragma unroll
+        for (int ni = 0; ni < (GST ? NT : 1); ++ni)
+            gq[ni] = *(const u32x2 *)(sG[set] + (16 * p + c) * kPR + 16 * (NT * hf + ni) + 4 * g);
+    };
+    auto load_gate = [&](int ch, bool ok) {  // (issued, empty, when not ok)
         const int c0 = ch * kL;
-        const Rsrc rg = rsrc(gate + cx.base(c0), cx.span(c0));
+        const Rsrc rg = rsrc(gate + cx.base(c0), ok ? cx.span(c0) : 0u);
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
 #pragma unroll
         for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
@@ -474,17 +513,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int ni = 0; ni < (EPI ? NT : 1); ++ni) {
             const float gv[4] = {bf16_lo(gq[ni].x), bf16_hi(gq[ni].x), bf16_lo(gq[ni].y),
                                  bf16_hi(gq[ni].y)};
+            f32x4 lw, lb;
+            if constexpr (LNREG) {
+                lw = lnw[ni];
+                lb = lnb[ni];
+            } else {
+                lw = ln_at(ni, ln_w);
+                lb = ln_at(ni, ln_b);
+            }
             f32x4 yv;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                yv[e] = fmaf((ot[ni][e] - mean) * rstd, lnw[ni][e], lnb[ni][e]) * silu(gv[e]);
+                yv[e] = fmaf((ot[ni][e] - mean) * rstd, lw[e], lb[e]) * silu(gv[e]);
             yq[ni] = pack4(yv[0], yv[1], yv[2], yv[3]);
         }
     };
-    auto epi_flush = [&]() {
-        if (!EPI || yq_ch < 0) return;
-        const int c0 = yq_ch * kL;
-        const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
+    auto epi_flush = [&]() {  // (nothing pending: issued over an empty range)
+        if (!EPI) return;
+        const int c0 = max(yq_ch, 0) * kL;
+        const Rsrc ro = rsrc(o + cx.base(c0), yq_ch >= 0 ? cx.span(c0) : 0u);
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
 #pragma unroll
         for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
@@ -504,10 +551,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         epi_ch = -1;
     };
 
-    auto store_out = [&](int ch, int set) {
+    // chunk ch's outputs (after a fast-decay chunk, ok is false: the stores
+    // are issued over an empty range, token_by_token having written them)
+    auto store_out = [&](int ch, int set, bool ok) {
         if (SAVE) return;
         const int c0 = ch * kL;
-        const Rsrc ro = rsrc(o + cx.base(c0), cx.span(c0));
+        const Rsrc ro = rsrc(o + cx.base(c0), ok ? cx.span(c0) : 0u);
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
         if (EPI) {
             // this wave's channels of token 16 p + c: 4 NT in this lane, the
@@ -530,9 +579,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             q += __shfl_xor(q, 32, 64);
             if (NH == 1) {  // the whole token is in this wave
                 epi_compute(mean, __builtin_amdgcn_rsqf(q * (1.0f / kN) + eps));
-                yq_ch = ch;
+                yq_ch = ok ? ch : -1;
                 epi_flush();
-            } else {
+            } else if (ok) {
                 if (g == 0) sStat[set][w][c] = f32x2{mean, q};
                 epi_ch = ch;
                 epi_set = set;
@@ -697,8 +746,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int j = 0; j < NW; ++j) r |= sBad[set][j];
         return r != 0;
     };
-    Raw<NW> buf;
-    int ch_end = nchunks;  // end of the current job's chunk range
 
     // Four waves, one tile set, two barriers per chunk.  buf holds chunk
     // ch + 1's inputs when step ch starts: its r, k, v were requested at the
@@ -706,17 +753,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // A had read the registers, a whole step earlier.
     auto step2 = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < ch_end;
-        if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
-        if (EPI && !unsafe) load_gate(ch);
+        load_in(ch + 1);
+        if (EPI) load_gate(ch, !unsafe);
         if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(0);
         else token_by_token(ch, 0);
         if (more) stageA(ch + 1, buf, 0);
-        if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
+        if (PT) load_x<NW>(buf, (ch + 2) * kL, cx, x, ch + 2 < ch_end);
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, 0);
-        if (!unsafe) store_out(ch, 0);
+        store_out(ch, 0, !unsafe);
         if (more) stage_state(0);
         return barrier_or(bad, 0);  // (Y) operands of ch + 1 staged
     };
@@ -728,17 +775,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto step1 = [&](int ch, bool unsafe) -> bool {
         const int cur = ch & 1, nxt = cur ^ 1;
         const bool more = ch + 1 < ch_end;
+        load_in(ch + 1);
+        if (PT) load_x<NW>(buf, (ch + 2) * kL, cx, x, ch + 2 < ch_end);
         epi_finish();  // the previous chunk's outputs, merged after its barrier
-        if (EPI && !unsafe) load_gate(ch);
-        if (more) load_rkv<NW>(buf, (ch + 1) * kL, cx, r, k, v);
-        if (PT && ch + 2 < ch_end) load_x<NW>(buf, (ch + 2) * kL, cx, x);
         if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(cur);
         else token_by_token(ch, cur);
+        if (EPI && !unsafe) gate_lds(cur);
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, nxt);
-        epi_flush();  // the previous chunk's y, after this step's loads were consumed
-        if (!unsafe) store_out(ch, cur);
+        epi_flush();  // the previous chunk's y
+        store_out(ch, cur, !unsafe);
         if (more) stage_state(nxt);
         if (ch + 2 < ch_end) stageA(ch + 2, buf, cur);
         return barrier_or(bad, cur);  // chunk ch + 1 staged, ch + 2's totals out
@@ -749,9 +796,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         ch_end = ch1;
         const int s0 = DB ? (ch0 & 1) : 0;
         if (PT) load_x<NW>(buf, ch0 * kL, cx, x);
-        load_rkv<NW>(buf, ch0 * kL, cx, r, k, v);
+        load_in(ch0);
         stageA(ch0, buf, s0);
-        if (PT && ch0 + 1 < ch1) load_x<NW>(buf, (ch0 + 1) * kL, cx, x);
+        if (PT) load_x<NW>(buf, (ch0 + 1) * kL, cx, x, ch0 + 1 < ch1);
         lds_barrier();
         const bool bad0 = stageB(ch0, buf, s0);
         stage_state(s0);

@@ -125,14 +125,18 @@ struct Ctx {
     __device__ size_t base(int c0) const { return seq_base + (size_t)c0 * tok_stride; }
 };
 
-// one thread's r, k, v of chunk c0 (rows past T read as zero)
+// one thread's r, k, v of chunk c0 (rows past T read as zero).  With
+// valid false the loads are still issued, over an empty range, and read
+// zero: a load issued on every path keeps the count of outstanding memory
+// operations the same on all of them, so that a later wait for an older
+// load is not made to wait for this one too.
 template <int NW>
 __device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
                                          const uint16_t *r, const uint16_t *k,
-                                         const uint16_t *v) {
+                                         const uint16_t *v, bool valid = true) {
     constexpr int TP = Raw<NW>::TP;
-    const size_t cb = cx.base(c0);
-    const uint32_t span = cx.span(c0);
+    const size_t cb = cx.base(valid ? c0 : 0);
+    const uint32_t span = valid ? cx.span(c0) : 0u;
     const Rsrc rr = rsrc(r + cb, span), rk = rsrc(k + cb, span), rv = rsrc(v + cb, span);
 #pragma unroll
     for (int e = 0; e < TP; ++e) {
@@ -145,11 +149,13 @@ __device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
         d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0, 0);
 }
 
-// one thread's Finch decay logits of chunk c0 (rows past T read as zero)
+// one thread's Finch decay logits of chunk c0 (rows past T read as zero;
+// valid as for load_rkv)
 template <int NW>
-__device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const float *x) {
+__device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const float *x,
+                                       bool valid = true) {
     constexpr int TP = Raw<NW>::TP;
-    const Rsrc rx = rsrc(x + cx.base(c0), 2 * cx.span(c0));
+    const Rsrc rx = rsrc(x + cx.base(valid ? c0 : 0), valid ? 2 * cx.span(c0) : 0u);
 #pragma unroll
     for (int e = 0; e < TP; ++e)
         d.x[e] = __builtin_bit_cast(

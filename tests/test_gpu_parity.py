@@ -772,6 +772,26 @@ def test_gated_extreme_decays(logit):
     gated_check(d, True)
 
 
+# 320 heads: eight waves with the extra heads in handed-on segments; 400
+# heads: four-wave workgroups, which load the gate per lane
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100)])
+def test_gated_more_heads_than_cus(per_token, B, T, H):
+    print(f"gated {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    gated_check(gated_case(B, T, H, 950 + H, per_token), per_token)
+
+
+def test_gated_four_waves_fast_decay():
+    # token-by-token chunks among ordinary ones on four-wave workgroups
+    print("gated four waves, mixed decays B=4 T=130 H=100", flush=True)
+    d = gated_case(4, 130, 100, 43, True)
+    x = d["x"].copy()
+    x[..., ::3] = 10.0
+    x[:, 70:90, :, 1::3] = -200.0
+    d["x"] = x
+    gated_check(d, True)
+
+
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 def test_gated_full_workload_sampled_heads(per_token):
     cfg = 4 if per_token else 3
