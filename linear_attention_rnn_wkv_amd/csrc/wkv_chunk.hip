@@ -778,16 +778,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         load_in(ch + 1);
         if (PT) load_x<NW>(buf, (ch + 2) * kL, cx, x, ch + 2 < ch_end);
         epi_finish();  // the previous chunk's outputs, merged after its barrier
+        if (EPI && !GST) load_gate(ch, !unsafe);
         if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(cur);
         else token_by_token(ch, cur);
-        if (EPI && !unsafe) gate_lds(cur);
+        if (GST && !unsafe) gate_lds(cur);
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, nxt);
-        epi_flush();  // the previous chunk's y
-        store_out(ch, cur, !unsafe);
         if (more) stage_state(nxt);
         if (ch + 2 < ch_end) stageA(ch + 2, buf, cur);
+        epi_flush();  // the previous chunk's y
+        store_out(ch, cur, !unsafe);
         return barrier_or(bad, cur);  // chunk ch + 1 staged, ch + 2's totals out
     };
     // chunks [ch0, ch1) of the current head from the state in S
@@ -811,56 +812,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         epi_flush();
     };
 
-    if (sp.extra == 0) {  // one head per workgroup
-        set_head(blockIdx.x);
-        load_state();
-        run_job(0, nchunks);
-        save_state();
-        return;
-    }
-
-    // Balanced split (eight waves, one workgroup per CU): workgroup i runs
-    // its own head i and one segment of one of the sp.extra remaining heads.
-    // The segments of an extra head run on workgroups i, i + sp.stride, ...
-    // (the same XCD, dispatched in order), and segment s starts after the
-    // workgroup's first s/K of its own head, by when segment s-1 is done:
+    // Balanced split (eight waves, one workgroup per CU, sp.extra > 0):
+    // workgroup i runs its own head i and one segment of one of the sp.extra
+    // remaining heads.  The segments of an extra head run on workgroups i,
+    // i + sp.stride, ... (the same XCD, dispatched in order), and segment s
+    // starts after the workgroup's first s/K of its own head, by when segment
+    // s-1 is done:
     //   own [0, a) -> extra segment s = [a, b) -> own [a, nchunks)
-    // The state between segments goes through the handoff workspace.
+    // The state between segments goes through the handoff workspace.  Jobs
+    // run in one loop, so that the chunk loop exists once in the code.
     const int own = blockIdx.x;
-    const int xcd = own % sp.stride, local = own / sp.stride;
-    const int chain = local / sp.K, seg = local % sp.K;
-    const int ext = xcd + sp.stride * chain;  // extra head index among sp.extra
-    if (chain >= sp.chains_per_xcd || ext >= sp.extra) {
-        set_head(own);
-        load_state();
-        run_job(0, nchunks);
-        save_state();
-        return;
+    int ext = 0, seg = 0, a = nchunks, e1 = nchunks;
+    bool split = false;
+    if (DB && sp.extra != 0) {  // (the launcher splits eight-wave launches only)
+        const int xcd = own % sp.stride, local = own / sp.stride;
+        const int chain = local / sp.K;
+        seg = local % sp.K;
+        ext = xcd + sp.stride * chain;  // extra head index among sp.extra
+        split = chain < sp.chains_per_xcd && ext < sp.extra;
+        a = seg * nchunks / sp.K;
+        e1 = (seg + 1) * nchunks / sp.K;
     }
-    const int a = seg * nchunks / sp.K, e1 = (seg + 1) * nchunks / sp.K;
     auto ld = [](const void *ptr) {
         return __hip_atomic_load((unsigned *)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto st = [](void *ptr, unsigned val) {
         __hip_atomic_store((unsigned *)ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    set_head(own);
-    load_state();
-    run_job(0, a);
-    f32x4 Sown[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) Sown[t] = S[t];
-
-    set_head(sp.first_extra + ext);
-    if (seg == 0) {
-        load_state();
-    } else {
-        // Slots and flags are touched only by agent-scope relaxed atomics,
-        // which act at the device's coherence point: the producer's stores
-        // complete before its flag store, and the state is read only after
-        // the flag was seen.  The consumer clears the flag for the next
-        // launch.  Polls are bounded (about a second): the producer has a
-        // lower workgroup index on the same XCD, so it is already running.
+    // the state entering segment seg, from the workgroup that ran seg - 1.
+    // Slots and flags are touched only by agent-scope relaxed atomics, which
+    // act at the device's coherence point: the producer's stores complete
+    // before its flag store, and the state is read only after the flag was
+    // seen.  The consumer clears the flag for the next launch.  Polls are
+    // bounded (about a second): the producer has a lower workgroup index on
+    // the same XCD, so it is already running.
+    auto receive = [&]() {
         const int slot = ext * (sp.K - 1) + seg - 1;
         const float *src = sp.slots + (size_t)slot * kN * kN;
         if (tid == 0) {
@@ -881,11 +867,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
         lds_barrier();
         if (tid == 0) st(sp.flags + slot, 0u);
-    }
-    run_job(a, e1);
-    if (seg + 1 == sp.K) {
-        save_state();
-    } else {
+    };
+    auto send = [&]() {
         const int slot = ext * (sp.K - 1) + seg;
         float *dst = sp.slots + (size_t)slot * kN * kN;
 #pragma unroll
@@ -895,13 +878,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
         lds_barrier();
         if (tid == 0) st(sp.flags + slot, 1u);
-    }
-
-    set_head(own);
+    };
+    f32x4 Sown[DB ? NT : 1];  // own head's state while the extra segment runs
+    const int njobs = split ? 3 : 1;
+#pragma clang loop unroll(disable)
+    for (int job = 0; job < njobs; ++job) {
+        const bool extra = split && job == 1;
+        set_head(extra ? sp.first_extra + ext : own);
+        if (split && job == 2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) S[t] = Sown[t];
-    run_job(a, nchunks);
-    save_state();
+            for (int t = 0; t < (DB ? NT : 1); ++t) S[t] = Sown[t];
+        } else if (extra && seg > 0) {
+            receive();
+        } else {
+            load_state();
+        }
+        run_job(split && job > 0 ? a : 0, split && job < 2 ? (job == 0 ? a : e1) : nchunks);
+        if (split && job == 0) {
+#pragma unroll
+            for (int t = 0; t < (DB ? NT : 1); ++t) Sown[t] = S[t];
+        } else if (extra && seg + 1 < sp.K) {
+            send();
+        } else {
+            save_state();
+        }
+    }
 }
 
 template <bool PT, int NW, bool SAVE = false, bool EPI = false>
