@@ -36,9 +36,11 @@ METRIC = "WKV tokens*channels/s & % HBM/MFMA roofline, Finch D2560 T4096; decode
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    # the clocks settle over the first few tens of back-to-back launches
-    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--steps", type=int, default=200)
+    # Back-to-back launches of the prefill kernels slow down by up to a fifth
+    # after the first few and recover over the next fifty or so (clocks and
+    # power settling): the timed launches start once that has passed.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
     ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
@@ -155,6 +157,27 @@ def finch_bwd_bytes(B, T, H, N=64):
     return tok * (2 * 4 + 4 + 2 * 3 + 4) + 4 * B * H * N * N * 4 + 2 * H * N * 4
 
 
+def finch_gated_bytes(B, T, H, N=64):
+    # the forward's bytes, the gate (bf16) read, the norm weight and bias read
+    return finch_bytes(B, T, H, N) + B * T * H * N * 2 + 2 * H * N * 4
+
+
+def finch_recompute_bytes(B, T, H, N=64, L=64):
+    # the backward's state recomputation: read r, k, v (bf16), x (fp32), u and
+    # the initial states; write the state entering every chunk and the last
+    tok, nch = B * T * H * N, (T + L - 1) // L
+    return tok * (2 * 3 + 4) + B * H * N * N * 4 + B * H * (nch + 1) * N * N * 4 + H * N * 4
+
+
+def finch_reverse_bytes(B, T, H, N=64, L=64):
+    # the reverse sweep: read r, k, v, d_o (bf16), x (fp32), u, the chunk
+    # states and the final state's gradient; write d_r, d_k, d_v (bf16), d_x
+    # (fp32), the initial state's gradient and the per-sequence d_u partials
+    tok, nch = B * T * H * N, (T + L - 1) // L
+    return (tok * (2 * 4 + 4 + 2 * 3 + 4) + B * H * (nch + 1) * N * N * 4
+            + 2 * B * H * N * N * 4 + H * N * 4 + B * H * N * 4)
+
+
 def chunk_mfma_flops(B, T, H, N=64, L=64):
     # per chunk and head, as executed: A^T (lower-triangular 16x16 tiles,
     # K = N), A V (causal K-blocks), Q S, Kh_hi V + Kh_lo V, all bf16 MFMA
@@ -206,7 +229,7 @@ def run_finch_gated(torch, W, S, H2D, args, d4=None):
                               g["ln_b"], 1e-5, state_in=g["s0"], state_out=so, y=y)
 
     res = time_launches(torch, launch, args.steps, args.warmup)
-    nbytes = finch_bytes(B, T, H) + B * T * H * 64 * 2 + 2 * H * 64 * 4  # + gate, norm params
+    nbytes = finch_gated_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_fwd_gated_B8_T4096_D2560_H40_N64_bf16",
                 "tokens_channels_per_s": B * T * H * 64 / sec,
@@ -381,6 +404,12 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
     "finch_fwd": ("wkv_chunk_kernel<true,", "wkv_chunk.hip", lambda: finch_bytes(8, 4096, 40)),
     "eagle_fwd": ("wkv_chunk_kernel<false,", "wkv_chunk.hip", lambda: eagle_bytes(8, 4096, 32)),
     "rwkv4_fwd": ("rwkv4_chain_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
+    "finch_fwd_gated": ("wkv_chunk_kernel<true, 8, false, true>", "wkv_chunk.hip",
+                        lambda: finch_gated_bytes(8, 4096, 40)),
+    "finch_bwd_recompute": ("wkv_chunk_kernel<true, 8, true, false>", "wkv_chunk.hip",
+                            lambda: finch_recompute_bytes(8, 4096, 40)),
+    "finch_bwd_reverse": ("wkv_bwd_kernel<true>", "wkv_chunk_bwd.hip",
+                          lambda: finch_reverse_bytes(8, 4096, 40)),
     "finch_decode": ("wkv_step_kernel<true>", "wkv_step.hip",
                      lambda: decode_bytes_per_step(256, 64)),
     "eagle_decode": ("wkv_step_kernel<false>", "wkv_step.hip",
@@ -389,6 +418,8 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
                      lambda: rwkv4_decode_bytes_per_step(256, 4096)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
+            "finch_fwd_gated": "finch_gated", "finch_bwd_recompute": "finch_bwd",
+            "finch_bwd_reverse": "finch_bwd",
             "finch_decode": "decode", "eagle_decode": "eagle_decode",
             "rwkv4_decode": "rwkv4_decode"}
 
@@ -514,6 +545,10 @@ def main():
     for key, rec in paths.items():  # counter-measured HBM bytes, while current
         if key in PMC_PATHS:
             rec["traffic_bytes"] = measured_traffic(PMC_PATHS[key][1], key)
+    if "finch_bwd" in paths:  # the backward's two main kernels, each on its own
+        paths["finch_bwd"]["traffic_bytes"] = {
+            k: measured_traffic(PMC_PATHS[k][1], k)
+            for k in ("finch_bwd_recompute", "finch_bwd_reverse")}
     finch = paths["finch_fwd"]
     spec = S.WORKLOADS[4]
     ms = finch["wall_s"] / args.steps * 1e3
