@@ -45,6 +45,9 @@ def _bind(lib):
                                       d, d, d, ctypes.c_int]
     lib.oracle_norm_gate.restype = ctypes.c_int
     lib.oracle_norm_gate.argtypes = [L, L, L, d, f, f, f, ctypes.c_double, d, ctypes.c_int]
+    lib.oracle_decay_lora.restype = ctypes.c_int
+    lib.oracle_decay_lora.argtypes = [L, L, L, L, L, f, f, f, f, f, f, f, f, f, ctypes.c_int, d,
+                                      ctypes.c_int]
     lib.oracle_wkv_matrix_bwd.restype = ctypes.c_int
     lib.oracle_wkv_matrix_bwd.argtypes = [L, L, L, L, f, f, f, f, ctypes.c_int, f,
                                           d, d, d, d, d, d, d, d, d, ctypes.c_int]
@@ -220,3 +223,39 @@ def norm_gate(o, g, ln_w, ln_b, eps, nthreads=None, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_norm_gate failed ({rc})")
     return y
+
+
+def decay_lora(x, mu_x, lam, A1, B1, omega, A2, B2, act="tanh", shift=None, nthreads=None,
+               lib=None):
+    """Finch decay logits d [B, T, D] (float64) from the block input x
+    [B, T, D] by ddlerp and LoRA_omega (see oracle_decay_lora).
+
+    mu_x, lam, omega: [D]; A1: [D, R1]; B1: [R1, D]; A2: [D, R2]; B2: [R2, D];
+    act: "identity" or "tanh"; shift: [B, D], the token before x[:, 0]
+    (None = zeros)."""
+    lib = lib or load()
+    x, xp = _f32(x)
+    B, T, D = x.shape
+    mu_x, mup = _f32(mu_x)
+    lam, lp = _f32(lam)
+    omega, op = _f32(omega)
+    A1, a1p = _f32(A1)
+    B1, b1p = _f32(B1)
+    A2, a2p = _f32(A2)
+    B2, b2p = _f32(B2)
+    R1, R2 = A1.shape[1], A2.shape[1]
+    assert mu_x.shape == (D,) and lam.shape == (D,) and omega.shape == (D,)
+    assert A1.shape == (D, R1) and B1.shape == (R1, D)
+    assert A2.shape == (D, R2) and B2.shape == (R2, D)
+    if shift is None:
+        sp = ctypes.POINTER(ctypes.c_float)()
+    else:
+        shift, sp = _f32(shift)
+        assert shift.shape == (B, D)
+    code = {"identity": 0, "tanh": 1}[act]
+    d = np.empty((B, T, D), np.float64)
+    rc = lib.oracle_decay_lora(B, T, D, R1, R2, xp, sp, mup, lp, a1p, b1p, op, a2p, b2p, code,
+                               _f64(d)[1], int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_decay_lora failed ({rc})")
+    return d

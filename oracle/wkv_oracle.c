@@ -334,3 +334,78 @@ int oracle_norm_gate(long rows, long H, long N, const double *o, const float *g,
     }
     return ORACLE_OK;
 }
+
+/*
+ * Finch decay producer (RWKV-5/6 summary: 4.1.1 "Eagle token shift", the
+ * linear interpolation between x_t and x_{t-1} with a learned mix per
+ * channel; 4.2.1 "Finch token shift", the data-dependent interpolation
+ * (ddlerp) whose mix is a learned vector lam plus a low-rank (LoRA) term
+ * with A in R^{D x R1}, B in R^{R1 x D}, the LoRA taking the Eagle-style
+ * shifted value, made with mu_x, as its input; LoRA_omega with
+ * A in R^{D x 64}, B in R^{64 x D}; 4.2.2 "Finch time mixing": the decay
+ * varies per token and channel, LoRA applied again after the interpolation).
+ * No formula is printed; the reading taken, per sequence and token t, with
+ * x_{-1} = shift (zeros when NULL):
+ *     dx  = x_{t-1} - x_t
+ *     y   = x_t + dx * mu_x                    (Eagle-style lerp)
+ *     m   = lam + act(y A1) B1                 (LoRA of the mix)
+ *     z   = x_t + dx * m                       (ddlerp)
+ *     d_t = omega + act(z A2) B2               (LoRA_omega: the decay logit)
+ * act is the identity (act = 0) or tanh (act = 1); w_t = exp(-exp(d_t)) is
+ * then the Finch decay of the WKV above.  Products are plain sums in order.
+ *   x       [B][T][D]      shift [B][D] or NULL
+ *   mu_x, lam, omega [D]
+ *   A1 [D][R1]  B1 [R1][D]  A2 [D][R2]  B2 [R2][D]
+ *   d       [B][T][D] output
+ */
+int oracle_decay_lora(long B, long T, long D, long R1, long R2, const float *x,
+                      const float *shift, const float *mu_x, const float *lam,
+                      const float *A1, const float *B1, const float *omega,
+                      const float *A2, const float *B2, int act, double *d, int nthreads)
+{
+    if (B < 0 || T < 0 || D < 1 || R1 < 1 || R2 < 1 || (act != 0 && act != 1) || nthreads < 1)
+        return ORACLE_BAD_ARG;
+    int bad = 0;
+#pragma omp parallel num_threads(nthreads) reduction(|| : bad)
+    {
+        double *dx = malloc(sizeof(double) * D), *y = malloc(sizeof(double) * D);
+        double *z = malloc(sizeof(double) * D);
+        double *h1 = malloc(sizeof(double) * R1), *h2 = malloc(sizeof(double) * R2);
+        if (!dx || !y || !z || !h1 || !h2) {
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (long bt = 0; bt < B * T; ++bt) {
+                long b = bt / T, t = bt % T;
+                const float *xt = x + bt * D;
+                for (long i = 0; i < D; ++i) {
+                    double prev = t > 0 ? (double)xt[i - D] : (shift ? (double)shift[b * D + i] : 0.0);
+                    dx[i] = prev - (double)xt[i];
+                    y[i] = (double)xt[i] + dx[i] * (double)mu_x[i];
+                }
+                for (long j = 0; j < R1; ++j) {
+                    double s = 0.0;
+                    for (long i = 0; i < D; ++i) s += y[i] * (double)A1[i * R1 + j];
+                    h1[j] = act ? tanh(s) : s;
+                }
+                for (long i = 0; i < D; ++i) {
+                    double m = (double)lam[i];
+                    for (long j = 0; j < R1; ++j) m += h1[j] * (double)B1[j * D + i];
+                    z[i] = (double)xt[i] + dx[i] * m;
+                }
+                for (long j = 0; j < R2; ++j) {
+                    double s = 0.0;
+                    for (long i = 0; i < D; ++i) s += z[i] * (double)A2[i * R2 + j];
+                    h2[j] = act ? tanh(s) : s;
+                }
+                for (long i = 0; i < D; ++i) {
+                    double s = (double)omega[i];
+                    for (long j = 0; j < R2; ++j) s += h2[j] * (double)B2[j * D + i];
+                    d[bt * D + i] = s;
+                }
+            }
+        }
+        free(dx); free(y); free(z); free(h1); free(h2);
+    }
+    return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+}

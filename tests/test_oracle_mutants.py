@@ -74,6 +74,22 @@ MUTANTS = {
     "ng_sigmoid_gate": ("double silu = gi / (1.0 + exp(-gi));", "double silu = 1.0 / (1.0 + exp(-gi));"),
     "ng_no_centering": ("double n = (ou[i] - mean) * rstd", "double n = ou[i] * rstd"),
     "ng_bias_wrong_head": ("(double)ln_b[h * N + i];", "(double)ln_b[((h + 1) % H) * N + i];"),
+    # decay producer
+    "dl_shift_sign": ("dx[i] = prev - (double)xt[i];", "dx[i] = (double)xt[i] - prev;"),
+    "dl_lerp_drops_mu": ("y[i] = (double)xt[i] + dx[i] * (double)mu_x[i];",
+                         "y[i] = (double)xt[i];"),
+    "dl_ignores_shift_row": ("(shift ? (double)shift[b * D + i] : 0.0)", "(shift ? 0.0 : 0.0)"),
+    "dl_first_shift_late": ("double prev = t > 0 ?", "double prev = t > 1 ?"),
+    "dl_mix_drops_lam": ("double m = (double)lam[i];", "double m = 0.0;"),
+    "dl_mix_not_scaled_by_dx": ("z[i] = (double)xt[i] + dx[i] * m;", "z[i] = (double)xt[i] + m;"),
+    "dl_mix_lora_drops_hidden": ("m += h1[j] * (double)B1[j * D + i];", "m += (double)B1[j * D + i];"),
+    "dl_mix_lora_rank_permuted": ("s += y[i] * (double)A1[i * R1 + j];",
+                                  "s += y[i] * (double)A1[i * R1 + (R1 - 1 - j)];"),
+    "dl_omega_lora_reads_lerp": ("s += z[i] * (double)A2[i * R2 + j];",
+                                 "s += y[i] * (double)A2[i * R2 + j];"),
+    "dl_omega_lora_no_activation": ("h2[j] = act ? tanh(s) : s;", "h2[j] = s;"),
+    "dl_omega_lora_channel_reversed": ("s += h2[j] * (double)B2[j * D + i];",
+                                       "s += h2[j] * (double)B2[j * D + (D - 1 - i)];"),
     "bwd_ignores_final_state_gradient": (
         "dS[i] = d_sT ? d_sT[(b * H + h) * NN + i] : 0.0;", "dS[i] = 0.0;"),
 }
@@ -98,6 +114,12 @@ PINS = [
     (P.test_norm_gate_is_group_norm_times_silu, {}),
     (P.test_norm_gate_normalises_each_head, {}),
     (P.test_norm_gate_affine_and_gate_structure, {}),
+    (P.test_decay_lora_without_offset_is_omega, {}),
+    (P.test_decay_lora_constant_sequence, {}),
+    (P.test_decay_lora_full_and_no_shift, {}),
+    (P.test_decay_lora_mix_lora_structure, {}),
+    (P.test_decay_lora_tanh_saturates, {}),
+    (P.test_decay_lora_split_and_channel_locality, {}),
 ]
 
 

@@ -516,3 +516,119 @@ def test_norm_gate_affine_and_gate_structure(oracle_lib):
     assert not np.any(oracle.norm_gate(o, np.zeros_like(gate), w, b, 1e-3, lib=oracle_lib))
     shifted = oracle.norm_gate(o + 7.0, gate, w, b, 1e-3, lib=oracle_lib)
     assert np.allclose(shifted, y, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Finch decay producer: ddlerp and LoRA_omega (RWKV-5/6 summary 4.2.1, 4.2.2)
+
+def _dl_case(seed, B=2, T=7, D=12, R1=3, R2=5):
+    g = np.random.default_rng(seed)
+    f = lambda *s: g.standard_normal(s).astype(np.float32)
+    return dict(x=f(B, T, D), shift=f(B, D), mu_x=g.random(D).astype(np.float32),
+                lam=g.random(D).astype(np.float32), A1=f(D, R1) * 0.3, B1=f(R1, D) * 0.3,
+                omega=f(D) - 3.0, A2=f(D, R2) * 0.3, B2=f(R2, D) * 0.4)
+
+
+def _dl(c, lib, act="tanh", **over):
+    a = dict(c)
+    a.update(over)
+    return oracle.decay_lora(a["x"], a["mu_x"], a["lam"], a["A1"], a["B1"], a["omega"],
+                             a["A2"], a["B2"], act=act, shift=a["shift"], lib=lib)
+
+
+def _prev(c):
+    # x_{t-1}, with the shift row before the first token
+    return np.concatenate([c["shift"][:, None, :], c["x"][:, :-1, :]], axis=1).astype(np.float64)
+
+
+def test_decay_lora_without_offset_is_omega(oracle_lib):
+    # B_omega = 0 (or A_omega = 0 under tanh) leaves the learned logit omega:
+    # Eagle's static decay, whatever the input
+    c = _dl_case(11)
+    for act in ("identity", "tanh"):
+        d = _dl(c, oracle_lib, act, B2=np.zeros_like(c["B2"]))
+        assert np.array_equal(d, np.broadcast_to(c["omega"].astype(np.float64), d.shape))
+    d = _dl(c, oracle_lib, "tanh", A2=np.zeros_like(c["A2"]))
+    assert np.array_equal(d, np.broadcast_to(c["omega"].astype(np.float64), d.shape))
+
+
+def test_decay_lora_constant_sequence(oracle_lib):
+    # x_t = x_{t-1} for every t: the interpolation returns x whatever its mix,
+    # so d = omega + act(x A2) B2 (numpy products), independent of mu, lam, A1, B1
+    c = _dl_case(12)
+    row = c["x"][:, :1, :]
+    c["x"] = np.repeat(row, c["x"].shape[1], axis=1)
+    c["shift"] = row[:, 0, :].copy()
+    xr = c["x"].astype(np.float64)
+    for act, fn in (("identity", lambda s: s), ("tanh", np.tanh)):
+        want = c["omega"].astype(np.float64) + fn(xr @ c["A2"].astype(np.float64)) @ c["B2"].astype(np.float64)
+        got = _dl(c, oracle_lib, act)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+        got2 = _dl(c, oracle_lib, act, mu_x=1 - c["mu_x"], lam=c["lam"] * 3, A1=-c["A1"],
+                   B1=c["B1"] * 2)
+        assert np.allclose(got2, got, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_lora_full_and_no_shift(oracle_lib):
+    # B1 = 0: the mix is lam alone.  lam = 1 takes the previous token (the
+    # shift row before the first), lam = 0 the current one; either way the
+    # decay is omega + act(. A2) B2 (numpy products)
+    c = _dl_case(13)
+    A2, B2, om = (c[n].astype(np.float64) for n in ("A2", "B2", "omega"))
+    for lam, src in ((1.0, _prev(c)), (0.0, c["x"].astype(np.float64))):
+        got = _dl(c, oracle_lib, "tanh", B1=np.zeros_like(c["B1"]),
+                  lam=np.full_like(c["lam"], lam))
+        assert np.allclose(got, om + np.tanh(src @ A2) @ B2, rtol=1e-12, atol=1e-12)
+    # lam = 1/2: the midpoint
+    got = _dl(c, oracle_lib, "identity", B1=np.zeros_like(c["B1"]),
+              lam=np.full_like(c["lam"], 0.5))
+    mid = 0.5 * (_prev(c) + c["x"].astype(np.float64))
+    assert np.allclose(got, om + (mid @ A2) @ B2, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_lora_mix_lora_structure(oracle_lib):
+    # A2 = B2 = I, omega = 0, identity: d exposes z = x + dx * m.  The part of
+    # z that the mix's LoRA adds, divided by dx, is (y A1) B1 = y (A1 B1) with
+    # y = x (mu = 0) or y = x_{t-1} (mu = 1), and it is linear in B1
+    c = _dl_case(14, R2=12)
+    D = c["x"].shape[-1]
+    eye = np.eye(D, dtype=np.float32)
+    base = dict(A2=eye, B2=eye, omega=np.zeros(D, np.float32))
+    dx = _prev(c) - c["x"].astype(np.float64)
+    AB = c["A1"].astype(np.float64) @ c["B1"].astype(np.float64)
+    z0 = _dl(c, oracle_lib, "identity", B1=np.zeros_like(c["B1"]), **base)
+    for mu, y in ((0.0, c["x"].astype(np.float64)), (1.0, _prev(c))):
+        z = _dl(c, oracle_lib, "identity", mu_x=np.full_like(c["mu_x"], mu), **base)
+        assert np.allclose((z - z0) / dx, y @ AB, rtol=1e-9, atol=1e-9)
+        z2 = _dl(c, oracle_lib, "identity", mu_x=np.full_like(c["mu_x"], mu),
+                 B1=c["B1"] * 2, **base)
+        assert np.allclose(z2 - z0, 2 * (z - z0), rtol=1e-12, atol=1e-12)
+
+
+def test_decay_lora_tanh_saturates(oracle_lib):
+    # a huge A_omega saturates tanh: d = omega + sign(x A2) B2 (mix lam = 0)
+    c = _dl_case(15)
+    got = _dl(c, oracle_lib, "tanh", A2=c["A2"] * 1e6, B1=np.zeros_like(c["B1"]),
+              lam=np.zeros_like(c["lam"]))
+    s = np.sign(c["x"].astype(np.float64) @ c["A2"].astype(np.float64))
+    want = c["omega"].astype(np.float64) + s @ c["B2"].astype(np.float64)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_lora_split_and_channel_locality(oracle_lib):
+    # a split sequence with the first part's last token as the shift row gives
+    # the same bits; channel i of d depends on column i of B2 and omega only
+    c = _dl_case(16, T=9)
+    full = _dl(c, oracle_lib)
+    a = dict(c, x=c["x"][:, :4].copy())
+    b = dict(c, x=c["x"][:, 4:].copy(), shift=c["x"][:, 3].copy())
+    assert np.array_equal(np.concatenate([_dl(a, oracle_lib), _dl(b, oracle_lib)], axis=1), full)
+    B2 = c["B2"].copy()
+    B2[:, 5] += 1.0
+    om = c["omega"].copy()
+    om[7] -= 2.0
+    got = _dl(c, oracle_lib, B2=B2, omega=om)
+    keep = [i for i in range(full.shape[-1]) if i not in (5, 7)]
+    assert np.array_equal(got[..., keep], full[..., keep])
+    assert np.allclose(got[..., 7], full[..., 7] - 2.0, rtol=0, atol=1e-12)
+    assert not np.allclose(got[..., 5], full[..., 5])
