@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
     ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
-                                       "rwkv4_decode", "finch_bwd", "finch_gated", "calib"],
+                                       "rwkv4_decode", "finch_bwd", "finch_gated", "finch_lora",
+                                       "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -162,6 +163,16 @@ def finch_gated_bytes(B, T, H, N=64):
     return finch_bytes(B, T, H, N) + B * T * H * N * 2 + 2 * H * N * 4
 
 
+def finch_lora_bytes(B, T, H, N=64):
+    # the fused forward: the producer reads the block input (bf16) and
+    # writes act(z A_omega) (64 bf16 per token); the chunked kernel reads r,
+    # k, v and that factor and writes o; the states in and out; the
+    # producer's weights and vectors once
+    D, rows = H * N, B * T
+    return (rows * D * 2 + 2 * rows * 64 * 2 + rows * D * (2 * 3 + 2)
+            + 2 * B * H * N * N * 4 + (2 * D * 32 + 2 * D * 64) * 2 + 4 * D * 4 + H * N * 4)
+
+
 def finch_recompute_bytes(B, T, H, N=64, L=64):
     # the backward's state recomputation: read r, k, v (bf16), x (fp32), u and
     # the initial states; write the state entering every chunk and the last
@@ -232,6 +243,33 @@ def run_finch_gated(torch, W, S, H2D, args, d4=None):
     nbytes = finch_gated_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_fwd_gated_B8_T4096_D2560_H40_N64_bf16",
+                "tokens_channels_per_s": B * T * H * 64 / sec,
+                "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+    return res
+
+
+def run_finch_lora(torch, W, S, H2D, args, d4=None):
+    """Finch workload with the decay logits made on the device from a block
+    input by ddlerp and LoRA_omega (tanh): the producer and the chunked
+    kernel, timed together as one call."""
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    d = dict(d4) if d4 is not None else S.workload(4)
+    d.update(S.decay_lora_inputs(B, T, H, 64, 4))
+    g = H2D({n: a for n, a in d.items() if a is not None})
+    o = torch.empty_like(g["r"])
+    so = torch.empty_like(g["s0"])
+
+    def launch():
+        W.rwkv6_wkv_fwd_lora(g["r"], g["k"], g["v"], g["xin"], g["mu_x"], g["lam"], g["A1"],
+                             g["B1"], g["omega"], g["A2"], g["B2"], g["u"], act="tanh",
+                             shift=g["shift"], state_in=g["s0"], state_out=so, o=o)
+
+    res = time_launches(torch, launch, args.steps, args.warmup)
+    nbytes = finch_lora_bytes(B, T, H)
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({"workload": "finch_fwd_lora_B8_T4096_D2560_H40_N64_bf16",
                 "tokens_channels_per_s": B * T * H * 64 / sec,
                 "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
@@ -524,6 +562,9 @@ def main():
     if not args.skip_paths and only in (None, "finch_gated"):
         print("finch forward with the epilogue ...", file=sys.stderr, flush=True)
         paths["finch_fwd_gated"] = run_finch_gated(torch, W, S, H2D, args, d4)
+    if not args.skip_paths and only in (None, "finch_lora"):
+        print("finch forward with the decay producer ...", file=sys.stderr, flush=True)
+        paths["finch_fwd_lora"] = run_finch_lora(torch, W, S, H2D, args, d4)
     if not args.skip_paths and only in (None, "finch_bwd"):
         print("finch backward ...", file=sys.stderr, flush=True)
         paths["finch_bwd"] = run_finch_bwd(torch, W, S, H2D, args, d4)

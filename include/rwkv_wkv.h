@@ -282,6 +282,62 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
                   float *d_x, float *d_u, float *d_state_in,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Finch decay producer (RWKV-5/6 summary, 4.1.1 "Eagle token shift",
+ * 4.2.1 "Finch token shift" and 4.2.2 "Finch time mixing": the decay logit
+ * of every token and channel from the block input by the data-dependent
+ * interpolation (ddlerp) with a LoRA of rank 32, then LoRA_omega of rank 64).
+ * Per sequence b and token t, with x_{-1} = shift[b] (zero when shift is
+ * NULL) and act the identity (act = 0) or tanh (act = 1):
+ *
+ *   dx = x_{t-1} - x_t
+ *   y  = x_t + dx * mu_x
+ *   m  = lam + act(y A1) B1
+ *   z  = x_t + dx * m
+ *   d  = omega + act(z A2) B2,     w_t = exp(-exp(d)) is Finch's decay.
+ *
+ *   x          [B][T][D] bf16 block input (D = H N, a multiple of 64, else
+ *              RWKV_E_UNSUPPORTED)
+ *   shift      [B][D] bf16, the token before x[b][0] (a previous segment's
+ *              last token), or NULL
+ *   mu_x, lam, omega [D] fp32
+ *   A1 [D][32], B1 [32][D], A2 [D][64], B2 [64][D] bf16 (row-major, as the
+ *              pages give their shapes)
+ *   d          [B][T][D] fp32 output: the logits rwkv6_wkv_fwd takes as x
+ *              (with D = H N in its [B][T][H][N] layout)
+ * The products run on bf16 matrix cores with fp32 accumulation (the mixed
+ * values and act(.) rounded to bf16 as operands).  B T must be below 2^31.
+ * Scratch: a per-stream workspace of B T 128 bytes (kept by the library,
+ * reused by later calls on the stream).  T = 0 does nothing.  All pointers
+ * need 16-byte alignment; d must not overlap an input.
+ */
+int rwkv6_decay_lora(int B, int T, int D, int act,
+                     const rwkv_bf16 *x, const rwkv_bf16 *shift,
+                     const float *mu_x, const float *lam,
+                     const rwkv_bf16 *A1, const rwkv_bf16 *B1,
+                     const float *omega, const rwkv_bf16 *A2, const rwkv_bf16 *B2,
+                     float *d, void *stream);
+
+/*
+ * Finch time-parallel forward fed by the decay producer: the same output and
+ * state as rwkv6_decay_lora followed by rwkv6_wkv_fwd with x = d, without
+ * the fp32 logits ever going to memory.  The producer writes act(z A2)
+ * (rank 64, bf16, B T 128 bytes of the per-stream workspace) and the chunked
+ * kernel forms each head's logits omega + act(z A2) B2 on the matrix cores.
+ * Arguments: r, k, v, u, state_in, state_out, o as rwkv6_wkv_fwd; x (the
+ * block input, [B][T][H N] bf16), shift, mu_x, lam, A1, B1, omega, A2, B2 and
+ * act as rwkv6_decay_lora with D = H N.
+ */
+int rwkv6_wkv_fwd_lora(int B, int T, int H, int N,
+                       const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                       const rwkv_bf16 *x, const rwkv_bf16 *shift,
+                       const float *mu_x, const float *lam,
+                       const rwkv_bf16 *A1, const rwkv_bf16 *B1,
+                       const float *omega, const rwkv_bf16 *A2, const rwkv_bf16 *B2,
+                       int act, const float *u,
+                       const float *state_in, float *state_out,
+                       rwkv_bf16 *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPO
 EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
            "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step", "rwkv5_wkv_bwd",
            "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes", "rwkv5_wkv_fwd_gated",
-           "rwkv6_wkv_fwd_gated")
+           "rwkv6_wkv_fwd_gated", "rwkv6_decay_lora", "rwkv6_wkv_fwd_lora")
 
 _lib = None
 
@@ -78,6 +78,10 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I] + [P] * 15 + [ctypes.c_size_t, P]
+        L.rwkv6_decay_lora.restype = I
+        L.rwkv6_decay_lora.argtypes = [I, I, I, I] + [P] * 11
+        L.rwkv6_wkv_fwd_lora.restype = I
+        L.rwkv6_wkv_fwd_lora.argtypes = [I, I, I, I] + [P] * 12 + [I] + [P] * 5
         _lib = L
     return _lib
 
@@ -333,3 +337,72 @@ def rwkv6_wkv_bwd(r, k, v, x, u, d_o, state_in=None, d_state_out=None, grads=Non
 def workspace_bytes(B, T, H, N=64):
     """Bytes of device workspace the backward needs."""
     return int(lib().rwkv_wkv_bwd_workspace_bytes(B, T, H, N))
+
+
+ACTS = {"identity": 0, "tanh": 1}
+
+
+def _lora_args(x, shift, mu_x, lam, A1, B1, omega, A2, B2, act):
+    import torch
+    B, T, D = x.shape
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect("x", x, (B, T, D), bf)
+    if shift is not None:
+        _expect("shift", shift, (B, D), bf)
+    for name, t in (("mu_x", mu_x), ("lam", lam), ("omega", omega)):
+        _expect(name, t, (D,), f32)
+    _expect("A1", A1, (D, 32), bf)
+    _expect("B1", B1, (32, D), bf)
+    _expect("A2", A2, (D, 64), bf)
+    _expect("B2", B2, (64, D), bf)
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    return B, T, D
+
+
+def rwkv6_decay_lora(x, mu_x, lam, A1, B1, omega, A2, B2, act="tanh", shift=None, d=None,
+                     stream=None):
+    """Finch decay logits d [B, T, D] fp32 from the block input x [B, T, D]
+    bf16: ddlerp with the mix's LoRA (A1 [D, 32], B1 [32, D] bf16, mu_x and
+    lam [D] fp32), then LoRA_omega (A2 [D, 64], B2 [64, D] bf16, omega [D]);
+    act "tanh" or "identity"; shift [B, D] bf16, the token before x[:, 0]
+    (None = zeros)."""
+    import torch
+    B, T, D = _lora_args(x, shift, mu_x, lam, A1, B1, omega, A2, B2, act)
+    if d is None:
+        d = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
+    _expect("d", d, (B, T, D), torch.float32)
+    _check("rwkv6_decay_lora", lib().rwkv6_decay_lora(
+        B, T, D, ACTS[act], _ptr(x), _ptr(shift), _ptr(mu_x), _ptr(lam), _ptr(A1), _ptr(B1),
+        _ptr(omega), _ptr(A2), _ptr(B2), _ptr(d), _stream(stream)))
+    return d
+
+
+def rwkv6_wkv_fwd_lora(r, k, v, x, mu_x, lam, A1, B1, omega, A2, B2, u, act="tanh",
+                       shift=None, state_in=None, state_out=None, o=None, return_state=True,
+                       stream=None):
+    """Finch WKV, chunked, with the decay logits made on the device from the
+    block input x [B, T, H*64] bf16 (as rwkv6_decay_lora): the result of
+    rwkv6_wkv_fwd(r, k, v, rwkv6_decay_lora(...).view(B, T, H, 64), u, ...)."""
+    import torch
+    B, T, H, N = r.shape
+    bf, f32 = torch.bfloat16, torch.float32
+    for name, t in (("r", r), ("k", k), ("v", v)):
+        _expect(name, t, (B, T, H, N), bf)
+    _expect("u", u, (H, N), f32)
+    _expect("x", x, (B, T, H * N), bf)
+    _lora_args(x, shift, mu_x, lam, A1, B1, omega, A2, B2, act)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), f32)
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=bf, device=r.device)
+    _expect("o", o, (B, T, H, N), bf)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, N, N), dtype=f32, device=r.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, H, N, N), f32)
+    _check("rwkv6_wkv_fwd_lora", lib().rwkv6_wkv_fwd_lora(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(shift), _ptr(mu_x), _ptr(lam),
+        _ptr(A1), _ptr(B1), _ptr(omega), _ptr(A2), _ptr(B2), ACTS[act], _ptr(u),
+        _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
+    return o, state_out

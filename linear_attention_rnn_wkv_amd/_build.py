@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "librwkv_wkv.so")
 SOURCES = ["rwkv_wkv_abi.hip", "rwkv4_scan.hip", "rwkv4_step.hip", "wkv_step.hip",
-           "wkv_chunk.hip", "wkv_chunk_bwd.hip"]
+           "wkv_chunk.hip", "wkv_chunk_bwd.hip", "decay_lora.hip"]
 # The RWKV-4 chain counts arrivals with one lane's returning atomic whose
 # result is only needed at the end of the workgroup; the atomic optimizer
 # would broadcast it at once and so wait for the round trip right there.

@@ -14,7 +14,7 @@ int device_cus();
 // stream run in order and may share it; a kernel that uses flags in it must
 // leave them cleared.  A larger request reallocates (synchronising the
 // stream first).  Kept until the process ends.
-enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1 };
+enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1, kWsDecayH = 2 };
 hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out);
 
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
@@ -43,7 +43,21 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
                               uint16_t *o, hipStream_t stream,
                               float *chunk_states = nullptr, const uint16_t *gate = nullptr,
                               const float *ln_w = nullptr, const float *ln_b = nullptr,
-                              float eps = 0.0f);
+                              float eps = 0.0f, const uint16_t *lora_h = nullptr,
+                              const uint16_t *lora_B2 = nullptr,
+                              const float *lora_omega = nullptr);
+
+// Finch decay producer (decay_lora.hip): h = act(z A2) per token, bf16
+// [rows][64], from the block input x [rows][D] (rows = B T, T tokens per
+// sequence), the shift row per sequence (NULL: zero), mu, lam [D] fp32,
+// A1 [D][32], B1 [32][D], A2 [D][64] bf16.  D a multiple of 64.
+hipError_t launch_decay_lora(int rows, int T, int D, bool tanh_act, const uint16_t *x,
+                             const uint16_t *shift, const float *mu, const float *lam,
+                             const uint16_t *A1, const uint16_t *B1, const uint16_t *A2,
+                             uint16_t *h, hipStream_t stream);
+// d = omega + h B2 [rows][D] fp32 (B2 [64][D] bf16, omega [D])
+hipError_t launch_lora_logits(int rows, int D, const uint16_t *h, const uint16_t *B2,
+                              const float *omega, float *d, hipStream_t stream);
 
 // Eagle / Finch chunked forward with the time-mixing epilogue (LayerNorm per
 // head, affine, SiLU gate) applied to the output: y instead of o.

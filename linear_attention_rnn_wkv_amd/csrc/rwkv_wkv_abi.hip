@@ -131,6 +131,29 @@ int matrix_fwd_gated(bool per_token, int B, int T, int H, int N, const rwkv_bf16
                                                     eps, y, s));
 }
 
+// Checks of the decay producer's arguments (D = H N channels); `out` is the
+// caller's output, which must not overlap them.
+constexpr int kLoraR1 = 32, kLoraR2 = 64;
+
+int check_lora(int B, int T, int D, int act, const void *x, const void *shift,
+               const void *mu_x, const void *lam, const void *A1, const void *B1,
+               const void *omega, const void *A2, const void *B2, Span out) {
+    if (B < 1 || T < 0 || D < 1 || (act != 0 && act != 1)) return RWKV_E_DIM;
+    const int64_t tok = checked_mul({B, T, D});
+    if (tok < 0) return RWKV_E_DIM;
+    if (D % 64 != 0 || (int64_t)B * T >= ((int64_t)1 << 31)) return RWKV_E_UNSUPPORTED;
+    if (T == 0) return RWKV_OK;
+    for (const void *p : {x, mu_x, lam, A1, B1, omega, A2, B2})
+        if (p == nullptr) return RWKV_E_NULL;
+    for (const void *p : {x, shift, mu_x, lam, A1, B1, omega, A2, B2})
+        if (p != nullptr && !aligned(p, 16)) return RWKV_E_ALIGN;
+    const int64_t vec = (int64_t)D * 4;
+    const Span sx{x, tok * 2}, ss{shift, (int64_t)B * D * 2}, smu{mu_x, vec}, sl{lam, vec},
+        sa1{A1, (int64_t)D * kLoraR1 * 2}, sb1{B1, (int64_t)D * kLoraR1 * 2}, so{omega, vec},
+        sa2{A2, (int64_t)D * kLoraR2 * 2}, sb2{B2, (int64_t)D * kLoraR2 * 2};
+    return check_outputs({out}, {sx, ss, smu, sl, sa1, sb1, so, sa2, sb2});
+}
+
 int matrix_step(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                 const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                 float *state, rwkv_bf16 *o, void *stream) {
@@ -333,6 +356,62 @@ int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf
                    const rwkv_bf16 *v, const float *x, const float *u, float *state,
                    rwkv_bf16 *o, void *stream) {
     return matrix_step(true, B, T, H, N, r, k, v, x, u, state, o, stream);
+}
+
+int rwkv6_decay_lora(int B, int T, int D, int act, const rwkv_bf16 *x, const rwkv_bf16 *shift,
+                     const float *mu_x, const float *lam, const rwkv_bf16 *A1,
+                     const rwkv_bf16 *B1, const float *omega, const rwkv_bf16 *A2,
+                     const rwkv_bf16 *B2, float *d, void *stream) {
+    const int64_t tok = checked_mul({B, T, D});
+    if (T > 0 && d == nullptr) return RWKV_E_NULL;
+    if (d != nullptr && !aligned(d, 16)) return RWKV_E_ALIGN;
+    int st = check_lora(B, T, D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2,
+                        Span{d, tok * 4});
+    if (st != RWKV_OK || T == 0) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int rows = B * T;
+    uint16_t *h = nullptr;
+    hipError_t e = wkv::stream_workspace(wkv::kWsDecayH, s, (size_t)rows * kLoraR2 * 2,
+                                         (void **)&h);
+    if (e != hipSuccess) return RWKV_E_HIP;
+    e = wkv::launch_decay_lora(rows, T, D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    if (e != hipSuccess) return RWKV_E_HIP;
+    return hip_status(wkv::launch_lora_logits(rows, D, h, B2, omega, d, s));
+}
+
+int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                       const rwkv_bf16 *v, const rwkv_bf16 *x, const rwkv_bf16 *shift,
+                       const float *mu_x, const float *lam, const rwkv_bf16 *A1,
+                       const rwkv_bf16 *B1, const float *omega, const rwkv_bf16 *A2,
+                       const rwkv_bf16 *B2, int act, const float *u, const float *state_in,
+                       float *state_out, rwkv_bf16 *o, void *stream) {
+    // the WKV's own arguments (u stands in for the logits, which are formed
+    // on the device), then the producer's against both outputs
+    int st = check_matrix(B, T, H, N, r, k, v, u, checked_mul({H, N}), u, state_in, state_out,
+                          false, o);
+    if (st != RWKV_OK) return st;
+    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
+    const int64_t D = (int64_t)H * N, tok = checked_mul({B, T, H, N});
+    const Span so{o, tok * 2}, sso{state_out, checked_mul({B, H, N, N}) * 4};
+    st = check_lora(B, T, (int)D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2, so);
+    if (st != RWKV_OK) return st;
+    if (T > 0) {
+        st = check_lora(B, T, (int)D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2, sso);
+        if (st != RWKV_OK) return st;
+    }
+    if (T == 0)
+        return matrix_fwd(true, B, T, H, N, r, k, v, u, u, state_in, state_out, o, stream);
+    hipStream_t s = (hipStream_t)stream;
+    const int rows = B * T;
+    uint16_t *h = nullptr;
+    hipError_t e = wkv::stream_workspace(wkv::kWsDecayH, s, (size_t)rows * kLoraR2 * 2,
+                                         (void **)&h);
+    if (e != hipSuccess) return RWKV_E_HIP;
+    e = wkv::launch_decay_lora(rows, T, (int)D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    if (e != hipSuccess) return RWKV_E_HIP;
+    return hip_status(wkv::launch_wkv_chunked(true, B, T, H, r, k, v, nullptr, u, state_in,
+                                              state_out, o, s, nullptr, nullptr, nullptr,
+                                              nullptr, 0.0f, h, B2, omega));
 }
 
 }  // extern "C"

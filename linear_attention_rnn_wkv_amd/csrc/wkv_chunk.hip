@@ -82,6 +82,14 @@ struct Split {
     unsigned *flags;  // [max_slots] slot flags, then an error word
 };
 
+// Finch decay logits from the decay producer: h [B T][64] bf16, the rank-64
+// factor of LoRA_omega of every token; B2 [64][H N] bf16 (B_omega) and
+// omega [H N] fp32.  A head's logits are d = omega + h B2[:, head].
+struct Lora {
+    const uint16_t *h, *B2;
+    const float *omega;
+};
+
 // SAVE: instead of the outputs and the final state, store the state entering
 // every chunk and the final state, [B H][nchunks + 1][64][64] fp32 key-major,
 // for the backward pass.
@@ -95,14 +103,15 @@ struct Split {
 // of squared deviations of its half, the halves are merged through LDS
 // after the step's barrier, and the chunk's outputs are written at the start
 // of the next step (before its products overwrite the accumulators).
-template <bool PT, int NW, bool SAVE, bool EPI = false>
+template <bool PT, int NW, bool SAVE, bool EPI = false, bool LORA = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x,
     const float *__restrict__ u, const float *state_in, float *state_out,
     uint16_t *__restrict__ o, Split sp, float *chunk_states,
     const uint16_t *__restrict__ gate, const float *__restrict__ ln_w,
-    const float *__restrict__ ln_b, float eps) {
+    const float *__restrict__ ln_b, float eps, Lora lr) {
+    static_assert(!LORA || (PT && !SAVE && !EPI), "the decay producer feeds the plain Finch forward");
     constexpr int NH = NW / 4;        // value / key halves split across waves
     constexpr int NT = 4 / NH;        // 16-wide value (P2) or key (P3) tiles per wave
     constexpr int TP = Raw<NW>::TP;   // tokens per staging thread
@@ -124,6 +133,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // its operands (four waves, short of registers, load it per lane)
     constexpr bool GST = EPI && NW == 8;
     __shared__ __align__(16) uint16_t sG[GST ? NS : 1][GST ? kL * kPR : 1];
+    // LORA: the head's block of B_omega, [rank][channel] bf16, and per wave
+    // its tokens' decay logits on their way from the product's layout to
+    // stage A's, [token][channel] fp32
+    constexpr int kDP = kN + 4;
+    __shared__ __align__(16) uint16_t sB2[LORA ? kN * kPC : 1];
+    __shared__ __align__(16) float sD[LORA ? NW : 1][LORA ? 4 * TP : 1][LORA ? kDP : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -162,6 +177,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // from chunk to chunk: their bases are computed once per head, and each
     // token's factor follows by one multiply.
     f32x4 uq, a2s, wq, eLL, eF1, eF2;
+    f32x4 omq;         // LORA: omega of this thread's four channels
+    size_t hrow0 = 0;  // LORA: the sequence's first row of h
     // EPI on eight waves: this lane's norm weight and bias, held per head (on
     // four waves, where registers are short, read when they are used)
     constexpr bool LNREG = EPI && NW == 8;
@@ -175,6 +192,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const int b = head / H, h = head % H;
         cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
         uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * cx.cq);
+        if (LORA) {
+            // the head's B_omega block: 64 rows of 128 bytes (no wave reads
+            // sB2 between the previous job's last barrier and this one)
+            omq = *(const f32x4 *)(lr.omega + (size_t)h * kN + 4 * cx.cq);
+            hrow0 = (size_t)b * T;
+            for (int q = tid; q < kN * 8; q += 64 * NW)
+                *(u32x4 *)(sB2 + (q >> 3) * kPC + 8 * (q & 7)) =
+                    *(const u32x4 *)(lr.B2 + (size_t)(q >> 3) * H * kN + (size_t)h * kN + 8 * (q & 7));
+            lds_barrier();
+        }
         if (LNREG) {
 #pragma unroll
             for (int ni = 0; ni < (LNREG ? NT : 1); ++ni) {
@@ -230,17 +257,78 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int e = 0; e < 4; ++e) state_out[base + sidx(t, e)] = S[t][e];
     };
 
+    // a chunk's inputs in registers between their load and their staging
+    // (EPI: the gate of the chunk, loaded in v's layout)
+    Raw<NW> buf;
+    u32x4 graw[GST ? Raw<NW>::NV : 1];
+    int ch_end = nchunks;  // end of the current job's chunk range
+
+    // ---- LORA: the decay logits of a chunk from h ---------------------
+    // A wave forms d^T = B2^T h^T for a 16-token tile holding its own 4 TP
+    // tokens (eight waves: the pair's tile, half of it kept): lane (c, g)
+    // loads h of token c, ranks 32 s + 8 g .. + 7, as the B operand of k-step s.
+    typedef u32x4 HOps[LORA ? 2 : 1];
+    HOps hq;
+    const int dlo = NW == 8 ? 8 * (w & 1) : 0;  // first own token in the tile
+    auto load_h_to = [&](HOps &dst, int ch, bool ok) {
+        const int c0 = ch * kL;
+        const int tile = NW == 8 ? 16 * (w >> 1) : 16 * w;
+        const uint16_t *base = lr.h + (hrow0 + (size_t)(ok ? c0 : 0)) * kN;
+        const Rsrc rh = rsrc(base, ok ? (uint32_t)min(kL, T - c0) * kN * 2 : 0u);
+#pragma unroll
+        for (int s2 = 0; s2 < (LORA ? 2 : 1); ++s2)
+            dst[s2] = __builtin_amdgcn_raw_buffer_load_b128(
+                rh, (uint32_t)((tile + c) * kN + 32 * s2 + 8 * g) * 2, 0, 0);
+    };
+    auto load_h = [&](int ch, bool ok) { load_h_to(hq, ch, ok); };
+    // the chunk's next decay operands: x, or h for the producer's logits
+    auto load_dec = [&](int ch, bool ok) {
+        if (LORA) load_h(ch, ok);
+        else if (PT) load_x<NW>(buf, ch * kL, cx, x, ok);
+    };
+    // this thread's logits (tokens TP tq + e, channels 4 cq + q) from the h
+    // operands hs of its tile: the product into the wave's sD rows, then
+    // read back in stage A's layout
+    auto lora_product = [&](const HOps &hs) {
+#pragma unroll
+        for (int M = 0; M < 4; ++M) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                acc = mfma(lds_col8(sB2, 32 * s2 + 8 * g, 16 * M, c),
+                           __builtin_bit_cast(bf16x8, hs[LORA ? s2 : 0]), acc);
+            if (c >= dlo && c < dlo + 4 * TP)
+                *(f32x4 *)&sD[LORA ? w : 0][LORA ? c - dlo : 0][16 * M + 4 * g] = acc;
+        }
+    };
+    auto lora_read = [&](f32x4(&xv)[TP]) {
+#pragma unroll
+        for (int e = 0; e < TP; ++e)
+            xv[e] = *(const f32x4 *)&sD[LORA ? w : 0][LORA ? TP * g + e : 0][4 * cx.cq] + omq;
+    };
+    auto lora_logits = [&](const HOps &hs, f32x4(&xv)[TP]) {
+        lora_product(hs);
+        lora_read(xv);
+    };
+
     // ---- stage A (Finch): log2 decays and the in-wave part of their scan --
     float a2[TP][4], lower[4];
     auto stageA = [&](int ch, const Raw<NW> &d, int set) {
         if (!PT) return;
         const int c0 = ch * kL;
+        f32x4 xv[TP];
+        if constexpr (LORA) {
+            lora_logits(hq, xv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < TP; ++e) xv[e] = d.x[e];
+        }
 #pragma unroll
         for (int e = 0; e < TP; ++e) {
             const bool valid = c0 + TP * cx.tq + e < T;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                a2[e][q] = valid ? -exp2_fast(d.x[e][q] * kLog2e) * kLog2e : 0.0f;
+                a2[e][q] = valid ? -exp2_fast(xv[e][q] * kLog2e) * kLog2e : 0.0f;
         }
         f32x4 wt;
 #pragma unroll
@@ -261,11 +349,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- stage B: prefix, factors and the operand tiles of a chunk --------
     // (Finch needs stage A of every wave, i.e. a barrier in between)
-    // a chunk's inputs in registers between their load and their staging
-    // (EPI: the gate of the chunk, loaded in v's layout)
-    Raw<NW> buf;
-    u32x4 graw[GST ? Raw<NW>::NV : 1];
-    int ch_end = nchunks;  // end of the current job's chunk range
     auto stageB = [&](int ch, const Raw<NW> &d, int set) -> bool {
         const int c0 = ch * kL;
         f32x4 LL, F1, F2;     // chunk total; 2^{lex_first - LL}; 2^{LL - lin_last}
@@ -615,6 +698,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                     Sc[m][e] = sS[(16 * m + 4 * g + e) * kN + 16 * w + c];
         }
         lds_barrier();
+        // LORA: the chunk's logits formed again from its h (hq already holds
+        // a later chunk's), in the same thread layout as stage A
+        f32x4 xl[LORA ? TP : 1];
+        if constexpr (LORA) {
+            HOps ht;
+            load_h_to(ht, ch, true);
+            lora_logits(ht, xl);
+        }
         // re-read r, k, x of the chunk one token row at a time (few registers)
 #pragma unroll 1
         for (int e = 0; e < TP; ++e) {
@@ -626,7 +717,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 const size_t off = cx.seq_base + (size_t)(c0 + tau) * cx.tok_stride + 4 * cx.cq;
                 rv = *(const u32x2 *)(r + off);
                 kv = *(const u32x2 *)(k + off);
-                if (PT) xv = *(const f32x4 *)(x + off);
+                if constexpr (LORA) {
+#pragma unroll
+                    for (int i = 0; i < (LORA ? TP : 1); ++i)
+                        if (e == i) xv = xl[i];
+                } else if (PT) {
+                    xv = *(const f32x4 *)(x + off);
+                }
             }
             f32x4 wv;
 #pragma unroll
@@ -759,7 +856,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (!unsafe) matrix(0);
         else token_by_token(ch, 0);
         if (more) stageA(ch + 1, buf, 0);
-        if (PT) load_x<NW>(buf, (ch + 2) * kL, cx, x, ch + 2 < ch_end);
+        load_dec(ch + 2, ch + 2 < ch_end);
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, 0);
@@ -776,7 +873,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const int cur = ch & 1, nxt = cur ^ 1;
         const bool more = ch + 1 < ch_end;
         load_in(ch + 1);
-        if (PT) load_x<NW>(buf, (ch + 2) * kL, cx, x, ch + 2 < ch_end);
+        load_dec(ch + 2, ch + 2 < ch_end);
         epi_finish();  // the previous chunk's outputs, merged after its barrier
         if (EPI && !GST) load_gate(ch, !unsafe);
         if (SAVE) save_chunk(ch);
@@ -796,10 +893,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (ch0 >= ch1) return;
         ch_end = ch1;
         const int s0 = DB ? (ch0 & 1) : 0;
-        if (PT) load_x<NW>(buf, ch0 * kL, cx, x);
+        load_dec(ch0, true);
         load_in(ch0);
         stageA(ch0, buf, s0);
-        if (PT) load_x<NW>(buf, (ch0 + 1) * kL, cx, x, ch0 + 1 < ch1);
+        load_dec(ch0 + 1, ch0 + 1 < ch1);
         lds_barrier();
         const bool bad0 = stageB(ch0, buf, s0);
         stage_state(s0);
@@ -905,15 +1002,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     }
 }
 
-template <bool PT, int NW, bool SAVE = false, bool EPI = false>
+template <bool PT, int NW, bool SAVE = false, bool EPI = false, bool LORA = false>
 void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, const uint16_t *v,
             const float *x, const float *u, const float *state_in, float *state_out,
             uint16_t *o, const Split &sp, hipStream_t stream, float *chunk_states = nullptr,
             const uint16_t *gate = nullptr, const float *ln_w = nullptr,
-            const float *ln_b = nullptr, float eps = 0.0f) {
-    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW, SAVE, EPI>), dim3((unsigned)blocks),
+            const float *ln_b = nullptr, float eps = 0.0f, Lora lr = Lora{}) {
+    hipLaunchKernelGGL((wkv_chunk_kernel<PT, NW, SAVE, EPI, LORA>), dim3((unsigned)blocks),
                        dim3(64 * NW), 0, stream, T, H, r, k, v, x, u, state_in, state_out, o,
-                       sp, chunk_states, gate, ln_w, ln_b, eps);
+                       sp, chunk_states, gate, ln_w, ln_b, eps, lr);
 }
 
 // XCDs of the device: workgroups are dealt to them round-robin
@@ -927,7 +1024,8 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
                               const float *u, const float *state_in, float *state_out,
                               uint16_t *o, hipStream_t stream, float *chunk_states,
                               const uint16_t *gate, const float *ln_w, const float *ln_b,
-                              float eps) {
+                              float eps, const uint16_t *lora_h, const uint16_t *lora_B2,
+                              const float *lora_omega) {
     // Eight waves per head while every head has a CU of its own.  With up to
     // half as many heads again, eight waves and the balanced split: one
     // workgroup per CU, each running one head plus one K-th of an extra
@@ -973,9 +1071,17 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
             else launch<false, 4, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
         }
     };
-    if (chunk_states != nullptr) go(std::true_type{}, std::false_type{});
-    else if (gate != nullptr) go(std::false_type{}, std::true_type{});
-    else go(std::false_type{}, std::false_type{});
+    if (lora_h != nullptr) {  // Finch, the decay logits from the decay producer
+        const Lora lr{lora_h, lora_B2, lora_omega};
+        if (wide) launch<true, 8, false, false, true>(blocks, T, H, r, k, v, nullptr, u, state_in, state_out, o, sp, stream, nullptr, nullptr, nullptr, nullptr, 0.0f, lr);
+        else launch<true, 4, false, false, true>(blocks, T, H, r, k, v, nullptr, u, state_in, state_out, o, sp, stream, nullptr, nullptr, nullptr, nullptr, 0.0f, lr);
+    } else if (chunk_states != nullptr) {
+        go(std::true_type{}, std::false_type{});
+    } else if (gate != nullptr) {
+        go(std::false_type{}, std::true_type{});
+    } else {
+        go(std::false_type{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 

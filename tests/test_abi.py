@@ -325,3 +325,62 @@ def test_gated_checks(L, fn):
     assert gated(L, fn, mis={"g": 8}) == E_ALIGN
     assert gated(L, fn, y=8) == E_ALIAS   # y on the gate
     assert gated(L, fn, y=1) == E_ALIAS   # y on r
+
+
+# ---------------------------------------------------------------------------
+# Finch decay producer and the forward it feeds
+
+LORA_NAMES = ("x", "sh", "mu", "lam", "a1", "b1", "om", "a2", "b2")
+
+
+def decay(L, B=2, T=8, D=128, act=1, **over):
+    names = LORA_NAMES + ("d",)
+    idx = {n: i + 1 for i, n in enumerate(names)}
+    idx.update({n: val for n, val in over.items() if n in idx})
+    mis = over.get("mis", {})
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
+    return L.rwkv6_decay_lora(B, T, D, act, *(a[n] for n in names), None)
+
+
+def fused(L, B=2, T=8, H=2, N=64, act=1, **over):
+    names = ("r", "k", "v") + LORA_NAMES + ("u", "si", "so", "o")
+    idx = {n: i + 1 for i, n in enumerate(names)}
+    idx.update({n: val for n, val in over.items() if n in idx})
+    mis = over.get("mis", {})
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
+    first = [a[n] for n in ("r", "k", "v") + LORA_NAMES]
+    return L.rwkv6_wkv_fwd_lora(B, T, H, N, *first, act, a["u"], a["si"], a["so"], a["o"], None)
+
+
+@pytest.mark.parametrize("missing", ["x", "mu", "lam", "a1", "b1", "om", "a2", "b2", "d"])
+def test_decay_lora_null(L, missing):
+    assert decay(L, **{missing: None}) == E_NULL
+
+
+def test_decay_lora_checks(L):
+    assert decay(L, D=96) == E_UNSUP          # D not a multiple of 64
+    assert decay(L, act=2) == E_DIM
+    assert decay(L, B=0) == E_DIM
+    assert decay(L, T=-1) == E_DIM
+    assert decay(L, B=1 << 16, T=1 << 15) == E_UNSUP  # B T >= 2^31 rows
+    assert decay(L, mis={"a2": 8}) == E_ALIGN
+    assert decay(L, mis={"sh": 4}) == E_ALIGN
+    assert decay(L, d=1) == E_ALIAS           # d on x
+    assert decay(L, d=9) == E_ALIAS           # d on B2
+    assert decay(L, T=0, d=None) == OK        # nothing to do
+    assert decay(L, sh=None, T=0) == OK
+
+
+@pytest.mark.parametrize("missing", ["r", "x", "a1", "b2", "om", "u", "o"])
+def test_fused_null(L, missing):
+    assert fused(L, **{missing: None}) == E_NULL
+
+
+def test_fused_checks(L):
+    assert fused(L, N=32) == E_UNSUP
+    assert fused(L, act=-1) == E_DIM
+    assert fused(L, B=1, T=1, H=65537, si=None, so=None) == E_UNSUP
+    assert fused(L, mis={"b1": 8}) == E_ALIGN
+    assert fused(L, o=4) == E_ALIAS           # o on the block input
+    assert fused(L, so=11) == E_ALIAS         # state_out on B2
+    assert fused(L, o=1) == E_ALIAS           # o on r

@@ -809,3 +809,162 @@ def test_gated_full_workload_sampled_heads(per_token):
         y_ref, n_ref, gate, s_ref = gated_ref(sub)
         assert_gated_close(bf16_host(y[b:b + 1, :, h:h + 1]), y_ref, n_ref, gate, f"y {(b, h)}")
         assert_matrix_close(f64_host(so[b:b + 1, h:h + 1]), s_ref, f"state {(b, h)}")
+
+
+# ---------------------------------------------------------------------------
+# Finch decay producer (ddlerp + LoRA_omega) and the forward it feeds.
+# Tolerance of the logits: the products run on bf16 operands (the mixed
+# values and act(.) rounded), so the error is measured against the spread of
+# the offset d - omega: RMS <= 5e-3 and max <= 3e-2 of rms(d_ref - omega).
+
+def lora_case(B, T, H, seed, shift=True, **kw):
+    return S.decay_lora_inputs(B, T, H, 64, seed, shift=shift, **kw)
+
+
+def lora_dev(d):
+    return {n: (None if a is None else to_dev(a, a.dtype == np.uint16)) for n, a in d.items()}
+
+
+def lora_ref(d, act="tanh"):
+    f = S.bf16_to_f32
+    return oracle.decay_lora(f(d["xin"]), d["mu_x"], d["lam"], f(d["A1"]), f(d["B1"]),
+                             d["omega"], f(d["A2"]), f(d["B2"]), act=act,
+                             shift=None if d["shift"] is None else f(d["shift"]))
+
+
+def assert_logits_close(got, ref, omega, what):
+    spread = np.sqrt(np.mean((ref - omega) ** 2))
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    rms, mx = np.sqrt(np.mean(err ** 2)) / spread, err.max() / spread
+    assert rms <= 5e-3 and mx <= 3e-2, f"{what}: rms {rms:.3e}, max {mx:.3e} of the spread"
+
+
+@pytest.mark.parametrize("act", ["tanh", "identity"])
+@pytest.mark.parametrize("B,T,H,shift", [(1, 1, 1, True), (1, 17, 2, False), (2, 130, 4, True),
+                                         (3, 50, 3, False), (1, 300, 40, True)])
+def test_decay_lora_vs_oracle(act, B, T, H, shift):
+    # 128-token tiles: T = 130 and T = 50 put sequence starts inside a tile
+    print(f"decay producer {act} B={B} T={T} H={H} shift={shift}", flush=True)
+    d = lora_case(B, T, H, 60 + T + H, shift=shift)
+    g = lora_dev(d)
+    got = W.rwkv6_decay_lora(g["xin"], g["mu_x"], g["lam"], g["A1"], g["B1"], g["omega"],
+                             g["A2"], g["B2"], act=act, shift=g["shift"])
+    sync()
+    assert_logits_close(f64_host(got), lora_ref(d, act), d["omega"], "d")
+
+
+def fused_run(g, m, act="tanh", state_in=True):
+    return W.rwkv6_wkv_fwd_lora(m["r"], m["k"], m["v"], g["xin"], g["mu_x"], g["lam"], g["A1"],
+                                g["B1"], g["omega"], g["A2"], g["B2"], m["u"], act=act,
+                                shift=g["shift"], state_in=m["s0"] if state_in else None)
+
+
+def fused_check(B, T, H, seed, act="tanh", shift=True):
+    m = matrix_case(B, T, H, seed, True)
+    d = lora_case(B, T, H, seed, shift=shift)
+    g, md = lora_dev(d), matrix_inputs_dev(m)
+    o, so = fused_run(g, md, act)
+    sync()
+    x = lora_ref(d, act).reshape(B, T, H, 64).astype(np.float32)
+    f = S.bf16_to_f32
+    o_ref, s_ref = oracle.wkv_matrix(f(m["r"]), f(m["k"]), f(m["v"]), x, m["u"], m["s0"])
+    assert_matrix_close(bf16_host(o), o_ref, "o")
+    assert_matrix_close(f64_host(so), s_ref, "state")
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 63, 1), (1, 65, 2), (2, 130, 3), (1, 300, 2)])
+def test_fused_forward_vs_oracle(B, T, H):
+    print(f"fused forward B={B} T={T} H={H}", flush=True)
+    fused_check(B, T, H, 70 + T + H)
+
+
+# 320 heads: eight waves and the balanced split; 400 heads: four waves
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100)])
+def test_fused_forward_more_heads_than_cus(B, T, H):
+    print(f"fused forward B={B} T={T} H={H}", flush=True)
+    fused_check(B, T, H, 80 + H, shift=False)
+
+
+@pytest.mark.parametrize("B,T,H", [(2, 150, 2), (4, 130, 100)])
+def test_fused_forward_fast_decay(B, T, H):
+    # omega = +10 on every third channel: those chunks run token by token and
+    # form their logits again from h; four waves at 400 heads
+    print(f"fused forward, fast decays B={B} T={T} H={H}", flush=True)
+    m = matrix_case(B, T, H, 31, True)
+    d = lora_case(B, T, H, 31)
+    d["omega"] = d["omega"].copy()
+    d["omega"][::3] = 10.0
+    g, md = lora_dev(d), matrix_inputs_dev(m)
+    o, so = fused_run(g, md)
+    sync()
+    x = lora_ref(d).reshape(B, T, H, 64).astype(np.float32)
+    f = S.bf16_to_f32
+    o_ref, s_ref = oracle.wkv_matrix(f(m["r"]), f(m["k"]), f(m["v"]), x, m["u"], m["s0"])
+    assert_matrix_close(bf16_host(o), o_ref, "o")
+    assert_matrix_close(f64_host(so), s_ref, "state")
+
+
+def test_fused_forward_identity_lora():
+    print("fused forward, identity LoRA, B=2 T=200 H=2", flush=True)
+    fused_check(2, 200, 2, 91, act="identity")
+
+
+def test_fused_forward_split_is_bitwise():
+    # a sequence cut at a multiple of 64: the second part takes the first's
+    # last block input as its shift row and its state as state_in
+    B, T, H, cut = 2, 320, 3, 192
+    m = matrix_inputs_dev(matrix_case(B, T, H, 13, True))
+    g = lora_dev(lora_case(B, T, H, 13))
+    o, so = fused_run(g, m)
+    part = lambda t, a, b: t[:, a:b].contiguous()
+    g1 = dict(g, xin=part(g["xin"], 0, cut))
+    g2 = dict(g, xin=part(g["xin"], cut, T), shift=g["xin"][:, cut - 1].contiguous())
+    m1 = {n: part(m[n], 0, cut) for n in ("r", "k", "v")}
+    m2 = {n: part(m[n], cut, T) for n in ("r", "k", "v")}
+    m1.update(u=m["u"], s0=m["s0"])
+    o1, s1 = fused_run(g1, m1)
+    m2.update(u=m["u"], s0=s1)
+    o2, s2 = fused_run(g2, m2)
+    sync()
+    assert torch.equal(torch.cat([o1, o2], 1), o) and torch.equal(s2, so)
+
+
+def test_fused_forward_matches_producer_then_forward():
+    # the two-call path (logits through memory) and the fused one agree to
+    # fp32 rounding of the logits' last product
+    B, T, H = 2, 257, 4
+    m = matrix_inputs_dev(matrix_case(B, T, H, 17, True))
+    g = lora_dev(lora_case(B, T, H, 17))
+    o, so = fused_run(g, m)
+    dl = W.rwkv6_decay_lora(g["xin"], g["mu_x"], g["lam"], g["A1"], g["B1"], g["omega"],
+                            g["A2"], g["B2"], shift=g["shift"])
+    o2, so2 = W.rwkv6_wkv_fwd(m["r"], m["k"], m["v"], dl.view(B, T, H, 64), m["u"],
+                              state_in=m["s0"])
+    sync()
+    assert_matrix_close(bf16_host(o), bf16_host(o2), "o")
+    assert_matrix_close(f64_host(so), f64_host(so2), "state")
+
+
+def test_fused_forward_full_workload_sampled_heads():
+    # Finch workload 4 with its logits made by the producer: heads of two
+    # sequences against the oracle (producer on those sequences, then WKV)
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    print(f"fused forward workload 4: B={B} T={T} H={H}", flush=True)
+    m = S.workload(4)
+    d = S.decay_lora_inputs(B, T, H, 64, 4)
+    g, md = lora_dev(d), matrix_inputs_dev(m)
+    o, so = fused_run(g, md)
+    sync()
+    f = S.bf16_to_f32
+    for b in (0, B - 1):
+        one = dict(d, xin=d["xin"][b:b + 1], shift=d["shift"][b:b + 1])
+        x = lora_ref(one).reshape(1, T, H, 64).astype(np.float32)
+        for h in (0, H // 2, H - 1):
+            head = lambda a: a[b:b + 1, :, h:h + 1]
+            o_ref, s_ref = oracle.wkv_matrix(f(head(m["r"])), f(head(m["k"])), f(head(m["v"])),
+                                             x[:, :, h:h + 1], m["u"][h:h + 1],
+                                             m["s0"][b:b + 1, h:h + 1])
+            assert_matrix_close(bf16_host(o[b:b + 1, :, h:h + 1]), o_ref, f"o {(b, h)}")
+            assert_matrix_close(f64_host(so[b:b + 1, h:h + 1]), s_ref, f"state {(b, h)}")
+    assert torch.isfinite(o.float()).all()

@@ -26,6 +26,8 @@ BLOCK = 1 << 20
 T_R, T_K, T_V, T_OMEGA, T_DELTA, T_U, T_S0, T_W = 1, 2, 3, 4, 5, 6, 7, 4
 T_DO, T_DST = 8, 9  # gradients arriving at the backward
 T_G, T_LNW, T_LNB = 10, 11, 12  # gate and norm parameters of the output epilogue
+# the Finch decay producer's block input, shift row and parameters
+T_XIN, T_SHIFT, T_MUX, T_LAM, T_A1, T_B1, T_A2, T_B2 = 13, 14, 15, 16, 17, 18, 19, 20
 
 
 def _threads():
@@ -147,6 +149,30 @@ def epilogue_inputs(B, T, H, N, cfg, g_sigma=1.0, w_sigma=0.1, b_sigma=0.1):
     return {"g": to_bf16(normal((B, T, H, N), g_sigma, cfg, T_G)),
             "ln_w": normal((H, N), w_sigma, cfg, T_LNW, mean=1.0),
             "ln_b": normal((H, N), b_sigma, cfg, T_LNB)}
+
+
+def decay_lora_inputs(B, T, H, N, cfg, omega=(-6.0, -0.5), shift=True, b1_sigma=0.05,
+                      b2_sigma=0.1):
+    """Finch decay producer: block input x bf16 bits [B,T,H N] ~ N(0, 1) (a
+    LayerNorm output); shift row bf16 [B, H N] ~ N(0, 1) (None when shift is
+    False); mu_x, lam ~ U(0, 1) fp32 [H N]; A1 [H N, 32] and A2 [H N, 64] bf16
+    ~ N(0, 1/sqrt(H N)), so that the LoRA inputs' products are of order one;
+    B1 [32, H N] ~ N(0, b1_sigma), B2 [64, H N] ~ N(0, b2_sigma) bf16; omega
+    ~ U(omega) fp32 [H N].  Under tanh the logit offset act(z A2) B2 then
+    spreads like the Finch workload's delta (RMS about 0.5)."""
+    D = H * N
+    a_sigma = 1.0 / np.sqrt(D)
+    return {
+        "xin": to_bf16(normal((B, T, D), 1.0, cfg, T_XIN)),
+        "shift": to_bf16(normal((B, D), 1.0, cfg, T_SHIFT)) if shift else None,
+        "mu_x": uniform((D,), 0.0, 1.0, cfg, T_MUX),
+        "lam": uniform((D,), 0.0, 1.0, cfg, T_LAM),
+        "A1": to_bf16(normal((D, 32), a_sigma, cfg, T_A1)),
+        "B1": to_bf16(normal((32, D), b1_sigma, cfg, T_B1)),
+        "omega": uniform((D,), omega[0], omega[1], cfg, T_OMEGA),
+        "A2": to_bf16(normal((D, 64), a_sigma, cfg, T_A2)),
+        "B2": to_bf16(normal((64, D), b2_sigma, cfg, T_B2)),
+    }
 
 
 def decode_inputs(B, steps, H, N, cfg, s0_sigma=0.1, rkv_sigma=0.125,
