@@ -179,6 +179,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     f32x4 uq, a2s, wq, eLL, eF1, eF2;
     f32x4 omq;         // LORA: omega of this thread's four channels
     size_t hrow0 = 0;  // LORA: the sequence's first row of h
+    // LORA, eight waves: the head's B_omega operands of the logits product,
+    // held in registers (four waves, short of registers, read them from sB2)
+    constexpr bool B2REG = LORA && NW == 8;
+    bf16x8 b2f[B2REG ? 8 : 1];
     // EPI on eight waves: this lane's norm weight and bias, held per head (on
     // four waves, where registers are short, read when they are used)
     constexpr bool LNREG = EPI && NW == 8;
@@ -201,6 +205,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 *(u32x4 *)(sB2 + (q >> 3) * kPC + 8 * (q & 7)) =
                     *(const u32x4 *)(lr.B2 + (size_t)(q >> 3) * H * kN + (size_t)h * kN + 8 * (q & 7));
             lds_barrier();
+            if constexpr (B2REG) {
+#pragma unroll
+                for (int f = 0; f < (B2REG ? 8 : 1); ++f)
+                    b2f[f] = lds_col8(sB2, 32 * (f & 1) + 8 * g, 16 * (f >> 1), c);
+            }
         }
         if (LNREG) {
 #pragma unroll
@@ -294,9 +303,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int M = 0; M < 4; ++M) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                acc = mfma(lds_col8(sB2, 32 * s2 + 8 * g, 16 * M, c),
-                           __builtin_bit_cast(bf16x8, hs[LORA ? s2 : 0]), acc);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bf16x8 a;
+                if constexpr (B2REG) a = b2f[B2REG ? 2 * M + s2 : 0];
+                else a = lds_col8(sB2, 32 * s2 + 8 * g, 16 * M, c);
+                acc = mfma(a, __builtin_bit_cast(bf16x8, hs[LORA ? s2 : 0]), acc);
+            }
             if (c >= dlo && c < dlo + 4 * TP)
                 *(f32x4 *)&sD[LORA ? w : 0][LORA ? c - dlo : 0][16 * M + 4 * g] = acc;
         }
@@ -313,12 +325,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 
     // ---- stage A (Finch): log2 decays and the in-wave part of their scan --
     float a2[TP][4], lower[4];
-    auto stageA = [&](int ch, const Raw<NW> &d, int set) {
+    // (LORA: with formed = true the product already ran, at the start of the
+    // step, and its rows wait in sD)
+    auto stageA = [&](int ch, const Raw<NW> &d, int set, bool formed = false) {
         if (!PT) return;
         const int c0 = ch * kL;
         f32x4 xv[TP];
         if constexpr (LORA) {
-            lora_logits(hq, xv);
+            if (formed) lora_read(xv);
+            else lora_logits(hq, xv);
         } else {
 #pragma unroll
             for (int e = 0; e < TP; ++e) xv[e] = d.x[e];
@@ -698,13 +713,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                     Sc[m][e] = sS[(16 * m + 4 * g + e) * kN + 16 * w + c];
         }
         lds_barrier();
-        // LORA: the chunk's logits formed again from its h (hq already holds
-        // a later chunk's), in the same thread layout as stage A
+        // LORA: the chunk's logits formed again from its h on the VALU (hq and
+        // sD hold a later chunk's), in the same thread layout as stage A
         f32x4 xl[LORA ? TP : 1];
         if constexpr (LORA) {
-            HOps ht;
-            load_h_to(ht, ch, true);
-            lora_logits(ht, xl);
+#pragma unroll
+            for (int e = 0; e < (LORA ? TP : 1); ++e) {
+                const int tau = TP * cx.tq + e;
+                const uint16_t *hr = lr.h + (hrow0 + (size_t)min(c0 + tau, T - 1)) * kN;
+                f32x4 acc = omq;
+                for (int j = 0; j < kN; j += 2) {
+                    const uint32_t hv = *(const uint32_t *)(hr + j);
+                    const u32x2 b0 = *(const u32x2 *)(sB2 + j * kPC + 4 * cx.cq);
+                    const u32x2 b1 = *(const u32x2 *)(sB2 + (j + 1) * kPC + 4 * cx.cq);
+                    const float h0 = bf16_lo(hv), h1 = bf16_hi(hv);
+                    acc[0] = fmaf(h0, bf16_lo(b0.x), fmaf(h1, bf16_lo(b1.x), acc[0]));
+                    acc[1] = fmaf(h0, bf16_hi(b0.x), fmaf(h1, bf16_hi(b1.x), acc[1]));
+                    acc[2] = fmaf(h0, bf16_lo(b0.y), fmaf(h1, bf16_lo(b1.y), acc[2]));
+                    acc[3] = fmaf(h0, bf16_hi(b0.y), fmaf(h1, bf16_hi(b1.y), acc[3]));
+                }
+                xl[e] = acc;
+            }
         }
         // re-read r, k, x of the chunk one token row at a time (few registers)
 #pragma unroll 1
@@ -850,12 +879,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // A had read the registers, a whole step earlier.
     auto step2 = [&](int ch, bool unsafe) -> bool {
         const bool more = ch + 1 < ch_end;
+        if (LORA && more) lora_product(hq);  // chunk ch + 1's logits, h loaded a step ago
         load_in(ch + 1);
         if (EPI) load_gate(ch, !unsafe);
         if (SAVE) save_chunk(ch);
         if (!unsafe) matrix(0);
         else token_by_token(ch, 0);
-        if (more) stageA(ch + 1, buf, 0);
+        if (more) stageA(ch + 1, buf, 0, LORA);
         load_dec(ch + 2, ch + 2 < ch_end);
         lds_barrier();  // (X) decay totals of ch + 1; chunk ch's tiles consumed
         bool bad = false;
@@ -872,8 +902,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto step1 = [&](int ch, bool unsafe) -> bool {
         const int cur = ch & 1, nxt = cur ^ 1;
         const bool more = ch + 1 < ch_end;
+        if (LORA && ch + 2 < ch_end) lora_product(hq);  // chunk ch + 2's, h loaded a step ago
         load_in(ch + 1);
-        load_dec(ch + 2, ch + 2 < ch_end);
+        if (LORA) load_dec(ch + 3, ch + 3 < ch_end);
+        else load_dec(ch + 2, ch + 2 < ch_end);
         epi_finish();  // the previous chunk's outputs, merged after its barrier
         if (EPI && !GST) load_gate(ch, !unsafe);
         if (SAVE) save_chunk(ch);
@@ -883,7 +915,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         bool bad = false;
         if (more) bad = stageB(ch + 1, buf, nxt);
         if (more) stage_state(nxt);
-        if (ch + 2 < ch_end) stageA(ch + 2, buf, cur);
+        if (ch + 2 < ch_end) stageA(ch + 2, buf, cur, LORA);
         epi_flush();  // the previous chunk's y
         store_out(ch, cur, !unsafe);
         return barrier_or(bad, cur);  // chunk ch + 1 staged, ch + 2's totals out
@@ -903,6 +935,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         // (DB: chunk ch0 + 1's scan after stage B of ch0 has used the scan
         // registers; the other parity's flags, next used two barriers later)
         if (DB && ch0 + 1 < ch1) stageA(ch0 + 1, buf, s0 ^ 1);
+        if (DB && LORA) load_dec(ch0 + 2, ch0 + 2 < ch1);  // (the steps request ch + 3)
         bool unsafe = barrier_or(bad0, DB ? (s0 ^ 1) : 0);
         for (int ch = ch0; ch < ch1; ++ch) unsafe = DB ? step1(ch, unsafe) : step2(ch, unsafe);
         epi_finish();
