@@ -173,6 +173,21 @@ def finch_lora_bytes(B, T, H, N=64):
             + 2 * B * H * N * N * 4 + (2 * D * 32 + 2 * D * 64) * 2 + 4 * D * 4 + H * N * 4)
 
 
+def lora_producer_bytes(B, T, H, N=64):
+    # the decay producer alone: the block input and the shift rows read, the
+    # weights and vectors once, act(z A_omega) written (64 bf16 per token)
+    D, rows = H * N, B * T
+    return rows * D * 2 + B * D * 2 + (2 * D * 32 + D * 64) * 2 + 2 * D * 4 + rows * 64 * 2
+
+
+def lora_wkv_bytes(B, T, H, N=64):
+    # the chunked kernel fed by it: r, k, v read and o written (bf16), the
+    # rank-64 factor once per token, B_omega, omega and u, the states
+    D, rows = H * N, B * T
+    return (rows * D * (2 * 3 + 2) + rows * 64 * 2 + 64 * D * 2 + D * 4 + H * N * 4
+            + 2 * B * H * N * N * 4)
+
+
 def finch_recompute_bytes(B, T, H, N=64, L=64):
     # the backward's state recomputation: read r, k, v (bf16), x (fp32), u and
     # the initial states; write the state entering every chunk and the last
@@ -442,12 +457,16 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
     "finch_fwd": ("wkv_chunk_kernel<true,", "wkv_chunk.hip", lambda: finch_bytes(8, 4096, 40)),
     "eagle_fwd": ("wkv_chunk_kernel<false,", "wkv_chunk.hip", lambda: eagle_bytes(8, 4096, 32)),
     "rwkv4_fwd": ("rwkv4_chain_kernel", "rwkv4_scan.hip", lambda: rwkv4_bytes(8, 1024, 768)),
-    "finch_fwd_gated": ("wkv_chunk_kernel<true, 8, false, true>", "wkv_chunk.hip",
+    "finch_fwd_gated": ("wkv_chunk_kernel<true, 8, false, true, false>", "wkv_chunk.hip",
                         lambda: finch_gated_bytes(8, 4096, 40)),
-    "finch_bwd_recompute": ("wkv_chunk_kernel<true, 8, true, false>", "wkv_chunk.hip",
+    "finch_bwd_recompute": ("wkv_chunk_kernel<true, 8, true, false, false>", "wkv_chunk.hip",
                             lambda: finch_recompute_bytes(8, 4096, 40)),
     "finch_bwd_reverse": ("wkv_bwd_kernel<true>", "wkv_chunk_bwd.hip",
                           lambda: finch_reverse_bytes(8, 4096, 40)),
+    "finch_lora_producer": ("decay_lora_kernel<true>", "decay_lora.hip",
+                            lambda: lora_producer_bytes(8, 4096, 40)),
+    "finch_lora_wkv": ("wkv_chunk_kernel<true, 8, false, false, true>", "wkv_chunk.hip",
+                       lambda: lora_wkv_bytes(8, 4096, 40)),
     "finch_decode": ("wkv_step_kernel<true>", "wkv_step.hip",
                      lambda: decode_bytes_per_step(256, 64)),
     "eagle_decode": ("wkv_step_kernel<false>", "wkv_step.hip",
@@ -457,7 +476,8 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
             "finch_fwd_gated": "finch_gated", "finch_bwd_recompute": "finch_bwd",
-            "finch_bwd_reverse": "finch_bwd",
+            "finch_bwd_reverse": "finch_bwd", "finch_lora_producer": "finch_lora",
+            "finch_lora_wkv": "finch_lora",
             "finch_decode": "decode", "eagle_decode": "eagle_decode",
             "rwkv4_decode": "rwkv4_decode"}
 
@@ -586,6 +606,10 @@ def main():
     for key, rec in paths.items():  # counter-measured HBM bytes, while current
         if key in PMC_PATHS:
             rec["traffic_bytes"] = measured_traffic(PMC_PATHS[key][1], key)
+    if "finch_fwd_lora" in paths:  # the producer and the chunked kernel, each on its own
+        paths["finch_fwd_lora"]["traffic_bytes"] = {
+            k: measured_traffic(PMC_PATHS[k][1], k)
+            for k in ("finch_lora_producer", "finch_lora_wkv")}
     if "finch_bwd" in paths:  # the backward's two main kernels, each on its own
         paths["finch_bwd"]["traffic_bytes"] = {
             k: measured_traffic(PMC_PATHS[k][1], k)
