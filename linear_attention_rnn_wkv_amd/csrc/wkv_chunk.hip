@@ -145,8 +145,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int p = w & 3;   // P1/P2 token tile
-    const int hf = w >> 2; // P2 value part
+    // P1/P2 token tile and P2 value part.  The causal products grow with the
+    // token tile, and after a barrier the waves' loads are taken in wave
+    // order, so with eight waves the first four take the two heavy tiles
+    // (both value halves) and the last four the light ones.  The wave holding
+    // the other half of a token tile is then w ^ 1.
+    const int hf = NW == 8 ? (w & 1) : 0;
+    const int p = NW == 8 ? 3 - (w >> 1) : w;
 
     Ctx cx;
     cx.T = T;
@@ -639,7 +644,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     int epi_ch = -1, epi_set = 0;  // eight waves: a chunk whose outputs wait for the merge
     auto epi_finish = [&]() {
         if (!EPI || epi_ch < 0) return;
-        const f32x2 a = sStat[epi_set][w][c], b = sStat[epi_set][w ^ 4][c];
+        const f32x2 a = sStat[epi_set][w][c], b = sStat[epi_set][w ^ 1][c];
         // two halves of 32 channels: n_a n_b / (n_a + n_b) = 16
         const float d = a[0] - b[0];
         const float mean = 0.5f * (a[0] + b[0]);
