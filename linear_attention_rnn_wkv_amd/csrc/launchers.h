@@ -14,7 +14,7 @@ int device_cus();
 // stream run in order and may share it; a kernel that uses flags in it must
 // leave them cleared.  A larger request reallocates (synchronising the
 // stream first).  Kept until the process ends.
-enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1, kWsDecayH = 2 };
+enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1, kWsDecayH = 2, kWsBwdSplit = 3 };
 hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out);
 
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.

@@ -49,6 +49,8 @@ namespace {
 using namespace tiles;
 
 constexpr int NW = 4;            // waves per workgroup
+constexpr int kXcds = 8;         // XCDs of the device: workgroups are dealt to them round-robin
+constexpr int kMaxSlots = 4096;  // hand-off slots of the balanced split
 constexpr int TP = 4;            // tokens per staging thread
 constexpr int kPF = 68;          // pitch (floats) of the fp32 gradient tiles
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -76,6 +78,22 @@ __device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
                  a[3] - bf16_hi(hi.y));
 }
 
+// Balanced split of the reverse sweep (as the forward's, mirrored): with up
+// to half as many heads again as CUs, workgroup i runs its own head and one
+// segment of one of the `extra` remaining heads.  The segments of an extra
+// head run on workgroups i, i + stride, ... (the same XCD, dispatched in
+// order); segment s covers chunks [e(s+1), e(s)) with e(s) = n - s n / K, and
+// runs after the workgroup's chunks [e(s), n) of its own head, by when
+// segment s-1 is done.  The sweep's state (dS, the dg carry, the du and dx
+// sums) goes between segments through `slots`, and the own head's waits in
+// `park` meanwhile, 32 floats per thread.
+struct BwdSplit {
+    int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    float *slots;     // [extra * (K - 1)][256][32]
+    float *park;      // [workgroups][256][32]
+    unsigned *flags;  // [max_slots] slot flags, then an error word
+};
+
 template <bool PT>
 __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
@@ -83,7 +101,8 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     const uint16_t *__restrict__ d_o, const float *__restrict__ d_sT,
     const float *__restrict__ chunk_states, uint16_t *__restrict__ d_r,
     uint16_t *__restrict__ d_k, uint16_t *__restrict__ d_v, float *__restrict__ d_x,
-    float *__restrict__ du_part, float *__restrict__ dx_part, float *__restrict__ d_s0) {
+    float *__restrict__ du_part, float *__restrict__ dx_part, float *__restrict__ d_s0,
+    BwdSplit sp) {
     __shared__ __align__(16) uint16_t sm[B_COUNT][kTile];
     __shared__ __align__(16) float sDR[kL * kPF];   // dr~ [token][channel]
     __shared__ __align__(16) float sDK[kL * kPF];   // dk^ [token][channel]
@@ -100,8 +119,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int bh = blockIdx.x;
-    const int b = bh / H, h = bh % H;
+    int bh = 0, h = 0;  // (sequence, head) of the current job
     const int nchunks = (T + kL - 1) / kL;
 
     Ctx cx;
@@ -114,7 +132,6 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     cx.tokb = (uint32_t)H * kN * 2;
     cx.off_rk = (uint32_t)(TP * cx.tq) * cx.tokb + 8 * cx.cq;
     cx.off_v = (uint32_t)cx.vt * cx.tokb + 16 * cx.vo;
-    cx.seq_base = (size_t)b * T * cx.tok_stride + (size_t)h * kN;
 
     // dS block of this wave (as the forward's state): key rows
     // [32 (w/2), +32) x value columns [32 (w%2), +32), four 16x16 tiles;
@@ -125,16 +142,31 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     auto sidx = [&](int t, int e) { return (skey(t) + 4 * g + e) * kN + sval(t) + c; };
     f32x4 dS[4];
 
-    const f32x4 uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * c);
-    f32x4 a2e = {0.f, 0.f, 0.f, 0.f};  // Eagle: log2-decay per channel
-    if (!PT) {
-        const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * c);
+    // per-head values of the current job
+    f32x4 uq, a2e;  // u; Eagle: log2-decay per channel
+    auto set_head = [&](int head) {
+        bh = head;
+        h = head % H;
+        cx.seq_base = (size_t)(head / H) * T * cx.tok_stride + (size_t)h * kN;
+        uq = *(const f32x4 *)(u + (size_t)h * kN + 4 * c);
+        a2e = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!PT) {
+            const f32x4 xs = *(const f32x4 *)(x + (size_t)h * kN + 4 * c);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a2e[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
-    }
+            for (int q = 0; q < 4; ++q) a2e[q] = -exp2_fast(xs[q] * kLog2e) * kLog2e;
+        }
+    };
 
-    // ---- initial dS = dL/dS_T and the final-state term of dg ---------------
-    {
+    // The sweep's state: dS; the carry of the dg suffix sum for this
+    // thread's channels 4 c .. 4 c + 3 (the final-state term, then the totals
+    // of the chunks already done); du and Eagle dx sums; threads < 64: Eagle
+    // dx of channel tid from fast-decay chunks.
+    f32x4 carry, du_acc, dx_acc;
+    float fb_dx;
+    // the state at the end of the sequence: dS = dL/dS_T and the final-state
+    // term of dg
+    auto init_state = [&]() {
+        lds_barrier();  // (the previous job's last reads of sCF are done)
         const size_t sbase = (size_t)bh * kN * kN;
         const float *ST = chunk_states + ((size_t)bh * (nchunks + 1) + nchunks) * kN * kN;
         f32x4 part[2];  // rows skey0 + 16 mi + 4 g + e: sum over this wave's columns
@@ -155,22 +187,67 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 *(f32x4 *)&sCF[w][skey0 + 16 * mi + 4 * g] = part[mi];
-    }
-    lds_barrier();
-    // carry of the dg suffix sum for this thread's channels 4 c .. 4 c + 3:
-    // the final-state term, then the totals of the chunks already done
-    f32x4 carry;
-    {
+        lds_barrier();
         const int wa = (4 * c) / 32 * 2;  // the two waves holding these key rows
         carry = *(const f32x4 *)&sCF[wa][4 * c] + *(const f32x4 *)&sCF[wa + 1][4 * c];
-    }
-    f32x4 du_acc = {0.f, 0.f, 0.f, 0.f}, dx_acc = {0.f, 0.f, 0.f, 0.f};
-    float fb_dx = 0.0f;  // threads < 64: Eagle dx of channel tid from fast-decay chunks
+        du_acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        dx_acc = du_acc;
+        fb_dx = 0.0f;
+    };
+    // the state to / from 32 floats per thread at p (plain or agent-scope
+    // atomic accesses: slots between workgroups use the latter)
+    auto put_state = [&](float *p, bool shared) {
+        float v[32];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * t + e] = dS[t][e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[16 + q] = carry[q];
+            v[20 + q] = du_acc[q];
+            v[24 + q] = dx_acc[q];
+        }
+        v[28] = fb_dx;
+        v[29] = v[30] = v[31] = 0.0f;
+        float *dst = p + (size_t)tid * 32;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (shared)
+                __hip_atomic_store((unsigned *)(dst + i), __float_as_uint(v[i]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                dst[i] = v[i];
+        }
+    };
+    auto get_state = [&](const float *p, bool shared) {
+        float v[32];
+        const float *src = p + (size_t)tid * 32;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            v[i] = shared ? __uint_as_float(__hip_atomic_load((const unsigned *)(src + i),
+                                                              __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT))
+                          : src[i];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS[t][e] = v[4 * t + e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            carry[q] = v[16 + q];
+            du_acc[q] = v[20 + q];
+            dx_acc[q] = v[24 + q];
+        }
+        fb_dx = v[28];
+    };
 
     // fixed thread mapping of the chunk-state tile: row tid/4, 16 columns
     const int sc_row = tid >> 2, sc_col = 16 * (tid & 3);
 
-    for (int ch = nchunks - 1; ch >= 0; --ch) {
+    // chunks [ch_lo, ch_hi) of the current head, from the last
+    auto run = [&](int ch_hi, int ch_lo) {
+    for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
         const int c0 = ch * kL;
         // ---- operands of the chunk ----------------------------------------
         Raw<NW> d;
@@ -662,8 +739,10 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
             carry += total;
         }
     }
+    };
 
     // ---- gradient of the initial state, partial du (and Eagle dx) ----------
+    auto finish = [&]() {
     if (d_s0 != nullptr) {
         const size_t sbase = (size_t)bh * kN * kN;
 #pragma unroll
@@ -695,6 +774,78 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
         du_part[(size_t)bh * kN + tid] = su;
         if (!PT) dx_part[(size_t)bh * kN + tid] = sx + fb_dx;
     }
+    };
+
+    // ---- jobs ------------------------------------------------------------
+    const int own = blockIdx.x;
+    int ext = 0, seg = 0;
+    bool split = false;
+    if (sp.extra != 0) {
+        const int xcd = own % sp.stride, local = own / sp.stride;
+        const int chain = local / sp.K;
+        seg = local % sp.K;
+        ext = xcd + sp.stride * chain;
+        split = chain < sp.chains_per_xcd && ext < sp.extra;
+    }
+    const int e0 = nchunks - seg * nchunks / max(sp.K, 1);
+    const int e1 = nchunks - (seg + 1) * nchunks / max(sp.K, 1);
+    // Split: own head chunks [e0, n) (then parked), the extra head's chunks
+    // [e1, e0), own head chunks [0, e0).  Slot flags and contents go through
+    // agent-scope relaxed atomics, which act at the device's coherence point:
+    // the producer's stores complete before its flag store, the consumer
+    // clears the flag for the next launch.  Polls are bounded (about a
+    // second); the producer has a lower workgroup index on the same XCD, so
+    // it is already running.  One loop, so that the sweep is compiled once.
+    auto receive = [&]() {
+        const int slot = ext * (sp.K - 1) + seg - 1;
+        if (tid == 0) {
+            int polls = 0;
+            while (__hip_atomic_load(sp.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                __builtin_amdgcn_s_sleep(8);
+                if (++polls > (1 << 20)) {
+                    __hip_atomic_store(sp.flags + sp.max_slots, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);  // error word
+                    break;
+                }
+            }
+        }
+        lds_barrier();
+        get_state(sp.slots + (size_t)slot * 256 * 32, true);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
+        lds_barrier();
+        if (tid == 0) __hip_atomic_store(sp.flags + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto send = [&]() {
+        const int slot = ext * (sp.K - 1) + seg;
+        put_state(sp.slots + (size_t)slot * 256 * 32, true);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
+        lds_barrier();
+        if (tid == 0) __hip_atomic_store(sp.flags + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    const int njobs = split ? 3 : 1;
+#pragma clang loop unroll(disable)
+    for (int job = 0; job < njobs; ++job) {
+        const bool extra = split && job == 1;
+        set_head(extra ? sp.first_extra + ext : own);
+        if (split && job == 2) {
+            get_state(sp.park + (size_t)own * 256 * 32, false);
+            lds_barrier();  // (the previous job's last reads of sCF are done)
+        } else if (extra && seg > 0) {
+            receive();
+        } else {
+            init_state();
+        }
+        int hi = nchunks, lo = 0;
+        if (split) {
+            if (job == 0) lo = e0;
+            else if (job == 1) hi = e0, lo = e1;
+            else hi = e0;
+        }
+        run(hi, lo);
+        if (split && job == 0) put_state(sp.park + (size_t)own * 256 * 32, false);
+        else if (extra && seg + 1 < sp.K) send();
+        else finish();
+    }
 }
 
 // out[h][i] = sum over b of part[b][h][i], in sequence order
@@ -725,14 +876,45 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
     hipError_t e = launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in,
                                       nullptr, nullptr, stream, chunk_states);
     if (e != hipSuccess) return e;
+    // One workgroup per head while every head has a CU of its own; with up to
+    // half as many heads again, the balanced split (one workgroup per CU);
+    // beyond that, the heads in rounds.
+    const int64_t heads = (int64_t)B * H;
+    const int cus = device_cus();
+    BwdSplit sp{};
+    int blocks = (int)heads;
+    if (heads > cus && cus % kXcds == 0 && T >= 4 * kL) {
+        const int64_t extra = heads - cus;
+        const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
+        const int64_t K = (cus / kXcds) / chains_per_xcd;
+        if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
+            const size_t per = (size_t)256 * 32 * 4;  // one sweep state
+            const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
+            const size_t slot_bytes = (size_t)extra * (K - 1) * per;
+            char *ws = nullptr;
+            e = stream_workspace(kWsBwdSplit, stream, flag_bytes + slot_bytes + (size_t)cus * per,
+                                 (void **)&ws);
+            if (e != hipSuccess) return e;
+            sp.extra = (int)extra;
+            sp.first_extra = cus;
+            sp.K = (int)K;
+            sp.stride = kXcds;
+            sp.chains_per_xcd = (int)chains_per_xcd;
+            sp.max_slots = kMaxSlots;
+            sp.flags = (unsigned *)ws;
+            sp.slots = (float *)(ws + flag_bytes);
+            sp.park = (float *)(ws + flag_bytes + slot_bytes);
+            blocks = cus;
+        }
+    }
     if (per_token_decay)
-        hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)(B * H)), dim3(256), 0, stream, T,
+        hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, T,
                            H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
-                           dx_part, d_s0);
+                           dx_part, d_s0, sp);
     else
-        hipLaunchKernelGGL(wkv_bwd_kernel<false>, dim3((unsigned)(B * H)), dim3(256), 0, stream, T,
+        hipLaunchKernelGGL(wkv_bwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, T,
                            H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
-                           dx_part, d_s0);
+                           dx_part, d_s0, sp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int HN = H * kN;
     hipLaunchKernelGGL(sum_over_batch_kernel, dim3((unsigned)((HN + 255) / 256)), dim3(256), 0,

@@ -614,6 +614,16 @@ def test_bwd_vs_oracle(per_token, B, T, H):
     bwd_check(bwd_case(B, T, H, 700 + T + H, per_token), per_token)
 
 
+# More heads than CUs: 320 heads in four segments (the extra heads' sweeps
+# hand dS, the dg carry and the du / dx sums from workgroup to workgroup),
+# 300 heads in five, 400 heads in rounds without the split
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (4, 130, 100)])
+def test_bwd_more_heads_than_cus(per_token, B, T, H):
+    print(f"bwd {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    bwd_check(bwd_case(B, T, H, 600 + H, per_token), per_token, f"{(B, T, H)}")
+
+
 @pytest.mark.parametrize("logit", [-200.0, 10.0, "mixed"])
 def test_bwd_extreme_decays(logit):
     # x = 10 gives w = 0 (a chunk of such decays runs token by token),
