@@ -31,10 +31,10 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The only
- *    memory the library allocates is two per-stream workspaces: the chain
- *    workspace of rwkv4_wkv_fwd and the hand-off workspace of the chunked
- *    Eagle/Finch calls (see there); no call keeps state that changes a
- *    later call's results.
+ *    memory the library allocates is four per-stream workspaces: the chain
+ *    workspace of rwkv4_wkv_fwd, the hand-off workspaces of the chunked
+ *    Eagle/Finch forward and backward, and the decay producer's factor
+ *    (see there); no call keeps state that changes a later call's results.
  *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
  *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
  *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
@@ -258,6 +258,11 @@ int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
  *              overlapping any other argument (RWKV_E_DIM if too small).  It
  *              holds the state entering every 64-token chunk, recomputed by
  *              the forward: 16 KiB per chunk and head.
+ * When B*H exceeds the device's compute units (at most by half again) and
+ * T >= 256, each workgroup sweeps its own head plus a segment of an extra
+ * head, and the segments hand the sweep's state on through a library
+ * workspace (32 KiB per hand-off and per workgroup), allocated, grown and
+ * kept as rwkv4_wkv_fwd's chain workspace, with the same rules.
  *
  * All pointers need 16-byte alignment; outputs may not overlap inputs or
  * each other.  H must be at most 65536.  T = 0 sets d_u (and rwkv5's d_x)
@@ -307,8 +312,10 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
  *              (with D = H N in its [B][T][H][N] layout)
  * The products run on bf16 matrix cores with fp32 accumulation (the mixed
  * values and act(.) rounded to bf16 as operands).  B T must be below 2^31.
- * Scratch: a per-stream workspace of B T 128 bytes (kept by the library,
- * reused by later calls on the stream).  T = 0 does nothing.  All pointers
+ * Scratch: a per-stream workspace of B T 128 bytes, allocated, grown and
+ * kept as rwkv4_wkv_fwd's chain workspace, with the same rules (a call that
+ * needs it larger synchronises the stream, so it must not be the first of
+ * its size on a stream under graph capture).  T = 0 does nothing.  All pointers
  * need 16-byte alignment; d must not overlap an input.
  */
 int rwkv6_decay_lora(int B, int T, int D, int act,
