@@ -301,8 +301,8 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
  *   z  = x_t + dx * m
  *   d  = omega + act(z A2) B2,     w_t = exp(-exp(d)) is Finch's decay.
  *
- *   x          [B][T][D] bf16 block input (D = H N, a multiple of 64, else
- *              RWKV_E_UNSUPPORTED)
+ *   x          [B][T][D] bf16 block input (D = H N, a multiple of 64 and at
+ *              most 64 * 65535, else RWKV_E_UNSUPPORTED)
  *   shift      [B][D] bf16, the token before x[b][0] (a previous segment's
  *              last token), or NULL
  *   mu_x, lam, omega [D] fp32

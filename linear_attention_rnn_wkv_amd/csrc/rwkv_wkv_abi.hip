@@ -141,7 +141,10 @@ int check_lora(int B, int T, int D, int act, const void *x, const void *shift,
     if (B < 1 || T < 0 || D < 1 || (act != 0 && act != 1)) return RWKV_E_DIM;
     const int64_t tok = checked_mul({B, T, D});
     if (tok < 0) return RWKV_E_DIM;
-    if (D % 64 != 0 || (int64_t)B * T >= ((int64_t)1 << 31)) return RWKV_E_UNSUPPORTED;
+    // (rows are int-indexed; the logits kernel takes one 64-channel block per
+    // grid row, at most 65535)
+    if (D % 64 != 0 || D / 64 > 65535 || (int64_t)B * T >= ((int64_t)1 << 31))
+        return RWKV_E_UNSUPPORTED;
     if (T == 0) return RWKV_OK;
     for (const void *p : {x, mu_x, lam, A1, B1, omega, A2, B2})
         if (p == nullptr) return RWKV_E_NULL;

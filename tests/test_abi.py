@@ -359,6 +359,7 @@ def test_decay_lora_null(L, missing):
 
 def test_decay_lora_checks(L):
     assert decay(L, D=96) == E_UNSUP          # D not a multiple of 64
+    assert decay(L, B=1, T=1, D=64 * 65536) == E_UNSUP  # more than 65535 channel blocks
     assert decay(L, act=2) == E_DIM
     assert decay(L, B=0) == E_DIM
     assert decay(L, T=-1) == E_DIM
