@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
     ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
                                        "rwkv4_decode", "finch_bwd", "finch_gated", "finch_lora",
-                                       "calib"],
+                                       "finch_train", "calib"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -285,6 +285,39 @@ def run_finch_lora(torch, W, S, H2D, args, d4=None):
     nbytes = finch_lora_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_fwd_lora_B8_T4096_D2560_H40_N64_bf16",
+                "tokens_channels_per_s": B * T * H * 64 / sec,
+                "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+    return res
+
+
+def run_finch_train(torch, W, S, H2D, args, d4=None):
+    """One training step of the operator on the Finch workload: the forward
+    that keeps the chunk states, then the backward that reads them (the
+    states are not recomputed), timed together."""
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    d = dict(d4) if d4 is not None else S.workload(4)
+    d.update(S.grad_inputs(B, T, H, 64, 4))
+    g = H2D(d)
+    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(g["r"])
+    so = torch.empty_like(g["s0"])
+    grads = {"d_r": torch.empty_like(g["r"]), "d_k": torch.empty_like(g["r"]),
+             "d_v": torch.empty_like(g["r"]), "d_x": torch.empty_like(g["x"]),
+             "d_u": torch.empty_like(g["u"]), "d_state_in": torch.empty_like(g["s0"])}
+
+    def launch():
+        W.rwkv6_wkv_fwd_save(g["r"], g["k"], g["v"], g["x"], g["u"], ws, state_in=g["s0"],
+                             state_out=so, o=o)
+        W.rwkv6_wkv_bwd_saved(g["r"], g["k"], g["v"], g["x"], g["u"], g["d_o"], ws,
+                              d_state_out=g["d_sT"], grads=grads)
+
+    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2))
+    nch = (T + 63) // 64
+    nbytes = finch_bytes(B, T, H) + B * H * (nch + 1) * 64 * 64 * 4 + finch_reverse_bytes(B, T, H)
+    sec = res["kernel_ms_mean"] / 1e3
+    res.update({"workload": "finch_train_step_B8_T4096_D2560_H40_N64_bf16",
                 "tokens_channels_per_s": B * T * H * 64 / sec,
                 "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
@@ -588,6 +621,10 @@ def main():
     if not args.skip_paths and only in (None, "finch_bwd"):
         print("finch backward ...", file=sys.stderr, flush=True)
         paths["finch_bwd"] = run_finch_bwd(torch, W, S, H2D, args, d4)
+    if not args.skip_paths and only in (None, "finch_train"):
+        print("finch training step (forward keeping the states + backward) ...",
+              file=sys.stderr, flush=True)
+        paths["finch_train"] = run_finch_train(torch, W, S, H2D, args, d4)
     if not args.skip_paths and only in (None, "decode"):
         print("finch decode ...", file=sys.stderr, flush=True)
         paths["finch_decode"] = run_decode(torch, W, S, H2D, args)

@@ -288,6 +288,46 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training pair that saves the backward's recomputation.  rwkv5/6_wkv_fwd_save
+ * is rwkv5/6_wkv_fwd (same arguments, outputs and errors) that also stores,
+ * in `workspace`, the state entering every 64-token chunk and the final
+ * state, as the backward's first pass would; rwkv5/6_wkv_bwd_saved is
+ * rwkv5/6_wkv_bwd without that pass, reading the states a matching
+ * *_fwd_save call (same r, k, v, x, u, state_in, B, T, H) left in the same
+ * workspace.  The pair gives bit for bit the gradients of the *_fwd and
+ * *_bwd pair.
+ *   workspace  device memory of at least rwkv_wkv_bwd_workspace_bytes(B, T,
+ *              H, N) bytes, 16-byte aligned, overlapping no other argument
+ *              (RWKV_E_DIM if too small; RWKV_E_NULL if NULL with T > 0).
+ * The backward's other arguments as rwkv5/6_wkv_bwd (it takes no state_in:
+ * the saved states hold it).
+ */
+int rwkv5_wkv_fwd_save(int B, int T, int H, int N,
+                       const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                       const float *x, const float *u,
+                       const float *state_in, float *state_out, rwkv_bf16 *o,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int rwkv6_wkv_fwd_save(int B, int T, int H, int N,
+                       const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                       const float *x, const float *u,
+                       const float *state_in, float *state_out, rwkv_bf16 *o,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int rwkv5_wkv_bwd_saved(int B, int T, int H, int N,
+                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                        const float *x, const float *u,
+                        const rwkv_bf16 *d_o, const float *d_state_out,
+                        rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
+                        float *d_x, float *d_u, float *d_state_in,
+                        void *workspace, size_t workspace_bytes, void *stream);
+int rwkv6_wkv_bwd_saved(int B, int T, int H, int N,
+                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                        const float *x, const float *u,
+                        const rwkv_bf16 *d_o, const float *d_state_out,
+                        rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
+                        float *d_x, float *d_u, float *d_state_in,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Finch decay producer (RWKV-5/6 summary, 4.1.1 "Eagle token shift",
  * 4.2.1 "Finch token shift" and 4.2.2 "Finch time mixing": the decay logit
  * of every token and channel from the block input by the data-dependent

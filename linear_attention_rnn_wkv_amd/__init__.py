@@ -34,7 +34,9 @@ STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPO
 EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
            "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step", "rwkv5_wkv_bwd",
            "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes", "rwkv5_wkv_fwd_gated",
-           "rwkv6_wkv_fwd_gated", "rwkv6_decay_lora", "rwkv6_wkv_fwd_lora")
+           "rwkv6_wkv_fwd_gated", "rwkv6_decay_lora", "rwkv6_wkv_fwd_lora",
+           "rwkv5_wkv_fwd_save", "rwkv6_wkv_fwd_save", "rwkv5_wkv_bwd_saved",
+           "rwkv6_wkv_bwd_saved")
 
 _lib = None
 
@@ -78,6 +80,14 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I] + [P] * 15 + [ctypes.c_size_t, P]
+        for name in ("rwkv5_wkv_fwd_save", "rwkv6_wkv_fwd_save"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I] + [P] * 9 + [ctypes.c_size_t, P]
+        for name in ("rwkv5_wkv_bwd_saved", "rwkv6_wkv_bwd_saved"):
+            f = getattr(L, name)
+            f.restype = I
+            f.argtypes = [I, I, I, I] + [P] * 14 + [ctypes.c_size_t, P]
         L.rwkv6_decay_lora.restype = I
         L.rwkv6_decay_lora.argtypes = [I, I, I, I] + [P] * 11
         L.rwkv6_wkv_fwd_lora.restype = I
@@ -277,7 +287,7 @@ def rwkv6_wkv_step(r, k, v, x, u, state, o=None, stream=None):
 
 
 def _matrix_bwd(name, per_token, r, k, v, x, u, d_o, state_in, d_state_out, grads,
-                workspace, stream):
+                workspace, stream, saved=False):
     import torch
     B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
     bf, f32 = torch.bfloat16, torch.float32
@@ -302,18 +312,26 @@ def _matrix_bwd(name, per_token, r, k, v, x, u, d_o, state_in, d_state_out, grad
         _expect(n, g[n], shape, dt)
     if g["d_state_in"] is not None:
         _expect("d_state_in", g["d_state_in"], (B, H, N, N), f32)
-    need = lib().rwkv_wkv_bwd_workspace_bytes(B, max(T, 1), H, N)
+    workspace = _workspace(workspace, B, T, H, N, dev, required=saved)
+    head = [_ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u)] + ([] if saved else [_ptr(state_in)])
+    _check(name, getattr(lib(), name)(
+        B, T, H, N, *head, _ptr(d_o), _ptr(d_state_out), _ptr(g["d_r"]), _ptr(g["d_k"]),
+        _ptr(g["d_v"]), _ptr(g["d_x"]), _ptr(g["d_u"]), _ptr(g["d_state_in"]),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return g
+
+
+def _workspace(workspace, B, T, H, N, dev, required=False):
+    import torch
     if workspace is None:
+        if required:
+            raise ValueError("workspace is required (it holds the forward's saved states)")
+        need = lib().rwkv_wkv_bwd_workspace_bytes(B, max(T, 1), H, N)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or \
             not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
-    _check(name, getattr(lib(), name)(
-        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in), _ptr(d_o),
-        _ptr(d_state_out), _ptr(g["d_r"]), _ptr(g["d_k"]), _ptr(g["d_v"]), _ptr(g["d_x"]),
-        _ptr(g["d_u"]), _ptr(g["d_state_in"]), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
-    return g
+    return workspace
 
 
 def rwkv5_wkv_bwd(r, k, v, x, u, d_o, state_in=None, d_state_out=None, grads=None,
@@ -332,6 +350,57 @@ def rwkv6_wkv_bwd(r, k, v, x, u, d_o, state_in=None, d_state_out=None, grads=Non
     """Finch backward: as rwkv5_wkv_bwd, with d_x [B, T, H, 64]."""
     return _matrix_bwd("rwkv6_wkv_bwd", True, r, k, v, x, u, d_o, state_in, d_state_out,
                        grads, workspace, stream)
+
+
+def _matrix_fwd_save(name, per_token, r, k, v, x, u, workspace, state_in, state_out, o,
+                     return_state, stream):
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, per_token)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=r.device)
+    _expect("o", o, (B, T, H, N), torch.bfloat16)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, H, N, N), torch.float32)
+    workspace = _workspace(workspace, B, T, H, N, r.device, required=True)
+    _check(name, getattr(lib(), name)(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in),
+        _ptr(state_out), _ptr(o), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, state_out
+
+
+def rwkv5_wkv_fwd_save(r, k, v, x, u, workspace, state_in=None, state_out=None, o=None,
+                       return_state=True, stream=None):
+    """rwkv5_wkv_fwd that also leaves in ``workspace`` (uint8, at least
+    workspace_bytes(B, T, H)) the states rwkv5_wkv_bwd_saved reads."""
+    return _matrix_fwd_save("rwkv5_wkv_fwd_save", False, r, k, v, x, u, workspace, state_in,
+                            state_out, o, return_state, stream)
+
+
+def rwkv6_wkv_fwd_save(r, k, v, x, u, workspace, state_in=None, state_out=None, o=None,
+                       return_state=True, stream=None):
+    """rwkv6_wkv_fwd that also leaves in ``workspace`` the states
+    rwkv6_wkv_bwd_saved reads."""
+    return _matrix_fwd_save("rwkv6_wkv_fwd_save", True, r, k, v, x, u, workspace, state_in,
+                            state_out, o, return_state, stream)
+
+
+def rwkv5_wkv_bwd_saved(r, k, v, x, u, d_o, workspace, d_state_out=None, grads=None,
+                        stream=None):
+    """rwkv5_wkv_bwd after rwkv5_wkv_fwd_save on the same inputs and
+    ``workspace``: the states it saved replace the backward's recomputation."""
+    return _matrix_bwd("rwkv5_wkv_bwd_saved", False, r, k, v, x, u, d_o, None, d_state_out,
+                       grads, workspace, stream, saved=True)
+
+
+def rwkv6_wkv_bwd_saved(r, k, v, x, u, d_o, workspace, d_state_out=None, grads=None,
+                        stream=None):
+    """rwkv6_wkv_bwd after rwkv6_wkv_fwd_save (as rwkv5_wkv_bwd_saved)."""
+    return _matrix_bwd("rwkv6_wkv_bwd_saved", True, r, k, v, x, u, d_o, None, d_state_out,
+                       grads, workspace, stream, saved=True)
 
 
 def workspace_bytes(B, T, H, N=64):

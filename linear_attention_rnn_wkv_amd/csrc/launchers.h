@@ -75,7 +75,8 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
                           const uint16_t *k, const uint16_t *v, const float *x, const float *u,
                           const float *state_in, const uint16_t *d_o, const float *d_sT,
                           uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
-                          float *d_s0, void *workspace, hipStream_t stream);
+                          float *d_s0, void *workspace, hipStream_t stream,
+                          bool states_saved = false);
 
 // Fill n floats with `value` (used for empty / zero states when T == 0).
 hipError_t launch_fill(float *dst, int64_t n, float value, hipStream_t stream);

@@ -172,7 +172,8 @@ int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                const float *state_in, const rwkv_bf16 *d_o, const float *d_state_out,
                rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
-               float *d_state_in, void *workspace, size_t workspace_bytes, void *stream) {
+               float *d_state_in, void *workspace, size_t workspace_bytes, void *stream,
+               bool states_saved = false) {
     if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
     const int64_t tok = checked_mul({B, T, H, N});
     const int64_t st = checked_mul({B, H, N, N});
@@ -213,7 +214,36 @@ int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
     }
     return hip_status(wkv::launch_wkv_bwd(per_token, B, T, H, r, k, v, x, u, state_in, d_o,
                                           d_state_out, d_r, d_k, d_v, d_x, d_u, d_state_in,
-                                          workspace, s));
+                                          workspace, s, states_saved));
+}
+
+// The forward that also stores, in a backward workspace, the state entering
+// every chunk (and the final state), as the backward's recomputation would.
+int matrix_fwd_save(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
+                    const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
+                    const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
+    int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
+    if (st != RWKV_OK) return st;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
+    if (T == 0) return matrix_fwd(per_token, B, T, H, N, r, k, v, x, u, state_in, state_out, o,
+                                  stream);
+    if (workspace == nullptr) return RWKV_E_NULL;
+    if (!aligned(workspace, 16)) return RWKV_E_ALIGN;
+    const size_t need = wkv::wkv_bwd_workspace_bytes(B, T, H);
+    if (workspace_bytes < need) return RWKV_E_DIM;
+    const int64_t tok = checked_mul({B, T, H, N}), sts = checked_mul({B, H, N, N});
+    const Span sws{workspace, (int64_t)need};
+    st = check_outputs({sws, Span{o, tok * 2}, Span{state_out, sts * 4}},
+                       {Span{r, tok * 2}, Span{k, tok * 2}, Span{v, tok * 2},
+                        Span{x, x_elems * 4}, Span{u, (int64_t)H * N * 4},
+                        Span{state_in, sts * 4}},
+                       state_out, state_in);
+    if (st != RWKV_OK) return st;
+    return hip_status(wkv::launch_wkv_chunked(per_token, B, T, H, r, k, v, x, u, state_in,
+                                              state_out, o, (hipStream_t)stream,
+                                              (float *)workspace));
 }
 
 }  // namespace
@@ -347,6 +377,42 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
                   void *workspace, size_t workspace_bytes, void *stream) {
     return matrix_bwd(true, B, T, H, N, r, k, v, x, u, state_in, d_o, d_state_out, d_r, d_k,
                       d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream);
+}
+
+int rwkv5_wkv_fwd_save(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                       const rwkv_bf16 *v, const float *x, const float *u,
+                       const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return matrix_fwd_save(false, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
+                           workspace_bytes, stream);
+}
+
+int rwkv6_wkv_fwd_save(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                       const rwkv_bf16 *v, const float *x, const float *u,
+                       const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return matrix_fwd_save(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
+                           workspace_bytes, stream);
+}
+
+int rwkv5_wkv_bwd_saved(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                        const rwkv_bf16 *v, const float *x, const float *u,
+                        const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
+                        rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
+                        float *d_state_in, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    return matrix_bwd(false, B, T, H, N, r, k, v, x, u, nullptr, d_o, d_state_out, d_r, d_k,
+                      d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream, true);
+}
+
+int rwkv6_wkv_bwd_saved(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                        const rwkv_bf16 *v, const float *x, const float *u,
+                        const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
+                        rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
+                        float *d_state_in, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    return matrix_bwd(true, B, T, H, N, r, k, v, x, u, nullptr, d_o, d_state_out, d_r, d_k,
+                      d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream, true);
 }
 
 int rwkv5_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,

@@ -259,10 +259,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int e = 0; e < 4; ++e) chunk_states[base + sidx(t, e)] = S[t][e];
     };
     auto save_state = [&]() {
-        if (SAVE) {
-            save_chunk(nchunks);
-            return;
-        }
+        if (SAVE) save_chunk(nchunks);
         if (state_out == nullptr) return;
         const size_t base = (size_t)bh * kN * kN;
 #pragma unroll
@@ -657,9 +654,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // chunk ch's outputs (after a fast-decay chunk, ok is false: the stores
     // are issued over an empty range, token_by_token having written them)
     auto store_out = [&](int ch, int set, bool ok) {
-        if (SAVE) return;
+        // (SAVE: the outputs too when the caller asked for them; the backward's
+        // recomputation passes none, and the stores are then dropped)
         const int c0 = ch * kL;
-        const Rsrc ro = rsrc(o + cx.base(c0), ok ? cx.span(c0) : 0u);
+        const Rsrc ro = rsrc(o + cx.base(c0), ok && (!SAVE || o != nullptr) ? cx.span(c0) : 0u);
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
         if (EPI) {
             // this wave's channels of token 16 p + c: 4 NT in this lane, the
@@ -1095,12 +1093,13 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         }
     }
     const int blocks = (int)(sp.extra ? sp.first_extra : heads);
-    // plain forward; the backward's state recomputation (SAVE); the forward
-    // with the output epilogue (EPI)
+    // plain forward; the forward that also stores the state entering every
+    // chunk (SAVE: the backward's recomputation, or a forward kept for the
+    // backward); the forward with the output epilogue (EPI)
     auto go = [&](auto save_tag, auto epi_tag) {
         constexpr bool SV = decltype(save_tag)::value, EP = decltype(epi_tag)::value;
-        float *so = SV ? nullptr : state_out;
-        uint16_t *out = SV ? nullptr : o;
+        float *so = state_out;
+        uint16_t *out = o;
         if (per_token_decay) {
             if (wide) launch<true, 8, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);
             else launch<true, 4, SV, EP>(blocks, T, H, r, k, v, x, u, state_in, so, out, sp, stream, chunk_states, gate, ln_w, ln_b, eps);

@@ -868,14 +868,17 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
                           const uint16_t *k, const uint16_t *v, const float *x, const float *u,
                           const float *state_in, const uint16_t *d_o, const float *d_sT,
                           uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
-                          float *d_s0, void *workspace, hipStream_t stream) {
+                          float *d_s0, void *workspace, hipStream_t stream, bool states_saved) {
     const size_t nchunks = (size_t)(T + kL - 1) / kL;
     float *chunk_states = (float *)workspace;
     float *du_part = chunk_states + (size_t)B * H * (nchunks + 1) * kN * kN;
     float *dx_part = du_part + (size_t)B * H * kN;
-    hipError_t e = launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in,
-                                      nullptr, nullptr, stream, chunk_states);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!states_saved) {  // (else a forward stored them there)
+        e = launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in, nullptr,
+                               nullptr, stream, chunk_states);
+        if (e != hipSuccess) return e;
+    }
     // One workgroup per head while every head has a CU of its own; with up to
     // half as many heads again, the balanced split (one workgroup per CU);
     // beyond that, the heads in rounds.

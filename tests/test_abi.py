@@ -385,3 +385,47 @@ def test_fused_checks(L):
     assert fused(L, o=4) == E_ALIAS           # o on the block input
     assert fused(L, so=11) == E_ALIAS         # state_out on B2
     assert fused(L, o=1) == E_ALIAS           # o on r
+
+
+# ---------------------------------------------------------------------------
+# the training pair: a forward that saves the states, a backward that uses them
+
+def fwd_save(L, fn="rwkv6_wkv_fwd_save", B=2, T=8, H=2, N=64, ws_bytes=None, **over):
+    names = ("r", "k", "v", "x", "u", "si", "so", "o", "ws")
+    idx = {n: i + 1 for i, n in enumerate(names)}
+    idx.update({n: val for n, val in over.items() if n in idx})
+    mis = over.get("mis", {})
+    a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
+    if ws_bytes is None:
+        ws_bytes = L.rwkv_wkv_bwd_workspace_bytes(B, max(T, 1), H, N)
+    return getattr(L, fn)(B, T, H, N, *(a[n] for n in names), ws_bytes, None)
+
+
+SAVES = ["rwkv5_wkv_fwd_save", "rwkv6_wkv_fwd_save"]
+
+
+@pytest.mark.parametrize("fn", SAVES)
+def test_fwd_save_checks(L, fn):
+    need = L.rwkv_wkv_bwd_workspace_bytes(2, 8, 2, 64)
+    assert fwd_save(L, fn, ws=None) == E_NULL
+    assert fwd_save(L, fn, ws_bytes=need - 1) == E_DIM
+    assert fwd_save(L, fn, mis={"ws": 8}) == E_ALIGN
+    assert fwd_save(L, fn, ws=1) == E_ALIAS    # workspace on r
+    assert fwd_save(L, fn, ws=8) == E_ALIAS    # workspace on o
+    assert fwd_save(L, fn, N=32) == E_UNSUP
+    assert fwd_save(L, fn, o=None) == E_NULL
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_bwd_saved", "rwkv6_wkv_bwd_saved"])
+def test_bwd_saved_checks(L, fn):
+    names = ("r", "k", "v", "x", "u", "do", "dso", "dr", "dk", "dv", "dx", "du", "dsi", "ws")
+    def call(ws_bytes=None, **over):
+        idx = {n: i + 1 for i, n in enumerate(names)}
+        idx.update(over)
+        a = {n: (addr(i) if i is not None else None) for n, i in idx.items()}
+        nb = L.rwkv_wkv_bwd_workspace_bytes(2, 8, 2, 64) if ws_bytes is None else ws_bytes
+        return getattr(L, fn)(2, 8, 2, 64, *(a[n] for n in names), nb, None)
+    assert call(ws=None) == E_NULL
+    assert call(ws_bytes=16) == E_DIM
+    assert call(dr=1) == E_ALIAS
+    assert call(do=None) == E_NULL

@@ -978,3 +978,31 @@ def test_fused_forward_full_workload_sampled_heads():
             assert_matrix_close(bf16_host(o[b:b + 1, :, h:h + 1]), o_ref, f"o {(b, h)}")
             assert_matrix_close(f64_host(so[b:b + 1, h:h + 1]), s_ref, f"state {(b, h)}")
     assert torch.isfinite(o.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# The training pair: a forward that keeps the chunk states for the backward,
+# and the backward that reads them instead of recomputing them.  Both are the
+# same arithmetic as the plain pair, so the results are compared bit for bit
+# (1 head, 3 heads, 320 heads: the balanced splits of both passes).
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+@pytest.mark.parametrize("B,T,H", [(1, 65, 1), (2, 300, 3), (4, 256, 80)])
+def test_training_pair_is_bitwise(per_token, B, T, H):
+    print(f"training pair {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
+    d = bwd_case(B, T, H, 700 + T + H, per_token)
+    g = matrix_inputs_dev(d)
+    d_o, d_sT = to_dev(d["d_o"], True), to_dev(d["d_sT"])
+    fwd = W.rwkv6_wkv_fwd if per_token else W.rwkv5_wkv_fwd
+    fsave = W.rwkv6_wkv_fwd_save if per_token else W.rwkv5_wkv_fwd_save
+    bwd = W.rwkv6_wkv_bwd if per_token else W.rwkv5_wkv_bwd
+    bsaved = W.rwkv6_wkv_bwd_saved if per_token else W.rwkv5_wkv_bwd_saved
+    o, so = fwd(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"])
+    ref = bwd(g["r"], g["k"], g["v"], g["x"], g["u"], d_o, state_in=g["s0"], d_state_out=d_sT)
+    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    o2, so2 = fsave(g["r"], g["k"], g["v"], g["x"], g["u"], ws, state_in=g["s0"])
+    got = bsaved(g["r"], g["k"], g["v"], g["x"], g["u"], d_o, ws, d_state_out=d_sT)
+    sync()
+    assert torch.equal(o, o2) and torch.equal(so, so2)
+    for n in ("d_r", "d_k", "d_v", "d_x", "d_u", "d_state_in"):
+        assert torch.equal(got[n], ref[n]), n
