@@ -635,6 +635,7 @@ def main():
         print("rwkv4 decode ...", file=sys.stderr, flush=True)
         paths["rwkv4_decode"] = run_decode(torch, W, S, H2D, args, cfg=7)
     torch.cuda.synchronize()
+    W.device_status()  # raises if any timed launch gave up a hand-off wait
 
     if "finch_fwd" not in paths:
         print(json.dumps({"paths": paths}))

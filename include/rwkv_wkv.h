@@ -70,11 +70,35 @@ enum rwkv_status {
     RWKV_E_UNSUPPORTED = -3, /* a valid shape this build does not implement */
     RWKV_E_ALIGN = -4,       /* a pointer is not 16-byte aligned where required */
     RWKV_E_ALIAS = -5,       /* an output overlaps an input or another output */
-    RWKV_E_HIP = -6          /* the HIP runtime rejected a launch or copy */
+    RWKV_E_HIP = -6,         /* the HIP runtime rejected a launch or copy */
+    RWKV_E_TIMEOUT = -7      /* a workgroup gave up waiting for another's
+                                hand-off (rwkv_wkv_device_status) */
 };
 
 /* Static, human-readable text of a status code. */
 const char *rwkv_wkv_strerror(int status);
+
+/* Whether any work enqueued on `stream` (hipStream_t, NULL = the default
+ * stream) of the current device gave up a wait.  Kernels that hand a state
+ * from one workgroup to another through a per-stream workspace
+ * (rwkv4_wkv_fwd's chain, the balanced split of the chunked Eagle/Finch
+ * forward and backward) poll for it a bounded number of times, about a
+ * second.  The producer always runs before or beside its consumer (it has
+ * a lower workgroup index), so the bound is never reached in normal
+ * operation; it only guarantees that every kernel ends.  A consumer that
+ * gives up sets an error word in the workspace and carries on with a wrong
+ * state, so that call's outputs are invalid.
+ *
+ * This call synchronises `stream`, reads the error words of its
+ * workspaces, and returns RWKV_E_TIMEOUT if any was set since the last
+ * check (RWKV_OK otherwise, RWKV_E_HIP if the runtime fails).  A workspace
+ * whose word was set is zero-filled again, as when first allocated, so
+ * that later calls start clean.  It is a
+ * diagnostic: call it after a batch of work, with the same stream handle
+ * the work was enqueued with, not from inside graph capture.  It allocates
+ * nothing.
+ */
+int rwkv_wkv_device_status(void *stream);
 
 /*
  * RWKV-4 WKV forward, fp32.  Channels are independent: C = H*N and any

@@ -30,13 +30,13 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librwkv_wkv.
 
 RWKV_OK = 0
 STATUS = {0: "RWKV_OK", -1: "RWKV_E_NULL", -2: "RWKV_E_DIM", -3: "RWKV_E_UNSUPPORTED",
-          -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP"}
+          -4: "RWKV_E_ALIGN", -5: "RWKV_E_ALIAS", -6: "RWKV_E_HIP", -7: "RWKV_E_TIMEOUT"}
 EXPORTS = ("rwkv_wkv_strerror", "rwkv4_wkv_fwd", "rwkv4_wkv_step", "rwkv5_wkv_fwd",
            "rwkv5_wkv_step", "rwkv6_wkv_fwd", "rwkv6_wkv_step", "rwkv5_wkv_bwd",
            "rwkv6_wkv_bwd", "rwkv_wkv_bwd_workspace_bytes", "rwkv5_wkv_fwd_gated",
            "rwkv6_wkv_fwd_gated", "rwkv6_decay_lora", "rwkv6_wkv_fwd_lora",
            "rwkv5_wkv_fwd_save", "rwkv6_wkv_fwd_save", "rwkv5_wkv_bwd_saved",
-           "rwkv6_wkv_bwd_saved")
+           "rwkv6_wkv_bwd_saved", "rwkv_wkv_device_status")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def lib():
         P, I = ctypes.c_void_p, ctypes.c_int
         L.rwkv_wkv_strerror.restype = ctypes.c_char_p
         L.rwkv_wkv_strerror.argtypes = [I]
+        L.rwkv_wkv_device_status.restype = I
+        L.rwkv_wkv_device_status.argtypes = [P]
         L.rwkv4_wkv_fwd.restype = I
         L.rwkv4_wkv_fwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
         for name in ("rwkv5_wkv_fwd", "rwkv6_wkv_fwd"):
@@ -123,6 +125,13 @@ def _expect(name, t, shape, dtype):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def device_status(stream=None):
+    """Waits for `stream` and raises WKVError (RWKV_E_TIMEOUT) if a kernel on
+    it gave up waiting for another workgroup's hand-off since the last check:
+    the outputs of that work are invalid.  Never raised in normal operation."""
+    _check("rwkv_wkv_device_status", lib().rwkv_wkv_device_status(_stream(stream)))
 
 
 def rwkv4_wkv_fwd(k, v, w, u, state_in=None, state_out=None, y=None, H=1,

@@ -17,6 +17,15 @@ int device_cus();
 enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1, kWsDecayH = 2, kWsBwdSplit = 3 };
 hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out);
 
+// Byte offset, in the workspace of each kind, of the word a kernel sets when
+// one of its bounded waits for another workgroup gives up (that workgroup's
+// results were then never seen, and the call's outputs are invalid); -1 for
+// a kind with no waits.  Only the host clears it (workspace_timed_out).
+constexpr long kWsErrorWord[] = {128, 4096 * 4, -1, 4096 * 4};
+// Waits for `stream`, then reads and clears the error words of its
+// workspaces on the current device; *timed_out is set when any was set.
+hipError_t workspace_timed_out(hipStream_t stream, bool *timed_out);
+
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,

@@ -27,6 +27,7 @@
 // sequences x channel blocks alone would not fill the chip.  k and v are read
 // from HBM once and y written once (12 bytes per token-channel).
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "launchers.h"
@@ -133,6 +134,7 @@ struct Ctrl {  // each word on a 128-byte line of its own
     };
     Line epoch, err, total, group[kGroups];
 };
+static_assert(offsetof(Ctrl, err) == kWsErrorWord[kWsRwkv4Chain], "error word of the chain workspace");
 // Bound on the polls of a predecessor's record (about a second):
 // predecessors have lower workgroup indices and are dispatched first, so the
 // wait always ends; the bound only guarantees that the kernel terminates.

@@ -260,8 +260,17 @@ const char *rwkv_wkv_strerror(int status) {
         case RWKV_E_ALIGN: return "pointer not aligned as required";
         case RWKV_E_ALIAS: return "an output overlaps an input or another output";
         case RWKV_E_HIP: return "the HIP runtime rejected a launch or copy";
+        case RWKV_E_TIMEOUT:
+            return "a workgroup gave up waiting for another's hand-off; outputs are invalid";
         default: return "unknown status";
     }
+}
+
+int rwkv_wkv_device_status(void *stream) {
+    bool timed_out = false;
+    if (wkv::workspace_timed_out((hipStream_t)stream, &timed_out) != hipSuccess)
+        return RWKV_E_HIP;
+    return timed_out ? RWKV_E_TIMEOUT : RWKV_OK;
 }
 
 int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
@@ -516,6 +525,35 @@ hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **o
         ws.bytes = n;
     }
     *out = ws.p;
+    return hipSuccess;
+}
+
+hipError_t workspace_timed_out(hipStream_t stream, bool *timed_out) {
+    *timed_out = false;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    for (int kind = 0; kind < (int)(sizeof(kWsErrorWord) / sizeof(kWsErrorWord[0])); ++kind) {
+        const long off = kWsErrorWord[kind];
+        if (off < 0) continue;
+        auto it = g_ws.find(std::make_tuple(kind, dev, stream));
+        if (it == g_ws.end() || it->second.bytes < (size_t)off + 4) continue;
+        unsigned *word = (unsigned *)((char *)it->second.p + off);
+        unsigned v = 0;
+        if ((e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+            (e = hipStreamSynchronize(stream)) != hipSuccess)
+            return e;
+        if (v == 0) continue;
+        *timed_out = true;
+        // A late producer may have raised a flag that no consumer cleared:
+        // back to the zero-filled state the workspace started in.
+        if ((e = launch_fill((float *)it->second.p, (int64_t)(it->second.bytes / 4), 0.0f,
+                             stream)) != hipSuccess ||
+            (e = hipStreamSynchronize(stream)) != hipSuccess)
+            return e;
+    }
     return hipSuccess;
 }
 

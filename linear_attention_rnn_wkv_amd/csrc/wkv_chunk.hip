@@ -1052,6 +1052,7 @@ void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, cons
 // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kXcds = 8;
 constexpr int kMaxSlots = 4096;
+static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsChunkHandoff], "error word after the slot flags");
 
 }  // namespace
 

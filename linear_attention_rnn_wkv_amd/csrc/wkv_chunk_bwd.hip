@@ -51,6 +51,7 @@ using namespace tiles;
 constexpr int NW = 4;            // waves per workgroup
 constexpr int kXcds = 8;         // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kMaxSlots = 4096;  // hand-off slots of the balanced split
+static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsBwdSplit], "error word after the slot flags");
 constexpr int TP = 4;            // tokens per staging thread
 constexpr int kPF = 68;          // pitch (floats) of the fp32 gradient tiles
 constexpr float kLn2 = 0.69314718055994530942f;

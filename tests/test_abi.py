@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_strerror_covers_every_status(L):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in W.STATUS:
         assert L.rwkv_wkv_strerror(st).decode() != "unknown status"
     assert L.rwkv_wkv_strerror(42).decode() == "unknown status"
 

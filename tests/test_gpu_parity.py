@@ -28,6 +28,14 @@ def _gpu():
     W.lib()  # raises when the library is missing
 
 
+@pytest.fixture(autouse=True)
+def _no_wait_gave_up():
+    # a workgroup that gave up waiting for another's hand-off leaves an error
+    # word in the stream's workspace; no test may leave one behind
+    yield
+    W.device_status()
+
+
 def sync():
     torch.cuda.synchronize()
 
@@ -108,6 +116,7 @@ def capture(fn):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         fn()
+    g.side_stream = s
     return g
 
 
@@ -127,6 +136,7 @@ def test_rwkv4_graph_replays():
         g.replay()
         sync()
         rwkv4_assert(d, y, so)
+    W.device_status(g.side_stream)
 
 
 def test_rwkv4_large_keys():
@@ -242,6 +252,7 @@ def test_chunked_graph_replays(per_token):
         o_ref, s_ref = oracle.wkv_matrix(*matrix_inputs_f32(d))
         assert_matrix_close(bf16_host(o), o_ref, "o")
         assert_matrix_close(f64_host(so), s_ref, "state")
+    W.device_status(graph.side_stream)
 
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
