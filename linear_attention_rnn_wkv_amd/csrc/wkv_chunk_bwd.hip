@@ -26,9 +26,10 @@
 //
 // Passes: the forward kernel first stores the state entering every chunk
 // (and the final state) in the workspace; this kernel then runs one
-// workgroup of four waves per (sequence, head) over the chunks from last to
-// first, carrying dS in registers.  Per chunk, products on the matrix cores
-// (wave w owns token tile w):
+// workgroup of eight waves (two per SIMD) per (sequence, head) over the
+// chunks from last to first, carrying dS in registers.  Per chunk, products
+// on the matrix cores (wave w owns token tile w % 4 and half w / 4 of the
+// output columns; both halves form the dA^T, dA and A tiles they need):
 //   dA^T (s <= t tiles), dA and A (t >= s tiles);
 //   dr~^T = K^^T dA^T + S_c dO^T (scaled by e^{Lam_L} per row),
 //   dk^^T = R~^T dA + dS_end V^T,  dv^T = dO^T A + dS_end^T K^^T,
@@ -48,11 +49,14 @@ namespace {
 
 using namespace tiles;
 
-constexpr int NW = 4;            // waves per workgroup
+constexpr int NW = 8;            // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * NW;
+constexpr int kTW = 4;           // waves that take a fast-decay chunk token by token
 constexpr int kXcds = 8;         // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kMaxSlots = 4096;  // hand-off slots of the balanced split
 static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsBwdSplit], "error word after the slot flags");
-constexpr int TP = 4;            // tokens per staging thread
+constexpr int TP = 16 / NW;      // tokens per staging thread
+constexpr int kSF = 24;          // floats of the sweep's state per thread
 constexpr int kPF = 68;          // pitch (floats) of the fp32 gradient tiles
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -90,13 +94,13 @@ __device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
 // `park` meanwhile, 32 floats per thread.
 struct BwdSplit {
     int extra, first_extra, K, stride, chains_per_xcd, max_slots;
-    float *slots;     // [extra * (K - 1)][256][32]
-    float *park;      // [workgroups][256][32]
+    float *slots;     // [extra * (K - 1)][kThreads][kSF]
+    float *park;      // [workgroups][kThreads][kSF]
     unsigned *flags;  // [max_slots] slot flags, then an error word
 };
 
 template <bool PT>
-__global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
     int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x, const float *__restrict__ u,
     const uint16_t *__restrict__ d_o, const float *__restrict__ d_sT,
@@ -134,14 +138,13 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     cx.off_rk = (uint32_t)(TP * cx.tq) * cx.tokb + 8 * cx.cq;
     cx.off_v = (uint32_t)cx.vt * cx.tokb + 16 * cx.vo;
 
-    // dS block of this wave (as the forward's state): key rows
-    // [32 (w/2), +32) x value columns [32 (w%2), +32), four 16x16 tiles;
-    // dS[t][e] = dS[skey(t) + 4 g + e][sval(t) + c]
-    const int skey0 = 32 * (w >> 1), sval0 = 32 * (w & 1);
-    auto skey = [&](int t) { return skey0 + 16 * (t >> 1); };
-    auto sval = [&](int t) { return sval0 + 16 * (t & 1); };
+    // dS block of this wave: key rows [16 (w/2), +16) x value columns
+    // [32 (w%2), +32), two 16x16 tiles; dS[t][e] = dS[skey0 + 4 g + e][sval(t) + c]
+    const int skey0 = 16 * (w >> 1), sval0 = 32 * (w & 1);
+    auto skey = [&](int) { return skey0; };
+    auto sval = [&](int t) { return sval0 + 16 * t; };
     auto sidx = [&](int t, int e) { return (skey(t) + 4 * g + e) * kN + sval(t) + c; };
-    f32x4 dS[4];
+    f32x4 dS[2];
 
     // per-head values of the current job
     f32x4 uq, a2e;  // u; Eagle: log2-decay per channel
@@ -170,50 +173,43 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
         lds_barrier();  // (the previous job's last reads of sCF are done)
         const size_t sbase = (size_t)bh * kN * kN;
         const float *ST = chunk_states + ((size_t)bh * (nchunks + 1) + nchunks) * kN * kN;
-        f32x4 part[2];  // rows skey0 + 16 mi + 4 g + e: sum over this wave's columns
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};  // rows skey0 + 4 g + e: sum over this wave's columns
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) part[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dS[t][e] = d_sT ? d_sT[sbase + sidx(t, e)] : 0.0f;
-                part[t >> 1][e] += dS[t][e] * ST[sidx(t, e)];
+                part[e] += dS[t][e] * ST[sidx(t, e)];
             }
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part[mi][e] = row_sum16(part[mi][e]);
-        if (c == 0)
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                *(f32x4 *)&sCF[w][skey0 + 16 * mi + 4 * g] = part[mi];
+        for (int e = 0; e < 4; ++e) part[e] = row_sum16(part[e]);
+        if (c == 0) *(f32x4 *)&sCF[w][skey0 + 4 * g] = part;
         lds_barrier();
-        const int wa = (4 * c) / 32 * 2;  // the two waves holding these key rows
+        const int wa = (4 * c) / 16 * 2;  // the two waves holding these key rows
         carry = *(const f32x4 *)&sCF[wa][4 * c] + *(const f32x4 *)&sCF[wa + 1][4 * c];
         du_acc = f32x4{0.f, 0.f, 0.f, 0.f};
         dx_acc = du_acc;
         fb_dx = 0.0f;
     };
-    // the state to / from 32 floats per thread at p (plain or agent-scope
+    // the state to / from kSF floats per thread at p (plain or agent-scope
     // atomic accesses: slots between workgroups use the latter)
     auto put_state = [&](float *p, bool shared) {
-        float v[32];
+        float v[kSF];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[4 * t + e] = dS[t][e];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            v[16 + q] = carry[q];
-            v[20 + q] = du_acc[q];
-            v[24 + q] = dx_acc[q];
+            v[8 + q] = carry[q];
+            v[12 + q] = du_acc[q];
+            v[16 + q] = dx_acc[q];
         }
-        v[28] = fb_dx;
-        v[29] = v[30] = v[31] = 0.0f;
-        float *dst = p + (size_t)tid * 32;
+        v[20] = fb_dx;
+        v[21] = v[22] = v[23] = 0.0f;
+        float *dst = p + (size_t)tid * kSF;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < kSF; ++i) {
             if (shared)
                 __hip_atomic_store((unsigned *)(dst + i), __float_as_uint(v[i]), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -222,34 +218,40 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
         }
     };
     auto get_state = [&](const float *p, bool shared) {
-        float v[32];
-        const float *src = p + (size_t)tid * 32;
+        float v[kSF];
+        const float *src = p + (size_t)tid * kSF;
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
+        for (int i = 0; i < kSF; ++i)
             v[i] = shared ? __uint_as_float(__hip_atomic_load((const unsigned *)(src + i),
                                                               __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT))
                           : src[i];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dS[t][e] = v[4 * t + e];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            carry[q] = v[16 + q];
-            du_acc[q] = v[20 + q];
-            dx_acc[q] = v[24 + q];
+            carry[q] = v[8 + q];
+            du_acc[q] = v[12 + q];
+            dx_acc[q] = v[16 + q];
         }
-        fb_dx = v[28];
+        fb_dx = v[20];
     };
 
-    // fixed thread mapping of the chunk-state tile: row tid/4, 16 columns
-    const int sc_row = tid >> 2, sc_col = 16 * (tid & 3);
+    // fixed thread mapping of the chunk-state tile: row tid/8, 8 columns
+    const int sc_row = tid >> 3, sc_col = 8 * (tid & 7);
 
     // chunks [ch_lo, ch_hi) of the current head, from the last
     auto run = [&](int ch_hi, int ch_lo) {
     for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
         const int c0 = ch * kL;
+        // The lane indices, opaque to the compiler inside each chunk: the
+        // LDS addresses derived from them are then formed where they are
+        // used instead of all being hoisted out of the loop and held in
+        // registers for the whole kernel.
+        int c = lane & 15, g = lane >> 4;
+        asm volatile("" : "+v"(c), "+v"(g));
         // ---- operands of the chunk ----------------------------------------
         Raw<NW> d;
         if (PT) load_x<NW>(d, c0, cx, x);
@@ -262,11 +264,11 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 dov[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, cx.off_v + j * 8 * NW * cx.tokb,
                                                                0, 0);
         }
-        f32x4 scv[4];
+        f32x4 scv[2];
         {
             const float *Sc = chunk_states + ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) scv[q] = *(const f32x4 *)(Sc + sc_row * kN + sc_col + 4 * q);
+            for (int q = 0; q < 2; ++q) scv[q] = *(const f32x4 *)(Sc + sc_row * kN + sc_col + 4 * q);
         }
 
         // ---- stage A: log2 decays and their in-wave scan -------------------
@@ -377,13 +379,13 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
             *(u32x4 *)(sm[B_DO] + (cx.vt + 8 * NW * j) * kPC + 8 * cx.vo) = dov[j];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2; ++q) {
             const u32x2 hi = pack4(scv[q][0], scv[q][1], scv[q][2], scv[q][3]);
             *(u32x2 *)(sm[B_SC] + sc_row * kPC + sc_col + 4 * q) = hi;
             *(u32x2 *)(sm[B_SCL] + sc_row * kPC + sc_col + 4 * q) = lo4(scv[q], hi);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 2; ++t) {
             const u32x2 hi = pack4(dS[t][0], dS[t][1], dS[t][2], dS[t][3]);
             *(u32x2 *)(sm[B_DST] + (sval(t) + c) * kPC + skey(t) + 4 * g) = hi;
             *(u32x2 *)(sm[B_DSTL] + (sval(t) + c) * kPC + skey(t) + 4 * g) = lo4(dS[t], hi);
@@ -392,20 +394,26 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
         const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
         if (lane == 0) sBad[w] = any ? 1 : 0;
         lds_barrier();
-        const bool unsafe = (sBad[0] | sBad[1] | sBad[2] | sBad[3]) != 0;
+        int anybad = 0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) anybad |= sBad[j];
+        const bool unsafe = anybad != 0;
         if (unsafe) {
             // ---- fast-decay chunk: its tokens one at a time, backwards -----
             // Raw r, k (bf16) and w (fp32) are staged in the factor tiles,
-            // whose products this chunk does not run.  Wave w holds columns
-            // [16 w, +16) of dS and of the recomputed state:
-            // X[m][e] = X[16 m + 4 g + e][16 w + c].  For each token the state
-            // before it is recomputed from S_c (quadratic in the chunk length,
-            // exact at any decay); the row sums over the columns are formed
-            // per wave and added over the waves through LDS.
+            // whose products this chunk does not run.  Waves w < kTW hold
+            // columns [16 w, +16) of dS and of the recomputed state:
+            // X[m][e] = X[16 m + 4 g + e][16 w + c] (the other waves only
+            // keep the barriers).  For each token the state before it is
+            // recomputed from S_c (quadratic in the chunk length, exact at any
+            // decay); the row sums over the columns are formed per wave and
+            // added over the waves through LDS.
             uint16_t *tr = sm[B_R], *tk = sm[B_RL];
-            float *tw = (float *)sm[B_SC];       // [64][64] fp32 over B_SC, B_DST
-            float *red = (float *)sm[B_K];       // [2][3][NW][64] partial row sums
+            float *tw = (float *)sm[B_SC];       // [64][64] fp32 over B_SC, B_SCL
+            float *red = (float *)sm[B_K];       // [2][3][kTW][64] partial row sums
             float *xfer = sDR;                   // layout changes of dS
+            const bool tbw = w < kTW;            // wave-uniform
+            const int wc = w & (kTW - 1);
 #pragma unroll
             for (int e = 0; e < TP; ++e) {
                 const int tau = TP * cx.tq + e;
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 *(f32x4 *)(tw + tau * kN + 4 * c) = wv;
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) xfer[(skey(t) + 4 * g + e) * kPF + sval(t) + c] = dS[t][e];
             if (tid < kL) {  // dbeta of every token of the chunk
@@ -427,22 +435,27 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 sDBeta[tid] = db;
             }
             lds_barrier();
-            f32x4 dSc[4], Sc0[4];
+            f32x4 dSc[4];
             const float *Sg = chunk_states + ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    dSc[m][e] = xfer[(16 * m + 4 * g + e) * kPF + 16 * w + c];
-                    Sc0[m][e] = Sg[(16 * m + 4 * g + e) * kN + 16 * w + c];
+                    dSc[m][e] = xfer[(16 * m + 4 * g + e) * kPF + 16 * wc + c];
                 }
             lds_barrier();  // xfer (sDR) is free again
             const int nvalid = min(kL, T - c0);
-            const int j = 16 * w + c;
+            const int j = 16 * wc + c;
+#pragma unroll 1
             for (int tau = nvalid - 1; tau >= 0; --tau) {
+                float *rb = red + (tau & 1) * 3 * kTW * kN;
+                if (tbw) {
                 f32x4 Sw[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) Sw[m] = Sc0[m];
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Sw[m][e] = Sg[(16 * m + 4 * g + e) * kN + j];
+#pragma unroll 1
                 for (int t2 = 0; t2 < tau; ++t2) {
                     const float vj = bf16_to_f32(sm[B_V][t2 * kPC + j]);
 #pragma unroll
@@ -456,7 +469,6 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 }
                 const float vj = bf16_to_f32(sm[B_V][tau * kPC + j]);
                 const float doj = bf16_to_f32(sm[B_DO][tau * kPC + j]);
-                float* rb = red + (tau & 1) * 3 * NW * kN;
                 float dvj = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -475,9 +487,9 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                         dSc[m][e] = fmaf(wv[e], dSc[m][e], r4[e] * doj);
                     }
                     if (c == 0) {
-                        *(f32x4 *)(rb + (0 * NW + w) * kN + 16 * m + 4 * g) = pr;
-                        *(f32x4 *)(rb + (1 * NW + w) * kN + 16 * m + 4 * g) = pk;
-                        *(f32x4 *)(rb + (2 * NW + w) * kN + 16 * m + 4 * g) = pw;
+                        *(f32x4 *)(rb + (0 * kTW + w) * kN + 16 * m + 4 * g) = pr;
+                        *(f32x4 *)(rb + (1 * kTW + w) * kN + 16 * m + 4 * g) = pk;
+                        *(f32x4 *)(rb + (2 * kTW + w) * kN + 16 * m + 4 * g) = pw;
                     }
                 }
                 dvj += __shfl_xor(dvj, 16, 64);
@@ -485,14 +497,15 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 if (g == 0)
                     d_v[cx.base(c0) + (size_t)tau * cx.tok_stride + j] =
                         (uint16_t)pack_bf16x2(fmaf(sBonus[tau], doj, dvj), 0.0f);
+                }
                 lds_barrier();
                 if (tid < kN) {
                     float a = 0.0f, bsum = 0.0f, dw = 0.0f;
 #pragma unroll
-                    for (int q = 0; q < NW; ++q) {
-                        a += rb[(0 * NW + q) * kN + tid];
-                        bsum += rb[(1 * NW + q) * kN + tid];
-                        dw += rb[(2 * NW + q) * kN + tid];
+                    for (int q = 0; q < kTW; ++q) {
+                        a += rb[(0 * kTW + q) * kN + tid];
+                        bsum += rb[(1 * kTW + q) * kN + tid];
+                        dw += rb[(2 * kTW + q) * kN + tid];
                     }
                     sDR[tau * kPF + tid] = a;
                     sDK[tau * kPF + tid] = bsum;
@@ -508,18 +521,22 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
             }
             // dS back to the block layout (after the last reads of w)
             lds_barrier();
+            if (tbw)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tw[(16 * m + 4 * g + e) * kN + 16 * w + c] = dSc[m][e];
+                    for (int e = 0; e < 4; ++e) tw[(16 * m + 4 * g + e) * kN + 16 * w + c] = dSc[m][e];
             lds_barrier();
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dS[t][e] = tw[(skey(t) + 4 * g + e) * kN + sval(t) + c];
         }
         // ---- products -----------------------------------------------------
         const Rsrc rdv = rsrc(d_v + cx.base(c0), cx.span(c0));
+        // wave w: token tile P = w % 4, output columns of half hf = w / 4
+        // (dA^T, dA and A are formed by both halves)
+        const int hf = w >> 2;
         auto products = [&](auto tile) {
             constexpr int P = decltype(tile)::value;
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -537,32 +554,16 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int sl = 4 * g + e;
-                if (sl == c) sDBeta[16 * P + c] = dat[P][e];
+                if (sl == c && hf == 0) sDBeta[16 * P + c] = dat[P][e];
                 dat[P][e] = sl < c ? dat[P][e] : 0.0f;
             }
-            // dA[t][s] and A[t][s]: t-tiles q >= P, s-tile P
-            f32x4 da[4 - P], aa[4 - P];
-#pragma unroll
-            for (int q = P; q < 4; ++q) {
-                da[q - P] = zero;
-                aa[q - P] = zero;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    da[q - P] = mfma(lds8(sm[B_DO] + (16 * q + c) * kPC + 32 * kb + 8 * g),
-                                     lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g), da[q - P]);
-                    aa[q - P] = mfma(lds8(sm[B_R] + (16 * q + c) * kPC + 32 * kb + 8 * g),
-                                     lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g), aa[q - P]);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {  // diagonal tile: keep t > s
-                const int tl = 4 * g + e;
-                da[0][e] = tl > c ? da[0][e] : 0.0f;
-                aa[0][e] = tl > c ? aa[0][e] : 0.0f;
-            }
             // dr~^T[i][t] (t = 16 P + c): K^^T dA^T + diag(e^{Lam_L}) S_c dO^T
+            bf16x8 Bdo[2];  // (the dO operand is the same for every i)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
+            for (int kb = 0; kb < 2; ++kb) Bdo[kb] = lds8(sm[B_DO] + (16 * P + c) * kPC + 32 * kb + 8 * g);
+#pragma unroll 1
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const int ii = 2 * hf + i2;
                 f32x4 acc = zero, st = zero;
 #pragma unroll
                 for (int bk = 0; 2 * bk <= P; ++bk) {
@@ -576,17 +577,33 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 Bd = lds8(sm[B_DO] + (16 * P + c) * kPC + 32 * kb + 8 * g);
-                    st = mfma(lds8(sm[B_SC] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bd, st);
-                    st = mfma(lds8(sm[B_SCL] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bd, st);
+                    st = mfma(lds8(sm[B_SC] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bdo[kb], st);
+                    st = mfma(lds8(sm[B_SCL] + (16 * ii + c) * kPC + 32 * kb + 8 * g), Bdo[kb], st);
                 }
                 const f32x4 dd = *(const f32x4 *)&sDecay[16 * ii + 4 * g];
                 acc += st * dd;
                 *(f32x4 *)&sDR[(16 * P + c) * kPF + 16 * ii + 4 * g] = acc;
             }
-            // dk^^T[i][s] (s = 16 P + c): R~^T dA + dS_end V^T
+            // dA[t][s]: t-tiles q >= P, s-tile P
+            f32x4 da[4 - P];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
+            for (int q = P; q < 4; ++q) {
+                da[q - P] = zero;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    da[q - P] = mfma(lds8(sm[B_DO] + (16 * q + c) * kPC + 32 * kb + 8 * g),
+                                     lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g), da[q - P]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)  // diagonal tile: keep t > s
+                da[0][e] = 4 * g + e > c ? da[0][e] : 0.0f;
+            // dk^^T[i][s] (s = 16 P + c): R~^T dA + dS_end V^T
+            bf16x8 Bv[2];  // (the V operand is the same for every i)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Bv[kb] = lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g);
+#pragma unroll 1
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const int ii = 2 * hf + i2;
                 f32x4 acc = zero;
 #pragma unroll
                 for (int bk = P / 2; bk < 2; ++bk) {
@@ -602,16 +619,32 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 Bv = lds8(sm[B_V] + (16 * P + c) * kPC + 32 * kb + 8 * g);
-                    acc = mfma(lds_col8(sm[B_DST], 32 * kb + 8 * g, 16 * ii, c), Bv, acc);
-                    acc = mfma(lds_col8(sm[B_DSTL], 32 * kb + 8 * g, 16 * ii, c), Bv, acc);
+                    acc = mfma(lds_col8(sm[B_DST], 32 * kb + 8 * g, 16 * ii, c), Bv[kb], acc);
+                    acc = mfma(lds_col8(sm[B_DSTL], 32 * kb + 8 * g, 16 * ii, c), Bv[kb], acc);
                 }
                 *(f32x4 *)&sDK[(16 * P + c) * kPF + 16 * ii + 4 * g] = acc;
             }
+            // A[t][s]: t-tiles q >= P, s-tile P
+            f32x4 aa[4 - P];
+#pragma unroll
+            for (int q = P; q < 4; ++q) {
+                aa[q - P] = zero;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    aa[q - P] = mfma(lds8(sm[B_R] + (16 * q + c) * kPC + 32 * kb + 8 * g),
+                                     lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g), aa[q - P]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)  // diagonal tile: keep t > s
+                aa[0][e] = 4 * g + e > c ? aa[0][e] : 0.0f;
             // dv^T[j][s] (s = 16 P + c): dO^T A + dS_end^T K^^T, plus beta_s do_s
             const float bon = sBonus[16 * P + c];
+            bf16x8 Bk[2];  // (the K^ operand is the same for every j)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int kb = 0; kb < 2; ++kb) Bk[kb] = lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g);
+#pragma unroll 1
+            for (int j2 = 0; j2 < 2; ++j2) {
+                const int jj = 2 * hf + j2;
                 f32x4 acc = zero;
 #pragma unroll
                 for (int bk = P / 2; bk < 2; ++bk) {
@@ -622,8 +655,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-                    acc = mfma(lds8(sm[B_DST] + (16 * jj + c) * kPC + 32 * kb + 8 * g),
-                               lds8(sm[B_K] + (16 * P + c) * kPC + 32 * kb + 8 * g), acc);
+                    acc = mfma(lds8(sm[B_DST] + (16 * jj + c) * kPC + 32 * kb + 8 * g), Bk[kb], acc);
                 const u32x2 dop = *(const u32x2 *)(sm[B_DO] + (16 * P + c) * kPC + 16 * jj + 4 * g);
                 acc[0] = fmaf(bon, bf16_lo(dop.x), acc[0]);
                 acc[1] = fmaf(bon, bf16_hi(dop.x), acc[1]);
@@ -640,22 +672,19 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
                 bf16x8 Bd[2];
 #pragma unroll
                 for (int vj = 0; vj < 2; ++vj) Bd[vj] = lds_col8(sm[B_DO], k0, sval0 + 16 * vj, c);
+                const bf16x8 Ah = lds_col8(sm[B_R], k0, skey0, c);
+                const bf16x8 Al = lds_col8(sm[B_RL], k0, skey0, c);
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
-                    const bf16x8 Ah = lds_col8(sm[B_R], k0, skey0 + 16 * mi, c);
-                    const bf16x8 Al = lds_col8(sm[B_RL], k0, skey0 + 16 * mi, c);
-#pragma unroll
-                    for (int vj = 0; vj < 2; ++vj) {
-                        dS[2 * mi + vj] = mfma(Ah, Bd[vj], dS[2 * mi + vj]);
-                        dS[2 * mi + vj] = mfma(Al, Bd[vj], dS[2 * mi + vj]);
-                    }
+                for (int vj = 0; vj < 2; ++vj) {
+                    dS[vj] = mfma(Ah, Bd[vj], dS[vj]);
+                    dS[vj] = mfma(Al, Bd[vj], dS[vj]);
                 }
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) dS[t] *= *(const f32x4 *)&sDecay[skey(t) + 4 * g];
+            for (int t = 0; t < 2; ++t) dS[t] *= *(const f32x4 *)&sDecay[skey(t) + 4 * g];
         };
         if (!unsafe) {
-            switch (w) {  // wave-uniform
+            switch (w & 3) {  // wave-uniform
                 case 0: products(std::integral_constant<int, 0>{}); break;
                 case 1: products(std::integral_constant<int, 1>{}); break;
                 case 2: products(std::integral_constant<int, 2>{}); break;
@@ -747,7 +776,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
     if (d_s0 != nullptr) {
         const size_t sbase = (size_t)bh * kN * kN;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) d_s0[sbase + sidx(t, e)] = dS[t][e];
     }
@@ -811,14 +840,14 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
             }
         }
         lds_barrier();
-        get_state(sp.slots + (size_t)slot * 256 * 32, true);
+        get_state(sp.slots + (size_t)slot * kThreads * kSF, true);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
         lds_barrier();
         if (tid == 0) __hip_atomic_store(sp.flags + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto send = [&]() {
         const int slot = ext * (sp.K - 1) + seg;
-        put_state(sp.slots + (size_t)slot * 256 * 32, true);
+        put_state(sp.slots + (size_t)slot * kThreads * kSF, true);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
         lds_barrier();
         if (tid == 0) __hip_atomic_store(sp.flags + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -829,7 +858,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
         const bool extra = split && job == 1;
         set_head(extra ? sp.first_extra + ext : own);
         if (split && job == 2) {
-            get_state(sp.park + (size_t)own * 256 * 32, false);
+            get_state(sp.park + (size_t)own * kThreads * kSF, false);
             lds_barrier();  // (the previous job's last reads of sCF are done)
         } else if (extra && seg > 0) {
             receive();
@@ -843,7 +872,7 @@ __global__ __launch_bounds__(256, 1) void wkv_bwd_kernel(
             else hi = e0;
         }
         run(hi, lo);
-        if (split && job == 0) put_state(sp.park + (size_t)own * 256 * 32, false);
+        if (split && job == 0) put_state(sp.park + (size_t)own * kThreads * kSF, false);
         else if (extra && seg + 1 < sp.K) send();
         else finish();
     }
@@ -892,7 +921,7 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
         const int64_t K = (cus / kXcds) / chains_per_xcd;
         if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
-            const size_t per = (size_t)256 * 32 * 4;  // one sweep state
+            const size_t per = (size_t)kThreads * kSF * 4;  // one sweep state
             const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
             const size_t slot_bytes = (size_t)extra * (K - 1) * per;
             char *ws = nullptr;
@@ -912,11 +941,11 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
         }
     }
     if (per_token_decay)
-        hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, T,
+        hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T,
                            H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
                            dx_part, d_s0, sp);
     else
-        hipLaunchKernelGGL(wkv_bwd_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, T,
+        hipLaunchKernelGGL(wkv_bwd_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T,
                            H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,
                            dx_part, d_s0, sp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
