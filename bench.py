@@ -558,6 +558,31 @@ def summarize_pmc(pmc_dir):
     return out
 
 
+def measure_copy(torch, nbytes=1 << 30, reps=20):
+    """Achievable HBM bandwidth on this GPU: a plain device-to-device copy
+    (torch copy_) of nbytes, read + write, median over reps launches."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    t = ms[len(ms) // 2] / 1e3
+    del a, b
+    return {"kind": "torch copy_ of 1 GiB fp32 on the device (reads 1 GiB, writes 1 GiB); "
+                    "a reference point, not a ceiling (the decode steps move more)",
+            "copy_GBps": 2 * nbytes / t / 1e9, "frac_of_peak": 2 * nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-pmc":
         print(json.dumps(summarize_pmc(sys.argv[2]), indent=1))
@@ -652,6 +677,11 @@ def main():
         paths["finch_bwd"]["traffic_bytes"] = {
             k: measured_traffic(PMC_PATHS[k][1], k)
             for k in ("finch_bwd_recompute", "finch_bwd_reverse")}
+    # the same bandwidths against what a plain copy reaches on this GPU
+    achievable = measure_copy(torch)
+    for rec in paths.values():
+        if "hbm_GBps" in rec:
+            rec["hbm_frac_of_copy"] = rec["hbm_GBps"] / achievable["copy_GBps"]
     finch = paths["finch_fwd"]
     spec = S.WORKLOADS[4]
     ms = finch["wall_s"] / args.steps * 1e3
@@ -679,6 +709,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": finch["hbm_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": finch["hbm_frac"], "traffic": traffic},
         "cpu_baseline": cpu,
+        "achievable_hbm": achievable,
         "paths": paths,
     }
     print(json.dumps(line))
