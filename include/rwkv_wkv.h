@@ -285,7 +285,7 @@ int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
  * When B*H exceeds the device's compute units (at most by half again) and
  * T >= 256, each workgroup sweeps its own head plus a segment of an extra
  * head, and the segments hand the sweep's state on through a library
- * workspace (32 KiB per hand-off and per workgroup), allocated, grown and
+ * workspace (48 KiB per hand-off and per workgroup), allocated, grown and
  * kept as rwkv4_wkv_fwd's chain workspace, with the same rules.
  *
  * All pointers need 16-byte alignment; outputs may not overlap inputs or

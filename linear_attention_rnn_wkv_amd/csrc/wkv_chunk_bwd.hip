@@ -91,7 +91,7 @@ __device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
 // runs after the workgroup's chunks [e(s), n) of its own head, by when
 // segment s-1 is done.  The sweep's state (dS, the dg carry, the du and dx
 // sums) goes between segments through `slots`, and the own head's waits in
-// `park` meanwhile, 32 floats per thread.
+// `park` meanwhile, kSF floats per thread.
 struct BwdSplit {
     int extra, first_extra, K, stride, chains_per_xcd, max_slots;
     float *slots;     // [extra * (K - 1)][kThreads][kSF]
