@@ -80,6 +80,8 @@ struct Split {
     int extra, first_extra, K, stride, chains_per_xcd, max_slots;
     float *slots;     // [extra * (K - 1)][64][64] states between segments
     unsigned *flags;  // [max_slots] slot flags, then an error word
+    float *park;      // [first_extra][64][64] own heads' states during the extra segment
+                      // (four-wave launches; eight waves keep them in registers)
 };
 
 // Finch decay logits from the decay producer: h [B T][64] bf16, the rank-64
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4;
-    const int c = lane & 15;
+    int g = lane >> 4;
+    int c = lane & 15;
     // P1/P2 token tile and P2 value part.  The causal products grow with the
     // token tile, and after a barrier the waves' loads are taken in wave
     // order, so with eight waves the first four take the two heavy tiles
@@ -881,6 +883,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     // start of the step, its x (Finch) right after the previous step's stage
     // A had read the registers, a whole step earlier.
     auto step2 = [&](int ch, bool unsafe) -> bool {
+        // The lane indices, opaque to the compiler in each step: the LDS
+        // addresses derived from them are formed where they are used instead
+        // of being hoisted out of the loop into registers (four-wave kernels
+        // have none to spare).
+        asm volatile("" : "+v"(c), "+v"(g));
         const bool more = ch + 1 < ch_end;
         if (LORA && more) lora_product(hq);  // chunk ch + 1's logits, h loaded a step ago
         load_in(ch + 1);
@@ -950,9 +957,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         epi_flush();
     };
 
-    // Balanced split (eight waves, one workgroup per CU, sp.extra > 0):
-    // workgroup i runs its own head i and one segment of one of the sp.extra
-    // remaining heads.  The segments of an extra head run on workgroups i,
+    // Balanced split (sp.extra > 0; eight waves and one workgroup per CU, or
+    // four waves and two): workgroup i runs its own head i and one segment of
+    // one of the sp.extra remaining heads.  The segments of an extra head run on workgroups i,
     // i + sp.stride, ... (the same XCD, dispatched in order), and segment s
     // starts after the workgroup's first s/K of its own head, by when segment
     // s-1 is done:
@@ -962,7 +969,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     const int own = blockIdx.x;
     int ext = 0, seg = 0, a = nchunks, e1 = nchunks;
     bool split = false;
-    if (DB && sp.extra != 0) {  // (the launcher splits eight-wave launches only)
+    if (sp.extra != 0) {
         const int xcd = own % sp.stride, local = own / sp.stride;
         const int chain = local / sp.K;
         seg = local % sp.K;
@@ -1024,8 +1031,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const bool extra = split && job == 1;
         set_head(extra ? sp.first_extra + ext : own);
         if (split && job == 2) {
+            if (DB) {
 #pragma unroll
-            for (int t = 0; t < (DB ? NT : 1); ++t) S[t] = Sown[t];
+                for (int t = 0; t < (DB ? NT : 1); ++t) S[t] = Sown[t];
+            } else {  // (the same threads stored it)
+                const float *park = sp.park + (size_t)own * kN * kN;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[t][e] = park[sidx(t, e)];
+            }
         } else if (extra && seg > 0) {
             receive();
         } else {
@@ -1033,8 +1048,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
         run_job(split && job > 0 ? a : 0, split && job < 2 ? (job == 0 ? a : e1) : nchunks);
         if (split && job == 0) {
+            if (DB) {
 #pragma unroll
-            for (int t = 0; t < (DB ? NT : 1); ++t) Sown[t] = S[t];
+                for (int t = 0; t < (DB ? NT : 1); ++t) Sown[t] = S[t];
+            } else {
+                float *park = sp.park + (size_t)own * kN * kN;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) park[sidx(t, e)] = S[t][e];
+            }
         } else if (extra && seg + 1 < sp.K) {
             send();
         } else {
@@ -1071,32 +1094,40 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
     // Eight waves per head while every head has a CU of its own.  With up to
     // half as many heads again, eight waves and the balanced split: one
     // workgroup per CU, each running one head plus one K-th of an extra
-    // head.  Beyond that, four waves so that two heads share a CU.
+    // head.  Beyond that, four waves so that two heads share a CU, and past
+    // two heads per CU the same split over the 2 x CUs workgroups.
     const int64_t heads = (int64_t)B * H;
     const int cus = device_cus();
     Split sp{};
     bool wide = heads <= cus;
-    if (!wide && cus % kXcds == 0 && T >= 4 * kL) {
-        const int64_t extra = heads - cus;
+    auto split = [&](int64_t first) -> hipError_t {
+        const int64_t extra = heads - first;
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        const int64_t K = (cus / kXcds) / chains_per_xcd;
-        if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
-            sp.extra = (int)extra;
-            sp.first_extra = cus;
-            sp.K = (int)K;
-            sp.stride = kXcds;
-            sp.chains_per_xcd = (int)chains_per_xcd;
-            sp.max_slots = kMaxSlots;
-            const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
-            const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
-            char *ws = nullptr;
-            hipError_t e = stream_workspace(kWsChunkHandoff, stream, flag_bytes + slot_bytes,
-                                            (void **)&ws);
-            if (e != hipSuccess) return e;
-            sp.flags = (unsigned *)ws;
-            sp.slots = (float *)(ws + flag_bytes);
-            wide = true;
-        }
+        const int64_t K = (first / kXcds) / chains_per_xcd;
+        if (K < 2 || extra * (K - 1) > kMaxSlots) return hipSuccess;
+        const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
+        const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
+        const size_t park_bytes = first > cus ? (size_t)first * kN * kN * 4 : 0;
+        char *ws = nullptr;
+        hipError_t e = stream_workspace(kWsChunkHandoff, stream,
+                                        flag_bytes + slot_bytes + park_bytes, (void **)&ws);
+        if (e != hipSuccess) return e;
+        sp.extra = (int)extra;
+        sp.first_extra = (int)first;
+        sp.K = (int)K;
+        sp.stride = kXcds;
+        sp.chains_per_xcd = (int)chains_per_xcd;
+        sp.max_slots = kMaxSlots;
+        sp.flags = (unsigned *)ws;
+        sp.slots = (float *)(ws + flag_bytes);
+        sp.park = park_bytes ? (float *)(ws + flag_bytes + slot_bytes) : nullptr;
+        return hipSuccess;
+    };
+    if (!wide && cus % kXcds == 0 && T >= 4 * kL) {
+        hipError_t e = split(cus);
+        if (e != hipSuccess) return e;
+        if (sp.extra != 0) wide = true;
+        else if (heads > 2 * (int64_t)cus && (e = split(2 * (int64_t)cus)) != hipSuccess) return e;
     }
     const int blocks = (int)(sp.extra ? sp.first_extra : heads);
     // plain forward; the forward that also stores the state entering every

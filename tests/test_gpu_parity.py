@@ -219,10 +219,12 @@ def test_chunked_shapes(per_token, B, T, H):
 # plus a segment of one of the remaining heads, whose state is handed from
 # segment to segment between workgroups.  320 heads: four segments; 300: five;
 # 270: sixteen segments for five chunks (empty segments pass the state on);
-# 400 heads: four-wave workgroups, two heads per CU.
+# 400 heads: four-wave workgroups, two heads per CU; 600 and 700 heads: four
+# waves and the same split over two workgroups per CU (the own head's state
+# parked in memory while the extra segment runs).
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 @pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (2, 320, 135),
-                                   (4, 130, 100)])
+                                   (4, 130, 100), (2, 320, 300), (1, 512, 700)])
 def test_chunked_more_heads_than_cus(per_token, B, T, H):
     print(f"chunked {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     g, o, so = chunked_check(matrix_case(B, T, H, 400 + H, per_token), per_token)
@@ -627,9 +629,10 @@ def test_bwd_vs_oracle(per_token, B, T, H):
 
 # More heads than CUs: 320 heads in four segments (the extra heads' sweeps
 # hand dS, the dg carry and the du / dx sums from workgroup to workgroup),
-# 300 heads in five, 400 heads in rounds without the split
+# 300 heads in five, 400 heads in rounds without the split; 600 heads: the
+# state recomputation takes the four-wave split
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
-@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (4, 130, 100)])
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (4, 130, 100), (2, 320, 300)])
 def test_bwd_more_heads_than_cus(per_token, B, T, H):
     print(f"bwd {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     bwd_check(bwd_case(B, T, H, 600 + H, per_token), per_token, f"{(B, T, H)}")
@@ -794,9 +797,10 @@ def test_gated_extreme_decays(logit):
 
 
 # 320 heads: eight waves with the extra heads in handed-on segments; 400
-# heads: four-wave workgroups, which load the gate per lane
+# heads: four-wave workgroups, which load the gate per lane; 600 heads: four
+# waves and the split
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
-@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100)])
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100), (2, 320, 300)])
 def test_gated_more_heads_than_cus(per_token, B, T, H):
     print(f"gated {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     gated_check(gated_case(B, T, H, 950 + H, per_token), per_token)
@@ -899,8 +903,9 @@ def test_fused_forward_vs_oracle(B, T, H):
     fused_check(B, T, H, 70 + T + H)
 
 
-# 320 heads: eight waves and the balanced split; 400 heads: four waves
-@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100)])
+# 320 heads: eight waves and the balanced split; 400 heads: four waves; 600
+# heads: four waves and the split
+@pytest.mark.parametrize("B,T,H", [(4, 256, 80), (4, 130, 100), (2, 320, 300)])
 def test_fused_forward_more_heads_than_cus(B, T, H):
     print(f"fused forward B={B} T={T} H={H}", flush=True)
     fused_check(B, T, H, 80 + H, shift=False)
