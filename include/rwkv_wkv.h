@@ -175,10 +175,12 @@ int rwkv4_wkv_step(int B, int T, int H, int N,
  * RWKV_E_UNSUPPORTED.
  *
  * Workspace: when B*H exceeds the device's compute units (at most by half
- * again) and T >= 256, each workgroup runs its own head plus a segment of an
- * extra head, and the segments hand the state on through a device workspace
- * (16 KB per hand-off, at most 4096).  It is allocated, grown and kept as
- * rwkv4_wkv_fwd's chain workspace, with the same rules.
+ * again), or twice their number, and T >= 256, each workgroup runs its own
+ * head plus a segment of an extra head, and the segments hand the state on
+ * through a device workspace (16 KB per hand-off, at most 4096; past twice
+ * the compute units also 16 KB per workgroup, where a workgroup's own state
+ * waits meanwhile).  It is allocated, grown and kept as rwkv4_wkv_fwd's chain
+ * workspace, with the same rules.
  */
 int rwkv5_wkv_fwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
