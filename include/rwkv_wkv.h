@@ -284,11 +284,13 @@ int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
  *              overlapping any other argument (RWKV_E_DIM if too small).  It
  *              holds the state entering every 64-token chunk, recomputed by
  *              the forward: 16 KiB per chunk and head.
- * When B*H exceeds the device's compute units (at most by half again) and
- * T >= 256, each workgroup sweeps its own head plus a segment of an extra
- * head, and the segments hand the sweep's state on through a library
- * workspace (48 KiB per hand-off and per workgroup), allocated, grown and
- * kept as rwkv4_wkv_fwd's chain workspace, with the same rules.
+ * When B*H exceeds the device's compute units and T >= 256, a workgroup per
+ * compute unit sweeps whole heads in rounds; when the last round's remainder
+ * is at most half the compute units, each workgroup sweeps its own head of
+ * that round plus a segment of an extra head, and the segments hand the
+ * sweep's state on through a library workspace (48 KiB per hand-off and per
+ * workgroup), allocated, grown and kept as rwkv4_wkv_fwd's chain workspace,
+ * with the same rules.
  *
  * All pointers need 16-byte alignment; outputs may not overlap inputs or
  * each other.  H must be at most 65536.  T = 0 sets d_u (and rwkv5's d_x)

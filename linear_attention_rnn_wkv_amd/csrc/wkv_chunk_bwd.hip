@@ -94,6 +94,7 @@ __device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
 // `park` meanwhile, kSF floats per thread.
 struct BwdSplit {
     int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    int nfull;        // whole heads per workgroup before the split round
     float *slots;     // [extra * (K - 1)][kThreads][kSF]
     float *park;      // [workgroups][kThreads][kSF]
     unsigned *flags;  // [max_slots] slot flags, then an error word
@@ -807,11 +808,15 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
     };
 
     // ---- jobs ------------------------------------------------------------
-    const int own = blockIdx.x;
+    // With more than two heads per CU, workgroup i first sweeps the whole
+    // heads i, i + grid, ... (sp.nfull of them), then its own head of the
+    // split round.
+    const int wg = blockIdx.x;
+    const int own = wg + sp.nfull * (int)gridDim.x;
     int ext = 0, seg = 0;
     bool split = false;
     if (sp.extra != 0) {
-        const int xcd = own % sp.stride, local = own / sp.stride;
+        const int xcd = wg % sp.stride, local = wg / sp.stride;
         const int chain = local / sp.K;
         seg = local % sp.K;
         ext = xcd + sp.stride * chain;
@@ -852,13 +857,14 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
         lds_barrier();
         if (tid == 0) __hip_atomic_store(sp.flags + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    const int njobs = split ? 3 : 1;
+    const int njobs = sp.nfull + (split ? 3 : 1);
 #pragma clang loop unroll(disable)
-    for (int job = 0; job < njobs; ++job) {
+    for (int j = 0; j < njobs; ++j) {
+        const int job = j - sp.nfull;  // (< 0: a whole head before the split round)
         const bool extra = split && job == 1;
-        set_head(extra ? sp.first_extra + ext : own);
+        set_head(job < 0 ? wg + j * (int)gridDim.x : extra ? sp.first_extra + ext : own);
         if (split && job == 2) {
-            get_state(sp.park + (size_t)own * kThreads * kSF, false);
+            get_state(sp.park + (size_t)wg * kThreads * kSF, false);
             lds_barrier();  // (the previous job's last reads of sCF are done)
         } else if (extra && seg > 0) {
             receive();
@@ -866,13 +872,13 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
             init_state();
         }
         int hi = nchunks, lo = 0;
-        if (split) {
+        if (split && job >= 0) {
             if (job == 0) lo = e0;
             else if (job == 1) hi = e0, lo = e1;
             else hi = e0;
         }
         run(hi, lo);
-        if (split && job == 0) put_state(sp.park + (size_t)own * kThreads * kSF, false);
+        if (split && job == 0) put_state(sp.park + (size_t)wg * kThreads * kSF, false);
         else if (extra && seg + 1 < sp.K) send();
         else finish();
     }
@@ -909,15 +915,17 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
                                nullptr, stream, chunk_states);
         if (e != hipSuccess) return e;
     }
-    // One workgroup per head while every head has a CU of its own; with up to
-    // half as many heads again, the balanced split (one workgroup per CU);
-    // beyond that, the heads in rounds.
+    // One workgroup per head while every head has a CU of its own.  Beyond
+    // that, one workgroup per CU: whole heads in rounds, and the last round's
+    // remainder, when it is at most half the CUs, as the balanced split (each
+    // workgroup sweeps its own head and one segment of an extra head).
+    // Otherwise the heads in rounds.
     const int64_t heads = (int64_t)B * H;
     const int cus = device_cus();
     BwdSplit sp{};
     int blocks = (int)heads;
-    if (heads > cus && cus % kXcds == 0 && T >= 4 * kL) {
-        const int64_t extra = heads - cus;
+    if (heads > cus && heads % cus != 0 && cus % kXcds == 0 && T >= 4 * kL) {
+        const int64_t extra = heads % cus, nfull = heads / cus - 1;
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
         const int64_t K = (cus / kXcds) / chains_per_xcd;
         if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
@@ -929,7 +937,8 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
                                  (void **)&ws);
             if (e != hipSuccess) return e;
             sp.extra = (int)extra;
-            sp.first_extra = cus;
+            sp.nfull = (int)nfull;
+            sp.first_extra = (int)((nfull + 1) * cus);
             sp.K = (int)K;
             sp.stride = kXcds;
             sp.chains_per_xcd = (int)chains_per_xcd;
