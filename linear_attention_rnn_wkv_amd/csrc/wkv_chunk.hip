@@ -74,13 +74,15 @@ using namespace tiles;
 enum { T_RS = 0, T_KRH, T_KRL, T_VR, T_ST, T_COUNT };
 __device__ constexpr int pitch(int t) { return (t == T_RS || t == T_ST) ? kPR : kPC; }
 
-// Balanced split of B*H = first_extra + extra heads over first_extra
-// workgroups (see the kernel); extra == 0: one head per workgroup.
+// Balanced split of B*H = first_extra + extra heads over first_extra /
+// (nfull + 1) workgroups, each of which first runs nfull whole heads (see the
+// kernel); extra == 0: one head per workgroup.
 struct Split {
     int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    int nfull;        // whole heads per workgroup before the split round
     float *slots;     // [extra * (K - 1)][64][64] states between segments
     unsigned *flags;  // [max_slots] slot flags, then an error word
-    float *park;      // [first_extra][64][64] own heads' states during the extra segment
+    float *park;      // [workgroups][64][64] own heads' states during the extra segment
                       // (four-wave launches; eight waves keep them in registers)
 };
 
@@ -966,11 +968,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     //   own [0, a) -> extra segment s = [a, b) -> own [a, nchunks)
     // The state between segments goes through the handoff workspace.  Jobs
     // run in one loop, so that the chunk loop exists once in the code.
-    const int own = blockIdx.x;
+    // Past the split's range, workgroup i first runs the whole heads i,
+    // i + grid, ... (sp.nfull of them), then its own head of the split round.
+    const int wg = blockIdx.x;
+    const int own = wg + sp.nfull * (int)gridDim.x;
     int ext = 0, seg = 0, a = nchunks, e1 = nchunks;
     bool split = false;
     if (sp.extra != 0) {
-        const int xcd = own % sp.stride, local = own / sp.stride;
+        const int xcd = wg % sp.stride, local = wg / sp.stride;
         const int chain = local / sp.K;
         seg = local % sp.K;
         ext = xcd + sp.stride * chain;  // extra head index among sp.extra
@@ -1025,17 +1030,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         if (tid == 0) st(sp.flags + slot, 1u);
     };
     f32x4 Sown[DB ? NT : 1];  // own head's state while the extra segment runs
-    const int njobs = split ? 3 : 1;
+    const int njobs = sp.nfull + (split ? 3 : 1);
 #pragma clang loop unroll(disable)
-    for (int job = 0; job < njobs; ++job) {
+    for (int j = 0; j < njobs; ++j) {
+        const int job = j - sp.nfull;  // (< 0: a whole head before the split round)
         const bool extra = split && job == 1;
-        set_head(extra ? sp.first_extra + ext : own);
+        set_head(job < 0 ? wg + j * (int)gridDim.x : extra ? sp.first_extra + ext : own);
         if (split && job == 2) {
             if (DB) {
 #pragma unroll
                 for (int t = 0; t < (DB ? NT : 1); ++t) S[t] = Sown[t];
             } else {  // (the same threads stored it)
-                const float *park = sp.park + (size_t)own * kN * kN;
+                const float *park = sp.park + (size_t)wg * kN * kN;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1046,13 +1052,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         } else {
             load_state();
         }
-        run_job(split && job > 0 ? a : 0, split && job < 2 ? (job == 0 ? a : e1) : nchunks);
+        const bool sj = split && job >= 0;
+        run_job(sj && job > 0 ? a : 0, sj && job < 2 ? (job == 0 ? a : e1) : nchunks);
         if (split && job == 0) {
             if (DB) {
 #pragma unroll
                 for (int t = 0; t < (DB ? NT : 1); ++t) Sown[t] = S[t];
             } else {
-                float *park = sp.park + (size_t)own * kN * kN;
+                float *park = sp.park + (size_t)wg * kN * kN;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1100,19 +1107,23 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
     const int cus = device_cus();
     Split sp{};
     bool wide = heads <= cus;
-    auto split = [&](int64_t first) -> hipError_t {
-        const int64_t extra = heads - first;
+    // (slots workgroups: whole heads in rounds, then the remainder split)
+    auto split = [&](int64_t slots) -> hipError_t {
+        const int64_t nfull = heads / slots - 1, extra = heads % slots;
+        if (extra == 0) return hipSuccess;
+        const int64_t first = (nfull + 1) * slots;
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        const int64_t K = (first / kXcds) / chains_per_xcd;
+        const int64_t K = (slots / kXcds) / chains_per_xcd;
         if (K < 2 || extra * (K - 1) > kMaxSlots) return hipSuccess;
         const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
         const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
-        const size_t park_bytes = first > cus ? (size_t)first * kN * kN * 4 : 0;
+        const size_t park_bytes = slots > cus ? (size_t)slots * kN * kN * 4 : 0;
         char *ws = nullptr;
         hipError_t e = stream_workspace(kWsChunkHandoff, stream,
                                         flag_bytes + slot_bytes + park_bytes, (void **)&ws);
         if (e != hipSuccess) return e;
         sp.extra = (int)extra;
+        sp.nfull = (int)nfull;
         sp.first_extra = (int)first;
         sp.K = (int)K;
         sp.stride = kXcds;
@@ -1124,12 +1135,12 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         return hipSuccess;
     };
     if (!wide && cus % kXcds == 0 && T >= 4 * kL) {
-        hipError_t e = split(cus);
+        hipError_t e = heads < 2 * (int64_t)cus ? split(cus) : hipSuccess;
         if (e != hipSuccess) return e;
         if (sp.extra != 0) wide = true;
         else if (heads > 2 * (int64_t)cus && (e = split(2 * (int64_t)cus)) != hipSuccess) return e;
     }
-    const int blocks = (int)(sp.extra ? sp.first_extra : heads);
+    const int blocks = (int)(sp.extra ? sp.first_extra / (sp.nfull + 1) : heads);
     // plain forward; the forward that also stores the state entering every
     // chunk (SAVE: the backward's recomputation, or a forward kept for the
     // backward); the forward with the output epilogue (EPI)

@@ -221,10 +221,12 @@ def test_chunked_shapes(per_token, B, T, H):
 # 270: sixteen segments for five chunks (empty segments pass the state on);
 # 400 heads: four-wave workgroups, two heads per CU; 600 and 700 heads: four
 # waves and the same split over two workgroups per CU (the own head's state
-# parked in memory while the extra segment runs).
+# parked in memory while the extra segment runs); 1200 heads: a whole head
+# per workgroup first, then the split.
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 @pytest.mark.parametrize("B,T,H", [(4, 256, 80), (1, 300, 300), (2, 320, 135),
-                                   (4, 130, 100), (2, 320, 300), (1, 512, 700)])
+                                   (4, 130, 100), (2, 320, 300), (1, 512, 700),
+                                   (4, 320, 300)])
 def test_chunked_more_heads_than_cus(per_token, B, T, H):
     print(f"chunked {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     g, o, so = chunked_check(matrix_case(B, T, H, 400 + H, per_token), per_token)
