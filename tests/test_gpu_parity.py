@@ -236,11 +236,13 @@ def test_chunked_more_heads_than_cus(per_token, B, T, H):
 
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
-def test_chunked_graph_replays(per_token):
+@pytest.mark.parametrize("B,T,H", [(1, 300, 300), (2, 320, 300)])
+def test_chunked_graph_replays(per_token, B, T, H):
     # 300 heads: the segments of the extra heads hand their states on through
-    # the stream's workspace, whose flags every launch leaves cleared
-    print(f"chunked {'finch' if per_token else 'eagle'} graph B=1 T=300 H=300", flush=True)
-    ds = [matrix_case(1, 300, 300, 500 + i, per_token) for i in range(2)]
+    # the stream's workspace, whose flags every launch leaves cleared; 600
+    # heads: the four-wave split, whose own states also wait in it
+    print(f"chunked {'finch' if per_token else 'eagle'} graph B={B} T={T} H={H}", flush=True)
+    ds = [matrix_case(B, T, H, 500 + i, per_token) for i in range(2)]
     g0 = matrix_inputs_dev(ds[0])
     o = torch.empty_like(g0["r"])
     so = torch.empty_like(g0["s0"])
@@ -674,6 +676,50 @@ def test_bwd_state_gradient_in_place():
     assert out["d_state_in"] is ds
     for n in ref:
         assert torch.equal(ref[n], out[n]), n
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 300, 300), (2, 320, 300)])
+def test_bwd_graph_replays(B, T, H):
+    # the backward (state recomputation, reverse sweep with its hand-offs, the
+    # sums over sequences) captured once and replayed on new inputs, with
+    # eager work in between; every replay matches the eager call bit for bit
+    print(f"bwd graph B={B} T={T} H={H}", flush=True)
+    ds = [bwd_case(B, T, H, 900 + i, True) for i in range(2)]
+    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    g0 = matrix_inputs_dev(ds[0])
+    dO = to_dev(ds[0]["d_o"], True)
+    dST = to_dev(ds[0]["d_sT"])
+    grads = {"d_r": torch.empty_like(g0["r"]), "d_k": torch.empty_like(g0["r"]),
+             "d_v": torch.empty_like(g0["r"]), "d_x": torch.empty_like(g0["x"]),
+             "d_u": torch.empty_like(g0["u"]), "d_state_in": torch.empty_like(g0["s0"])}
+    graph = capture(lambda: W.rwkv6_wkv_bwd(g0["r"], g0["k"], g0["v"], g0["x"], g0["u"], dO,
+                                            state_in=g0["s0"], d_state_out=dST, grads=grads,
+                                            workspace=ws))
+    for d in ds + ds:
+        for n, t in matrix_inputs_dev(d).items():
+            g0[n].copy_(t)
+        dO.copy_(to_dev(d["d_o"], True))
+        dST.copy_(to_dev(d["d_sT"]))
+        sync()
+        graph.replay()
+        sync()
+        want = bwd_run(d, True)
+        for n in grads:
+            assert torch.equal(grads[n], want[n]), n
+    W.device_status(graph.side_stream)
+
+
+def test_device_status_on_a_fresh_stream():
+    # a stream with no workspaces yet reports nothing; so does one whose
+    # split launches all completed their hand-offs
+    s = torch.cuda.Stream()
+    W.device_status(s)
+    g = matrix_inputs_dev(matrix_case(1, 300, 300, 77, True))
+    sync()
+    with torch.cuda.stream(s):
+        run_chunked(g, True)
+    W.device_status(s)
+    sync()
 
 
 def test_bwd_deterministic_and_workspace_reuse():
