@@ -1051,7 +1051,7 @@ def test_fused_forward_full_workload_sampled_heads():
 # (1 head, 3 heads, 320 heads: the balanced splits of both passes).
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
-@pytest.mark.parametrize("B,T,H", [(1, 65, 1), (2, 300, 3), (4, 256, 80)])
+@pytest.mark.parametrize("B,T,H", [(1, 65, 1), (2, 300, 3), (4, 256, 80), (2, 320, 300)])
 def test_training_pair_is_bitwise(per_token, B, T, H):
     print(f"training pair {'finch' if per_token else 'eagle'} B={B} T={T} H={H}", flush=True)
     d = bwd_case(B, T, H, 700 + T + H, per_token)
@@ -1070,3 +1070,46 @@ def test_training_pair_is_bitwise(per_token, B, T, H):
     assert torch.equal(o, o2) and torch.equal(so, so2)
     for n in ("d_r", "d_k", "d_v", "d_x", "d_u", "d_state_in"):
         assert torch.equal(got[n], ref[n]), n
+
+
+def test_training_pair_graph_replays():
+    # the forward keeping the states and the backward reading them, captured
+    # as one graph (600 heads: the four-wave split, whole heads then the
+    # backward's split) and replayed on new inputs; every replay matches the
+    # eager pair bit for bit
+    B, T, H = 2, 320, 300
+    print(f"training pair graph B={B} T={T} H={H}", flush=True)
+    ds = [bwd_case(B, T, H, 950 + i, True) for i in range(2)]
+    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    g0 = matrix_inputs_dev(ds[0])
+    dO = to_dev(ds[0]["d_o"], True)
+    dST = to_dev(ds[0]["d_sT"])
+    o = torch.empty_like(g0["r"])
+    so = torch.empty_like(g0["s0"])
+    grads = {"d_r": torch.empty_like(g0["r"]), "d_k": torch.empty_like(g0["r"]),
+             "d_v": torch.empty_like(g0["r"]), "d_x": torch.empty_like(g0["x"]),
+             "d_u": torch.empty_like(g0["u"]), "d_state_in": torch.empty_like(g0["s0"])}
+
+    def step():
+        W.rwkv6_wkv_fwd_save(g0["r"], g0["k"], g0["v"], g0["x"], g0["u"], ws, state_in=g0["s0"],
+                             state_out=so, o=o)
+        W.rwkv6_wkv_bwd_saved(g0["r"], g0["k"], g0["v"], g0["x"], g0["u"], dO, ws,
+                              d_state_out=dST, grads=grads)
+    graph = capture(step)
+    for d in ds + ds:
+        for n, t in matrix_inputs_dev(d).items():
+            g0[n].copy_(t)
+        dO.copy_(to_dev(d["d_o"], True))
+        dST.copy_(to_dev(d["d_sT"]))
+        sync()
+        graph.replay()
+        sync()
+        g = matrix_inputs_dev(d)
+        o_ref, s_ref = W.rwkv6_wkv_fwd(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"])
+        want = W.rwkv6_wkv_bwd(g["r"], g["k"], g["v"], g["x"], g["u"], to_dev(d["d_o"], True),
+                               state_in=g["s0"], d_state_out=to_dev(d["d_sT"]))
+        sync()
+        assert torch.equal(o, o_ref) and torch.equal(so, s_ref)
+        for n in grads:
+            assert torch.equal(grads[n], want[n]), n
+    W.device_status(graph.side_stream)
