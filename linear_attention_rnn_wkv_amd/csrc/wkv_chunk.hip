@@ -1087,6 +1087,7 @@ void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, cons
 // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kXcds = 8;
 constexpr int kMaxSlots = 4096;
+constexpr int kMaxSegs = 16;     // segments per extra head
 static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsChunkHandoff], "error word after the slot flags");
 
 }  // namespace
@@ -1113,7 +1114,9 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const u
         if (extra == 0) return hipSuccess;
         const int64_t first = (nfull + 1) * slots;
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        const int64_t K = (slots / kXcds) / chains_per_xcd;
+        // (at most kMaxSegs segments: each hand-off adds its latency to the
+        // chain of an extra head's segments)
+        const int64_t K = std::min<int64_t>((slots / kXcds) / chains_per_xcd, kMaxSegs);
         if (K < 2 || extra * (K - 1) > kMaxSlots) return hipSuccess;
         const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
         const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;

@@ -54,6 +54,7 @@ constexpr int kThreads = 64 * NW;
 constexpr int kTW = 4;           // waves that take a fast-decay chunk token by token
 constexpr int kXcds = 8;         // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kMaxSlots = 4096;  // hand-off slots of the balanced split
+constexpr int kMaxSegs = 16;     // segments per extra head
 static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsBwdSplit], "error word after the slot flags");
 constexpr int TP = 16 / NW;      // tokens per staging thread
 constexpr int kSF = 24;          // floats of the sweep's state per thread
@@ -927,7 +928,9 @@ hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint1
     if (heads > cus && heads % cus != 0 && cus % kXcds == 0 && T >= 4 * kL) {
         const int64_t extra = heads % cus, nfull = heads / cus - 1;
         const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        const int64_t K = (cus / kXcds) / chains_per_xcd;
+        // (at most kMaxSegs segments: each hand-off adds its latency to the
+        // chain of an extra head's segments)
+        const int64_t K = std::min<int64_t>((cus / kXcds) / chains_per_xcd, kMaxSegs);
         if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
             const size_t per = (size_t)kThreads * kSF * 4;  // one sweep state
             const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
