@@ -37,15 +37,20 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # Back-to-back launches of the prefill kernels slow down by up to a fifth
-    # after the first few and recover over the next fifty or so (clocks and
-    # power settling): the timed launches start once that has passed.
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # From idle, the GPU's power management first lowers the shader clock
+    # under a sustained load (2400 MHz to about 2070 MHz) and then brings it
+    # back over about a hundred prefill launches: the first launches after
+    # an idle period run up to a fifth slower.  Before the warm-up steps each
+    # path therefore runs back-to-back for this long; the headline also
+    # reports the unsettled ("cold") figure it measured first.
+    ap.add_argument("--settle-s", type=float, default=0.5)
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
-    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "eagle_decode",
+    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "decode_big",
+                                       "eagle_decode",
                                        "rwkv4_decode", "finch_bwd", "finch_gated", "finch_lora",
-                                       "finch_train", "calib"],
+                                       "finch_train", "calib", "stream"],
                     help="time one path only (for profiling)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     return ap.parse_args()
@@ -100,7 +105,41 @@ def flush(torch, buf):
     buf.sum()
 
 
-def time_launches(torch, launch, steps, warmup, flush_buf=None):
+def settle(torch, launch, seconds):
+    """Back-to-back launches for about `seconds` (the GPU's clocks settle)."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        launch()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return {"launches": n, "seconds": time.perf_counter() - t0}
+
+
+def time_launches(torch, launch, steps, warmup, flush_buf=None, settle_s=0.0, cold=False):
+    """Per-launch HIP-event times of `steps` launches after `warmup` untimed
+    ones.  cold: first, from an idle GPU, the same warmup + steps without
+    settling (reported under "cold"); settle_s: back-to-back launches before
+    the warm-up."""
+    out = {}
+    if cold:
+        timer = Timer(torch)
+        for i in range(warmup + steps):
+            if flush_buf is not None:
+                flush(torch, flush_buf)
+            if i < warmup:
+                launch()
+            else:
+                with timer:
+                    launch()
+        torch.cuda.synchronize()
+        ms = timer.ms()
+        out["cold"] = {"kernel_ms_mean": sum(ms) / len(ms), "kernel_ms_min": min(ms),
+                       "kernel_ms_max": max(ms), "per_launch_us": [round(m * 1e3, 1) for m in ms]}
+    if settle_s > 0:
+        out["settle"] = settle(torch, launch, settle_s)
     for _ in range(warmup):
         if flush_buf is not None:
             flush(torch, flush_buf)
@@ -116,8 +155,41 @@ def time_launches(torch, launch, steps, warmup, flush_buf=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = timer.ms()
-    return {"kernel_ms_mean": sum(ms) / len(ms), "kernel_ms_min": min(ms),
-            "kernel_ms_max": max(ms), "wall_s": wall}
+    out.update({"kernel_ms_mean": sum(ms) / len(ms), "kernel_ms_min": min(ms),
+                "kernel_ms_max": max(ms), "wall_s": wall})
+    return out
+
+
+def time_rotating(torch, launches, steps, warmup, settle_s=0.0):
+    """Mean time per launch of `steps` back-to-back launches that cycle
+    through `launches` (each on its own copy of the inputs, so that a copy's
+    bytes leave the last-level cache before it is used again), between two
+    HIP events: per-launch events would add their own overhead to a launch
+    of a few microseconds."""
+    n = len(launches)
+    i = 0
+
+    def one():
+        nonlocal i
+        launches[i % n]()
+        i += 1
+    out = {}
+    if settle_s > 0:
+        out["settle"] = settle(torch, one, settle_s)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    out.update({"kernel_ms_mean": e0.elapsed_time(e1) / steps,
+                "wall_s": time.perf_counter() - t0, "copies": n})
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -219,12 +291,16 @@ def run_finch(torch, W, S, H2D, args, cfg=4):
     o = torch.empty_like(g["r"])
     so = torch.empty_like(g["s0"])
     fn = W.rwkv6_wkv_fwd if cfg == 4 else W.rwkv5_wkv_fwd
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    ws = W.new_workspace(W.fwd_workspace_bytes(B, T, H))
 
     def launch():
-        fn(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"], state_out=so, o=o)
+        fn(g["r"], g["k"], g["v"], g["x"], g["u"], state_in=g["s0"], state_out=so, o=o,
+           workspace=ws)
 
-    res = time_launches(torch, launch, args.steps, args.warmup)
-    B, T, H = spec["B"], spec["T"], spec["H"]
+    res = time_launches(torch, launch, args.steps, args.warmup, settle_s=args.settle_s,
+                        cold=cfg == 4)
+    W.workspace_status(ws)
     nbytes = finch_bytes(B, T, H) if cfg == 4 else eagle_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({
@@ -249,12 +325,15 @@ def run_finch_gated(torch, W, S, H2D, args, d4=None):
     g = H2D(d)
     y = torch.empty_like(g["r"])
     so = torch.empty_like(g["s0"])
+    ws = W.new_workspace(W.fwd_workspace_bytes(B, T, H))
 
     def launch():
         W.rwkv6_wkv_fwd_gated(g["r"], g["k"], g["v"], g["x"], g["u"], g["g"], g["ln_w"],
-                              g["ln_b"], 1e-5, state_in=g["s0"], state_out=so, y=y)
+                              g["ln_b"], 1e-5, state_in=g["s0"], state_out=so, y=y,
+                              workspace=ws)
 
-    res = time_launches(torch, launch, args.steps, args.warmup)
+    res = time_launches(torch, launch, args.steps, args.warmup, settle_s=args.settle_s)
+    W.workspace_status(ws)
     nbytes = finch_gated_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_fwd_gated_B8_T4096_D2560_H40_N64_bf16",
@@ -275,19 +354,41 @@ def run_finch_lora(torch, W, S, H2D, args, d4=None):
     g = H2D({n: a for n, a in d.items() if a is not None})
     o = torch.empty_like(g["r"])
     so = torch.empty_like(g["s0"])
+    ws = W.new_workspace(W.fwd_lora_workspace_bytes(B, T, H))
 
     def launch():
         W.rwkv6_wkv_fwd_lora(g["r"], g["k"], g["v"], g["xin"], g["mu_x"], g["lam"], g["A1"],
                              g["B1"], g["omega"], g["A2"], g["B2"], g["u"], act="tanh",
-                             shift=g["shift"], state_in=g["s0"], state_out=so, o=o)
+                             shift=g["shift"], state_in=g["s0"], state_out=so, o=o,
+                             workspace=ws)
 
-    res = time_launches(torch, launch, args.steps, args.warmup)
+    res = time_launches(torch, launch, args.steps, args.warmup, settle_s=args.settle_s)
+    W.workspace_status(ws)
     nbytes = finch_lora_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_fwd_lora_B8_T4096_D2560_H40_N64_bf16",
                 "tokens_channels_per_s": B * T * H * 64 / sec,
                 "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+
+    # The same result in two calls: the producer writes the fp32 logits, the
+    # plain chunked forward reads them
+    dl = torch.empty((B, T, H * 64), dtype=torch.float32, device="cuda")
+    lws = torch.empty(W.lora_workspace_bytes(B, T, H * 64), dtype=torch.uint8, device="cuda")
+    fws = W.new_workspace(W.fwd_workspace_bytes(B, T, H))
+
+    def two_calls():
+        W.rwkv6_decay_lora(g["xin"], g["mu_x"], g["lam"], g["A1"], g["B1"], g["omega"],
+                           g["A2"], g["B2"], act="tanh", shift=g["shift"], d=dl, workspace=lws)
+        W.rwkv6_wkv_fwd(g["r"], g["k"], g["v"], dl.view(B, T, H, 64), g["u"],
+                        state_in=g["s0"], state_out=so, o=o, workspace=fws)
+
+    two = time_launches(torch, two_calls, args.steps, args.warmup, settle_s=args.settle_s)
+    W.workspace_status(fws)
+    res["two_calls"] = {"kernel_ms_mean": two["kernel_ms_mean"],
+                        "kernel_ms_min": two["kernel_ms_min"],
+                        "note": "rwkv6_decay_lora (fp32 logits to memory) + rwkv6_wkv_fwd",
+                        "fused_speedup": two["kernel_ms_mean"] / res["kernel_ms_mean"]}
     return res
 
 
@@ -300,7 +401,7 @@ def run_finch_train(torch, W, S, H2D, args, d4=None):
     d = dict(d4) if d4 is not None else S.workload(4)
     d.update(S.grad_inputs(B, T, H, 64, 4))
     g = H2D(d)
-    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    ws = W.new_workspace(W.workspace_bytes(B, T, H))
     o = torch.empty_like(g["r"])
     so = torch.empty_like(g["s0"])
     grads = {"d_r": torch.empty_like(g["r"]), "d_k": torch.empty_like(g["r"]),
@@ -313,7 +414,9 @@ def run_finch_train(torch, W, S, H2D, args, d4=None):
         W.rwkv6_wkv_bwd_saved(g["r"], g["k"], g["v"], g["x"], g["u"], g["d_o"], ws,
                               d_state_out=g["d_sT"], grads=grads)
 
-    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2))
+    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2),
+                        settle_s=args.settle_s)
+    W.workspace_status(ws)
     nch = (T + 63) // 64
     nbytes = finch_bytes(B, T, H) + B * H * (nch + 1) * 64 * 64 * 4 + finch_reverse_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
@@ -333,7 +436,7 @@ def run_finch_bwd(torch, W, S, H2D, args, d4=None):
     d = dict(d4) if d4 is not None else S.workload(4)
     d.update(S.grad_inputs(B, T, H, 64, 4))
     g = H2D(d)
-    ws = torch.empty(W.workspace_bytes(B, T, H), dtype=torch.uint8, device="cuda")
+    ws = W.new_workspace(W.workspace_bytes(B, T, H))
     grads = {"d_r": torch.empty_like(g["r"]), "d_k": torch.empty_like(g["r"]),
              "d_v": torch.empty_like(g["r"]), "d_x": torch.empty_like(g["x"]),
              "d_u": torch.empty_like(g["u"]), "d_state_in": torch.empty_like(g["s0"])}
@@ -342,7 +445,9 @@ def run_finch_bwd(torch, W, S, H2D, args, d4=None):
         W.rwkv6_wkv_bwd(g["r"], g["k"], g["v"], g["x"], g["u"], g["d_o"], state_in=g["s0"],
                         d_state_out=g["d_sT"], grads=grads, workspace=ws)
 
-    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2))
+    res = time_launches(torch, launch, max(10, args.steps // 2), max(5, args.warmup // 2),
+                        settle_s=args.settle_s)
+    W.workspace_status(ws)
     nbytes = finch_bwd_bytes(B, T, H)
     sec = res["kernel_ms_mean"] / 1e3
     res.update({"workload": "finch_bwd_B8_T4096_D2560_H40_N64_bf16",
@@ -354,34 +459,62 @@ def run_finch_bwd(torch, W, S, H2D, args, d4=None):
     return res
 
 
+RWKV4_COPIES = 8  # 8 x 75.65 MB: a copy's bytes leave the 256 MB cache between uses
+
+
 def run_rwkv4(torch, W, S, H2D, args, flush_buf):
+    """RWKV-4 scan, B8 T1024 C768.  Main figure: back-to-back launches that
+    cycle through 8 copies of the inputs and outputs (each launch reads its
+    k, v from HBM), timed between two events.  Also: single launches after a
+    read of a 1 GiB buffer that evicts the caches, each between its own pair
+    of events (that figure includes the events' own overhead)."""
     spec = S.WORKLOADS[2]
+    B, T, C = spec["B"], spec["T"], spec["C"]
     d = S.workload(2)
     k, v, w, u = (H2D({"a": d[n]})["a"] for n in ("k", "v", "w", "u"))
-    y = torch.empty_like(k)
-    so = torch.empty((spec["B"], 3, spec["C"]), dtype=torch.float32, device="cuda")
+    nws = W.rwkv4_workspace_bytes(B, T, C)
+    sets = []
+    for i in range(RWKV4_COPIES):
+        kc, vc = (k, v) if i == 0 else (k.clone(), v.clone())
+        sets.append((kc, vc, torch.empty_like(k), torch.empty((B, 3, C), device="cuda"),
+                     W.new_workspace(nws)))
 
-    def launch():
-        W.rwkv4_wkv_fwd(k, v, w, u, state_out=so, y=y)
+    def launcher(kc, vc, y, so, ws):
+        return lambda: W.rwkv4_wkv_fwd(kc, vc, w, u, state_out=so, y=y, workspace=ws)
 
-    res = time_launches(torch, launch, max(args.steps, 20), args.warmup, flush_buf)
-    nbytes = rwkv4_bytes(spec["B"], spec["T"], spec["C"])
+    launches = [launcher(*st) for st in sets]
+    res = time_rotating(torch, launches, max(args.steps, 20) * RWKV4_COPIES // 4, args.warmup,
+                        settle_s=args.settle_s)
+    iso = time_launches(torch, launches[0], max(args.steps, 20), min(args.warmup, 20), flush_buf)
+    for st in sets:
+        W.workspace_status(st[4])
+    nbytes = rwkv4_bytes(B, T, C)
     sec = res["kernel_ms_mean"] / 1e3
-    res.update({"workload": S.WORKLOAD_NAMES[2], "cache": "flushed before each launch",
-                "tokens_channels_per_s": spec["B"] * spec["T"] * spec["C"] / sec,
+    res.update({"workload": S.WORKLOAD_NAMES[2],
+                "timing": f"back-to-back launches over {RWKV4_COPIES} copies of the "
+                          "inputs and outputs, two events around them",
+                "tokens_channels_per_s": B * T * C / sec,
                 "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
-                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS})
+                "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                "isolated": {"cache": "flushed before each launch",
+                             "kernel_ms_mean": iso["kernel_ms_mean"],
+                             "kernel_ms_min": iso["kernel_ms_min"],
+                             "hbm_frac": nbytes / (iso["kernel_ms_mean"] / 1e3) / 1e9
+                                         / HBM_PEAK_GBS}})
     return res
 
 
-def run_decode(torch, W, S, H2D, args, cfg=5):
+def run_decode(torch, W, S, H2D, args, cfg=5, batch=None):
     """Back-to-back single-token steps: Finch (workload 5) over distinct
     per-step inputs; Eagle (6) and RWKV-4 (7) cycle through 64 distinct
-    steps' inputs (the bytes each step moves are the same)."""
-    spec = S.WORKLOADS[cfg]
+    steps' inputs (the bytes each step moves are the same).  batch: Finch
+    with that many sequences instead of 256, over 64 distinct steps."""
+    spec = dict(S.WORKLOADS[cfg])
+    if batch is not None:
+        spec["B"] = batch
     steps = args.decode_steps
-    distinct = steps if cfg == 5 else min(steps, 64)
-    d = S.workload(cfg, steps=distinct)
+    distinct = steps if (cfg == 5 and batch is None) else min(steps, 64)
+    d = S.workload(cfg, steps=distinct, B=spec["B"])
     g = H2D(d)
     if cfg == 7:
         st = torch.zeros((spec["B"], 3, spec["C"]), device="cuda")
@@ -413,6 +546,7 @@ def run_decode(torch, W, S, H2D, args, cfg=5):
 
     for s in range(min(8, steps)):  # warm-up on a scratch copy of the state
         one(s)
+    settle(torch, lambda: one(0), args.settle_s)
     st.copy_(s0)
     torch.cuda.synchronize()
     timer = Timer(torch)
@@ -452,7 +586,10 @@ def run_decode(torch, W, S, H2D, args, cfg=5):
     end.record()
     torch.cuda.synchronize()
     graph_ms = start.elapsed_time(end) / (reps * distinct)
-    return {"workload": S.WORKLOAD_NAMES[cfg], "steps": reps * distinct,
+    name = S.WORKLOAD_NAMES[cfg]
+    if batch is not None:
+        name = name.replace(f"B{S.WORKLOADS[cfg]['B']}", f"B{batch}")
+    return {"workload": name, "steps": reps * distinct,
             "distinct_steps": distinct, "timing": "graph replay",
             "steps_per_s": 1e3 / graph_ms, "ms_per_step": graph_ms,
             "algorithmic_bytes_per_step": nbytes,
@@ -477,10 +614,38 @@ def cpu_baseline(S, d4, min_seconds=10.0):
         if sec >= min_seconds:
             break
     B, T, H, N = d4["r"].shape
+    # the RWKV-4 workloads, single-threaded
+    single = {}
+    for cfg in (1, 2):
+        d = S.workload(cfg)
+        reps = 0
+        t1 = time.perf_counter()
+        while True:
+            oracle.rwkv4_fwd(d["k"], d["v"], d["w"], d["u"], nthreads=1)
+            reps += 1
+            el = time.perf_counter() - t1
+            if el >= 1.0:
+                break
+        b, t, c = d["k"].shape
+        single[S.WORKLOAD_NAMES[cfg]] = {"seconds_per_pass": el / reps,
+                                         "tokens_channels_per_s": reps * b * t * c / el,
+                                         "threads": 1}
     return {"value": passes * B * T * H * N / sec, "unit": "tokens*channels/s",
             "cores": nthreads, "kind": "oracle", "seconds": sec,
             "sample": f"the full Finch workload (B={B}, T={T}, H={H}, N={N}), "
-                      f"{passes} passes"}
+                      f"{passes} passes",
+            "cpu_model": cpu_model(), "single_thread": single}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -558,12 +723,60 @@ def summarize_pmc(pmc_dir):
     return out
 
 
-def measure_copy(torch, nbytes=1 << 30, reps=20):
-    """Achievable HBM bandwidth on this GPU: a plain device-to-device copy
-    (torch copy_) of nbytes, read + write, median over reps launches."""
+def measure_stream(torch, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth on this GPU: plain streaming kernels
+    (libstream_probe.so: 16-byte loads / stores, eight in flight per thread)
+    reading, copying and writing 1 GiB buffers (four times the last-level
+    cache), best launch shape of a small sweep, median of `reps` launches."""
+    import ctypes
+    from linear_attention_rnn_wkv_amd import _build
+    L = ctypes.CDLL(_build.PROBE_LIBRARY)
+    L.stream_probe.restype = ctypes.c_int
+    L.stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(5):
+    sink = torch.empty(1 << 14, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {"kind": "plain streaming kernels of this repository over 1 GiB buffers "
+                   "(read; copy = read + write; write), best of a launch-shape sweep",
+           "bytes": nbytes}
+    for kind, name, moved in ((0, "read", nbytes), (1, "copy", 2 * nbytes), (2, "write", nbytes)):
+        best = None
+        for blocks, threads in ((1024, 256), (2048, 256), (4096, 256), (2048, 512)):
+            dst = sink if kind == 0 else b
+
+            def go():
+                st = L.stream_probe(kind, a.data_ptr(), dst.data_ptr(), nbytes, blocks, threads,
+                                    stream)
+                if st != 0:
+                    raise RuntimeError(f"stream_probe({kind}) returned {st}")
+            for _ in range(3):
+                go()
+            torch.cuda.synchronize()
+            ms = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                go()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            ms.sort()
+            gbs = moved / (ms[len(ms) // 2] / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, threads)
+        out[f"{name}_GBps"] = best[0]
+        out[f"{name}_frac_of_peak"] = best[0] / HBM_PEAK_GBS
+        out[f"{name}_launch"] = [best[1], best[2]]
+    out["copy_GBps_torch"] = measure_torch_copy(torch, a, b, reps)
+    del a, b
+    return out
+
+
+def measure_torch_copy(torch, a, b, reps):
+    for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
     ms = []
@@ -576,11 +789,7 @@ def measure_copy(torch, nbytes=1 << 30, reps=20):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     ms.sort()
-    t = ms[len(ms) // 2] / 1e3
-    del a, b
-    return {"kind": "torch copy_ of 1 GiB fp32 on the device (reads 1 GiB, writes 1 GiB); "
-                    "a reference point, not a ceiling (the decode steps move more)",
-            "copy_GBps": 2 * nbytes / t / 1e9, "frac_of_peak": 2 * nbytes / t / 1e9 / HBM_PEAK_GBS}
+    return 2 * a.numel() * 4 / (ms[len(ms) // 2] / 1e3) / 1e9
 
 
 def main():
@@ -613,6 +822,9 @@ def main():
 
     paths = {}
     only = args.only
+    if only == "stream":
+        print(json.dumps(measure_stream(torch)))
+        return 0
     if only == "calib":
         # a plain streaming kernel of known size: reads 1 GiB, writes 1 GiB;
         # its FETCH_SIZE / WRITE_SIZE readings calibrate the HBM counters
@@ -653,6 +865,11 @@ def main():
     if not args.skip_paths and only in (None, "decode"):
         print("finch decode ...", file=sys.stderr, flush=True)
         paths["finch_decode"] = run_decode(torch, W, S, H2D, args)
+    if not args.skip_paths and only in (None, "decode_big"):
+        # a state of 1.07 GB, four times the 256 MB last-level cache: every
+        # step's state bytes come from HBM
+        print("finch decode, 1024 sequences ...", file=sys.stderr, flush=True)
+        paths["finch_decode_B1024"] = run_decode(torch, W, S, H2D, args, batch=1024)
     if not args.skip_paths and only in (None, "eagle_decode"):
         print("eagle decode ...", file=sys.stderr, flush=True)
         paths["eagle_decode"] = run_decode(torch, W, S, H2D, args, cfg=6)
@@ -660,7 +877,6 @@ def main():
         print("rwkv4 decode ...", file=sys.stderr, flush=True)
         paths["rwkv4_decode"] = run_decode(torch, W, S, H2D, args, cfg=7)
     torch.cuda.synchronize()
-    W.device_status()  # raises if any timed launch gave up a hand-off wait
 
     if "finch_fwd" not in paths:
         print(json.dumps({"paths": paths}))
@@ -677,13 +893,25 @@ def main():
         paths["finch_bwd"]["traffic_bytes"] = {
             k: measured_traffic(PMC_PATHS[k][1], k)
             for k in ("finch_bwd_recompute", "finch_bwd_reverse")}
-    # the same bandwidths against what a plain copy reaches on this GPU
-    achievable = measure_copy(torch)
+    # the same bandwidths against what plain streaming kernels reach on this
+    # GPU (each path against the copy: it reads and writes, as they do)
+    achievable = measure_stream(torch)
     for rec in paths.values():
         if "hbm_GBps" in rec:
             rec["hbm_frac_of_copy"] = rec["hbm_GBps"] / achievable["copy_GBps"]
     finch = paths["finch_fwd"]
     spec = S.WORKLOADS[4]
+    cold = None
+    if "cold" in finch:  # the same steps from an idle GPU, before the clocks settle
+        c = finch.pop("cold")
+        nb = finch["algorithmic_bytes"]
+        cold = {"steps": args.steps, "warmup": args.warmup,
+                "kernel_ms_mean": c["kernel_ms_mean"], "kernel_ms_min": c["kernel_ms_min"],
+                "kernel_ms_max": c["kernel_ms_max"],
+                "frac": nb / (c["kernel_ms_mean"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "per_launch_us": c["per_launch_us"][:64],
+                "note": "timed launches before the settle phase; value and roofline are "
+                        "measured after it"}
     ms = finch["wall_s"] / args.steps * 1e3
     cpu = None
     if not args.skip_cpu:
@@ -708,6 +936,7 @@ def main():
                    "state": "fp32", "decay_logits": "fp32 per token"},
         "roofline": {"bound": "hbm", "achieved": finch["hbm_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": finch["hbm_frac"], "traffic": traffic},
+        "cold": cold,
         "cpu_baseline": cpu,
         "achievable_hbm": achievable,
         "paths": paths,

@@ -30,18 +30,17 @@
  * length).
  *
  * Conventions for every entry point
- *  - All tensor pointers are DEVICE pointers owned by the caller.  The only
- *    memory the library allocates is four per-stream workspaces: the chain
- *    workspace of rwkv4_wkv_fwd, the hand-off workspaces of the chunked
- *    Eagle/Finch forward and backward, and the decay producer's factor
- *    (see there); no call keeps state that changes a later call's results.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, frees nothing and never synchronises a stream inside
+ *    a call; its only state is a per-device cache of two attributes (compute
+ *    units and XCDs) read on first use.
  *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
  *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
  *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
  *    nearest, ties to even.
- *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
- *    enqueued; nothing waits for it.  Errors raised by a running kernel
- *    surface at the caller's next synchronisation.
+ *  - `stream` is the hipStream_t the work is enqueued on (NULL = the default
+ *    stream).  Errors raised by a running kernel surface at the caller's next
+ *    synchronisation.  Every call may be made during HIP graph capture.
  *  - Return value: RWKV_OK, or a negative status.  Arguments are validated on
  *    the host before any HIP call; on a validation error nothing is
  *    launched and no output is touched.
@@ -50,6 +49,25 @@
  *  - T == 0 is valid: the state is copied from state_in to state_out (or set
  *    to the empty / zero state when state_in is NULL); r, k, v, x, y, o may
  *    then be NULL.
+ *
+ * Workspaces.  Entry points whose kernels need device scratch take a
+ * `workspace` pointer and its size in bytes; a matching *_workspace_bytes()
+ * call gives the size needed for a shape on the current device (0: the call
+ * needs none, and workspace may be NULL).  The caller owns the workspace; it
+ * must be 16-byte aligned, must not overlap any other argument of the call,
+ * and, where the entry point says so, must be ZERO-FILLED before its first
+ * use.  Such a workspace carries hand-offs between workgroups: its first
+ * 16 KiB are a control block (an epoch advanced by every launch, and an
+ * error word), and the kernels leave it valid for the next call, so it is
+ * zero-filled once and then reused for any number of calls of the same
+ * family (rwkv4_wkv_fwd; or the Eagle/Finch chunked entry points), also as
+ * replays of a captured HIP graph.  Two calls that use one workspace must
+ * not run concurrently (different streams, or two graphs replayed at once).
+ * A hand-off wait is bounded (about a second) so that every kernel ends; it
+ * is never reached in normal operation, since a producer always has a lower
+ * workgroup index than its consumer and runs before or beside it.  A
+ * consumer that gave up continues from a NaN state, so the affected outputs
+ * read NaN, and it sets the error word (rwkv_wkv_workspace_status).
  */
 #ifndef RWKV_WKV_H
 #define RWKV_WKV_H
@@ -60,6 +78,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* HIP's stream handle, declared as HIP declares it (a pointer to an opaque
+ * struct), so that this header compiles with or without the HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
 
 typedef uint16_t rwkv_bf16; /* raw bfloat16 bits */
 
@@ -72,33 +95,22 @@ enum rwkv_status {
     RWKV_E_ALIAS = -5,       /* an output overlaps an input or another output */
     RWKV_E_HIP = -6,         /* the HIP runtime rejected a launch or copy */
     RWKV_E_TIMEOUT = -7      /* a workgroup gave up waiting for another's
-                                hand-off (rwkv_wkv_device_status) */
+                                hand-off (rwkv_wkv_workspace_status) */
 };
 
 /* Static, human-readable text of a status code. */
 const char *rwkv_wkv_strerror(int status);
 
-/* Whether any work enqueued on `stream` (hipStream_t, NULL = the default
- * stream) of the current device gave up a wait.  Kernels that hand a state
- * from one workgroup to another through a per-stream workspace
- * (rwkv4_wkv_fwd's chain, the balanced split of the chunked Eagle/Finch
- * forward and backward) poll for it a bounded number of times, about a
- * second.  The producer always runs before or beside its consumer (it has
- * a lower workgroup index), so the bound is never reached in normal
- * operation; it only guarantees that every kernel ends.  A consumer that
- * gives up sets an error word in the workspace and carries on with a wrong
- * state, so that call's outputs are invalid.
- *
- * This call synchronises `stream`, reads the error words of its
- * workspaces, and returns RWKV_E_TIMEOUT if any was set since the last
- * check (RWKV_OK otherwise, RWKV_E_HIP if the runtime fails).  A workspace
- * whose word was set is zero-filled again, as when first allocated, so
- * that later calls start clean.  It is a
- * diagnostic: call it after a batch of work, with the same stream handle
- * the work was enqueued with, not from inside graph capture.  It allocates
- * nothing.
+/* Whether a kernel that used `workspace` (a zero-filled workspace of one of
+ * the entry points with hand-offs: rwkv4_wkv_fwd, the chunked Eagle/Finch
+ * forwards and backwards) gave up a hand-off wait since the last check.
+ * It synchronises `stream`, reads the workspace's error word, and returns
+ * RWKV_E_TIMEOUT if it was set (then clears it), RWKV_OK if not, RWKV_E_HIP
+ * if the runtime fails, RWKV_E_NULL / RWKV_E_DIM / RWKV_E_ALIGN for a NULL,
+ * shorter than 16 KiB or misaligned workspace.  A diagnostic: call it after
+ * a batch of work, outside graph capture.  It allocates nothing.
  */
-int rwkv_wkv_device_status(void *stream);
+int rwkv_wkv_workspace_status(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * RWKV-4 WKV forward, fp32.  Channels are independent: C = H*N and any
@@ -115,27 +127,31 @@ int rwkv_wkv_device_status(void *stream);
  *              state_in exactly (in-place update) but not partially overlap.
  *   y          [B][T][C] fp32 output
  *
- * Pointers need 4-byte alignment.  C = H*N must be at most 2^20 and
- * B * C below 2^36, else RWKV_E_UNSUPPORTED.
+ *   workspace  rwkv4_wkv_fwd_workspace_bytes(B, T, H, N) bytes, ZERO-FILLED
+ *              before first use (see Workspaces above); NULL when that is 0
+ *              (T <= 256).  RWKV_E_NULL if NULL, RWKV_E_DIM if shorter,
+ *              RWKV_E_ALIGN / RWKV_E_ALIAS as for the tensors.
  *
- * Workspace: the 256-token passes of a sequence's channel block run in
- * separate workgroups that hand the state on through a device workspace
- * (1.5 KB per workgroup of a launch, at most 8192 workgroups per launch,
- * plus 8.5 KB of counters).  It is allocated on the first call for each
- * (device, stream), grown when a call needs more (that call then
- * synchronises the stream), and kept until the process ends.  Calls on one
- * stream share it safely, also as replays of a captured graph (the kernels
- * keep every piece of their bookkeeping on the device); the first call on a
- * stream must not be made during graph capture.  Outputs of sequences longer
- * than one pass may differ from run to run in the last bits: how far back a
- * pass finds a finished predecessor depends on timing, and so does the order
- * in which the carried state is combined.
+ * Pointers need 4-byte alignment (the workspace 16).  C = H*N must be at
+ * most 2^20 and B * C below 2^36, else RWKV_E_UNSUPPORTED.
+ *
+ * The 256-token passes of a sequence's block of 32 channels run in separate
+ * workgroups that hand the state on through the workspace (1.5 KiB of
+ * records per workgroup of a launch, at most 8192 workgroups per launch;
+ * longer inputs take several launches, the state carried between them in
+ * the workspace).  Outputs of sequences longer than one pass may differ from
+ * run to run in the last bits: how far back a pass finds a finished
+ * predecessor depends on timing, and so does the order in which the carried
+ * state is combined.
  */
+size_t rwkv4_wkv_fwd_workspace_bytes(int B, int T, int H, int N);
+
 int rwkv4_wkv_fwd(int B, int T, int H, int N,
                   const float *k, const float *v,
                   const float *w, const float *u,
                   const float *state_in, float *state_out,
-                  float *y, void *stream);
+                  float *y, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * RWKV-4 WKV, serial (RNN) mode (RWKV paper summary, section "RNN-like
@@ -156,7 +172,7 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N,
 int rwkv4_wkv_step(int B, int T, int H, int N,
                    const float *k, const float *v,
                    const float *w, const float *u,
-                   float *state, float *y, void *stream);
+                   float *state, float *y, hipStream_t stream);
 
 /*
  * Eagle (RWKV-5) WKV forward, time-parallel (chunked) mode.  N must be 64.
@@ -171,22 +187,27 @@ int rwkv4_wkv_step(int B, int T, int H, int N,
  *              state_in exactly, but not partially overlap it.
  *   o          [B][T][H][N] bf16 output
  *
- * All pointers need 16-byte alignment.  H must be at most 65536, else
- * RWKV_E_UNSUPPORTED.
+ *   workspace  rwkv_wkv_fwd_workspace_bytes(B, T, H, N) bytes, ZERO-FILLED
+ *              before first use (see Workspaces above); NULL when that is 0.
+ *              It is 0 unless B*H exceeds the device's compute units and
+ *              T >= 256: then each workgroup runs its own head plus a segment
+ *              of an extra head, and the segments hand the state on through
+ *              the workspace (16 KiB per hand-off, at most 4096; past twice
+ *              the compute units also 16 KiB per workgroup, where a
+ *              workgroup's own state waits meanwhile).  The size depends on
+ *              the current device: query it with the device current.
  *
- * Workspace: when B*H exceeds the device's compute units (at most by half
- * again), or twice their number, and T >= 256, each workgroup runs its own
- * head plus a segment of an extra head, and the segments hand the state on
- * through a device workspace (16 KB per hand-off, at most 4096; past twice
- * the compute units also 16 KB per workgroup, where a workgroup's own state
- * waits meanwhile).  It is allocated, grown and kept as rwkv4_wkv_fwd's chain
- * workspace, with the same rules.
+ * All pointers need 16-byte alignment.  H must be at most 65536 and B*H below
+ * 2^31, else RWKV_E_UNSUPPORTED.
  */
+size_t rwkv_wkv_fwd_workspace_bytes(int B, int T, int H, int N);
+
 int rwkv5_wkv_fwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                   const float *x, const float *u,
                   const float *state_in, float *state_out,
-                  rwkv_bf16 *o, void *stream);
+                  rwkv_bf16 *o, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * Finch (RWKV-6) WKV forward, time-parallel (chunked) mode.  N must be 64.
@@ -200,7 +221,8 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                   const float *x, const float *u,
                   const float *state_in, float *state_out,
-                  rwkv_bf16 *o, void *stream);
+                  rwkv_bf16 *o, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * Finch (RWKV-6) WKV, serial (RNN) mode: tokens are applied one at a time to
@@ -216,7 +238,7 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N,
 int rwkv6_wkv_step(int B, int T, int H, int N,
                    const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                    const float *x, const float *u,
-                   float *state, rwkv_bf16 *o, void *stream);
+                   float *state, rwkv_bf16 *o, hipStream_t stream);
 
 /*
  * Eagle (RWKV-5) WKV, serial (RNN) mode.  As rwkv6_wkv_step, except that x
@@ -226,7 +248,7 @@ int rwkv6_wkv_step(int B, int T, int H, int N,
 int rwkv5_wkv_step(int B, int T, int H, int N,
                    const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                    const float *x, const float *u,
-                   float *state, rwkv_bf16 *o, void *stream);
+                   float *state, rwkv_bf16 *o, hipStream_t stream);
 
 /*
  * Eagle / Finch time-parallel forward with the time-mixing epilogue fused
@@ -244,22 +266,25 @@ int rwkv5_wkv_step(int B, int T, int H, int N,
  *   ln_w, ln_b [H][N] fp32 per-channel weight and bias of the norm
  *   eps        added to the variance; finite and >= 0, else RWKV_E_DIM
  *   y          [B][T][H][N] bf16 output (in place of o)
- * Other arguments, the state and the error codes as rwkv6_wkv_fwd (rwkv5:
- * x is [H][N]).  All pointers need 16-byte alignment.
+ * Other arguments, the state, the workspace (rwkv_wkv_fwd_workspace_bytes)
+ * and the error codes as rwkv6_wkv_fwd (rwkv5: x is [H][N]).  All pointers
+ * need 16-byte alignment.
  */
 int rwkv5_wkv_fwd_gated(int B, int T, int H, int N,
                         const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                         const float *x, const float *u,
                         const float *state_in, float *state_out,
                         const rwkv_bf16 *g, const float *ln_w, const float *ln_b,
-                        float eps, rwkv_bf16 *y, void *stream);
+                        float eps, rwkv_bf16 *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
                         const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                         const float *x, const float *u,
                         const float *state_in, float *state_out,
                         const rwkv_bf16 *g, const float *ln_w, const float *ln_b,
-                        float eps, rwkv_bf16 *y, void *stream);
+                        float eps, rwkv_bf16 *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Eagle / Finch backward of the time-parallel forward (rwkv5_wkv_fwd,
@@ -279,18 +304,21 @@ int rwkv6_wkv_fwd_gated(int B, int T, int H, int N,
  *   d_u        [H][N] fp32 output, summed over sequences and tokens
  *   d_state_in [B][H][N][N] fp32 output dL/dS_0, or NULL; it may equal
  *              d_state_out exactly (in place)
- *   workspace  device memory of at least rwkv_wkv_bwd_workspace_bytes(B, T,
- *              H, N) bytes, 16-byte aligned, owned by the caller and not
- *              overlapping any other argument (RWKV_E_DIM if too small).  It
- *              holds the state entering every 64-token chunk, recomputed by
- *              the forward: 16 KiB per chunk and head.
+ *   workspace  rwkv_wkv_bwd_workspace_bytes(B, T, H, N) bytes, 16-byte
+ *              aligned, ZERO-FILLED before first use (see Workspaces above),
+ *              not overlapping any other argument (RWKV_E_DIM if too small).
+ *              It holds the hand-off area of the balanced splits (the
+ *              recomputation's and the reverse sweep's, when B*H exceeds the
+ *              compute units and T >= 256: 48 KiB per hand-off and per
+ *              workgroup for the sweep), the state entering every 64-token
+ *              chunk, recomputed by the forward (16 KiB per chunk and head),
+ *              and the per-sequence partial sums of d_u and Eagle's d_x.
+ *              The size depends on the current device.
  * When B*H exceeds the device's compute units and T >= 256, a workgroup per
  * compute unit sweeps whole heads in rounds; when the last round's remainder
  * is at most half the compute units, each workgroup sweeps its own head of
  * that round plus a segment of an extra head, and the segments hand the
- * sweep's state on through a library workspace (48 KiB per hand-off and per
- * workgroup), allocated, grown and kept as rwkv4_wkv_fwd's chain workspace,
- * with the same rules.
+ * sweep's state on through the workspace.
  *
  * All pointers need 16-byte alignment; outputs may not overlap inputs or
  * each other.  H must be at most 65536.  T = 0 sets d_u (and rwkv5's d_x)
@@ -305,7 +333,7 @@ int rwkv5_wkv_bwd(int B, int T, int H, int N,
                   const rwkv_bf16 *d_o, const float *d_state_out,
                   rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
                   float *d_x, float *d_u, float *d_state_in,
-                  void *workspace, size_t workspace_bytes, void *stream);
+                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 int rwkv6_wkv_bwd(int B, int T, int H, int N,
                   const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
@@ -313,7 +341,7 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
                   const rwkv_bf16 *d_o, const float *d_state_out,
                   rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
                   float *d_x, float *d_u, float *d_state_in,
-                  void *workspace, size_t workspace_bytes, void *stream);
+                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Training pair that saves the backward's recomputation.  rwkv5/6_wkv_fwd_save
@@ -324,9 +352,10 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N,
  * *_fwd_save call (same r, k, v, x, u, state_in, B, T, H) left in the same
  * workspace.  The pair gives bit for bit the gradients of the *_fwd and
  * *_bwd pair.
- *   workspace  device memory of at least rwkv_wkv_bwd_workspace_bytes(B, T,
- *              H, N) bytes, 16-byte aligned, overlapping no other argument
- *              (RWKV_E_DIM if too small; RWKV_E_NULL if NULL with T > 0).
+ *   workspace  rwkv_wkv_bwd_workspace_bytes(B, T, H, N) bytes, 16-byte
+ *              aligned, zero-filled before first use, overlapping no other
+ *              argument (RWKV_E_DIM if too small; RWKV_E_NULL if NULL with
+ *              T > 0).
  * The backward's other arguments as rwkv5/6_wkv_bwd (it takes no state_in:
  * the saved states hold it).
  */
@@ -334,26 +363,26 @@ int rwkv5_wkv_fwd_save(int B, int T, int H, int N,
                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                        const float *x, const float *u,
                        const float *state_in, float *state_out, rwkv_bf16 *o,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 int rwkv6_wkv_fwd_save(int B, int T, int H, int N,
                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                        const float *x, const float *u,
                        const float *state_in, float *state_out, rwkv_bf16 *o,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 int rwkv5_wkv_bwd_saved(int B, int T, int H, int N,
                         const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                         const float *x, const float *u,
                         const rwkv_bf16 *d_o, const float *d_state_out,
                         rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
                         float *d_x, float *d_u, float *d_state_in,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 int rwkv6_wkv_bwd_saved(int B, int T, int H, int N,
                         const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                         const float *x, const float *u,
                         const rwkv_bf16 *d_o, const float *d_state_out,
                         rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v,
                         float *d_x, float *d_u, float *d_state_in,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Finch decay producer (RWKV-5/6 summary, 4.1.1 "Eagle token shift",
@@ -378,31 +407,40 @@ int rwkv6_wkv_bwd_saved(int B, int T, int H, int N,
  *              pages give their shapes)
  *   d          [B][T][D] fp32 output: the logits rwkv6_wkv_fwd takes as x
  *              (with D = H N in its [B][T][H][N] layout)
+ *   workspace  rwkv6_decay_lora_workspace_bytes(B, T, D) bytes (B T 128:
+ *              act(z A2) of every token, rank 64, bf16), 16-byte aligned, not
+ *              overlapping any other argument; no zero-filling needed.
  * The products run on bf16 matrix cores with fp32 accumulation (the mixed
  * values and act(.) rounded to bf16 as operands).  B T must be below 2^31.
- * Scratch: a per-stream workspace of B T 128 bytes, allocated, grown and
- * kept as rwkv4_wkv_fwd's chain workspace, with the same rules (a call that
- * needs it larger synchronises the stream, so it must not be the first of
- * its size on a stream under graph capture).  T = 0 does nothing.  All pointers
- * need 16-byte alignment; d must not overlap an input.
+ * T = 0 does nothing.  All pointers need 16-byte alignment; d must not
+ * overlap an input.
  */
+size_t rwkv6_decay_lora_workspace_bytes(int B, int T, int D);
+
 int rwkv6_decay_lora(int B, int T, int D, int act,
                      const rwkv_bf16 *x, const rwkv_bf16 *shift,
                      const float *mu_x, const float *lam,
                      const rwkv_bf16 *A1, const rwkv_bf16 *B1,
                      const float *omega, const rwkv_bf16 *A2, const rwkv_bf16 *B2,
-                     float *d, void *stream);
+                     float *d, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /*
  * Finch time-parallel forward fed by the decay producer: the same output and
  * state as rwkv6_decay_lora followed by rwkv6_wkv_fwd with x = d, without
  * the fp32 logits ever going to memory.  The producer writes act(z A2)
- * (rank 64, bf16, B T 128 bytes of the per-stream workspace) and the chunked
- * kernel forms each head's logits omega + act(z A2) B2 on the matrix cores.
+ * (rank 64, bf16, B T 128 bytes of the workspace) and the chunked kernel
+ * forms each head's logits omega + act(z A2) B2 on the matrix cores.
  * Arguments: r, k, v, u, state_in, state_out, o as rwkv6_wkv_fwd; x (the
  * block input, [B][T][H N] bf16), shift, mu_x, lam, A1, B1, omega, A2, B2 and
  * act as rwkv6_decay_lora with D = H N.
+ *   workspace  rwkv6_wkv_fwd_lora_workspace_bytes(B, T, H, N) bytes: the
+ *              chunked forward's hand-off area (as rwkv_wkv_fwd_workspace_
+ *              bytes) followed by the producer's factor.  16-byte aligned,
+ *              ZERO-FILLED before first use, overlapping no other argument.
  */
+size_t rwkv6_wkv_fwd_lora_workspace_bytes(int B, int T, int H, int N);
+
 int rwkv6_wkv_fwd_lora(int B, int T, int H, int N,
                        const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
                        const rwkv_bf16 *x, const rwkv_bf16 *shift,
@@ -411,7 +449,8 @@ int rwkv6_wkv_fwd_lora(int B, int T, int H, int N,
                        const float *omega, const rwkv_bf16 *A2, const rwkv_bf16 *B2,
                        int act, const float *u,
                        const float *state_in, float *state_out,
-                       rwkv_bf16 *o, void *stream);
+                       rwkv_bf16 *o, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

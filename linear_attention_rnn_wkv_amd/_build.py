@@ -1,4 +1,5 @@
-"""Build librwkv_wkv.so (the C-ABI library) for gfx950 with hipcc.
+"""Build librwkv_wkv.so (the C-ABI library) and libstream_probe.so (the
+bench's bandwidth reference) for gfx950 with hipcc.
 
 Usage: python -m linear_attention_rnn_wkv_amd._build [--verbose]
 The library is written next to this file; objects go to <repo>/_build/.
@@ -17,6 +18,9 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "librwkv_wkv.so")
 SOURCES = ["rwkv_wkv_abi.hip", "rwkv4_scan.hip", "rwkv4_step.hip", "wkv_step.hip",
            "wkv_chunk.hip", "wkv_chunk_bwd.hip", "decay_lora.hip"]
+# plain streaming kernels: the HBM bandwidth the bench measures against
+PROBE_LIBRARY = os.path.join(PKG, "libstream_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 # The RWKV-4 chain counts arrivals with one lane's returning atomic whose
 # result is only needed at the end of the workgroup; the atomic optimizer
 # would broadcast it at once and so wait for the round trip right there.
@@ -53,26 +57,28 @@ def _run(cmds, verbose):
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
 
 
-def build(verbose: bool = False, extra_flags=(), output: str = LIBRARY,
-          objdir: str = OBJDIR, sources=None) -> str:
-    """Compile every HIP source and link librwkv_wkv.so; returns its path.
-
-    ``extra_flags``, ``output``, ``objdir`` and ``sources`` (a map from the
-    default source name to another file) build variants for comparison."""
-    os.makedirs(objdir, exist_ok=True)
-    objs = []
-    cmds = []
-    for src in SOURCES:
-        path = (sources or {}).get(src, os.path.join(CSRC, src))
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+def _compile_link(sources, output, verbose):
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs, cmds = [], []
+    for src in sources:
+        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c", path, "-o",
-                     obj])
+        cmds.append([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     _run(cmds, verbose)
     tmp = output + ".tmp"
     _run([[HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)
     os.replace(tmp, output)
     return output
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source, link librwkv_wkv.so (the operators) and
+    libstream_probe.so (the bench's bandwidth reference); returns the
+    operator library's path."""
+    _compile_link(SOURCES, LIBRARY, verbose)
+    _compile_link(PROBE_SOURCES, PROBE_LIBRARY, verbose)
+    return LIBRARY
 
 
 if __name__ == "__main__":

@@ -2,34 +2,57 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace wkv {
 
-// Compute units of the current device (read once per device).
+// Compute units and XCDs (accelerator dies) of the current device, read once
+// per device.  Workgroups of a launch are dealt to the XCDs round-robin.
 int device_cus();
+int device_xcds();
 
-// Device workspace of one kind for (current device, stream), at least `bytes`
-// long and zero-filled when first allocated (on `stream`).  Launches on one
-// stream run in order and may share it; a kernel that uses flags in it must
-// leave them cleared.  A larger request reallocates (synchronising the
-// stream first).  Kept until the process ends.
-enum { kWsRwkv4Chain = 0, kWsChunkHandoff = 1, kWsDecayH = 2, kWsBwdSplit = 3 };
-hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out);
+// Control block at the start of every workspace whose kernels hand a state
+// from one workgroup to another.  Each word sits on a 128-byte line of its
+// own:
+//   epoch  advanced once per launch, after every workgroup of the launch has
+//          read it.  A hand-off word is valid only while it carries the
+//          launch's tag (epoch + 1), so nothing is cleared between launches
+//          and a word written late by an earlier launch is never taken for
+//          a current one.
+//   err    set to 1 when a bounded wait for another workgroup gave up; that
+//          consumer continued with a NaN state, so the affected outputs read
+//          NaN.  Read and cleared by rwkv_wkv_workspace_status.
+//   done   workgroups of the current launch that have finished (chunked
+//          kernels), reset by the last one
+//   total, group[]  the RWKV-4 chain's two-level count of finished chains
+// A zero-filled block is a valid start (epoch 0, nothing pending).
+constexpr int kWsGroups = 64;
+struct WsCtrl {
+    struct Line {
+        unsigned n, pad[31];
+    };
+    Line epoch, err, done, total, group[kWsGroups];
+};
+constexpr size_t kWsCtrlBytes = 16384;  // the control block, rounded up
+static_assert(sizeof(WsCtrl) <= kWsCtrlBytes, "control block");
+constexpr size_t kWsErrOffset = offsetof(WsCtrl, err);
 
-// Byte offset, in the workspace of each kind, of the word a kernel sets when
-// one of its bounded waits for another workgroup gives up (that workgroup's
-// results were then never seen, and the call's outputs are invalid); -1 for
-// a kind with no waits.  Only the host clears it (workspace_timed_out).
-constexpr long kWsErrorWord[] = {128, 4096 * 4, -1, 4096 * 4};
-// Waits for `stream`, then reads and clears the error words of its
-// workspaces on the current device; *timed_out is set when any was set.
-hipError_t workspace_timed_out(hipStream_t stream, bool *timed_out);
+// Bytes of caller workspace each launcher below needs (0: none), for the
+// current device.  A workspace is zero-filled by its owner before first use.
+size_t rwkv4_workspace_bytes(int B, int T, int C);
+size_t chunk_workspace_bytes(int B, int T, int H);   // chunked forward, gated forward
+size_t bwd_workspace_bytes(int B, int T, int H);     // backward; forward + backward pair
+size_t bwd_states_offset(int B, int T, int H);       // where the saved chunk states start
+size_t lora_workspace_bytes(int B, int T);           // decay producer (act(z A2) per token)
+size_t lora_fwd_workspace_bytes(int B, int T, int H);  // producer + chunked forward
+size_t lora_fwd_factor_offset(int B, int T, int H);  // where act(z A2) starts in it
 
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
+// ws: rwkv4_workspace_bytes(B, T, C) bytes (may be NULL when that is 0).
 hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
                         const float *w, const float *u, const float *state_in,
-                        float *state_out, float *y, hipStream_t stream);
+                        float *state_out, float *y, void *ws, hipStream_t stream);
 
 // RWKV-4 serial (RNN-mode) path, (a, b, p) state updated in place.
 hipError_t launch_rwkv4_step(int B, int T, int C, const float *k, const float *v,
@@ -42,14 +65,16 @@ hipError_t launch_wkv_step(bool per_token_decay, int B, int T, int H, const uint
                            const uint16_t *k, const uint16_t *v, const float *x,
                            const float *u, float *state, uint16_t *o, hipStream_t stream);
 
-// Eagle / Finch chunked (time-parallel) path, N = 64.  With chunk_states
-// non-NULL it writes, instead of o and state_out, the state entering every
-// chunk and the final state: [B H][ceil(T/64) + 1][64][64] fp32.
+// Eagle / Finch chunked (time-parallel) path, N = 64.  ws: the hand-off area
+// of the balanced split, chunk_workspace_bytes(B, T, H) bytes (NULL when
+// that is 0).  With chunk_states non-NULL it writes, instead of o and
+// state_out, the state entering every chunk and the final state:
+// [B H][ceil(T/64) + 1][64][64] fp32.
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
                               const uint16_t *r, const uint16_t *k,
                               const uint16_t *v, const float *x, const float *u,
                               const float *state_in, float *state_out,
-                              uint16_t *o, hipStream_t stream,
+                              uint16_t *o, void *ws, hipStream_t stream,
                               float *chunk_states = nullptr, const uint16_t *gate = nullptr,
                               const float *ln_w = nullptr, const float *ln_b = nullptr,
                               float eps = 0.0f, const uint16_t *lora_h = nullptr,
@@ -74,17 +99,18 @@ hipError_t launch_wkv_chunked_gated(bool per_token_decay, int B, int T, int H,
                                     const uint16_t *r, const uint16_t *k, const uint16_t *v,
                                     const float *x, const float *u, const float *state_in,
                                     float *state_out, const uint16_t *gate, const float *ln_w,
-                                    const float *ln_b, float eps, uint16_t *y,
+                                    const float *ln_b, float eps, uint16_t *y, void *ws,
                                     hipStream_t stream);
 
-// Eagle / Finch chunked backward, N = 64: workspace size and launch (the
-// forward's state recomputation, the reverse sweep, the sums over sequences).
-size_t wkv_bwd_workspace_bytes(int B, int T, int H);
+// Eagle / Finch chunked backward, N = 64 (the forward's state recomputation,
+// the reverse sweep, the sums over sequences).  ws: bwd_workspace_bytes(B,
+// T, H) bytes: the hand-off area of both kernels' splits at offset 0, the
+// chunk states at bwd_states_offset(B, T, H).
 hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint16_t *r,
                           const uint16_t *k, const uint16_t *v, const float *x, const float *u,
                           const float *state_in, const uint16_t *d_o, const float *d_sT,
                           uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
-                          float *d_s0, void *workspace, hipStream_t stream,
+                          float *d_s0, void *ws, hipStream_t stream,
                           bool states_saved = false);
 
 // Fill n floats with `value` (used for empty / zero states when T == 0).

@@ -123,18 +123,13 @@ struct Seg {  // one lane's tokens of a pass
 // pass of the chain has published a tagged record (walks reach back to an
 // inclusive state, whose publisher walked before it, down to pass 0), i.e.
 // after each of them has read the epoch.  The last passes of the chains then
-// arrive at one of kGroups counters, and the last arrival of each group at a
-// total; the last arrival there advances the epoch.  Two levels keep any one
-// counter to a few dozen atomics (a single counter hit by every workgroup
-// serialises and stalls the memory system).
-constexpr int kGroups = 64;
-struct Ctrl {  // each word on a 128-byte line of its own
-    struct Line {
-        unsigned n, pad[31];
-    };
-    Line epoch, err, total, group[kGroups];
-};
-static_assert(offsetof(Ctrl, err) == kWsErrorWord[kWsRwkv4Chain], "error word of the chain workspace");
+// arrive at one of kWsGroups counters of the control block (WsCtrl), and
+// the last arrival of each group at a total; the last arrival there advances
+// the epoch.  Two levels keep any one counter to a few dozen atomics (a
+// single counter hit by every workgroup serialises and stalls the memory
+// system).
+using Ctrl = WsCtrl;
+constexpr int kGroups = kWsGroups;
 // Bound on the polls of a predecessor's record (about a second):
 // predecessors have lower workgroup indices and are dispatched first, so the
 // wait always ends; the bound only guarantees that the kernel terminates.
@@ -227,7 +222,7 @@ __global__ __launch_bounds__(NT, 3 * NT / 256) void rwkv4_chain_kernel(
     };
     // the epoch is read with the operands
     unsigned epoch = 0;
-    if (tid == 0) epoch = ld32(&ctrl->epoch.n);
+    if (tid == 0 && nq > 1) epoch = ld32(&ctrl->epoch.n);
 
     // FULL: every row of the pass exists (uniform over the workgroup)
     auto pass = [&](auto full_tag) {
@@ -314,8 +309,7 @@ __global__ __launch_bounds__(NT, 3 * NT / 256) void rwkv4_chain_kernel(
                 int polls = 0;
                 auto give_up = [&]() {  // cannot happen: see kSpinLimit
                     if (++polls <= kSpinLimit) return false;
-                    __hip_atomic_fetch_or(&ctrl->err.n, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+                    ws_fail(ctrl);
                     return true;
                 };
                 excl = acc;
@@ -347,7 +341,11 @@ __global__ __launch_bounds__(NT, 3 * NT / 256) void rwkv4_chain_kernel(
                             shown = ok(ld64(word(lj, 1, 2))) || (j > 0 && ok(ld64(word(lj, 0, 2))));
                         if (__shfl(shown, 0, 64) || (late = give_up())) break;
                     }
-                    if (late) break;
+                    if (late) {  // go on from NaN: the pass's outputs show it
+                        const float nan = __builtin_nanf("");
+                        excl = St{nan, nan, nan};
+                        break;
+                    }
                 }
             }
             const St incl = combine(excl, rnw, run);
@@ -416,31 +414,30 @@ __global__ void fill_kernel(float *dst, int64_t n, float value) {
 
 }  // namespace
 
-hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
-                        const float *w, const float *u, const float *state_in,
-                        float *state_out, float *y, hipStream_t stream) {
-    // one pass of 32 channels (128-byte rows) x 16 segments of 16 tokens per
-    // workgroup; the passes of a (sequence, channel block) form a chain
+size_t rwkv4_workspace_bytes(int B, int T, int C) {
     constexpr int NT = 512, CB = 32, SEG = 16, kPass = (NT / CB) * SEG;
     const int64_t units = (int64_t)B * ((C + CB - 1) / CB);
     const int64_t passes = (T + kPass - 1) / kPass;
-    // a launch covers at most kMaxLinks workgroups; longer sequences take
-    // several launches, the state carried between them in the workspace
+    const int64_t per_launch = std::max<int64_t>(1, std::min<int64_t>(passes, 8192 / units));
+    if (passes <= 1) return 0;
+    return kWsCtrlBytes + (size_t)(per_launch * units) * 6 * CB * 8 +
+           (per_launch < passes ? (size_t)B * 3 * C * 4 : 0);
+}
+
+hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
+                        const float *w, const float *u, const float *state_in,
+                        float *state_out, float *y, void *wsp, hipStream_t stream) {
+    constexpr int NT = 512, CB = 32, SEG = 16, kPass = (NT / CB) * SEG;
+    const int64_t units = (int64_t)B * ((C + CB - 1) / CB);
+    const int64_t passes = (T + kPass - 1) / kPass;
     constexpr int64_t kMaxLinks = 8192;
     const int64_t per_launch = std::max<int64_t>(1, std::min<int64_t>(passes, kMaxLinks / units));
-    const bool windows = per_launch < passes;
-    // layout: control block, records, carry
     const int64_t links = per_launch * units;
-    const size_t ctrl_bytes = (sizeof(Ctrl) + 255) / 256 * 256;
     const size_t rec_bytes = (size_t)links * 6 * CB * 8;
-    const size_t carry_bytes = windows ? (size_t)B * 3 * C * 4 : 0;
-    char *ws = nullptr;
-    hipError_t e = stream_workspace(kWsRwkv4Chain, stream, ctrl_bytes + rec_bytes + carry_bytes,
-                                    (void **)&ws);
-    if (e != hipSuccess) return e;
+    char *ws = (char *)wsp;
     Ctrl *ctrl = (Ctrl *)ws;
-    unsigned long long *recs = (unsigned long long *)(ws + ctrl_bytes);
-    float *carry = (float *)(ws + ctrl_bytes + rec_bytes);
+    unsigned long long *recs = ws ? (unsigned long long *)(ws + kWsCtrlBytes) : nullptr;
+    float *carry = ws ? (float *)(ws + kWsCtrlBytes + rec_bytes) : nullptr;
     for (int64_t q0 = 0; q0 < passes; q0 += per_launch) {
         const int64_t nq = std::min(per_launch, passes - q0);
         const float *si = q0 == 0 ? state_in : carry;
@@ -448,7 +445,7 @@ hipError_t launch_rwkv4(int B, int T, int C, const float *k, const float *v,
         hipLaunchKernelGGL((rwkv4_chain_kernel<NT, CB, SEG>), dim3((unsigned)(nq * units)),
                            dim3(NT), 0, stream, T, (int)(q0 * kPass), (int)nq, C, k, v, w, u,
                            si, so, y, recs, ctrl);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -3,11 +3,11 @@
 // Every entry point validates its arguments completely before the first HIP
 // call, so a rejected call launches nothing and touches no output.
 #include <stdint.h>
+
+#include <algorithm>
 #include <string.h>
 
-#include <map>
-#include <mutex>
-#include <tuple>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -62,6 +62,20 @@ int check_outputs(std::initializer_list<Span> outs, std::initializer_list<Span> 
     return RWKV_OK;
 }
 
+// The caller's workspace: at least `need` bytes (then non-NULL and 16-byte
+// aligned) and overlapping none of the call's other buffers.
+int check_workspace(const void *ws, size_t ws_bytes, size_t need,
+                    const std::vector<Span> &others) {
+    if (need == 0) return RWKV_OK;
+    if (ws == nullptr) return RWKV_E_NULL;
+    if (ws_bytes < need) return RWKV_E_DIM;
+    if (!aligned(ws, 16)) return RWKV_E_ALIGN;
+    const Span sw{ws, (int64_t)need};
+    for (const Span &o : others)
+        if (overlaps(sw, o)) return RWKV_E_ALIAS;
+    return RWKV_OK;
+}
+
 // Shared checks of the Eagle / Finch entry points.  x_elems: elements of x.
 int check_matrix(int B, int T, int H, int N, const void *r, const void *k, const void *v,
                  const void *x, int64_t x_elems, const void *u, const void *s_in,
@@ -88,13 +102,13 @@ constexpr int64_t kMaxRwkv4Channels = 1 << 20;
 
 int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
-               const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
+               const float *state_in, float *state_out, rwkv_bf16 *o, void *ws,
+               size_t ws_bytes, hipStream_t s) {
     const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
     int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
     if (st != RWKV_OK) return st;
     // a chunk's rows are addressed with 32-bit byte offsets
-    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
-    hipStream_t s = (hipStream_t)stream;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
     if (T == 0) {
         if (state_out == nullptr || state_out == state_in) return RWKV_OK;
         const int64_t n = (int64_t)B * H * N * N;
@@ -102,19 +116,25 @@ int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
         return hip_status(hipMemcpyAsync(state_out, state_in, n * 4,
                                          hipMemcpyDeviceToDevice, s));
     }
+    const int64_t tok = checked_mul({B, T, H, N}), sts = checked_mul({B, H, N, N});
+    st = check_workspace(ws, ws_bytes, wkv::chunk_workspace_bytes(B, T, H),
+                         {Span{r, tok * 2}, Span{k, tok * 2}, Span{v, tok * 2},
+                          Span{x, x_elems * 4}, Span{u, (int64_t)H * N * 4},
+                          Span{state_in, sts * 4}, Span{state_out, sts * 4}, Span{o, tok * 2}});
+    if (st != RWKV_OK) return st;
     return hip_status(wkv::launch_wkv_chunked(per_token, B, T, H, r, k, v, x, u,
-                                              state_in, state_out, o, s));
+                                              state_in, state_out, o, ws, s));
 }
 
 int matrix_fwd_gated(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                      const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                      const float *state_in, float *state_out, const rwkv_bf16 *gate,
-                     const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
-                     void *stream) {
+                     const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y, void *ws,
+                     size_t ws_bytes, hipStream_t s) {
     const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
     int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, y);
     if (st != RWKV_OK) return st;
-    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
     if (!(eps >= 0.0f) || eps > 1e30f) return RWKV_E_DIM;  // also rejects NaN
     if (T > 0 && (gate == nullptr || ln_w == nullptr || ln_b == nullptr)) return RWKV_E_NULL;
     for (const void *p : {(const void *)gate, (const void *)ln_w, (const void *)ln_b})
@@ -123,12 +143,16 @@ int matrix_fwd_gated(bool per_token, int B, int T, int H, int N, const rwkv_bf16
     const Span sy{y, tok * 2}, sso{state_out, st_el * 4}, sg{gate, tok * 2},
         sw{ln_w, (int64_t)H * N * 4}, sb{ln_b, (int64_t)H * N * 4};
     if (T > 0 && check_outputs({sy, sso}, {sg, sw, sb}) != RWKV_OK) return RWKV_E_ALIAS;
-    hipStream_t s = (hipStream_t)stream;
     if (T == 0) return matrix_fwd(per_token, B, T, H, N, r, k, v, x, u, state_in, state_out,
-                                  y, stream);
+                                  y, ws, ws_bytes, s);
+    st = check_workspace(ws, ws_bytes, wkv::chunk_workspace_bytes(B, T, H),
+                         {Span{r, tok * 2}, Span{k, tok * 2}, Span{v, tok * 2},
+                          Span{x, x_elems * 4}, Span{u, (int64_t)H * N * 4},
+                          Span{state_in, st_el * 4}, sso, sy, sg, sw, sb});
+    if (st != RWKV_OK) return st;
     return hip_status(wkv::launch_wkv_chunked_gated(per_token, B, T, H, r, k, v, x, u,
                                                     state_in, state_out, gate, ln_w, ln_b,
-                                                    eps, y, s));
+                                                    eps, y, ws, s));
 }
 
 // Checks of the decay producer's arguments (D = H N channels); `out` is the
@@ -157,22 +181,39 @@ int check_lora(int B, int T, int D, int act, const void *x, const void *shift,
     return check_outputs({out}, {sx, ss, smu, sl, sa1, sb1, so, sa2, sb2});
 }
 
+// The decay producer's inputs and `out`, as spans.
+std::vector<Span> lora_spans(int B, int T, int D, const void *x, const void *shift,
+                             const void *mu_x, const void *lam, const void *A1, const void *B1,
+                             const void *omega, const void *A2, const void *B2, Span out) {
+    const int64_t tok = (int64_t)B * T * D, vec = (int64_t)D * 4;
+    return {Span{x, tok * 2},
+            Span{shift, (int64_t)B * D * 2},
+            Span{mu_x, vec},
+            Span{lam, vec},
+            Span{A1, (int64_t)D * kLoraR1 * 2},
+            Span{B1, (int64_t)D * kLoraR1 * 2},
+            Span{omega, vec},
+            Span{A2, (int64_t)D * kLoraR2 * 2},
+            Span{B2, (int64_t)D * kLoraR2 * 2},
+            out};
+}
+
 int matrix_step(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                 const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
-                float *state, rwkv_bf16 *o, void *stream) {
+                float *state, rwkv_bf16 *o, hipStream_t stream) {
     const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
     int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state, state, true, o);
     if (st != RWKV_OK) return st;
     if (T == 0) return RWKV_OK;
     return hip_status(wkv::launch_wkv_step(per_token, B, T, H, r, k, v, x, u, state, o,
-                                           (hipStream_t)stream));
+                                           stream));
 }
 
 int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                const float *state_in, const rwkv_bf16 *d_o, const float *d_state_out,
                rwkv_bf16 *d_r, rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
-               float *d_state_in, void *workspace, size_t workspace_bytes, void *stream,
+               float *d_state_in, void *workspace, size_t workspace_bytes, hipStream_t s,
                bool states_saved = false) {
     if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
     const int64_t tok = checked_mul({B, T, H, N});
@@ -193,7 +234,7 @@ int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                           (const void *)d_v, (const void *)d_x, (const void *)d_u,
                           (const void *)d_state_in, (const void *)workspace})
         if (p != nullptr && !aligned(p, 16)) return RWKV_E_ALIGN;
-    const size_t need = T > 0 ? wkv::wkv_bwd_workspace_bytes(B, T, H) : 0;
+    const size_t need = T > 0 ? wkv::bwd_workspace_bytes(B, T, H) : 0;
     if (T > 0 && workspace_bytes < need) return RWKV_E_DIM;
     const Span sr{r, tok * 2}, sk{k, tok * 2}, sv{v, tok * 2}, sx{x, x_elems * 4},
         su{u, hn * 4}, ssi{state_in, st * 4}, sdo{d_o, tok * 2}, sdso{d_state_out, st * 4},
@@ -202,7 +243,6 @@ int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
     const int chk = check_outputs({sdr, sdk, sdv, sdx, sdu, sdsi, sws},
                                   {sr, sk, sv, sx, su, ssi, sdo, sdso}, d_state_in, d_state_out);
     if (chk != RWKV_OK) return chk;
-    hipStream_t s = (hipStream_t)stream;
     if (T == 0) {  // no tokens: dS_0 = dS_T; the parameter gradients are zero
         hipError_t e = wkv::launch_fill(d_u, hn, 0.0f, s);
         if (e == hipSuccess && !per_token) e = wkv::launch_fill(d_x, hn, 0.0f, s);
@@ -222,16 +262,16 @@ int matrix_bwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
 int matrix_fwd_save(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
                     const rwkv_bf16 *k, const rwkv_bf16 *v, const float *x, const float *u,
                     const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+                    size_t workspace_bytes, hipStream_t s) {
     const int64_t x_elems = per_token ? checked_mul({B, T, H, N}) : checked_mul({H, N});
     int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
     if (st != RWKV_OK) return st;
     if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
     if (T == 0) return matrix_fwd(per_token, B, T, H, N, r, k, v, x, u, state_in, state_out, o,
-                                  stream);
+                                  nullptr, 0, s);
     if (workspace == nullptr) return RWKV_E_NULL;
     if (!aligned(workspace, 16)) return RWKV_E_ALIGN;
-    const size_t need = wkv::wkv_bwd_workspace_bytes(B, T, H);
+    const size_t need = wkv::bwd_workspace_bytes(B, T, H);
     if (workspace_bytes < need) return RWKV_E_DIM;
     const int64_t tok = checked_mul({B, T, H, N}), sts = checked_mul({B, H, N, N});
     const Span sws{workspace, (int64_t)need};
@@ -241,9 +281,9 @@ int matrix_fwd_save(bool per_token, int B, int T, int H, int N, const rwkv_bf16 
                         Span{state_in, sts * 4}},
                        state_out, state_in);
     if (st != RWKV_OK) return st;
+    float *states = (float *)((char *)workspace + wkv::bwd_states_offset(B, T, H));
     return hip_status(wkv::launch_wkv_chunked(per_token, B, T, H, r, k, v, x, u, state_in,
-                                              state_out, o, (hipStream_t)stream,
-                                              (float *)workspace));
+                                              state_out, o, workspace, s, states));
 }
 
 }  // namespace
@@ -266,16 +306,34 @@ const char *rwkv_wkv_strerror(int status) {
     }
 }
 
-int rwkv_wkv_device_status(void *stream) {
-    bool timed_out = false;
-    if (wkv::workspace_timed_out((hipStream_t)stream, &timed_out) != hipSuccess)
-        return RWKV_E_HIP;
-    return timed_out ? RWKV_E_TIMEOUT : RWKV_OK;
+int rwkv_wkv_workspace_status(void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (workspace == nullptr) return RWKV_E_NULL;
+    if (workspace_bytes < wkv::kWsCtrlBytes) return RWKV_E_DIM;
+    if (!aligned(workspace, 16)) return RWKV_E_ALIGN;
+    unsigned *word = (unsigned *)((char *)workspace + wkv::kWsErrOffset);
+    unsigned v = 0;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return RWKV_E_HIP;
+    if (v == 0) return RWKV_OK;
+    static const unsigned zero = 0;
+    e = hipMemcpyAsync(word, &zero, 4, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return e == hipSuccess ? RWKV_E_TIMEOUT : RWKV_E_HIP;
+}
+
+size_t rwkv4_wkv_fwd_workspace_bytes(int B, int T, int H, int N) {
+    if (B < 1 || T < 1 || H < 1 || N < 1) return 0;
+    const int64_t C = checked_mul({H, N});
+    if (C < 0 || C > kMaxRwkv4Channels || (int64_t)B * ((C + 31) / 32) > INT32_MAX) return 0;
+    return wkv::rwkv4_workspace_bytes(B, T, (int)C);
 }
 
 int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
                   const float *w, const float *u, const float *state_in,
-                  float *state_out, float *y, void *stream) {
+                  float *state_out, float *y, void *workspace, size_t workspace_bytes,
+                  hipStream_t s) {
     if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
     const int64_t C = checked_mul({H, N});
     const int64_t tok = checked_mul({B, T, H, N});
@@ -297,7 +355,6 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
     int chk = (T == 0) ? check_outputs({sso}, {ssi}, state_out, state_in)
                        : check_outputs({sy, sso}, {sk, sv, sw, su, ssi}, state_out, state_in);
     if (chk != RWKV_OK) return chk;
-    hipStream_t s = (hipStream_t)stream;
     if (T == 0) {
         if (state_out == nullptr || state_out == state_in) return RWKV_OK;
         if (state_in == nullptr)
@@ -305,12 +362,15 @@ int rwkv4_wkv_fwd(int B, int T, int H, int N, const float *k, const float *v,
         return hip_status(hipMemcpyAsync(state_out, state_in, st * 4,
                                          hipMemcpyDeviceToDevice, s));
     }
+    chk = check_workspace(workspace, workspace_bytes, wkv::rwkv4_workspace_bytes(B, T, (int)C),
+                          {sk, sv, sw, su, ssi, sso, sy});
+    if (chk != RWKV_OK) return chk;
     return hip_status(
-        wkv::launch_rwkv4(B, T, (int)C, k, v, w, u, state_in, state_out, y, s));
+        wkv::launch_rwkv4(B, T, (int)C, k, v, w, u, state_in, state_out, y, workspace, s));
 }
 
 int rwkv4_wkv_step(int B, int T, int H, int N, const float *k, const float *v,
-                   const float *w, const float *u, float *state, float *y, void *stream) {
+                   const float *w, const float *u, float *state, float *y, hipStream_t stream) {
     if (B < 1 || H < 1 || N < 1 || T < 0) return RWKV_E_DIM;
     const int64_t C = checked_mul({H, N});
     const int64_t tok = checked_mul({B, T, H, N});
@@ -331,50 +391,62 @@ int rwkv4_wkv_step(int B, int T, int H, int N, const float *k, const float *v,
     // state is read and written in place: it must not overlap the inputs or y
     const int chk = check_outputs({sy, ss}, {sk, sv, sw, su});
     if (chk != RWKV_OK) return chk;
-    return hip_status(wkv::launch_rwkv4_step(B, T, (int)C, k, v, w, u, state, y,
-                                             (hipStream_t)stream));
+    return hip_status(wkv::launch_rwkv4_step(B, T, (int)C, k, v, w, u, state, y, stream));
+}
+
+size_t rwkv_wkv_fwd_workspace_bytes(int B, int T, int H, int N) {
+    if (B < 1 || T < 1 || H < 1 || N != 64 || H > kMaxChunkedHeads ||
+        (int64_t)B * H > INT32_MAX)
+        return 0;
+    return wkv::chunk_workspace_bytes(B, T, H);
 }
 
 int rwkv5_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                   const rwkv_bf16 *v, const float *x, const float *u,
-                  const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
-    return matrix_fwd(false, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+                  const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    return matrix_fwd(false, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
+                      workspace_bytes, stream);
 }
 
 int rwkv6_wkv_fwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                   const rwkv_bf16 *v, const float *x, const float *u,
-                  const float *state_in, float *state_out, rwkv_bf16 *o, void *stream) {
-    return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, stream);
+                  const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
+                      workspace_bytes, stream);
 }
 
 int rwkv5_wkv_fwd_gated(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                         const rwkv_bf16 *v, const float *x, const float *u,
                         const float *state_in, float *state_out, const rwkv_bf16 *gate,
                         const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
-                        void *stream) {
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return matrix_fwd_gated(false, B, T, H, N, r, k, v, x, u, state_in, state_out, gate, ln_w,
-                            ln_b, eps, y, stream);
+                            ln_b, eps, y, workspace, workspace_bytes, stream);
 }
 
 int rwkv6_wkv_fwd_gated(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                         const rwkv_bf16 *v, const float *x, const float *u,
                         const float *state_in, float *state_out, const rwkv_bf16 *gate,
                         const float *ln_w, const float *ln_b, float eps, rwkv_bf16 *y,
-                        void *stream) {
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return matrix_fwd_gated(true, B, T, H, N, r, k, v, x, u, state_in, state_out, gate, ln_w,
-                            ln_b, eps, y, stream);
+                            ln_b, eps, y, workspace, workspace_bytes, stream);
 }
 
 size_t rwkv_wkv_bwd_workspace_bytes(int B, int T, int H, int N) {
-    if (B < 1 || T < 1 || H < 1 || N != 64) return 0;
-    return wkv::wkv_bwd_workspace_bytes(B, T, H);
+    if (B < 1 || T < 1 || H < 1 || N != 64 || H > kMaxChunkedHeads ||
+        (int64_t)B * H > INT32_MAX)
+        return 0;
+    return wkv::bwd_workspace_bytes(B, T, H);
 }
 
 int rwkv5_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                   const rwkv_bf16 *v, const float *x, const float *u, const float *state_in,
                   const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
                   rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u, float *d_state_in,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return matrix_bwd(false, B, T, H, N, r, k, v, x, u, state_in, d_o, d_state_out, d_r, d_k,
                       d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream);
 }
@@ -383,7 +455,7 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
                   const rwkv_bf16 *v, const float *x, const float *u, const float *state_in,
                   const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
                   rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u, float *d_state_in,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return matrix_bwd(true, B, T, H, N, r, k, v, x, u, state_in, d_o, d_state_out, d_r, d_k,
                       d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream);
 }
@@ -391,7 +463,7 @@ int rwkv6_wkv_bwd(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf1
 int rwkv5_wkv_fwd_save(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                        const rwkv_bf16 *v, const float *x, const float *u,
                        const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       size_t workspace_bytes, hipStream_t stream) {
     return matrix_fwd_save(false, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
                            workspace_bytes, stream);
 }
@@ -399,7 +471,7 @@ int rwkv5_wkv_fwd_save(int B, int T, int H, int N, const rwkv_bf16 *r, const rwk
 int rwkv6_wkv_fwd_save(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                        const rwkv_bf16 *v, const float *x, const float *u,
                        const float *state_in, float *state_out, rwkv_bf16 *o, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       size_t workspace_bytes, hipStream_t stream) {
     return matrix_fwd_save(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, workspace,
                            workspace_bytes, stream);
 }
@@ -409,7 +481,7 @@ int rwkv5_wkv_bwd_saved(int B, int T, int H, int N, const rwkv_bf16 *r, const rw
                         const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
                         rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
                         float *d_state_in, void *workspace, size_t workspace_bytes,
-                        void *stream) {
+                        hipStream_t stream) {
     return matrix_bwd(false, B, T, H, N, r, k, v, x, u, nullptr, d_o, d_state_out, d_r, d_k,
                       d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream, true);
 }
@@ -419,42 +491,59 @@ int rwkv6_wkv_bwd_saved(int B, int T, int H, int N, const rwkv_bf16 *r, const rw
                         const rwkv_bf16 *d_o, const float *d_state_out, rwkv_bf16 *d_r,
                         rwkv_bf16 *d_k, rwkv_bf16 *d_v, float *d_x, float *d_u,
                         float *d_state_in, void *workspace, size_t workspace_bytes,
-                        void *stream) {
+                        hipStream_t stream) {
     return matrix_bwd(true, B, T, H, N, r, k, v, x, u, nullptr, d_o, d_state_out, d_r, d_k,
                       d_v, d_x, d_u, d_state_in, workspace, workspace_bytes, stream, true);
 }
 
 int rwkv5_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                    const rwkv_bf16 *v, const float *x, const float *u, float *state,
-                   rwkv_bf16 *o, void *stream) {
+                   rwkv_bf16 *o, hipStream_t stream) {
     return matrix_step(false, B, T, H, N, r, k, v, x, u, state, o, stream);
 }
 
 int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
                    const rwkv_bf16 *v, const float *x, const float *u, float *state,
-                   rwkv_bf16 *o, void *stream) {
+                   rwkv_bf16 *o, hipStream_t stream) {
     return matrix_step(true, B, T, H, N, r, k, v, x, u, state, o, stream);
+}
+
+size_t rwkv6_decay_lora_workspace_bytes(int B, int T, int D) {
+    if (B < 1 || T < 1 || D < 64 || D % 64 != 0 || D / 64 > 65535 ||
+        (int64_t)B * T >= ((int64_t)1 << 31))
+        return 0;
+    return wkv::lora_workspace_bytes(B, T);
 }
 
 int rwkv6_decay_lora(int B, int T, int D, int act, const rwkv_bf16 *x, const rwkv_bf16 *shift,
                      const float *mu_x, const float *lam, const rwkv_bf16 *A1,
                      const rwkv_bf16 *B1, const float *omega, const rwkv_bf16 *A2,
-                     const rwkv_bf16 *B2, float *d, void *stream) {
+                     const rwkv_bf16 *B2, float *d, void *workspace, size_t workspace_bytes,
+                     hipStream_t s) {
     const int64_t tok = checked_mul({B, T, D});
     if (T > 0 && d == nullptr) return RWKV_E_NULL;
     if (d != nullptr && !aligned(d, 16)) return RWKV_E_ALIGN;
     int st = check_lora(B, T, D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2,
                         Span{d, tok * 4});
     if (st != RWKV_OK || T == 0) return st;
-    hipStream_t s = (hipStream_t)stream;
+    st = check_workspace(workspace, workspace_bytes, wkv::lora_workspace_bytes(B, T),
+                         lora_spans(B, T, D, x, shift, mu_x, lam, A1, B1, omega, A2, B2,
+                                    Span{d, tok * 4}));
+    if (st != RWKV_OK) return st;
     const int rows = B * T;
-    uint16_t *h = nullptr;
-    hipError_t e = wkv::stream_workspace(wkv::kWsDecayH, s, (size_t)rows * kLoraR2 * 2,
-                                         (void **)&h);
-    if (e != hipSuccess) return RWKV_E_HIP;
-    e = wkv::launch_decay_lora(rows, T, D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    uint16_t *h = (uint16_t *)workspace;
+    hipError_t e =
+        wkv::launch_decay_lora(rows, T, D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
     if (e != hipSuccess) return RWKV_E_HIP;
     return hip_status(wkv::launch_lora_logits(rows, D, h, B2, omega, d, s));
+}
+
+size_t rwkv6_wkv_fwd_lora_workspace_bytes(int B, int T, int H, int N) {
+    if (B < 1 || T < 1 || H < 1 || N != 64 || H > kMaxChunkedHeads ||
+        (int64_t)B * H > INT32_MAX || (int64_t)H * N / 64 > 65535 ||
+        (int64_t)B * T >= ((int64_t)1 << 31))
+        return 0;
+    return wkv::lora_fwd_workspace_bytes(B, T, H);
 }
 
 int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
@@ -462,15 +551,17 @@ int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwk
                        const float *mu_x, const float *lam, const rwkv_bf16 *A1,
                        const rwkv_bf16 *B1, const float *omega, const rwkv_bf16 *A2,
                        const rwkv_bf16 *B2, int act, const float *u, const float *state_in,
-                       float *state_out, rwkv_bf16 *o, void *stream) {
+                       float *state_out, rwkv_bf16 *o, void *workspace, size_t workspace_bytes,
+                       hipStream_t s) {
     // the WKV's own arguments (u stands in for the logits, which are formed
     // on the device), then the producer's against both outputs
     int st = check_matrix(B, T, H, N, r, k, v, u, checked_mul({H, N}), u, state_in, state_out,
                           false, o);
     if (st != RWKV_OK) return st;
-    if (H > kMaxChunkedHeads) return RWKV_E_UNSUPPORTED;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
     const int64_t D = (int64_t)H * N, tok = checked_mul({B, T, H, N});
-    const Span so{o, tok * 2}, sso{state_out, checked_mul({B, H, N, N}) * 4};
+    const int64_t sts = checked_mul({B, H, N, N});
+    const Span so{o, tok * 2}, sso{state_out, sts * 4};
     st = check_lora(B, T, (int)D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2, so);
     if (st != RWKV_OK) return st;
     if (T > 0) {
@@ -478,18 +569,22 @@ int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwk
         if (st != RWKV_OK) return st;
     }
     if (T == 0)
-        return matrix_fwd(true, B, T, H, N, r, k, v, u, u, state_in, state_out, o, stream);
-    hipStream_t s = (hipStream_t)stream;
+        return matrix_fwd(true, B, T, H, N, r, k, v, u, u, state_in, state_out, o, nullptr, 0, s);
+    std::vector<Span> spans =
+        lora_spans(B, T, (int)D, x, shift, mu_x, lam, A1, B1, omega, A2, B2, so);
+    spans.insert(spans.end(), {sso, Span{r, tok * 2}, Span{k, tok * 2}, Span{v, tok * 2},
+                               Span{u, (int64_t)H * N * 4}, Span{state_in, sts * 4}});
+    st = check_workspace(workspace, workspace_bytes, wkv::lora_fwd_workspace_bytes(B, T, H),
+                         spans);
+    if (st != RWKV_OK) return st;
     const int rows = B * T;
-    uint16_t *h = nullptr;
-    hipError_t e = wkv::stream_workspace(wkv::kWsDecayH, s, (size_t)rows * kLoraR2 * 2,
-                                         (void **)&h);
-    if (e != hipSuccess) return RWKV_E_HIP;
-    e = wkv::launch_decay_lora(rows, T, (int)D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    uint16_t *h = (uint16_t *)((char *)workspace + wkv::lora_fwd_factor_offset(B, T, H));
+    hipError_t e =
+        wkv::launch_decay_lora(rows, T, (int)D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
     if (e != hipSuccess) return RWKV_E_HIP;
     return hip_status(wkv::launch_wkv_chunked(true, B, T, H, r, k, v, nullptr, u, state_in,
-                                              state_out, o, s, nullptr, nullptr, nullptr,
-                                              nullptr, 0.0f, h, B2, omega));
+                                              state_out, o, workspace, s, nullptr, nullptr,
+                                              nullptr, nullptr, 0.0f, h, B2, omega));
 }
 
 }  // extern "C"
@@ -497,78 +592,35 @@ int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwk
 namespace wkv {
 
 namespace {
-struct Workspace {
-    void *p = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::tuple<int, int, hipStream_t>, Workspace> g_ws;
+// Per-device attribute cache (the library's only state).
+int device_attr(hipDeviceAttribute_t attr, int fallback, int (&cache)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+    int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess || n <= 0) n = fallback;
+        __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+int g_cus[64], g_xcds[64];
 }  // namespace
 
-hipError_t stream_workspace(int kind, hipStream_t stream, size_t bytes, void **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &ws = g_ws[std::make_tuple(kind, dev, stream)];
-    if (ws.bytes < bytes) {
-        if (ws.p != nullptr) {
-            if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-            if ((e = hipFree(ws.p)) != hipSuccess) return e;
-            ws.p = nullptr;
-            ws.bytes = 0;
-        }
-        const size_t n = (bytes + 255) / 256 * 256;
-        if ((e = hipMalloc(&ws.p, n)) != hipSuccess) return e;
-        if ((e = launch_fill((float *)ws.p, (int64_t)(n / 4), 0.0f, stream)) != hipSuccess)
-            return e;
-        ws.bytes = n;
-    }
-    *out = ws.p;
-    return hipSuccess;
+int device_cus() { return device_attr(hipDeviceAttributeMultiprocessorCount, 256, g_cus); }
+
+// (1 when the runtime cannot say: the segments of a split then need no
+// particular placement to stay on one die)
+int device_xcds() { return device_attr(hipDeviceAttributeNumberOfXccs, 1, g_xcds); }
+
+size_t lora_workspace_bytes(int B, int T) { return (size_t)B * T * 64 * 2; }
+
+// (after the chunked forward's hand-off area, and at least its control block)
+size_t lora_fwd_factor_offset(int B, int T, int H) {
+    return (std::max(kWsCtrlBytes, chunk_workspace_bytes(B, T, H)) + 255) / 256 * 256;
 }
 
-hipError_t workspace_timed_out(hipStream_t stream, bool *timed_out) {
-    *timed_out = false;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    for (int kind = 0; kind < (int)(sizeof(kWsErrorWord) / sizeof(kWsErrorWord[0])); ++kind) {
-        const long off = kWsErrorWord[kind];
-        if (off < 0) continue;
-        auto it = g_ws.find(std::make_tuple(kind, dev, stream));
-        if (it == g_ws.end() || it->second.bytes < (size_t)off + 4) continue;
-        unsigned *word = (unsigned *)((char *)it->second.p + off);
-        unsigned v = 0;
-        if ((e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-            (e = hipStreamSynchronize(stream)) != hipSuccess)
-            return e;
-        if (v == 0) continue;
-        *timed_out = true;
-        // A late producer may have raised a flag that no consumer cleared:
-        // back to the zero-filled state the workspace started in.
-        if ((e = launch_fill((float *)it->second.p, (int64_t)(it->second.bytes / 4), 0.0f,
-                             stream)) != hipSuccess ||
-            (e = hipStreamSynchronize(stream)) != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
-}
-
-int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
+size_t lora_fwd_workspace_bytes(int B, int T, int H) {
+    return lora_fwd_factor_offset(B, T, H) + lora_workspace_bytes(B, T);
 }
 
 }  // namespace wkv

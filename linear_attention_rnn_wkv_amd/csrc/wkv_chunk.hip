@@ -58,6 +58,7 @@
 // without leaving registers.  The transposing load: in each group of 16
 // lanes, lane j supplies the address of 4 consecutive elements of row j/4 of
 // a 4 x 16 block and receives column j of that block (rows 0..3).
+#include <algorithm>
 #include <type_traits>
 
 #include "launchers.h"
@@ -78,10 +79,11 @@ __device__ constexpr int pitch(int t) { return (t == T_RS || t == T_ST) ? kPR : 
 // (nfull + 1) workgroups, each of which first runs nfull whole heads (see the
 // kernel); extra == 0: one head per workgroup.
 struct Split {
-    int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    int extra, first_extra, K, stride, chains_per_xcd;
     int nfull;        // whole heads per workgroup before the split round
+    WsCtrl *ctrl;     // control block of the hand-off workspace (epoch, error word)
+    unsigned *flags;  // [extra * (K - 1)] slot flags: the launch's tag once a slot is full
     float *slots;     // [extra * (K - 1)][64][64] states between segments
-    unsigned *flags;  // [max_slots] slot flags, then an error word
     float *park;      // [workgroups][64][64] own heads' states during the extra segment
                       // (four-wave launches; eight waves keep them in registers)
 };
@@ -983,40 +985,43 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         a = seg * nchunks / sp.K;
         e1 = (seg + 1) * nchunks / sp.K;
     }
-    auto ld = [](const void *ptr) {
-        return __hip_atomic_load((unsigned *)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto st = [](void *ptr, unsigned val) {
-        __hip_atomic_store((unsigned *)ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
+    auto ld = [](const void *ptr) { return ld_agent((const unsigned *)ptr); };
+    auto st = [](void *ptr, unsigned val) { st_agent((unsigned *)ptr, val); };
+    // the launch's tag (thread 0 alone polls and raises the flags)
+    const unsigned tag = (sp.extra != 0 && tid == 0) ? ws_tag(sp.ctrl) : 0u;
+    __shared__ int s_late;
     // the state entering segment seg, from the workgroup that ran seg - 1.
-    // Slots and flags are touched only by agent-scope relaxed atomics, which
-    // act at the device's coherence point: the producer's stores complete
-    // before its flag store, and the state is read only after the flag was
-    // seen.  The consumer clears the flag for the next launch.  Polls are
-    // bounded (about a second): the producer has a lower workgroup index on
-    // the same XCD, so it is already running.
+    // Slots and flags are touched only by agent-scope relaxed atomics: the
+    // producer's state stores complete before its flag store, and the state
+    // is read only after the flag shows this launch's tag.  Polls are
+    // bounded (about a second); the producer has a lower workgroup index on
+    // the same XCD, so it is already running and the bound is never reached.
+    // If it were, the segment would go on from a NaN state (its outputs and
+    // the head's final state read NaN) and the error word is set.
     auto receive = [&]() {
         const int slot = ext * (sp.K - 1) + seg - 1;
         const float *src = sp.slots + (size_t)slot * kN * kN;
         if (tid == 0) {
-            int polls = 0;
-            while (ld(sp.flags + slot) == 0u) {
+            int polls = 0, late = 0;
+            while (ld(sp.flags + slot) != tag) {
                 __builtin_amdgcn_s_sleep(8);
                 if (++polls > (1 << 20)) {
-                    st(sp.flags + sp.max_slots, 1u);  // error word
+                    ws_fail(sp.ctrl);
+                    late = 1;
                     break;
                 }
             }
+            s_late = late;
         }
         lds_barrier();
+        const bool late = s_late != 0;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[t][e] = __uint_as_float(ld(src + sidx(t, e)));
+            for (int e = 0; e < 4; ++e)
+                S[t][e] = late ? __builtin_nanf("") : __uint_as_float(ld(src + sidx(t, e)));
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
         lds_barrier();
-        if (tid == 0) st(sp.flags + slot, 0u);
     };
     auto send = [&]() {
         const int slot = ext * (sp.K - 1) + seg;
@@ -1027,7 +1032,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             for (int e = 0; e < 4; ++e) st(dst + sidx(t, e), __float_as_uint(S[t][e]));
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
         lds_barrier();
-        if (tid == 0) st(sp.flags + slot, 1u);
+        if (tid == 0) st(sp.flags + slot, tag);
     };
     f32x4 Sown[DB ? NT : 1];  // own head's state while the extra segment runs
     const int njobs = sp.nfull + (split ? 3 : 1);
@@ -1071,6 +1076,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             save_state();
         }
     }
+    if (sp.extra != 0 && tid == 0) ws_finish(sp.ctrl, tag);
 }
 
 template <bool PT, int NW, bool SAVE = false, bool EPI = false, bool LORA = false>
@@ -1084,66 +1090,92 @@ void launch(int blocks, int T, int H, const uint16_t *r, const uint16_t *k, cons
                        sp, chunk_states, gate, ln_w, ln_b, eps, lr);
 }
 
-// XCDs of the device: workgroups are dealt to them round-robin
-constexpr int kXcds = 8;
-constexpr int kMaxSlots = 4096;
+constexpr int kMaxSlots = 4096;  // hand-offs of one launch
 constexpr int kMaxSegs = 16;     // segments per extra head
-static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsChunkHandoff], "error word after the slot flags");
+
+// How the heads of a launch are spread over workgroups (see the kernel).
+struct Plan {
+    bool wide;                  // eight waves per workgroup (else four)
+    int blocks;                 // workgroups
+    int64_t extra, nfull, first, K, chains_per_xcd;
+    size_t slot_bytes, park_bytes;  // hand-off slots, parked own states
+};
+
+// Eight waves per head while every head has a CU of its own.  With up to half
+// as many heads again, eight waves and the balanced split: one workgroup per
+// CU, each running one head plus one K-th of an extra head.  Beyond that,
+// four waves so that two heads share a CU, and past two heads per CU the same
+// split over the 2 x CUs workgroups.  The segments of an extra head must sit
+// on one XCD, so the split needs the CU count to be a multiple of the XCDs.
+Plan plan(int64_t heads, int T) {
+    const int cus = device_cus(), xcds = device_xcds();
+    Plan p{};
+    p.wide = heads <= cus;
+    p.blocks = (int)heads;
+    // (slots workgroups: whole heads in rounds, then the remainder split)
+    auto split = [&](int64_t slots) {
+        const int64_t nfull = heads / slots - 1, extra = heads % slots;
+        if (extra == 0) return false;
+        const int64_t chains_per_xcd = (extra + xcds - 1) / xcds;
+        // (at most kMaxSegs segments: each hand-off adds its latency to the
+        // chain of an extra head's segments)
+        const int64_t K = std::min<int64_t>((slots / xcds) / chains_per_xcd, kMaxSegs);
+        if (K < 2 || extra * (K - 1) > kMaxSlots) return false;
+        p.extra = extra;
+        p.nfull = nfull;
+        p.first = (nfull + 1) * slots;
+        p.K = K;
+        p.chains_per_xcd = chains_per_xcd;
+        p.slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
+        p.park_bytes = slots > cus ? (size_t)slots * kN * kN * 4 : 0;
+        p.blocks = (int)slots;
+        return true;
+    };
+    if (!p.wide && xcds > 0 && cus % xcds == 0 && T >= 4 * kL) {
+        if (heads < 2 * (int64_t)cus && split(cus)) p.wide = true;
+        else if (heads > 2 * (int64_t)cus) split(2 * (int64_t)cus);
+    }
+    return p;
+}
+
+constexpr size_t kFlagBytes = (size_t)kMaxSlots * 4;
+
+size_t handoff_bytes(const Plan &p) {
+    return p.extra ? kWsCtrlBytes + kFlagBytes + p.slot_bytes + p.park_bytes : 0;
+}
 
 }  // namespace
+
+size_t chunk_workspace_bytes(int B, int T, int H) {
+    return handoff_bytes(plan((int64_t)B * H, T));
+}
 
 hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H, const uint16_t *r,
                               const uint16_t *k, const uint16_t *v, const float *x,
                               const float *u, const float *state_in, float *state_out,
-                              uint16_t *o, hipStream_t stream, float *chunk_states,
+                              uint16_t *o, void *ws, hipStream_t stream, float *chunk_states,
                               const uint16_t *gate, const float *ln_w, const float *ln_b,
                               float eps, const uint16_t *lora_h, const uint16_t *lora_B2,
                               const float *lora_omega) {
-    // Eight waves per head while every head has a CU of its own.  With up to
-    // half as many heads again, eight waves and the balanced split: one
-    // workgroup per CU, each running one head plus one K-th of an extra
-    // head.  Beyond that, four waves so that two heads share a CU, and past
-    // two heads per CU the same split over the 2 x CUs workgroups.
-    const int64_t heads = (int64_t)B * H;
-    const int cus = device_cus();
+    const Plan p = plan((int64_t)B * H, T);
     Split sp{};
-    bool wide = heads <= cus;
-    // (slots workgroups: whole heads in rounds, then the remainder split)
-    auto split = [&](int64_t slots) -> hipError_t {
-        const int64_t nfull = heads / slots - 1, extra = heads % slots;
-        if (extra == 0) return hipSuccess;
-        const int64_t first = (nfull + 1) * slots;
-        const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        // (at most kMaxSegs segments: each hand-off adds its latency to the
-        // chain of an extra head's segments)
-        const int64_t K = std::min<int64_t>((slots / kXcds) / chains_per_xcd, kMaxSegs);
-        if (K < 2 || extra * (K - 1) > kMaxSlots) return hipSuccess;
-        const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
-        const size_t slot_bytes = (size_t)extra * (K - 1) * kN * kN * 4;
-        const size_t park_bytes = slots > cus ? (size_t)slots * kN * kN * 4 : 0;
-        char *ws = nullptr;
-        hipError_t e = stream_workspace(kWsChunkHandoff, stream,
-                                        flag_bytes + slot_bytes + park_bytes, (void **)&ws);
-        if (e != hipSuccess) return e;
-        sp.extra = (int)extra;
-        sp.nfull = (int)nfull;
-        sp.first_extra = (int)first;
-        sp.K = (int)K;
-        sp.stride = kXcds;
-        sp.chains_per_xcd = (int)chains_per_xcd;
-        sp.max_slots = kMaxSlots;
-        sp.flags = (unsigned *)ws;
-        sp.slots = (float *)(ws + flag_bytes);
-        sp.park = park_bytes ? (float *)(ws + flag_bytes + slot_bytes) : nullptr;
-        return hipSuccess;
-    };
-    if (!wide && cus % kXcds == 0 && T >= 4 * kL) {
-        hipError_t e = heads < 2 * (int64_t)cus ? split(cus) : hipSuccess;
-        if (e != hipSuccess) return e;
-        if (sp.extra != 0) wide = true;
-        else if (heads > 2 * (int64_t)cus && (e = split(2 * (int64_t)cus)) != hipSuccess) return e;
+    if (p.extra != 0) {
+        if (ws == nullptr) return hipErrorInvalidValue;  // (the entry points check the size)
+        char *base = (char *)ws;
+        sp.extra = (int)p.extra;
+        sp.nfull = (int)p.nfull;
+        sp.first_extra = (int)p.first;
+        sp.K = (int)p.K;
+        sp.stride = device_xcds();
+        sp.chains_per_xcd = (int)p.chains_per_xcd;
+        sp.ctrl = (WsCtrl *)base;
+        sp.flags = (unsigned *)(base + kWsCtrlBytes);
+        sp.slots = (float *)(base + kWsCtrlBytes + kFlagBytes);
+        sp.park = p.park_bytes ? (float *)(base + kWsCtrlBytes + kFlagBytes + p.slot_bytes)
+                               : nullptr;
     }
-    const int blocks = (int)(sp.extra ? sp.first_extra / (sp.nfull + 1) : heads);
+    const bool wide = p.wide;
+    const int blocks = p.blocks;
     // plain forward; the forward that also stores the state entering every
     // chunk (SAVE: the backward's recomputation, or a forward kept for the
     // backward); the forward with the output epilogue (EPI)
@@ -1177,10 +1209,10 @@ hipError_t launch_wkv_chunked_gated(bool per_token_decay, int B, int T, int H,
                                     const uint16_t *r, const uint16_t *k, const uint16_t *v,
                                     const float *x, const float *u, const float *state_in,
                                     float *state_out, const uint16_t *gate, const float *ln_w,
-                                    const float *ln_b, float eps, uint16_t *y,
+                                    const float *ln_b, float eps, uint16_t *y, void *ws,
                                     hipStream_t stream) {
     return launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in, state_out, y,
-                              stream, nullptr, gate, ln_w, ln_b, eps);
+                              ws, stream, nullptr, gate, ln_w, ln_b, eps);
 }
 
 }  // namespace wkv

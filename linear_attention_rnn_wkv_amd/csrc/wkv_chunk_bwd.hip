@@ -38,6 +38,7 @@
 // factors and the bonus terms and run the decay-gradient scan.  A chunk
 // whose decay falls below the factorised range (as in the forward) is taken
 // token by token on the VALU, with the states inside it recomputed from S_c.
+#include <algorithm>
 #include <type_traits>
 
 #include "launchers.h"
@@ -52,10 +53,8 @@ using namespace tiles;
 constexpr int NW = 8;            // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * NW;
 constexpr int kTW = 4;           // waves that take a fast-decay chunk token by token
-constexpr int kXcds = 8;         // XCDs of the device: workgroups are dealt to them round-robin
 constexpr int kMaxSlots = 4096;  // hand-off slots of the balanced split
 constexpr int kMaxSegs = 16;     // segments per extra head
-static_assert((long)kMaxSlots * 4 == kWsErrorWord[kWsBwdSplit], "error word after the slot flags");
 constexpr int TP = 16 / NW;      // tokens per staging thread
 constexpr int kSF = 24;          // floats of the sweep's state per thread
 constexpr int kPF = 68;          // pitch (floats) of the fp32 gradient tiles
@@ -94,11 +93,12 @@ __device__ __forceinline__ u32x2 lo4(const f32x4 &a, u32x2 hi) {
 // sums) goes between segments through `slots`, and the own head's waits in
 // `park` meanwhile, kSF floats per thread.
 struct BwdSplit {
-    int extra, first_extra, K, stride, chains_per_xcd, max_slots;
+    int extra, first_extra, K, stride, chains_per_xcd;
     int nfull;        // whole heads per workgroup before the split round
+    WsCtrl *ctrl;     // control block of the hand-off workspace (epoch, error word)
+    unsigned *flags;  // [extra * (K - 1)] slot flags: the launch's tag once a slot is full
     float *slots;     // [extra * (K - 1)][kThreads][kSF]
     float *park;      // [workgroups][kThreads][kSF]
-    unsigned *flags;  // [max_slots] slot flags, then an error word
 };
 
 template <bool PT>
@@ -219,15 +219,15 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
                 dst[i] = v[i];
         }
     };
-    auto get_state = [&](const float *p, bool shared) {
+    // (poison: the hand-off never came; continue from NaN)
+    auto get_state = [&](const float *p, bool shared, bool poison = false) {
         float v[kSF];
         const float *src = p + (size_t)tid * kSF;
 #pragma unroll
         for (int i = 0; i < kSF; ++i)
-            v[i] = shared ? __uint_as_float(__hip_atomic_load((const unsigned *)(src + i),
-                                                              __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT))
-                          : src[i];
+            v[i] = poison   ? __builtin_nanf("")
+                   : shared ? __uint_as_float(ld_agent((const unsigned *)(src + i)))
+                            : src[i];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -828,35 +828,40 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
     // Split: own head chunks [e0, n) (then parked), the extra head's chunks
     // [e1, e0), own head chunks [0, e0).  Slot flags and contents go through
     // agent-scope relaxed atomics, which act at the device's coherence point:
-    // the producer's stores complete before its flag store, the consumer
-    // clears the flag for the next launch.  Polls are bounded (about a
-    // second); the producer has a lower workgroup index on the same XCD, so
-    // it is already running.  One loop, so that the sweep is compiled once.
+    // the producer's stores complete before its flag store (the launch's
+    // tag), and the consumer reads the state only after it saw that tag.
+    // Polls are bounded (about a second); the producer has a lower workgroup
+    // index on the same XCD, so it is already running and the bound is never
+    // reached.  If it were, the segment would go on from a NaN state (its
+    // gradients read NaN) and the error word is set.  One loop, so that the
+    // sweep is compiled once.
+    const unsigned tag = (sp.extra != 0 && tid == 0) ? ws_tag(sp.ctrl) : 0u;
+    __shared__ int s_late;
     auto receive = [&]() {
         const int slot = ext * (sp.K - 1) + seg - 1;
         if (tid == 0) {
-            int polls = 0;
-            while (__hip_atomic_load(sp.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            int polls = 0, late = 0;
+            while (ld_agent(sp.flags + slot) != tag) {
                 __builtin_amdgcn_s_sleep(8);
                 if (++polls > (1 << 20)) {
-                    __hip_atomic_store(sp.flags + sp.max_slots, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);  // error word
+                    ws_fail(sp.ctrl);
+                    late = 1;
                     break;
                 }
             }
+            s_late = late;
         }
         lds_barrier();
-        get_state(sp.slots + (size_t)slot * kThreads * kSF, true);
+        get_state(sp.slots + (size_t)slot * kThreads * kSF, true, s_late != 0);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has been read
         lds_barrier();
-        if (tid == 0) __hip_atomic_store(sp.flags + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto send = [&]() {
         const int slot = ext * (sp.K - 1) + seg;
         put_state(sp.slots + (size_t)slot * kThreads * kSF, true);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
         lds_barrier();
-        if (tid == 0) __hip_atomic_store(sp.flags + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) st_agent(sp.flags + slot, tag);
     };
     const int njobs = sp.nfull + (split ? 3 : 1);
 #pragma clang loop unroll(disable)
@@ -883,6 +888,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
         else if (extra && seg + 1 < sp.K) send();
         else finish();
     }
+    if (sp.extra != 0 && tid == 0) ws_finish(sp.ctrl, tag);
 }
 
 // out[h][i] = sum over b of part[b][h][i], in sequence order
@@ -894,64 +900,98 @@ __global__ void sum_over_batch_kernel(int B, int HN, const float *part, float *o
     out[i] = s;
 }
 
+// The balanced split of the reverse sweep (see the kernel), or none.
+struct BwdPlan {
+    int blocks;
+    int64_t extra, nfull, K, chains_per_xcd;
+    size_t slot_bytes, park_bytes;
+};
+
+// One workgroup per head while every head has a CU of its own.  Beyond that,
+// one workgroup per CU: whole heads in rounds, and the last round's
+// remainder, when it is at most half the CUs, as the balanced split (each
+// workgroup sweeps its own head and one segment of an extra head).
+// Otherwise the heads in rounds.
+BwdPlan bwd_plan(int64_t heads, int T) {
+    const int cus = device_cus(), xcds = device_xcds();
+    BwdPlan p{};
+    p.blocks = (int)heads;
+    if (heads > cus && heads % cus != 0 && xcds > 0 && cus % xcds == 0 && T >= 4 * kL) {
+        const int64_t extra = heads % cus, nfull = heads / cus - 1;
+        const int64_t chains_per_xcd = (extra + xcds - 1) / xcds;
+        // (at most kMaxSegs segments: each hand-off adds its latency to the
+        // chain of an extra head's segments)
+        const int64_t K = std::min<int64_t>((cus / xcds) / chains_per_xcd, kMaxSegs);
+        if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
+            const size_t per = (size_t)kThreads * kSF * 4;  // one sweep state
+            p.extra = extra;
+            p.nfull = nfull;
+            p.K = K;
+            p.chains_per_xcd = chains_per_xcd;
+            p.slot_bytes = (size_t)extra * (K - 1) * per;
+            p.park_bytes = (size_t)cus * per;
+            p.blocks = cus;
+        }
+    }
+    return p;
+}
+
+constexpr size_t kFlagBytes = (size_t)kMaxSlots * 4;
+
+size_t bwd_handoff_bytes(const BwdPlan &p) {
+    return p.extra ? kWsCtrlBytes + kFlagBytes + p.slot_bytes + p.park_bytes : 0;
+}
+
 }  // namespace
 
-size_t wkv_bwd_workspace_bytes(int B, int T, int H) {
+// Layout of the backward's workspace: the hand-off area that both the
+// state recomputation (a chunked forward) and the reverse sweep use, one
+// after the other (at least the control block, so that the workspace's
+// error word is always where rwkv_wkv_workspace_status reads it), then the
+// chunk states, then the per-sequence partial sums of d_u and Eagle's d_x.
+size_t bwd_states_offset(int B, int T, int H) {
+    const size_t h = std::max({kWsCtrlBytes, chunk_workspace_bytes(B, T, H),
+                               bwd_handoff_bytes(bwd_plan((int64_t)B * H, T))});
+    return (h + 255) / 256 * 256;
+}
+
+size_t bwd_workspace_bytes(int B, int T, int H) {
     const size_t nchunks = (size_t)(T + kL - 1) / kL;
-    return (size_t)B * H * (nchunks + 1) * kN * kN * 4 + 2 * (size_t)B * H * kN * 4;
+    return bwd_states_offset(B, T, H) + (size_t)B * H * (nchunks + 1) * kN * kN * 4 +
+           2 * (size_t)B * H * kN * 4;
 }
 
 hipError_t launch_wkv_bwd(bool per_token_decay, int B, int T, int H, const uint16_t *r,
                           const uint16_t *k, const uint16_t *v, const float *x, const float *u,
                           const float *state_in, const uint16_t *d_o, const float *d_sT,
                           uint16_t *d_r, uint16_t *d_k, uint16_t *d_v, float *d_x, float *d_u,
-                          float *d_s0, void *workspace, hipStream_t stream, bool states_saved) {
+                          float *d_s0, void *ws, hipStream_t stream, bool states_saved) {
     const size_t nchunks = (size_t)(T + kL - 1) / kL;
-    float *chunk_states = (float *)workspace;
+    char *base = (char *)ws;
+    float *chunk_states = (float *)(base + bwd_states_offset(B, T, H));
     float *du_part = chunk_states + (size_t)B * H * (nchunks + 1) * kN * kN;
     float *dx_part = du_part + (size_t)B * H * kN;
     hipError_t e = hipSuccess;
     if (!states_saved) {  // (else a forward stored them there)
         e = launch_wkv_chunked(per_token_decay, B, T, H, r, k, v, x, u, state_in, nullptr,
-                               nullptr, stream, chunk_states);
+                               nullptr, ws, stream, chunk_states);
         if (e != hipSuccess) return e;
     }
-    // One workgroup per head while every head has a CU of its own.  Beyond
-    // that, one workgroup per CU: whole heads in rounds, and the last round's
-    // remainder, when it is at most half the CUs, as the balanced split (each
-    // workgroup sweeps its own head and one segment of an extra head).
-    // Otherwise the heads in rounds.
-    const int64_t heads = (int64_t)B * H;
-    const int cus = device_cus();
+    const BwdPlan p = bwd_plan((int64_t)B * H, T);
     BwdSplit sp{};
-    int blocks = (int)heads;
-    if (heads > cus && heads % cus != 0 && cus % kXcds == 0 && T >= 4 * kL) {
-        const int64_t extra = heads % cus, nfull = heads / cus - 1;
-        const int64_t chains_per_xcd = (extra + kXcds - 1) / kXcds;
-        // (at most kMaxSegs segments: each hand-off adds its latency to the
-        // chain of an extra head's segments)
-        const int64_t K = std::min<int64_t>((cus / kXcds) / chains_per_xcd, kMaxSegs);
-        if (K >= 2 && extra * (K - 1) <= kMaxSlots) {
-            const size_t per = (size_t)kThreads * kSF * 4;  // one sweep state
-            const size_t flag_bytes = (size_t)kMaxSlots * 4 + 256;
-            const size_t slot_bytes = (size_t)extra * (K - 1) * per;
-            char *ws = nullptr;
-            e = stream_workspace(kWsBwdSplit, stream, flag_bytes + slot_bytes + (size_t)cus * per,
-                                 (void **)&ws);
-            if (e != hipSuccess) return e;
-            sp.extra = (int)extra;
-            sp.nfull = (int)nfull;
-            sp.first_extra = (int)((nfull + 1) * cus);
-            sp.K = (int)K;
-            sp.stride = kXcds;
-            sp.chains_per_xcd = (int)chains_per_xcd;
-            sp.max_slots = kMaxSlots;
-            sp.flags = (unsigned *)ws;
-            sp.slots = (float *)(ws + flag_bytes);
-            sp.park = (float *)(ws + flag_bytes + slot_bytes);
-            blocks = cus;
-        }
+    if (p.extra != 0) {
+        sp.extra = (int)p.extra;
+        sp.nfull = (int)p.nfull;
+        sp.first_extra = (int)((p.nfull + 1) * p.blocks);
+        sp.K = (int)p.K;
+        sp.stride = device_xcds();
+        sp.chains_per_xcd = (int)p.chains_per_xcd;
+        sp.ctrl = (WsCtrl *)base;
+        sp.flags = (unsigned *)(base + kWsCtrlBytes);
+        sp.slots = (float *)(base + kWsCtrlBytes + kFlagBytes);
+        sp.park = (float *)(base + kWsCtrlBytes + kFlagBytes + p.slot_bytes);
     }
+    const int blocks = p.blocks;
     if (per_token_decay)
         hipLaunchKernelGGL(wkv_bwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T,
                            H, r, k, v, x, u, d_o, d_sT, chunk_states, d_r, d_k, d_v, d_x, du_part,

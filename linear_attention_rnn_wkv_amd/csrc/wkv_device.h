@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launchers.h"
+
 namespace wkv {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -49,6 +51,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // fp32 rounded to bf16 and widened back (exact value of the rounded number).
 __device__ __forceinline__ float round_bf16(float f) {
     return bf16_lo(pack_bf16x2(f, 0.0f));
+}
+
+// Hand-off words between workgroups are only accessed with agent-scope
+// relaxed atomics: they act at the device's coherence point, so a word one
+// workgroup stores is seen by another without cache write-back or
+// invalidation.
+__device__ __forceinline__ unsigned ld_agent(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned *p, unsigned val) {
+    __hip_atomic_store(p, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The launch's hand-off tag: the epoch of the control block + 1 (never 0, so
+// a zero-filled word is never valid).  Read by every workgroup that takes
+// part, before any of them calls ws_finish.
+__device__ __forceinline__ unsigned ws_tag(WsCtrl *c) { return ld_agent(&c->epoch.n) + 1u; }
+
+// One thread of every workgroup of the launch, after its last hand-off: the
+// last one resets the count and advances the epoch to the launch's tag, which
+// makes every word the launch wrote stale for the next one.
+__device__ __forceinline__ void ws_finish(WsCtrl *c, unsigned tag) {
+    const unsigned n =
+        __hip_atomic_fetch_add(&c->done.n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n + 1u == gridDim.x) {
+        st_agent(&c->done.n, 0u);
+        st_agent(&c->epoch.n, tag == 0xffffffffu ? 0u : tag);
+    }
+}
+
+// A bounded wait gave up: record it in the control block.
+__device__ __forceinline__ void ws_fail(WsCtrl *c) {
+    __hip_atomic_fetch_or(&c->err.n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace wkv

@@ -61,3 +61,42 @@ def matrix_inputs_f32(d):
     """The exact fp32 values the GPU sees, for the oracle."""
     return (S.bf16_to_f32(d["r"]), S.bf16_to_f32(d["k"]), S.bf16_to_f32(d["v"]),
             d["x"], d["u"], d["s0"])
+
+
+def assert_heads_close(got, ref, axes, what):
+    """The bf16 tolerances applied to every (sequence, head) on its own:
+    `axes` are the axes of one head's elements (tokens and channels of an
+    output [B, T, H, N]: (1, 3); a state [B, H, N, N]: (2, 3)).  Returns the
+    worst head's (rms_rel, max_rel, index)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    n = int(np.prod([ref.shape[a] for a in axes]))
+    diff = got - ref
+    nr = np.sqrt(np.sum(ref * ref, axis=axes, keepdims=True))
+    rms = nr / np.sqrt(n)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rms_rel = np.sqrt(np.sum(diff * diff, axis=axes, keepdims=True)) / nr
+        max_rel = np.max(np.abs(diff) / np.maximum(np.abs(ref), rms), axis=axes, keepdims=True)
+    # an all-zero reference head must come out exactly zero
+    zero = nr == 0
+    rms_rel = np.where(zero, np.sqrt(np.sum(diff * diff, axis=axes, keepdims=True)), rms_rel)
+    max_rel = np.where(zero, np.max(np.abs(diff), axis=axes, keepdims=True), max_rel)
+    rms_rel, max_rel = np.squeeze(rms_rel, axis=axes), np.squeeze(max_rel, axis=axes)
+    i = np.unravel_index(int(np.argmax(rms_rel)), rms_rel.shape)
+    j = np.unravel_index(int(np.argmax(max_rel)), max_rel.shape)
+    assert rms_rel[i] <= RMS_TOL, f"{what}: head {i} rms_rel {rms_rel[i]:.3e}"
+    assert max_rel[j] <= MAX_TOL, f"{what}: head {j} max_rel {max_rel[j]:.3e}"
+    return float(rms_rel[i]), float(max_rel[j]), tuple(int(a) for a in i)
+
+
+def ulp_diff(a, b):
+    """Distance between two fp32 arrays in units in the last place (0 where
+    bit-identical); signed zeros count as equal."""
+    ia = np.ascontiguousarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.ascontiguousarray(b, np.float32).view(np.int32).astype(np.int64)
+    # map the sign-magnitude bits onto a monotonic integer line
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)

@@ -55,18 +55,24 @@ def addr(i, misalign=0):
     return ctypes.c_void_p(BASE + i * SPAN + misalign)
 
 
-def rwkv4(L, B=2, T=8, H=1, N=16, k=1, v=2, w=3, u=4, si=5, so=6, y=7, **mis):
+def rwkv4(L, B=2, T=8, H=1, N=16, k=1, v=2, w=3, u=4, si=5, so=6, y=7, ws=8, ws_bytes=None,
+          **mis):
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
-         for n, i in dict(k=k, v=v, w=w, u=u, si=si, so=so, y=y).items()}
+         for n, i in dict(k=k, v=v, w=w, u=u, si=si, so=so, y=y, ws=ws).items()}
+    if ws_bytes is None:
+        ws_bytes = L.rwkv4_wkv_fwd_workspace_bytes(B, T, H, N)
     return L.rwkv4_wkv_fwd(B, T, H, N, a["k"], a["v"], a["w"], a["u"], a["si"], a["so"],
-                           a["y"], None)
+                           a["y"], a["ws"], ws_bytes, None)
 
 
-def matrix(L, fn, B=2, T=8, H=2, N=64, r=1, k=2, v=3, x=4, u=5, si=6, so=7, o=8, **mis):
+def matrix(L, fn, B=2, T=8, H=2, N=64, r=1, k=2, v=3, x=4, u=5, si=6, so=7, o=8, ws=9,
+           ws_bytes=None, **mis):
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None)
-         for n, i in dict(r=r, k=k, v=v, x=x, u=u, si=si, so=so, o=o).items()}
+         for n, i in dict(r=r, k=k, v=v, x=x, u=u, si=si, so=so, o=o, ws=ws).items()}
+    if ws_bytes is None:
+        ws_bytes = L.rwkv_wkv_fwd_workspace_bytes(B, T, H, N)
     return getattr(L, fn)(B, T, H, N, a["r"], a["k"], a["v"], a["x"], a["u"], a["si"],
-                          a["so"], a["o"], None)
+                          a["so"], a["o"], a["ws"], ws_bytes, None)
 
 
 def step(L, B=2, T=1, H=2, N=64, r=1, k=2, v=3, x=4, u=5, s=6, o=7, fn="rwkv6_wkv_step",
@@ -104,7 +110,7 @@ def test_rwkv4_misaligned(L, which):
     kw = {"k": 1, "v": 2, "w": 3, "u": 4, "si": 5, "so": 6, "y": 7}
     a = {n: addr(i, 2 if n == which else 0) for n, i in kw.items()}
     st = L.rwkv4_wkv_fwd(2, 8, 1, 16, a["k"], a["v"], a["w"], a["u"], a["si"], a["so"],
-                         a["y"], None)
+                         a["y"], None, 0, None)
     assert st == E_ALIGN
 
 
@@ -123,7 +129,7 @@ def test_rwkv4_state_partial_overlap(L):
     si = ctypes.c_void_p(BASE + 5 * SPAN)
     so = ctypes.c_void_p(BASE + 5 * SPAN + 4)  # overlaps but is not equal
     assert L.rwkv4_wkv_fwd(2, 8, 1, 16, a["k"], a["v"], a["w"], a["u"], si, so,
-                           addr(7), None) == E_ALIAS
+                           addr(7), None, 0, None) == E_ALIAS
 
 
 @pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
@@ -157,7 +163,7 @@ def test_matrix_misaligned(L, fn, which):
     kw = {"r": 1, "k": 2, "v": 3, "x": 4, "u": 5, "si": 6, "so": 7, "o": 8}
     a = {n: addr(i, 8 if n == which else 0) for n, i in kw.items()}
     st = getattr(L, fn)(2, 8, 2, 64, a["r"], a["k"], a["v"], a["x"], a["u"], a["si"],
-                        a["so"], a["o"], None)
+                        a["so"], a["o"], None, 0, None)
     assert st == E_ALIGN
 
 
@@ -166,6 +172,58 @@ def test_matrix_aliasing(L, fn):
     assert matrix(L, fn, o=1) == E_ALIAS    # o == r
     assert matrix(L, fn, o=4) == E_ALIAS    # o == x
     assert matrix(L, fn, so=8) == E_ALIAS   # state_out == o
+
+
+# ---------------------------------------------------------------------------
+# caller workspaces of the forwards
+
+def test_rwkv4_workspace_size(L):
+    # none for a single 256-token pass; else the 16 KiB control block and
+    # 1.5 KiB of records (6 x 32 channels x 8 bytes) per workgroup:
+    # B x ceil(C / 32) channel blocks x ceil(T / 256) passes
+    assert L.rwkv4_wkv_fwd_workspace_bytes(8, 256, 1, 768) == 0
+    assert L.rwkv4_wkv_fwd_workspace_bytes(8, 1024, 1, 768) == 16384 + 8 * 24 * 4 * 1536
+    assert L.rwkv4_wkv_fwd_workspace_bytes(2, 300, 1, 40) == 16384 + 2 * 2 * 2 * 1536
+    assert L.rwkv4_wkv_fwd_workspace_bytes(0, 300, 1, 40) == 0
+
+
+def test_rwkv4_workspace_checks(L):
+    need = L.rwkv4_wkv_fwd_workspace_bytes(2, 300, 1, 16)
+    assert need > 0
+    assert rwkv4(L, T=300, ws=None) == E_NULL
+    assert rwkv4(L, T=300, ws_bytes=need - 1) == E_DIM
+    assert rwkv4(L, T=300, ws=1) == E_ALIAS      # workspace on k
+    assert rwkv4(L, T=300, ws=7) == E_ALIAS      # workspace on y
+
+
+def test_rwkv4_workspace_misaligned(L):
+    a = [addr(i) for i in range(1, 8)]
+    need = L.rwkv4_wkv_fwd_workspace_bytes(2, 300, 1, 16)
+    assert L.rwkv4_wkv_fwd(2, 300, 1, 16, *a, addr(8, 4), need, None) == E_ALIGN
+
+
+@pytest.mark.parametrize("fn", ["rwkv5_wkv_fwd", "rwkv6_wkv_fwd"])
+def test_matrix_workspace(L, fn):
+    # none while every head has a compute unit; with more heads than units
+    # (T >= 256) the balanced split's hand-off area
+    assert L.rwkv_wkv_fwd_workspace_bytes(2, 8, 2, 64) == 0
+    assert L.rwkv_wkv_fwd_workspace_bytes(1, 4096, 200, 64) == 0
+    need = L.rwkv_wkv_fwd_workspace_bytes(1, 300, 300, 64)
+    assert need > 32768
+    assert L.rwkv_wkv_fwd_workspace_bytes(1, 300, 300, 32) == 0
+    assert matrix(L, fn, B=1, T=300, H=300, ws=None) == E_NULL
+    assert matrix(L, fn, B=1, T=300, H=300, ws_bytes=need - 1) == E_DIM
+    a = [addr(i) for i in range(1, 9)]
+    assert getattr(L, fn)(1, 300, 300, 64, *a, addr(9, 8), need, None) == E_ALIGN
+    assert matrix(L, fn, B=1, T=300, H=300, ws=1) == E_ALIAS   # on r
+    assert matrix(L, fn, B=1, T=300, H=300, ws=8) == E_ALIAS   # on o
+    assert matrix(L, fn, B=1, T=300, H=300, ws=7) == E_ALIAS   # on state_out
+
+
+def test_workspace_status_checks(L):
+    assert L.rwkv_wkv_workspace_status(None, 1 << 20, None) == E_NULL
+    assert L.rwkv_wkv_workspace_status(addr(1), 4096, None) == E_DIM
+    assert L.rwkv_wkv_workspace_status(addr(1, 8), 1 << 20, None) == E_ALIGN
 
 
 STEPS = ["rwkv5_wkv_step", "rwkv6_wkv_step"]
@@ -248,10 +306,16 @@ BWDS = ["rwkv5_wkv_bwd", "rwkv6_wkv_bwd"]
 
 
 def test_bwd_workspace_size(L):
-    # the state entering each 64-token chunk plus the final state, per head,
-    # and two per-head partial sums
-    assert L.rwkv_wkv_bwd_workspace_bytes(2, 130, 3, 64) == 2 * 3 * 4 * 64 * 64 * 4 + 2 * 2 * 3 * 64 * 4
+    # the 16 KiB control block, the state entering each 64-token chunk plus
+    # the final state, per head, and two per-head partial sums (no hand-off
+    # area beyond the control block while every head has a compute unit)
+    assert L.rwkv_wkv_bwd_workspace_bytes(2, 130, 3, 64) == \
+        16384 + 2 * 3 * 4 * 64 * 64 * 4 + 2 * 2 * 3 * 64 * 4
     assert L.rwkv_wkv_bwd_workspace_bytes(2, 130, 3, 32) == 0
+    # with the splits, the hand-off area comes first (256-byte aligned)
+    states = 1 * 300 * 6 * 64 * 64 * 4 + 2 * 300 * 64 * 4
+    total = L.rwkv_wkv_bwd_workspace_bytes(1, 300, 300, 64)
+    assert total > states + 32768 and (total - states) % 256 == 0
 
 
 @pytest.mark.parametrize("fn", BWDS)
@@ -305,7 +369,7 @@ def gated(L, fn="rwkv6_wkv_fwd_gated", B=2, T=8, H=2, N=64, eps=1e-5, **over):
     idx.update({n: val for n, val in over.items() if n in idx})
     mis = over.get("mis", {})
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
-    return getattr(L, fn)(B, T, H, N, *(a[n] for n in names[:10]), eps, a["y"], None)
+    return getattr(L, fn)(B, T, H, N, *(a[n] for n in names[:10]), eps, a["y"], None, 0, None)
 
 
 GATED = ["rwkv5_wkv_fwd_gated", "rwkv6_wkv_fwd_gated"]
@@ -339,7 +403,10 @@ def decay(L, B=2, T=8, D=128, act=1, **over):
     idx.update({n: val for n, val in over.items() if n in idx})
     mis = over.get("mis", {})
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
-    return L.rwkv6_decay_lora(B, T, D, act, *(a[n] for n in names), None)
+    ws = over.get("ws", 12)
+    nb = over.get("ws_bytes", L.rwkv6_decay_lora_workspace_bytes(B, T, D))
+    return L.rwkv6_decay_lora(B, T, D, act, *(a[n] for n in names),
+                              None if ws is None else addr(ws), nb, None)
 
 
 def fused(L, B=2, T=8, H=2, N=64, act=1, **over):
@@ -349,7 +416,10 @@ def fused(L, B=2, T=8, H=2, N=64, act=1, **over):
     mis = over.get("mis", {})
     a = {n: (addr(i, mis.get(n, 0)) if i is not None else None) for n, i in idx.items()}
     first = [a[n] for n in ("r", "k", "v") + LORA_NAMES]
-    return L.rwkv6_wkv_fwd_lora(B, T, H, N, *first, act, a["u"], a["si"], a["so"], a["o"], None)
+    ws = over.get("ws", 20)
+    nb = over.get("ws_bytes", L.rwkv6_wkv_fwd_lora_workspace_bytes(B, T, H, N))
+    return L.rwkv6_wkv_fwd_lora(B, T, H, N, *first, act, a["u"], a["si"], a["so"], a["o"],
+                                None if ws is None else addr(ws), nb, None)
 
 
 @pytest.mark.parametrize("missing", ["x", "mu", "lam", "a1", "b1", "om", "a2", "b2", "d"])
@@ -370,6 +440,25 @@ def test_decay_lora_checks(L):
     assert decay(L, d=9) == E_ALIAS           # d on B2
     assert decay(L, T=0, d=None) == OK        # nothing to do
     assert decay(L, sh=None, T=0) == OK
+
+
+def test_decay_lora_workspace(L):
+    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 128) == 2 * 8 * 128
+    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 96) == 0
+    assert decay(L, ws=None) == E_NULL
+    assert decay(L, ws_bytes=2 * 8 * 128 - 1) == E_DIM
+    assert decay(L, ws=1) == E_ALIAS          # on x
+    assert decay(L, ws=10) == E_ALIAS         # on d
+
+
+def test_fused_workspace(L):
+    # the producer's factor (B T 128 bytes) after the chunked forward's
+    # hand-off area (here only its 16 KiB control block)
+    assert L.rwkv6_wkv_fwd_lora_workspace_bytes(2, 8, 2, 64) == 16384 + 2 * 8 * 128
+    assert fused(L, ws=None) == E_NULL
+    assert fused(L, ws_bytes=100) == E_DIM
+    assert fused(L, ws=1) == E_ALIAS          # on r
+    assert fused(L, ws=16) == E_ALIAS         # on state_out
 
 
 @pytest.mark.parametrize("missing", ["r", "x", "a1", "b2", "om", "u", "o"])
