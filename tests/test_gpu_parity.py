@@ -877,15 +877,27 @@ def gated_ref(d):
 
 
 def assert_gated_close(y, y_ref, n_ref, gate, o_ref, what):
-    """The gate multiplies exactly, so y carries the normalised value's error
-    times |silu(g)| plus its own bf16 rounding: the forward's bounds apply to
-    the normalised value (RMS 5e-3 of y as a whole; per element 3e-2 of
-    max(|n|, rms(n)), scaled by |silu(g)|)."""
+    """y = (n * ln_w + ln_b) * silu(g) with n = (o - mean_t) / std_t over a
+    token's channels of one head.  The gate multiplies exactly, so y carries
+    the normalised value's error times |silu(g)| plus its own bf16 rounding.
+    The normalised value carries the error the WKV's own bound allows in o,
+    divided by the token's channel standard deviation std_t: the forward's
+    per-element bound (3e-2 of max(|o|, rms(o)), with rms over the head)
+    becomes 3e-2 of max(|n|, rms(n)) * max(1, rms(o) / std_t), scaled by
+    |silu(g)|.  On well-spread tokens (std_t >= rms(o)) that is the plain
+    bound on n; a token whose channels are nearly equal (small std_t) is
+    ill-conditioned for the normalisation and gets the larger bound its
+    conditioning implies.  RMS: 5e-3 of y as a whole.  o_ref: the oracle's
+    WKV output of the same head ([.., T, .., 64])."""
     rms, _ = rel_errors(y, y_ref)
     assert rms <= 5e-3, f"{what}: rms_rel {rms:.3e}"
     sg = np.abs(gate / (1.0 + np.exp(-gate.astype(np.float64))))
-    scale = np.maximum(np.abs(n_ref), np.sqrt(np.mean(n_ref ** 2))) * sg + np.abs(y_ref) * 2.0 ** -8
-    mx = float(np.max(np.abs(y - y_ref) / np.maximum(scale, 1e-30)))
+    std_t = np.std(o_ref, axis=-1, keepdims=True)
+    cond = np.maximum(1.0, np.sqrt(np.mean(o_ref ** 2)) / np.maximum(std_t, 1e-300))
+    scale = (np.maximum(np.abs(n_ref), np.sqrt(np.mean(n_ref ** 2))) * cond * sg
+             + np.abs(y_ref) * 2.0 ** -8)
+    ratio = np.abs(y - y_ref) / np.maximum(scale, 1e-30)
+    mx = float(np.max(ratio))
     assert mx <= 3e-2, f"{what}: max error {mx:.3e} of the gated scale"
     return mx
 
