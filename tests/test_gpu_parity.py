@@ -81,12 +81,31 @@ def test_rwkv4_workload2_full():
     rwkv4_check(S.workload(2))
 
 
+# Many (sequence, 32-channel block) units: ragged last passes, ragged
+# channel blocks, one token, a state handed in
+@pytest.mark.parametrize("B,T,C", [(160, 300, 64), (130, 1, 5), (128, 1000, 33),
+                                   (64, 513, 128), (256, 256, 32)])
+def test_rwkv4_many_units(B, T, C):
+    print(f"rwkv4 B={B} T={T} C={C}", flush=True)
+    rwkv4_check(S.rwkv4_inputs(B, T, C, 150 + T + C, k_sigma=2.0))
+
+
+def test_rwkv4_many_units_state_handoff():
+    print("rwkv4 state handoff B=160 T=700 C=64", flush=True)
+    d = S.rwkv4_inputs(160, 700, 64, 18, k_sigma=2.0)
+    head = {n: d[n][:, :333] if n in "kv" else d[n] for n in d}
+    tail = {n: d[n][:, 333:] if n in "kv" else d[n] for n in d}
+    _, s1, _ = rwkv4_check(head)
+    rwkv4_check(tail, state_in=s1.cpu().numpy())
+
+
 def test_rwkv4_split_over_launches():
-    # 4100 (sequence, 32-channel block) pairs x 2 passes exceed one launch's
-    # workgroup budget: the passes run in two launches, the state carried
-    # between them through the library's workspace
-    print("rwkv4 B=4100 T=257 C=32 (two launches)", flush=True)
-    rwkv4_check(S.rwkv4_inputs(4100, 257, 32, 11, k_sigma=2.0))
+    # 70 (sequence, 32-channel block) pairs x 118 passes exceed one launch's
+    # budget of 8192 chained passes: they run in two launches, the state
+    # carried between them through the workspace
+    print("rwkv4 B=70 T=30000 C=32 (two launches)", flush=True)
+    assert W.rwkv4_workspace_bytes(70, 30000, 32) > 0
+    rwkv4_check(S.rwkv4_inputs(70, 30000, 32, 11, k_sigma=2.0))
 
 
 def test_rwkv4_repeated_calls_take_fresh_records():
