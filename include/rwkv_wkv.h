@@ -225,6 +225,26 @@ int rwkv6_wkv_fwd(int B, int T, int H, int N,
                   hipStream_t stream);
 
 /*
+ * rwkv6_wkv_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): the same
+ * arguments, outputs and status codes without the workspace.  The hand-off
+ * area of the balanced split lives in a file-scope device array of 8 MiB,
+ * one per GPU, held until the process ends; a shape that needs more
+ * (rwkv_wkv_fwd_workspace_bytes(B, T, H, N) > 8 MiB: on 256 compute units,
+ * more than 512 heads with T >= 256) returns RWKV_E_UNSUPPORTED and
+ * launches nothing.  Every call on one GPU shares that GPU's array; it
+ * starts zero-filled and the kernels leave it valid for the next call, so
+ * nothing is cleared between calls, but calls that overlap in time on one
+ * GPU (two streams, or two graphs replayed at once) race.  It allocates
+ * nothing; its first call on a device looks up the array's address.
+ */
+int rwkv6_wkv_fwd_noalloc(int B, int T, int H, int N,
+                          const rwkv_bf16 *r, const rwkv_bf16 *k, const rwkv_bf16 *v,
+                          const float *x, const float *u,
+                          const float *state_in, float *state_out,
+                          rwkv_bf16 *o, hipStream_t stream);
+
+/*
  * Finch (RWKV-6) WKV, serial (RNN) mode: tokens are applied one at a time to
  * a state that stays in registers.  Decoding calls it with T == 1.  N must
  * be 64.  Arguments as rwkv6_wkv_fwd, except:

@@ -44,7 +44,7 @@ EXPORTS = ("rwkv_wkv_strerror", "rwkv_wkv_workspace_status", "rwkv4_wkv_fwd",
            "rwkv5_wkv_fwd_gated", "rwkv6_wkv_fwd_gated", "rwkv6_decay_lora",
            "rwkv6_decay_lora_workspace_bytes", "rwkv6_wkv_fwd_lora",
            "rwkv6_wkv_fwd_lora_workspace_bytes", "rwkv5_wkv_fwd_save", "rwkv6_wkv_fwd_save",
-           "rwkv5_wkv_bwd_saved", "rwkv6_wkv_bwd_saved")
+           "rwkv5_wkv_bwd_saved", "rwkv6_wkv_bwd_saved", "rwkv6_wkv_fwd_noalloc")
 
 _lib = None
 
@@ -81,6 +81,8 @@ def lib():
             f = getattr(L, name)
             f.restype = I
             f.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        L.rwkv6_wkv_fwd_noalloc.restype = I
+        L.rwkv6_wkv_fwd_noalloc.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P]
         L.rwkv4_wkv_step.restype = I
         L.rwkv4_wkv_step.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
         for name in ("rwkv5_wkv_step", "rwkv6_wkv_step"):
@@ -296,6 +298,29 @@ def rwkv6_wkv_fwd(r, k, v, x, u, state_in=None, state_out=None, o=None,
     """Finch WKV, chunked.  As rwkv5_wkv_fwd but x: [B, T, H, 64] fp32."""
     return _matrix_fwd("rwkv6_wkv_fwd", True, r, k, v, x, u, state_in, state_out, o,
                        return_state, workspace, stream)
+
+
+def rwkv6_wkv_fwd_noalloc(r, k, v, x, u, state_in=None, state_out=None, o=None,
+                          return_state=True, stream=None):
+    """rwkv6_wkv_fwd with its hand-off scratch in the library's fixed device
+    array instead of a workspace (for callers that cannot allocate; shapes
+    needing more than 8 MiB of it raise RWKV_E_UNSUPPORTED; calls that overlap
+    on one GPU race)."""
+    import torch
+    B, T, H, N = _matrix_args(r, k, v, x, u, True)
+    if state_in is not None:
+        _expect("state_in", state_in, (B, H, N, N), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=r.device)
+    _expect("o", o, (B, T, H, N), torch.bfloat16)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    if state_out is not None:
+        _expect("state_out", state_out, (B, H, N, N), torch.float32)
+    _check("rwkv6_wkv_fwd_noalloc", lib().rwkv6_wkv_fwd_noalloc(
+        B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(x), _ptr(u), _ptr(state_in),
+        _ptr(state_out), _ptr(o), _stream(stream)))
+    return o, state_out
 
 
 def _matrix_step(name, per_token, r, k, v, x, u, state, o, stream):

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -98,6 +99,36 @@ int check_matrix(int B, int T, int H, int N, const void *r, const void *k, const
 }
 
 constexpr int kMaxChunkedHeads = 65536;
+
+// Scratch of rwkv6_wkv_fwd_noalloc: the chunked forward's hand-off area in a
+// fixed device array (one copy per GPU, zero at load as static storage is,
+// kept until the process ends).  Host code never uses the array's name as a
+// device address: the address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on its first use).
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 constexpr int64_t kMaxRwkv4Channels = 1 << 20;
 
 int matrix_fwd(bool per_token, int B, int T, int H, int N, const rwkv_bf16 *r,
@@ -506,6 +537,21 @@ int rwkv6_wkv_step(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf
                    const rwkv_bf16 *v, const float *x, const float *u, float *state,
                    rwkv_bf16 *o, hipStream_t stream) {
     return matrix_step(true, B, T, H, N, r, k, v, x, u, state, o, stream);
+}
+
+int rwkv6_wkv_fwd_noalloc(int B, int T, int H, int N, const rwkv_bf16 *r, const rwkv_bf16 *k,
+                          const rwkv_bf16 *v, const float *x, const float *u,
+                          const float *state_in, float *state_out, rwkv_bf16 *o,
+                          hipStream_t stream) {
+    const int64_t x_elems = checked_mul({B, T, H, N});
+    const int st = check_matrix(B, T, H, N, r, k, v, x, x_elems, u, state_in, state_out, false, o);
+    if (st != RWKV_OK) return st;
+    if (H > kMaxChunkedHeads || (int64_t)B * H > INT32_MAX) return RWKV_E_UNSUPPORTED;
+    const size_t need = T > 0 ? wkv::chunk_workspace_bytes(B, T, H) : 0;
+    if (need > kStaticScratchBytes) return RWKV_E_UNSUPPORTED;
+    void *ws = nullptr;
+    if (need > 0 && scratch_address(&ws) != hipSuccess) return RWKV_E_HIP;
+    return matrix_fwd(true, B, T, H, N, r, k, v, x, u, state_in, state_out, o, ws, need, stream);
 }
 
 size_t rwkv6_decay_lora_workspace_bytes(int B, int T, int D) {

@@ -518,3 +518,25 @@ def test_bwd_saved_checks(L, fn):
     assert call(ws_bytes=16) == E_DIM
     assert call(dr=1) == E_ALIAS
     assert call(do=None) == E_NULL
+
+
+# ---------------------------------------------------------------------------
+# the allocation-free Finch forward
+
+def noalloc(L, B=2, T=8, H=2, N=64, **over):
+    names = ("r", "k", "v", "x", "u", "si", "so", "o")
+    idx = {n: i + 1 for i, n in enumerate(names)}
+    idx.update({n: val for n, val in over.items() if n in idx})
+    a = {n: (addr(i) if i is not None else None) for n, i in idx.items()}
+    return L.rwkv6_wkv_fwd_noalloc(B, T, H, N, *(a[n] for n in names), None)
+
+
+def test_noalloc_checks(L):
+    assert noalloc(L, N=32) == E_UNSUP
+    assert noalloc(L, B=0) == E_DIM
+    assert noalloc(L, r=None) == E_NULL
+    assert noalloc(L, o=1) == E_ALIAS
+    # a hand-off area beyond its fixed 8 MiB scratch: 600 heads (the four-wave
+    # split and its parked states) on 256 compute units
+    assert L.rwkv_wkv_fwd_workspace_bytes(2, 320, 300, 64) > 8 << 20
+    assert noalloc(L, B=2, T=320, H=300) == E_UNSUP
