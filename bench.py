@@ -671,13 +671,15 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
                      lambda: eagle_decode_bytes_per_step(256, 64)),
     "rwkv4_decode": ("rwkv4_decode4_kernel", "rwkv4_step.hip",
                      lambda: rwkv4_decode_bytes_per_step(256, 4096)),
+    "finch_decode_B1024": ("wkv_step_kernel<true>", "wkv_step.hip",
+                           lambda: decode_bytes_per_step(1024, 64)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",
             "finch_fwd_gated": "finch_gated", "finch_bwd_recompute": "finch_bwd",
             "finch_bwd_reverse": "finch_bwd", "finch_lora_producer": "finch_lora",
             "finch_lora_wkv": "finch_lora",
             "finch_decode": "decode", "eagle_decode": "eagle_decode",
-            "rwkv4_decode": "rwkv4_decode"}
+            "rwkv4_decode": "rwkv4_decode", "finch_decode_B1024": "decode_big"}
 
 
 def _pmc_mean(csv_path, fragment, counter):
@@ -721,6 +723,23 @@ def summarize_pmc(pmc_dir):
     with open(dst, "w") as fh:
         json.dump(out, fh, indent=1)
     return out
+
+
+def summarize_trace(csv_path):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv
+    (durations in ns there, microseconds here), longest total first."""
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda x: -x[2])
+    out = ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for name, calls, _, avg, mn, mx in rows:
+        out.append(f"| {name[:120]} | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | "
+                   f"{mx / 1e3:.1f} |")
+    return "\n".join(out)
 
 
 def measure_stream(torch, nbytes=1 << 30, reps=10):
@@ -795,6 +814,9 @@ def measure_torch_copy(torch, a, b, reps):
 def main():
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-pmc":
         print(json.dumps(summarize_pmc(sys.argv[2]), indent=1))
+        return 0
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
+        print(summarize_trace(sys.argv[2]))
         return 0
     args = parse()
     if args.gpus != 1:
