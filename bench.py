@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5)
     ap.add_argument("--skip-paths", action="store_true", help="time only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="do not time the oracle")
-    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "decode", "decode_big",
+    ap.add_argument("--only", choices=["finch", "eagle", "rwkv4", "serial", "decode", "decode_big",
                                        "eagle_decode",
                                        "rwkv4_decode", "finch_bwd", "finch_gated", "finch_lora",
                                        "finch_train", "calib", "stream"],
@@ -599,6 +599,31 @@ def run_decode(torch, W, S, H2D, args, cfg=5, batch=None):
                       "interval_ms": total_ms, "kernel_ms_mean": per, "wall_s": wall}}
 
 
+def run_serial_segments(torch, W, S, H2D, args, T=64):
+    """The serial (decode) kernel applying T tokens per call to 256 x 64 heads
+    whose states stay in registers through the call: the cost of carrying
+    the state token by token, the arithmetic a chunked forward would repeat
+    to make its carried state bit-identical to the serial mode's."""
+    B, H = 256, 64
+    d = S.wkv_inputs(B, T, H, 64, 5, True, 0.1)
+    g = H2D(d)
+    st = g["s0"].clone()
+    o = torch.empty_like(g["r"])
+
+    def launch():
+        W.rwkv6_wkv_step(g["r"], g["k"], g["v"], g["x"], g["u"], st, o=o)
+
+    res = time_launches(torch, launch, max(10, args.steps // 4), args.warmup,
+                        settle_s=args.settle_s)
+    sec = res["kernel_ms_mean"] / 1e3
+    token_heads = B * H * T
+    res.update({"workload": f"finch_serial_B{B}_H{H}_T{T}",
+                "ns_per_token_head": sec / token_heads * 1e9,
+                "note": "each token: the output (4096 multiply-adds) and the state update "
+                        "(4096 multiplies and 4096 fused multiply-adds) of one head"})
+    return res
+
+
 def cpu_baseline(S, d4, min_seconds=10.0):
     """The fp64 oracle on the whole Finch workload, all host threads, repeated
     until about `min_seconds` of CPU work have run (at least one pass)."""
@@ -884,6 +909,9 @@ def main():
         print("finch training step (forward keeping the states + backward) ...",
               file=sys.stderr, flush=True)
         paths["finch_train"] = run_finch_train(torch, W, S, H2D, args, d4)
+    if not args.skip_paths and only in (None, "serial"):
+        print("finch serial mode, 64 tokens per call ...", file=sys.stderr, flush=True)
+        paths["finch_serial_T64"] = run_serial_segments(torch, W, S, H2D, args)
     if not args.skip_paths and only in (None, "decode"):
         print("finch decode ...", file=sys.stderr, flush=True)
         paths["finch_decode"] = run_decode(torch, W, S, H2D, args)
