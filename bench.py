@@ -686,7 +686,7 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
                             lambda: finch_recompute_bytes(8, 4096, 40)),
     "finch_bwd_reverse": ("wkv_bwd_kernel<true>", "wkv_chunk_bwd.hip",
                           lambda: finch_reverse_bytes(8, 4096, 40)),
-    "finch_lora_producer": ("decay_lora_kernel<true>", "decay_lora.hip",
+    "finch_lora_producer": ("decay_once_kernel<true, 5, false>", "decay_lora.hip",
                             lambda: lora_producer_bytes(8, 4096, 40)),
     "finch_lora_wkv": ("wkv_chunk_kernel<true, 8, false, false, true>", "wkv_chunk.hip",
                        lambda: lora_wkv_bytes(8, 4096, 40)),

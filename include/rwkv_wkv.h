@@ -427,9 +427,12 @@ int rwkv6_wkv_bwd_saved(int B, int T, int H, int N,
  *              pages give their shapes)
  *   d          [B][T][D] fp32 output: the logits rwkv6_wkv_fwd takes as x
  *              (with D = H N in its [B][T][H][N] layout)
- *   workspace  rwkv6_decay_lora_workspace_bytes(B, T, D) bytes (B T 128:
- *              act(z A2) of every token, rank 64, bf16), 16-byte aligned, not
- *              overlapping any other argument; no zero-filling needed.
+ *   workspace  rwkv6_decay_lora_workspace_bytes(B, T, D) bytes: act(z A2)
+ *              of every token (rank 64, bf16, B T 128 bytes), then, for D up
+ *              to 2560, the weights laid out as the products' operands (D/64
+ *              x 16 KiB; the block input is then read once); 16-byte
+ *              aligned, not overlapping any other argument; no zero-filling
+ *              needed.
  * The products run on bf16 matrix cores with fp32 accumulation (the mixed
  * values and act(.) rounded to bf16 as operands).  B T must be below 2^31.
  * T = 0 does nothing.  All pointers need 16-byte alignment; d must not
@@ -449,8 +452,9 @@ int rwkv6_decay_lora(int B, int T, int D, int act,
  * Finch time-parallel forward fed by the decay producer: the same output and
  * state as rwkv6_decay_lora followed by rwkv6_wkv_fwd with x = d, without
  * the fp32 logits ever going to memory.  The producer writes act(z A2)
- * (rank 64, bf16, B T 128 bytes of the workspace) and the chunked kernel
- * forms each head's logits omega + act(z A2) B2 on the matrix cores.
+ * (rank 64, bf16, B T 128 bytes of the workspace, beside its packed weights)
+ * and the chunked kernel forms each head's logits omega + act(z A2) B2 on
+ * the matrix cores.
  * Arguments: r, k, v, u, state_in, state_out, o as rwkv6_wkv_fwd; x (the
  * block input, [B][T][H N] bf16), shift, mu_x, lam, A1, B1, omega, A2, B2 and
  * act as rwkv6_decay_lora with D = H N.

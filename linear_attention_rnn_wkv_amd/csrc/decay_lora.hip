@@ -9,25 +9,32 @@
 //     dx = x_{t-1} - x_t,   y = x_t + dx * mu,   m = lam + act(y A1) B1,
 //     z  = x_t + dx * m,    h = act(z A2),       d = omega + h B2.
 //
-// decay_lora_kernel writes h (rank 64, bf16) for every token; the chunked
-// Finch kernel forms d from it per head, and lora_logits_kernel writes d
-// for callers that want the logits themselves.
+// The producer writes h (rank 64, bf16) for every token; the chunked Finch
+// kernel forms d from it per head, and lora_logits_kernel writes d for
+// callers that want the logits themselves.  Two producer kernels:
+// decay_once_kernel (D up to 2560) reads the block input once and keeps it
+// in registers between its two passes; decay_lora_kernel (any D) streams it
+// through LDS twice.
 //
 // Layout of the products: every product is taken transposed, weights as the
 // A operand and tokens as the B operand columns (lane c of a 16-lane group
-// = token c of the wave's 16), so the result of one product is already the
-// B operand of the next:
+// = one token of a 16-token tile), so the result of one product is already
+// the B operand of the next:
 //   pass 1:  (y A1)^T  [32 x 16]  += A1^T [32 x 64 ch] . y^T [64 ch x 16]
 //   pass 2:  m^T       [64 x 16]   = B1^T [64 ch x 32] . act(y A1)^T
 //            (z A2)^T  [64 x 16]  += A2^T [64 x 64 ch] . z^T
-// with k-slots (g, e) of lane group g taken as {4g + e, 16 + 4g + e} of each
+// The rank k-slots (g, e) of lane group g are {4g + e, 16 + 4g + e} of each
 // 32-wide step: the accumulator rows a lane holds (4g + e of two 16-row
-// tiles) are then exactly the k-slots of the next product's B operand.  A
-// 64-channel block's weights and the workgroup's 128 token rows (and their
-// previous-token rows) are staged through LDS with row-contiguous loads,
-// shared by the eight waves; the weights are read down their columns with
-// the transposing LDS load.  Two passes stream the channels: the mix of
-// every channel needs act(y A1), a sum over all of them.
+// tiles) are then exactly the k-slots of the next product's B operand.  Two
+// passes over the channels are needed because the mix of every channel
+// needs act(y A1), a sum over all of them.
+//
+// decay_lora_kernel: a 64-channel block's weights and the workgroup's 128
+// token rows (and their previous-token rows) are staged through LDS with
+// row-contiguous loads, shared by the eight waves; the weights are read
+// down their columns with the transposing LDS load.
+#include <type_traits>
+
 #include "launchers.h"
 #include "wkv_tiles.h"
 
@@ -228,6 +235,306 @@ __global__ __launch_bounds__(512, 1) void decay_lora_kernel(
     }
 }
 
+// The same products with the block input read once, for D up to 8 x 5
+// blocks of 64 channels.  A workgroup takes 32 consecutive token rows, lane c
+// of a 16-lane group holding tokens 2c and 2c + 1 (product column c of the
+// two token tiles n = 0, 1), and its eight waves split the channel blocks
+// (wave w: blocks w, w + 8, ...).  Each wave keeps x_t of its blocks in
+// registers from pass 1 to pass 2.  x_{t-1} is never loaded: for token
+// 2c + 1 it is token 2c of the same lane, for token 2c it is token 2c - 1
+// of lane c - 1, one DPP row shift; the tile's first token takes the row
+// before the tile (or the shift row, or zero) from LDS, and a tile with a
+// sequence start inside it loads those tokens' shift rows separately.  The
+// sums over the channels, act(y A1) after pass 1 and act(z A2) after
+// pass 2, are added over the waves through LDS in a fixed order.  The
+// weights reach every wave as ready-made product operands: lora_pack_kernel
+// lays A1, B1 and A2 out per block in the A operand's lane order once per
+// call, 16 KB per block, which the workgroups read from L2 with one 16-byte
+// load per lane and product.  Channel order inside a 32-channel half block
+// s: lane group g holds channels 32 s + 8 g + j, j = 0..7, as the k-slots of
+// the products that contract over channels, and as rows 4 g + e of the two
+// 16-row tiles q of m^T (channel 32 s + 8 g + 4 q + e); the rank k-slots of
+// m^T's product follow the accumulator rows of (y A1)^T, {4g + j, 16 + 4g +
+// j - 4}.
+constexpr int kFragsA1 = 4, kFragsB1 = 4, kFragsA2 = 8;  // per block: (s, m), (s, q), (s, M)
+constexpr int kFrags = kFragsA1 + kFragsB1 + kFragsA2;
+constexpr int kOnceWaves = 8, kOnceMaxKB = 5;  // blocks per wave held in registers
+constexpr int kOnceMaxD = kOnceWaves * kOnceMaxKB * kKB;
+constexpr int kOnceTok = 32;                   // tokens per workgroup
+// operand register sets of the two passes (one step loaded ahead; deeper
+// prefetch measured no faster)
+constexpr int kP1 = 2, kP2 = 2;
+// cache policy of the block input's loads: non-temporal (nt), so that the
+// stream of rows, read once, does not evict the operand fragments from an
+// XCD's L2, where every workgroup on it reads them again (measured: HBM
+// reads 1.13x -> 1.04x of the input, 5 % less time)
+constexpr int kStreamNT = 2;
+
+// rank k-slot j of lane group g
+__device__ __forceinline__ int kslot(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+
+// One thread per (block, fragment, lane): the 8 bf16 of that lane's operand.
+__global__ void lora_pack_kernel(int D, const uint16_t *__restrict__ A1,
+                                 const uint16_t *__restrict__ B1,
+                                 const uint16_t *__restrict__ A2, bf16x8 *__restrict__ packed) {
+    const int nkb = D / kKB;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= nkb * kFrags * 64) return;
+    const int lane = idx & 63, f = (idx >> 6) % kFrags, kb = idx / (64 * kFrags);
+    const int g = lane >> 4, c = lane & 15, ch0 = kb * kKB;
+    uint16_t v[8];
+    if (f < kFragsA1) {  // A1^T: row rank 16 m + c, k-slot j channel 32 s + 8 g + j
+        const int s = f >> 1, m = f & 1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = A1[(size_t)(ch0 + 32 * s + 8 * g + j) * kR1 + 16 * m + c];
+    } else if (f < kFragsA1 + kFragsB1) {  // B1^T: row channel of m^T row c, k-slot rank kslot
+        const int s = (f - kFragsA1) >> 1, q = (f - kFragsA1) & 1;
+        const int ch = ch0 + 32 * s + 8 * (c >> 2) + 4 * q + (c & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = B1[(size_t)kslot(g, j) * D + ch];
+    } else {  // A2^T: row rank 16 M + c, k-slot j channel 32 s + 8 g + j
+        const int s = (f - kFragsA1 - kFragsB1) >> 2, M = (f - kFragsA1 - kFragsB1) & 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = A2[(size_t)(ch0 + 32 * s + 8 * g + j) * kR2 + 16 * M + c];
+    }
+    const u32x4 m4 = {v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                      v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+    packed[idx] = __builtin_bit_cast(bf16x8, m4);
+}
+
+template <bool TANH, int KB, bool INNER>
+__global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
+    int rows, int T, int D, const uint16_t *__restrict__ x, const uint16_t *__restrict__ shift,
+    const float *__restrict__ mu, const float *__restrict__ lam,
+    const bf16x8 *__restrict__ packed, uint16_t *__restrict__ h) {
+    constexpr int NW = kOnceWaves;
+    __shared__ __align__(16) float sMu[kOnceMaxD], sLam[kOnceMaxD];
+    __shared__ __align__(16) uint16_t sBnd[kOnceMaxD];  // x_{t-1} of the tile's first token
+    __shared__ __align__(16) f32x4 sRed1[NW][4][64];    // partial (y A1)^T: [wave][2 m + n]
+    __shared__ __align__(16) u32x2 sH1[2][2][64];       // act(y A1)^T, bf16: [n][m]
+    __shared__ __align__(16) f32x4 sRed2[NW][8][64];    // partial (z A2)^T: [wave][2 M + n]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: block offsets in SGPRs)
+    const int c = lane & 15, g = lane >> 4;
+    const int nkb = D / kKB;
+    const int r0 = blockIdx.x * kOnceTok, t0 = r0 % T;
+    // a sequence starts inside the tile (its first token aside); only
+    // possible, and only compiled in, when T is not a multiple of the tile
+    const bool inner = INNER && T - t0 < kOnceTok && r0 + (T - t0) < rows;
+
+    // mu, lam and the row before the tile go to LDS; every thread issues the
+    // same five loads (past the end they read zero)
+    const Rsrc rmu = rsrc(mu, (uint32_t)D * 4), rlam = rsrc(lam, (uint32_t)D * 4);
+    const uint16_t *bnd = t0 > 0 ? x + (size_t)(r0 - 1) * D : shift ? shift + (size_t)(r0 / T) * D : x;
+    const Rsrc rbnd = rsrc(bnd, t0 > 0 || shift ? (uint32_t)D * 2 : 0u);
+    f32x4 smu[2], slam[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        smu[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rmu, (tid + 512 * j) * 16, 0, 0));
+        slam[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rlam, (tid + 512 * j) * 16, 0, 0));
+    }
+    const u32x4 sb = __builtin_amdgcn_raw_buffer_load_b128(rbnd, tid * 16, 0, 0);
+
+    // this lane's x_t: token 2c + n of the tile, channels 32 s + 8 g .. + 7
+    // of each of its blocks (rows past the end read zero and store nothing)
+    const Rsrc rx = rsrc(x + (size_t)r0 * D, (uint32_t)min(rows - r0, kOnceTok) * D * 2);
+    const int vo0 = 2 * c * D * 2 + 16 * g, vo1 = vo0 + D * 2;
+    auto blk = [&](int i) { return min(w + NW * i, nkb - 1); };  // (past the last: reread, unused)
+    auto live = [&](int i) { return w + NW * i < nkb; };
+    u32x4 xv[KB][2][2];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int so = blk(i) * kKB * 2 + 64 * s;
+            xv[i][s][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo0, so, kStreamNT);
+            xv[i][s][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo1, so, kStreamNT);
+        }
+    const Rsrc rp = rsrc(packed, (uint32_t)nkb * kFrags * 64 * 16);
+    auto frag = [&](int kb, int f) {
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rp, lane * 16, (kb * kFrags + f) * 1024, 0));
+    };
+    auto f4lo = [](const u32x4 &p) { return f32x4{bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)}; };
+    auto f4hi = [](const u32x4 &p) { return f32x4{bf16_lo(p.z), bf16_hi(p.z), bf16_lo(p.w), bf16_hi(p.w)}; };
+    // x_{t-1} of this lane's two tokens at channel ch (= 32 s + 8 g of block)
+    auto prev = [&](const u32x4 &x0, const u32x4 &x1, int ch, u32x4 &p0, u32x4 &p1) {
+        const u32x4 b = *(const u32x4 *)&sBnd[ch];
+        p0.x = __builtin_amdgcn_update_dpp(b.x, x1.x, 0x111, 0xf, 0xf, false);  // row_shr:1
+        p0.y = __builtin_amdgcn_update_dpp(b.y, x1.y, 0x111, 0xf, 0xf, false);
+        p0.z = __builtin_amdgcn_update_dpp(b.z, x1.z, 0x111, 0xf, 0xf, false);
+        p0.w = __builtin_amdgcn_update_dpp(b.w, x1.w, 0x111, 0xf, 0xf, false);
+        p1 = x0;
+        if (inner) {  // tokens that start a sequence inside the tile
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int r = r0 + 2 * c + n;
+                if (2 * c + n > 0 && r < rows && r % T == 0) {
+                    const u32x4 v = shift ? *(const u32x4 *)(shift + (size_t)(r / T) * D + ch)
+                                          : u32x4{0u, 0u, 0u, 0u};
+                    if (n == 0) p0 = v;
+                    else p1 = v;
+                }
+            }
+        }
+    };
+
+    // stage mu, lam and the boundary row
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = 4 * (tid + 512 * j);
+        if (e < D) {
+            *(f32x4 *)&sMu[e] = smu[j];
+            *(f32x4 *)&sLam[e] = slam[j];
+        }
+    }
+    if (8 * tid < D) *(u32x4 *)&sBnd[8 * tid] = sb;
+
+    // ---- pass 1: (y A1)^T, this wave's blocks, kP1 - 1 blocks of operands
+    // ahead
+    struct P1 {
+        bf16x8 a[4];  // A1^T operands (s, m)
+    };
+    auto load1 = [&](P1 &p, int i) {
+#pragma unroll
+        for (int f = 0; f < kFragsA1; ++f) p.a[f] = frag(blk(i), f);
+    };
+    f32x4 acc1[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc1[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    P1 r1[kP1];
+#pragma unroll
+    for (int j = 0; j < kP1 - 1; ++j)
+        if (j < KB) load1(r1[j], j);
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        if (i + kP1 - 1 < KB) load1(r1[(i + kP1 - 1) % kP1], i + kP1 - 1);
+        if (live(i)) {
+            const P1 &cur = r1[i % kP1];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ch = blk(i) * kKB + 32 * s + 8 * g;
+                const f32x4 m0 = *(const f32x4 *)&sMu[ch], m1 = *(const f32x4 *)&sMu[ch + 4];
+                u32x4 p[2];
+                prev(xv[i][s][0], xv[i][s][1], ch, p[0], p[1]);
+                bf16x8 Bop[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const f32x4 xl = f4lo(xv[i][s][n]), xh = f4hi(xv[i][s][n]);
+                    const f32x4 yl = xl + (f4lo(p[n]) - xl) * m0, yh = xh + (f4hi(p[n]) - xh) * m1;
+                    Bop[n] = pack8(yl, yh);
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) acc1[m][n] = mfma(cur.a[2 * s + m], Bop[n], acc1[m][n]);
+            }
+        }
+        // (keeps the scheduler from hoisting later blocks' loads: the kP1
+        // register sets are the whole prefetch)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sRed1[w][2 * m + n][lane] = acc1[m][n];
+    lds_barrier();
+    if (w < 4) {  // tile (m, n) = (w / 2, w % 2): the sum over the waves, act
+        f32x4 sum = sRed1[0][w][lane];
+#pragma unroll
+        for (int j = 1; j < NW; ++j) sum += sRed1[j][w][lane];
+        sH1[w & 1][w >> 1][lane] = pack4(act<TANH>(sum[0]), act<TANH>(sum[1]),
+                                          act<TANH>(sum[2]), act<TANH>(sum[3]));
+    }
+    lds_barrier();
+    // act(y A1)^T of token tile n as the B operand of the mix: k-slots
+    // {4g + e, 16 + 4g + e}
+    bf16x8 Bh1[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const u32x2 lo = sH1[n][0][lane], hi = sH1[n][1][lane];
+        Bh1[n] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+
+    // ---- pass 2: m, z and (z A2)^T, in half blocks (32 channels) ----------
+    // (x_t taken as new values here: pass 1's conversions of it are
+    // recomputed, not kept alive in registers through the reduction)
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) __asm__ volatile("" : "+v"(xv[i][s][n]));
+    struct P2 {
+        bf16x8 b[2];  // B1^T operands, m^T tiles q
+        bf16x8 a[4];  // A2^T operands, rank tiles M
+    };
+    auto load2 = [&](P2 &p, int hs) {  // half step hs: block hs / 2, s = hs % 2
+        const int kb = blk(hs >> 1), s = hs & 1;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) p.b[q] = frag(kb, kFragsA1 + 2 * s + q);
+#pragma unroll
+        for (int M = 0; M < 4; ++M) p.a[M] = frag(kb, kFragsA1 + kFragsB1 + 4 * s + M);
+    };
+    f32x4 acc2[4][2];
+#pragma unroll
+    for (int M = 0; M < 4; ++M)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc2[M][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    P2 r2[kP2];
+#pragma unroll
+    for (int j = 0; j < kP2 - 1; ++j)
+        if (j < 2 * KB) load2(r2[j], j);
+#pragma unroll
+    for (int hs = 0; hs < 2 * KB; ++hs) {
+        const int i = hs >> 1, s = hs & 1;
+        if (hs + kP2 - 1 < 2 * KB) load2(r2[(hs + kP2 - 1) % kP2], hs + kP2 - 1);
+        if (live(i)) {
+            const P2 &cur = r2[hs % kP2];
+            const int ch = blk(i) * kKB + 32 * s + 8 * g;
+            const f32x4 l0 = *(const f32x4 *)&sLam[ch], l1 = *(const f32x4 *)&sLam[ch + 4];
+            u32x4 p[2];
+            prev(xv[i][s][0], xv[i][s][1], ch, p[0], p[1]);
+            bf16x8 Bz[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                // m^T rows 4 g + e of tiles q: channels ch + 4 q + e
+                const f32x4 mt0 = mfma(cur.b[0], Bh1[n], f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 mt1 = mfma(cur.b[1], Bh1[n], f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 xl = f4lo(xv[i][s][n]), xh = f4hi(xv[i][s][n]);
+                const f32x4 zl = xl + (f4lo(p[n]) - xl) * (l0 + mt0);
+                const f32x4 zh = xh + (f4hi(p[n]) - xh) * (l1 + mt1);
+                Bz[n] = pack8(zl, zh);
+            }
+#pragma unroll
+            for (int M = 0; M < 4; ++M)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) acc2[M][n] = mfma(cur.a[M], Bz[n], acc2[M][n]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int M = 0; M < 4; ++M)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sRed2[w][2 * M + n][lane] = acc2[M][n];
+    lds_barrier();
+    // h = act(z A2): wave w adds tile (M, n) = (w / 2, w % 2) over the waves
+    // and stores ranks 16 M + 4 g + e of token 2c + n
+    {
+        f32x4 sum = sRed2[0][w][lane];
+#pragma unroll
+        for (int j = 1; j < NW; ++j) sum += sRed2[j][w][lane];
+        const int row = r0 + 2 * c + (w & 1);
+        if (row < rows)
+            *(u32x2 *)(h + (size_t)row * kR2 + 16 * (w >> 1) + 4 * g) =
+                pack4(act<TANH>(sum[0]), act<TANH>(sum[1]), act<TANH>(sum[2]), act<TANH>(sum[3]));
+    }
+}
+
 // d = omega + h B2 for 64 tokens x one 64-channel head per workgroup (four
 // waves, 16 tokens each): d^T [64 ch x 16 tok] = B2^T . h^T on bf16 MFMA,
 // B2's head block staged in LDS.
@@ -265,11 +572,51 @@ __global__ __launch_bounds__(256) void lora_logits_kernel(int rows, int D,
 
 }  // namespace
 
+size_t lora_packed_bytes(int D) {
+    return D / kKB <= kOnceWaves * kOnceMaxKB ? (size_t)(D / kKB) * kFrags * 64 * 16 : 0;
+}
+
 hipError_t launch_decay_lora(int rows, int T, int D, bool tanh_act, const uint16_t *x,
                              const uint16_t *shift, const float *mu, const float *lam,
                              const uint16_t *A1, const uint16_t *B1, const uint16_t *A2,
-                             uint16_t *h, hipStream_t stream) {
+                             uint16_t *h, void *packed, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
+    const int nkb = D / kKB;
+    if (lora_packed_bytes(D) != 0) {  // the block input read once
+        if (packed == nullptr) return hipErrorInvalidValue;  // (the entry points size it)
+        const int n = nkb * kFrags * 64;
+        hipLaunchKernelGGL(lora_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, D, A1, B1, A2, (bf16x8 *)packed);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const dim3 grid((unsigned)((rows + kOnceTok - 1) / kOnceTok));
+        const int kb_per_wave = (nkb + kOnceWaves - 1) / kOnceWaves;
+        const bool aligned = T % kOnceTok == 0;  // no sequence starts inside a tile
+        auto go = [&](auto tanh_tag, auto kb_tag) {
+            constexpr bool TA = decltype(tanh_tag)::value;
+            constexpr int K = decltype(kb_tag)::value;
+            if (aligned)
+                hipLaunchKernelGGL((decay_once_kernel<TA, K, false>), grid, dim3(64 * kOnceWaves),
+                                   0, stream, rows, T, D, x, shift, mu, lam,
+                                   (const bf16x8 *)packed, h);
+            else
+                hipLaunchKernelGGL((decay_once_kernel<TA, K, true>), grid, dim3(64 * kOnceWaves),
+                                   0, stream, rows, T, D, x, shift, mu, lam,
+                                   (const bf16x8 *)packed, h);
+        };
+        auto by_kb = [&](auto tanh_tag) {
+            switch (kb_per_wave) {
+                case 1: go(tanh_tag, std::integral_constant<int, 1>{}); break;
+                case 2: go(tanh_tag, std::integral_constant<int, 2>{}); break;
+                case 3: go(tanh_tag, std::integral_constant<int, 3>{}); break;
+                case 4: go(tanh_tag, std::integral_constant<int, 4>{}); break;
+                default: go(tanh_tag, std::integral_constant<int, 5>{}); break;
+            }
+        };
+        if (tanh_act) by_kb(std::true_type{});
+        else by_kb(std::false_type{});
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((rows + kTokWG - 1) / kTokWG));
     if (tanh_act)
         hipLaunchKernelGGL(decay_lora_kernel<true>, grid, dim3(512), 0, stream, rows, T, D, x,

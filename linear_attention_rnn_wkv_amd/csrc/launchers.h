@@ -44,9 +44,11 @@ size_t rwkv4_workspace_bytes(int B, int T, int C);
 size_t chunk_workspace_bytes(int B, int T, int H);   // chunked forward, gated forward
 size_t bwd_workspace_bytes(int B, int T, int H);     // backward; forward + backward pair
 size_t bwd_states_offset(int B, int T, int H);       // where the saved chunk states start
-size_t lora_workspace_bytes(int B, int T);           // decay producer (act(z A2) per token)
+size_t lora_workspace_bytes(int B, int T, int D);    // decay producer: act(z A2), packed weights
+size_t lora_packed_offset(int B, int T);             // where the packed weights start in it
+size_t lora_packed_bytes(int D);                     // the packed weights (0: not used for D)
 size_t lora_fwd_workspace_bytes(int B, int T, int H);  // producer + chunked forward
-size_t lora_fwd_factor_offset(int B, int T, int H);  // where act(z A2) starts in it
+size_t lora_fwd_factor_offset(int B, int T, int H);  // where the producer's part starts in it
 
 // RWKV-4 time-split scan: y and the (a, b, p) state for C = H*N channels.
 // ws: rwkv4_workspace_bytes(B, T, C) bytes (may be NULL when that is 0).
@@ -84,11 +86,13 @@ hipError_t launch_wkv_chunked(bool per_token_decay, int B, int T, int H,
 // Finch decay producer (decay_lora.hip): h = act(z A2) per token, bf16
 // [rows][64], from the block input x [rows][D] (rows = B T, T tokens per
 // sequence), the shift row per sequence (NULL: zero), mu, lam [D] fp32,
-// A1 [D][32], B1 [32][D], A2 [D][64] bf16.  D a multiple of 64.
+// A1 [D][32], B1 [32][D], A2 [D][64] bf16.  D a multiple of 64.  packed:
+// lora_packed_bytes(D) bytes of scratch for the weights laid out as product
+// operands (unused when that is 0).
 hipError_t launch_decay_lora(int rows, int T, int D, bool tanh_act, const uint16_t *x,
                              const uint16_t *shift, const float *mu, const float *lam,
                              const uint16_t *A1, const uint16_t *B1, const uint16_t *A2,
-                             uint16_t *h, hipStream_t stream);
+                             uint16_t *h, void *packed, hipStream_t stream);
 // d = omega + h B2 [rows][D] fp32 (B2 [64][D] bf16, omega [D])
 hipError_t launch_lora_logits(int rows, int D, const uint16_t *h, const uint16_t *B2,
                               const float *omega, float *d, hipStream_t stream);

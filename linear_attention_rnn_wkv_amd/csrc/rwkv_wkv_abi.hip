@@ -558,7 +558,7 @@ size_t rwkv6_decay_lora_workspace_bytes(int B, int T, int D) {
     if (B < 1 || T < 1 || D < 64 || D % 64 != 0 || D / 64 > 65535 ||
         (int64_t)B * T >= ((int64_t)1 << 31))
         return 0;
-    return wkv::lora_workspace_bytes(B, T);
+    return wkv::lora_workspace_bytes(B, T, D);
 }
 
 int rwkv6_decay_lora(int B, int T, int D, int act, const rwkv_bf16 *x, const rwkv_bf16 *shift,
@@ -572,14 +572,15 @@ int rwkv6_decay_lora(int B, int T, int D, int act, const rwkv_bf16 *x, const rwk
     int st = check_lora(B, T, D, act, x, shift, mu_x, lam, A1, B1, omega, A2, B2,
                         Span{d, tok * 4});
     if (st != RWKV_OK || T == 0) return st;
-    st = check_workspace(workspace, workspace_bytes, wkv::lora_workspace_bytes(B, T),
+    st = check_workspace(workspace, workspace_bytes, wkv::lora_workspace_bytes(B, T, D),
                          lora_spans(B, T, D, x, shift, mu_x, lam, A1, B1, omega, A2, B2,
                                     Span{d, tok * 4}));
     if (st != RWKV_OK) return st;
     const int rows = B * T;
     uint16_t *h = (uint16_t *)workspace;
-    hipError_t e =
-        wkv::launch_decay_lora(rows, T, D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    void *packed = (char *)workspace + wkv::lora_packed_offset(B, T);
+    hipError_t e = wkv::launch_decay_lora(rows, T, D, act == 1, x, shift, mu_x, lam, A1, B1, A2,
+                                          h, packed, s);
     if (e != hipSuccess) return RWKV_E_HIP;
     return hip_status(wkv::launch_lora_logits(rows, D, h, B2, omega, d, s));
 }
@@ -624,9 +625,11 @@ int rwkv6_wkv_fwd_lora(int B, int T, int H, int N, const rwkv_bf16 *r, const rwk
                          spans);
     if (st != RWKV_OK) return st;
     const int rows = B * T;
-    uint16_t *h = (uint16_t *)((char *)workspace + wkv::lora_fwd_factor_offset(B, T, H));
-    hipError_t e =
-        wkv::launch_decay_lora(rows, T, (int)D, act == 1, x, shift, mu_x, lam, A1, B1, A2, h, s);
+    char *part = (char *)workspace + wkv::lora_fwd_factor_offset(B, T, H);
+    uint16_t *h = (uint16_t *)part;
+    void *packed = part + wkv::lora_packed_offset(B, T);
+    hipError_t e = wkv::launch_decay_lora(rows, T, (int)D, act == 1, x, shift, mu_x, lam, A1, B1,
+                                          A2, h, packed, s);
     if (e != hipSuccess) return RWKV_E_HIP;
     return hip_status(wkv::launch_wkv_chunked(true, B, T, H, r, k, v, nullptr, u, state_in,
                                               state_out, o, workspace, s, nullptr, nullptr,
@@ -658,7 +661,13 @@ int device_cus() { return device_attr(hipDeviceAttributeMultiprocessorCount, 256
 // particular placement to stay on one die)
 int device_xcds() { return device_attr(hipDeviceAttributeNumberOfXccs, 1, g_xcds); }
 
-size_t lora_workspace_bytes(int B, int T) { return (size_t)B * T * 64 * 2; }
+// the decay producer's scratch: act(z A2) of every token (128 bytes each),
+// then the weights laid out as product operands
+size_t lora_packed_offset(int B, int T) { return ((size_t)B * T * 64 * 2 + 255) / 256 * 256; }
+
+size_t lora_workspace_bytes(int B, int T, int D) {
+    return lora_packed_offset(B, T) + lora_packed_bytes(D);
+}
 
 // (after the chunked forward's hand-off area, and at least its control block)
 size_t lora_fwd_factor_offset(int B, int T, int H) {
@@ -666,7 +675,7 @@ size_t lora_fwd_factor_offset(int B, int T, int H) {
 }
 
 size_t lora_fwd_workspace_bytes(int B, int T, int H) {
-    return lora_fwd_factor_offset(B, T, H) + lora_workspace_bytes(B, T);
+    return lora_fwd_factor_offset(B, T, H) + lora_workspace_bytes(B, T, 64 * H);
 }
 
 }  // namespace wkv

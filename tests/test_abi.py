@@ -443,18 +443,23 @@ def test_decay_lora_checks(L):
 
 
 def test_decay_lora_workspace(L):
-    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 128) == 2 * 8 * 128
+    # act(z A2) of every token (128 bytes, rounded to 256), then the weights
+    # laid out as product operands: 16 KiB per block of 64 channels (none
+    # past 40 blocks, where the producer streams the block input twice)
+    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 128) == 2 * 8 * 128 + 2 * 16384
+    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 2560) == 2 * 8 * 128 + 40 * 16384
+    assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 2624) == 2 * 8 * 128
     assert L.rwkv6_decay_lora_workspace_bytes(2, 8, 96) == 0
     assert decay(L, ws=None) == E_NULL
-    assert decay(L, ws_bytes=2 * 8 * 128 - 1) == E_DIM
+    assert decay(L, ws_bytes=2 * 8 * 128 + 2 * 16384 - 1) == E_DIM
     assert decay(L, ws=1) == E_ALIAS          # on x
     assert decay(L, ws=10) == E_ALIAS         # on d
 
 
 def test_fused_workspace(L):
-    # the producer's factor (B T 128 bytes) after the chunked forward's
-    # hand-off area (here only its 16 KiB control block)
-    assert L.rwkv6_wkv_fwd_lora_workspace_bytes(2, 8, 2, 64) == 16384 + 2 * 8 * 128
+    # the producer's factor (B T 128 bytes) and packed weights after the
+    # chunked forward's hand-off area (here only its 16 KiB control block)
+    assert L.rwkv6_wkv_fwd_lora_workspace_bytes(2, 8, 2, 64) == 16384 + 2 * 8 * 128 + 2 * 16384
     assert fused(L, ws=None) == E_NULL
     assert fused(L, ws_bytes=100) == E_DIM
     assert fused(L, ws=1) == E_ALIAS          # on r

@@ -1024,9 +1024,13 @@ def assert_logits_close(got, ref, omega, what):
 
 @pytest.mark.parametrize("act", ["tanh", "identity"])
 @pytest.mark.parametrize("B,T,H,shift", [(1, 1, 1, True), (1, 17, 2, False), (2, 130, 4, True),
-                                         (3, 50, 3, False), (1, 300, 40, True)])
+                                         (3, 50, 3, False), (1, 300, 40, True), (2, 64, 5, False),
+                                         (3, 96, 40, True), (2, 160, 41, False)])
 def test_decay_lora_vs_oracle(act, B, T, H, shift):
-    # 128-token tiles: T = 130 and T = 50 put sequence starts inside a tile
+    # 32-token tiles: T = 1, 17, 130, 50 and 300 put sequence starts inside
+    # a tile; T = 64, 96 and 160 do not (each tile's first token takes the
+    # row before it, the shift row or zero).  H = 40: five channel blocks per
+    # wave; H = 41: past that, the two-pass kernel.
     print(f"decay producer {act} B={B} T={T} H={H} shift={shift}", flush=True)
     d = lora_case(B, T, H, 60 + T + H, shift=shift)
     g = lora_dev(d)
