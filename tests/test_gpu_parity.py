@@ -1152,6 +1152,23 @@ def test_fused_forward_full_workload_every_head():
     print("state", assert_heads_close(f64_host(so), s_ref, (2, 3), "state"), flush=True)
 
 
+def test_decay_lora_full_workload_every_token():
+    # the producer alone (fp32 logits to memory) at workload 4's shape, five
+    # blocks per wave, 1024 tiles of 32 tokens: every logit against the oracle
+    spec = S.WORKLOADS[4]
+    B, T, H = spec["B"], spec["T"], spec["H"]
+    print(f"decay producer workload 4: B={B} T={T} D={H * 64}", flush=True)
+    d = S.decay_lora_inputs(B, T, H, 64, 4)
+    g = lora_dev(d)
+    got = W.rwkv6_decay_lora(g["xin"], g["mu_x"], g["lam"], g["A1"], g["B1"], g["omega"],
+                             g["A2"], g["B2"], act="tanh", shift=g["shift"])
+    sync()
+    print("gpu done; oracle producer", flush=True)
+    ref = lora_ref(d)
+    for b in range(B):  # (per sequence: every token of every sequence)
+        assert_logits_close(f64_host(got[b]), ref[b], d["omega"], f"d, sequence {b}")
+
+
 # ---------------------------------------------------------------------------
 # The training pair: a forward that keeps the chunk states for the backward,
 # and the backward that reads them instead of recomputing them.  Both are the
