@@ -1152,6 +1152,40 @@ def test_fused_forward_full_workload_every_head():
     print("state", assert_heads_close(f64_host(so), s_ref, (2, 3), "state"), flush=True)
 
 
+def test_fused_forward_graph_replays():
+    # the producer (its operand packing rewrites the workspace each call) and
+    # the forward it feeds, captured once and replayed on changing inputs;
+    # T = 300: tiles with sequence starts inside; H = 40: five channel blocks
+    # per wave
+    B, T, H = 2, 300, 40
+    print(f"fused forward graph B={B} T={T} H={H}", flush=True)
+    cases = [(matrix_case(B, T, H, 900 + i, True), lora_case(B, T, H, 900 + i)) for i in range(2)]
+    m0, d0 = cases[0]
+    g, md = lora_dev(d0), matrix_inputs_dev(m0)
+    o = torch.empty_like(md["r"])
+    so = torch.empty_like(md["s0"])
+    ws = W.new_workspace(W.fwd_lora_workspace_bytes(B, T, H))
+    graph = capture(lambda: W.rwkv6_wkv_fwd_lora(
+        md["r"], md["k"], md["v"], g["xin"], g["mu_x"], g["lam"], g["A1"], g["B1"], g["omega"],
+        g["A2"], g["B2"], md["u"], act="tanh", shift=g["shift"], state_in=md["s0"],
+        state_out=so, o=o, workspace=ws))
+    f = S.bf16_to_f32
+    for m, d in cases + cases:
+        for n, t in lora_dev(d).items():
+            if t is not None:
+                g[n].copy_(t)
+        for n, t in matrix_inputs_dev(m).items():
+            md[n].copy_(t)
+        sync()
+        graph.replay()
+        sync()
+        x = lora_ref(d).reshape(B, T, H, 64).astype(np.float32)
+        o_ref, s_ref = oracle.wkv_matrix(f(m["r"]), f(m["k"]), f(m["v"]), x, m["u"], m["s0"])
+        assert_matrix_close(bf16_host(o), o_ref, "o")
+        assert_matrix_close(f64_host(so), s_ref, "state")
+    W.workspace_status(ws, graph.side_stream)
+
+
 def test_decay_lora_full_workload_every_token():
     # the producer alone (fp32 logits to memory) at workload 4's shape, five
     # blocks per wave, 1024 tiles of 32 tokens: every logit against the oracle
