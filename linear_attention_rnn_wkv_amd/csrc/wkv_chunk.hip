@@ -146,6 +146,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     __shared__ __align__(16) uint16_t sB2[LORA ? kN * kPC : 1];
     __shared__ __align__(16) float sD[LORA ? NW : 1][LORA ? 4 * TP : 1][LORA ? kDP : 1];
 
+    // SAVE with no outputs (the backward's recomputation): the chunk states
+    // need neither r nor the output products, so r is not read, the r~ and
+    // decayed-state tiles are not staged, and only P3 runs (uniform)
+    const bool states_only = SAVE && o == nullptr;
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -464,7 +469,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             khl[1] = kh[1] - bf16_hi(hi.x);
             khl[2] = kh[2] - bf16_lo(hi.y);
             khl[3] = kh[3] - bf16_hi(hi.y);
-            *(u32x2 *)(sm[set][T_RS] + tau * pitch(T_RS) + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
+            if (!states_only)
+                *(u32x2 *)(sm[set][T_RS] + tau * pitch(T_RS) + 4 * cx.cq) = pack4(rt[0], rt[1], rt[2], rt[3]);
             *(u32x2 *)(sm[set][T_KRH] + tau * pitch(T_KRH) + 4 * cx.cq) = hi;
             *(u32x2 *)(sm[set][T_KRL] + tau * pitch(T_KRL) + 4 * cx.cq) = pack4(khl[0], khl[1], khl[2], khl[3]);
             bs[e] = row_sum16(sb);  // bonus r_t diag(u) k_t^T over the token's 64 channels
@@ -492,8 +498,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         for (int t = 0; t < NT; ++t) {
             const f32x4 dd = *(const f32x4 *)&sDecay[w][skey(t) + 4 * g];
             SD[t] = S[t] * dd;
-            *(u32x2 *)(sm[set][T_ST] + (sval(t) + c) * pitch(T_ST) + skey(t) + 4 * g) =
-                pack4(SD[t][0], SD[t][1], SD[t][2], SD[t][3]);
+            if (!states_only)
+                *(u32x2 *)(sm[set][T_ST] + (sval(t) + c) * pitch(T_ST) + skey(t) + 4 * g) =
+                    pack4(SD[t][0], SD[t][1], SD[t][2], SD[t][3]);
         }
     };
 
@@ -502,14 +509,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     auto matrix_p = [&](auto tile, int set) {
         constexpr int P = decltype(tile)::value;
         f32x4 at[P + 1];
+        if (!states_only) {
 #pragma unroll
-        for (int q = 0; q <= P; ++q) {  // P1: A^T tiles (sigma-tile q, tau-tile P)
-            at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q <= P; ++q) {  // P1: A^T tiles (sigma-tile q, tau-tile P)
+                at[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 A = lds8(sm[set][T_KRH] + (16 * q + c) * pitch(T_KRH) + 32 * kb + 8 * g);
-                const bf16x8 B = lds8(sm[set][T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
-                at[q] = mfma(A, B, at[q]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 A = lds8(sm[set][T_KRH] + (16 * q + c) * pitch(T_KRH) + 32 * kb + 8 * g);
+                    const bf16x8 B = lds8(sm[set][T_RS] + (16 * P + c) * pitch(T_RS) + 32 * kb + 8 * g);
+                    at[q] = mfma(A, B, at[q]);
+                }
             }
         }
         // P3: S' = diag(decay) S + (K^_hi + K^_lo)^T V (independent of P1)
@@ -533,6 +542,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) S[t] = SD[t];
+        if (states_only) return;
         // P2 part 2: (decayed S)^T R~^T
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) ot[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -583,7 +593,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
     u32x2 gq[EPI ? NT : 1];
     auto load_in = [&](int ch) {  // (past the job's chunks: issued, empty)
         const bool ok = ch < ch_end;
-        load_rkv<NW>(buf, ch * kL, cx, r, k, v, ok);
+        load_rkv<NW>(buf, ch * kL, cx, r, k, v, ok, !states_only);
         if (GST) {
             const int c0 = ch * kL;
             const Rsrc rg = rsrc(gate + cx.base(ok ? c0 : 0), ok ? cx.span(c0) : 0u);

@@ -129,15 +129,18 @@ struct Ctx {
 // valid false the loads are still issued, over an empty range, and read
 // zero: a load issued on every path keeps the count of outstanding memory
 // operations the same on all of them, so that a later wait for an older
-// load is not made to wait for this one too.
+// load is not made to wait for this one too.  With_r false does the same
+// for r alone (reads zero, no memory traffic).
 template <int NW>
 __device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
                                          const uint16_t *r, const uint16_t *k,
-                                         const uint16_t *v, bool valid = true) {
+                                         const uint16_t *v, bool valid = true,
+                                         bool with_r = true) {
     constexpr int TP = Raw<NW>::TP;
     const size_t cb = cx.base(valid ? c0 : 0);
     const uint32_t span = valid ? cx.span(c0) : 0u;
-    const Rsrc rr = rsrc(r + cb, span), rk = rsrc(k + cb, span), rv = rsrc(v + cb, span);
+    const Rsrc rr = rsrc(r + cb, with_r ? span : 0u), rk = rsrc(k + cb, span),
+               rv = rsrc(v + cb, span);
 #pragma unroll
     for (int e = 0; e < TP; ++e) {
         const uint32_t off = cx.off_rk + e * cx.tokb;
