@@ -261,10 +261,11 @@ def lora_wkv_bytes(B, T, H, N=64):
 
 
 def finch_recompute_bytes(B, T, H, N=64, L=64):
-    # the backward's state recomputation: read r, k, v (bf16), x (fp32), u and
-    # the initial states; write the state entering every chunk and the last
+    # the backward's state recomputation: read k, v (bf16), x (fp32) and the
+    # initial states (the states need no r); write the state entering every
+    # chunk and the last
     tok, nch = B * T * H * N, (T + L - 1) // L
-    return tok * (2 * 3 + 4) + B * H * N * N * 4 + B * H * (nch + 1) * N * N * 4 + H * N * 4
+    return tok * (2 * 2 + 4) + B * H * N * N * 4 + B * H * (nch + 1) * N * N * 4
 
 
 def finch_reverse_bytes(B, T, H, N=64, L=64):
