@@ -33,7 +33,9 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing, frees nothing and never synchronises a stream inside
  *    a call; its only state is a per-device cache of two attributes (compute
- *    units and XCDs) read on first use.
+ *    units and XCDs) read on first use, and the device address of the static
+ *    scratch array of rwkv6_wkv_fwd_noalloc (part of the code object, one per
+ *    device), looked up on that entry point's first call on a device.
  *  - Layouts are row-major, channel fastest: [B][T][H][N] is the same memory
  *    as [B][T][D] with D = H*N and head h owning channels [h*N, (h+1)*N).
  *  - bf16 tensors hold raw bfloat16 bits (rwkv_bf16); outputs are rounded to
