@@ -272,6 +272,12 @@ constexpr int kStreamNT = 2;
 
 // rank k-slot j of lane group g
 __device__ __forceinline__ int kslot(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+// b, or zeros when keep is false
+__device__ __forceinline__ bf16x8 zero_unless(bool keep, const bf16x8 &b) {
+    const u32x4 u = __builtin_bit_cast(u32x4, b);
+    const u32x4 z = {keep ? u.x : 0u, keep ? u.y : 0u, keep ? u.z : 0u, keep ? u.w : 0u};
+    return __builtin_bit_cast(bf16x8, z);
+}
 
 // One thread per (block, fragment, lane): the 8 bf16 of that lane's operand.
 __global__ void lora_pack_kernel(int D, const uint16_t *__restrict__ A1,
@@ -308,8 +314,10 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
     const float *__restrict__ mu, const float *__restrict__ lam,
     const bf16x8 *__restrict__ packed, uint16_t *__restrict__ h) {
     constexpr int NW = kOnceWaves;
-    __shared__ __align__(16) float sMu[kOnceMaxD], sLam[kOnceMaxD];
-    __shared__ __align__(16) uint16_t sBnd[kOnceMaxD];  // x_{t-1} of the tile's first token
+    // (mu, lam and the boundary row are staged by every thread, unconditionally:
+    // 1024 x 4 floats and 512 x 8 bf16, zero past D)
+    __shared__ __align__(16) float sMu[4 * 1024], sLam[4 * 1024];
+    __shared__ __align__(16) uint16_t sBnd[8 * 512];  // x_{t-1} of the tile's first token
     __shared__ __align__(16) f32x4 sRed1[NW][4][64];    // partial (y A1)^T: [wave][2 m + n]
     __shared__ __align__(16) u32x2 sH1[2][2][64];       // act(y A1)^T, bf16: [n][m]
     __shared__ __align__(16) f32x4 sRed2[NW][8][64];    // partial (z A2)^T: [wave][2 M + n]
@@ -335,6 +343,7 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
         slam[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rlam, (tid + 512 * j) * 16, 0, 0));
     }
     const u32x4 sb = __builtin_amdgcn_raw_buffer_load_b128(rbnd, tid * 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // (issued first: their LDS writes wait for them)
 
     // this lane's x_t: token 2c + n of the tile, channels 32 s + 8 g .. + 7
     // of each of its blocks (rows past the end read zero and store nothing)
@@ -343,14 +352,15 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
     auto blk = [&](int i) { return min(w + NW * i, nkb - 1); };  // (past the last: reread, unused)
     auto live = [&](int i) { return w + NW * i < nkb; };
     u32x4 xv[KB][2][2];
-#pragma unroll
-    for (int i = 0; i < KB; ++i)
+    auto load_x = [&](int i) {  // (issued with pass 1's operands of block i, so that
+                                // pass 1 computes while later blocks arrive)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int so = blk(i) * kKB * 2 + 64 * s;
             xv[i][s][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo0, so, kStreamNT);
             xv[i][s][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, vo1, so, kStreamNT);
         }
+    };
     const Rsrc rp = rsrc(packed, (uint32_t)nkb * kFrags * 64 * 16);
     auto frag = [&](int kb, int f) {
         return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -380,40 +390,46 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
         }
     };
 
-    // stage mu, lam and the boundary row
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = 4 * (tid + 512 * j);
-        if (e < D) {
-            *(f32x4 *)&sMu[e] = smu[j];
-            *(f32x4 *)&sLam[e] = slam[j];
-        }
-    }
-    if (8 * tid < D) *(u32x4 *)&sBnd[8 * tid] = sb;
-
     // ---- pass 1: (y A1)^T, this wave's blocks, kP1 - 1 blocks of operands
     // ahead
     struct P1 {
         bf16x8 a[4];  // A1^T operands (s, m)
     };
     auto load1 = [&](P1 &p, int i) {
+        load_x(i);
 #pragma unroll
         for (int f = 0; f < kFragsA1; ++f) p.a[f] = frag(blk(i), f);
     };
+    P1 r1[kP1];
+    // the first block's rows and operands go out before the staging waits
+#pragma unroll
+    for (int j = 0; j < kP1 - 1; ++j)
+        if (j < KB) load1(r1[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage mu, lam and the boundary row
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = 4 * (tid + 512 * j);
+        *(f32x4 *)&sMu[e] = smu[j];
+        *(f32x4 *)&sLam[e] = slam[j];
+    }
+    *(u32x4 *)&sBnd[8 * tid] = sb;
+
     f32x4 acc1[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n) acc1[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    P1 r1[kP1];
-#pragma unroll
-    for (int j = 0; j < kP1 - 1; ++j)
-        if (j < KB) load1(r1[j], j);
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
         if (i + kP1 - 1 < KB) load1(r1[(i + kP1 - 1) % kP1], i + kP1 - 1);
-        if (live(i)) {
+        __builtin_amdgcn_sched_barrier(0);  // (the loads stay ahead of the block's products)
+        {
+            // (no branch on a dead block, a repeat of the last one: its
+            // operand is zeroed instead, so that the loads above stay where
+            // they are rather than being moved into the branch)
+            const bool lv = live(i);
             const P1 &cur = r1[i % kP1];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -426,7 +442,7 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
                 for (int n = 0; n < 2; ++n) {
                     const f32x4 xl = f4lo(xv[i][s][n]), xh = f4hi(xv[i][s][n]);
                     const f32x4 yl = xl + (f4lo(p[n]) - xl) * m0, yh = xh + (f4hi(p[n]) - xh) * m1;
-                    Bop[n] = pack8(yl, yh);
+                    Bop[n] = zero_unless(lv, pack8(yl, yh));
                 }
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
@@ -493,7 +509,8 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
     for (int hs = 0; hs < 2 * KB; ++hs) {
         const int i = hs >> 1, s = hs & 1;
         if (hs + kP2 - 1 < 2 * KB) load2(r2[(hs + kP2 - 1) % kP2], hs + kP2 - 1);
-        if (live(i)) {
+        {
+            const bool lv = live(i);
             const P2 &cur = r2[hs % kP2];
             const int ch = blk(i) * kKB + 32 * s + 8 * g;
             const f32x4 l0 = *(const f32x4 *)&sLam[ch], l1 = *(const f32x4 *)&sLam[ch + 4];
@@ -508,7 +525,7 @@ __global__ __launch_bounds__(64 * kOnceWaves, 1) void decay_once_kernel(
                 const f32x4 xl = f4lo(xv[i][s][n]), xh = f4hi(xv[i][s][n]);
                 const f32x4 zl = xl + (f4lo(p[n]) - xl) * (l0 + mt0);
                 const f32x4 zh = xh + (f4hi(p[n]) - xh) * (l1 + mt1);
-                Bz[n] = pack8(zl, zh);
+                Bz[n] = zero_unless(lv, pack8(zl, zh));
             }
 #pragma unroll
             for (int M = 0; M < 4; ++M)
