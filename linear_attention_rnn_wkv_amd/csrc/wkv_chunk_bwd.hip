@@ -246,6 +246,11 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
 
     // chunks [ch_lo, ch_hi) of the current head, from the last
     auto run = [&](int ch_hi, int ch_lo) {
+    // Finch: the decay logits of the next chunk in sweep order are requested
+    // a chunk ahead, after this chunk's operands and before its gradient
+    // stores, so that stage A waits neither for them nor for the stores
+    Raw<NW> xn;
+    if (PT) load_x<NW>(xn, (ch_hi - 1) * kL, cx, x, ch_hi > ch_lo);
     for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
         const int c0 = ch * kL;
         // The lane indices, opaque to the compiler inside each chunk: the
@@ -256,7 +261,6 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
         asm volatile("" : "+v"(c), "+v"(g));
         // ---- operands of the chunk ----------------------------------------
         Raw<NW> d;
-        if (PT) load_x<NW>(d, c0, cx, x);
         load_rkv<NW>(d, c0, cx, r, k, v);
         u32x4 dov[Raw<NW>::NV];
         {
@@ -271,6 +275,11 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
             const float *Sc = chunk_states + ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
 #pragma unroll
             for (int q = 0; q < 2; ++q) scv[q] = *(const f32x4 *)(Sc + sc_row * kN + sc_col + 4 * q);
+        }
+        if (PT) {
+#pragma unroll
+            for (int e = 0; e < TP; ++e) d.x[e] = xn.x[e];
+            load_x<NW>(xn, (ch - 1) * kL, cx, x, ch > ch_lo);
         }
 
         // ---- stage A: log2 decays and their in-wave scan -------------------
