@@ -262,12 +262,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
                 S[t][e] = state_in ? state_in[base + sidx(t, e)] : 0.0f;
     };
     // the state entering chunk ch of the current head (SAVE)
+    // A lane holds rows 4 g + e (e = 0..3) of column c of each of its state
+    // tiles; a 4 x 4 transpose inside each quad of lanes (two DPP exchanges,
+    // lane bit 1 with register bit 1, then bit 0 with bit 0) gives lane c
+    // row 4 g + (c & 3), columns 4 (c >> 2) .. + 3, stored as one 16-byte
+    // write instead of four 4-byte ones (the memory pipeline the next
+    // chunk's loads queue in is shared with these stores).
     auto save_chunk = [&](int ch) {
         const size_t base = ((size_t)bh * (nchunks + 1) + ch) * kN * kN;
+        const int q = c & 3;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) chunk_states[base + sidx(t, e)] = S[t][e];
+        for (int t = 0; t < NT; ++t) {
+            f32x4 x = S[t];
+            f32x4 y = {dpp<0x4e>(x[0]), dpp<0x4e>(x[1]), dpp<0x4e>(x[2]), dpp<0x4e>(x[3])};
+            if (q & 2) x[0] = y[2], x[1] = y[3];
+            else x[2] = y[0], x[3] = y[1];
+            y = f32x4{dpp<0xb1>(x[0]), dpp<0xb1>(x[1]), dpp<0xb1>(x[2]), dpp<0xb1>(x[3])};
+            if (q & 1) x[0] = y[1], x[2] = y[3];
+            else x[1] = y[0], x[3] = y[2];
+            *(f32x4 *)(chunk_states + base + (size_t)(skey(t) + 4 * g + q) * kN + sval(t) +
+                       4 * (c >> 2)) = x;
+        }
     };
     auto save_state = [&]() {
         if (SAVE) save_chunk(nchunks);
