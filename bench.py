@@ -460,13 +460,16 @@ def run_finch_bwd(torch, W, S, H2D, args, d4=None):
     return res
 
 
-RWKV4_COPIES = 8  # 8 x 75.65 MB: a copy's bytes leave the 256 MB cache between uses
+# 32 x 75.65 MB = 2.4 GB between two uses of a copy.  With the kernel's
+# non-temporal loads, 8 copies (605 MB) still let part of the inputs come from
+# the 256 MB cache (18.4 against 19.4 us per launch); 32 and more read HBM.
+RWKV4_COPIES = 32
 
 
 def run_rwkv4(torch, W, S, H2D, args, flush_buf):
     """RWKV-4 scan, B8 T1024 C768.  Main figure: back-to-back launches that
-    cycle through 8 copies of the inputs and outputs (each launch reads its
-    k, v from HBM), timed between two events.  Also: single launches after a
+    cycle through RWKV4_COPIES copies of the inputs and outputs (each launch
+    reads its k, v from HBM), timed between two events.  Also: single launches after a
     read of a 1 GiB buffer that evicts the caches, each between its own pair
     of events (that figure includes the events' own overhead)."""
     spec = S.WORKLOADS[2]

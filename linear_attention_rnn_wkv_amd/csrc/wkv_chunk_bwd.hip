@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void wkv_bwd_kernel(
 #pragma unroll
             for (int j = 0; j < Raw<NW>::NV; ++j)
                 dov[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, cx.off_v + j * 8 * NW * cx.tokb,
-                                                               0, 0);
+                                                               0, kReadOnce);
         }
         f32x4 scv[2];
         {

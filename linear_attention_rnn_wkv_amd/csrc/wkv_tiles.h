@@ -114,6 +114,11 @@ __device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
 }
 
+// cache policy of the loads of r, k, v and the decay logits, each byte of
+// which a kernel reads once: non-temporal (measured 1 % faster on the Finch
+// forward and 3.5 % on the Eagle forward, the same bytes read)
+constexpr int kReadOnce = 2;
+
 struct Ctx {
     int T, tq, cq, vt, vo;
     size_t seq_base, tok_stride;  // elements
@@ -144,12 +149,13 @@ __device__ __forceinline__ void load_rkv(Raw<NW> &d, int c0, const Ctx &cx,
 #pragma unroll
     for (int e = 0; e < TP; ++e) {
         const uint32_t off = cx.off_rk + e * cx.tokb;
-        d.r[e] = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
-        d.k[e] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+        d.r[e] = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, kReadOnce);
+        d.k[e] = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, kReadOnce);
     }
 #pragma unroll
     for (int j = 0; j < Raw<NW>::NV; ++j)
-        d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0, 0);
+        d.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cx.off_v + j * 8 * NW * cx.tokb, 0,
+                                                       kReadOnce);
 }
 
 // one thread's Finch decay logits of chunk c0 (rows past T read as zero;
@@ -162,7 +168,8 @@ __device__ __forceinline__ void load_x(Raw<NW> &d, int c0, const Ctx &cx, const 
 #pragma unroll
     for (int e = 0; e < TP; ++e)
         d.x[e] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (cx.off_rk + e * cx.tokb), 0, 0));
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * (cx.off_rk + e * cx.tokb), 0,
+                                                         kReadOnce));
 }
 
 }  // namespace tiles

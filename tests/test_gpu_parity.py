@@ -179,6 +179,20 @@ def test_rwkv4_large_keys():
     rwkv4_check(S.rwkv4_inputs(2, 300, 24, 7, k_sigma=25.0))
 
 
+def test_rwkv4_extreme_decay_and_bonus():
+    # A wave holds 32 channels.  Channels 40, 41 decay by e^-60 and e^-300
+    # per step and channel 45 has the bonus u = 40, so |u - w| > 30 in the
+    # second block of 32: that wave's replay takes the output's own
+    # exponential, the other blocks' the fold's.  T spans several passes, so
+    # the chain carries the extreme channels' states too.
+    print("rwkv4 extreme decay and bonus", flush=True)
+    d = S.rwkv4_inputs(2, 600, 96, 11, k_sigma=2.0)
+    d["w"] = d["w"].copy()
+    d["u"] = d["u"].copy()
+    d["w"][40], d["w"][41], d["u"][45] = 60.0, 300.0, 40.0
+    rwkv4_check(d)
+
+
 def test_rwkv4_state_handoff():
     print("rwkv4 state handoff", flush=True)
     d = S.rwkv4_inputs(2, 700, 48, 8, k_sigma=2.0)
