@@ -57,9 +57,24 @@ def parse():
 
 
 def source_hash(name):
-    path = os.path.join(ROOT, "linear_attention_rnn_wkv_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 over a kernel source and the headers
+    of this package that it includes, directly or through other headers, so
+    that counters taken before a change to any of them no longer match."""
+    import re
+    csrc = os.path.join(ROOT, "linear_attention_rnn_wkv_amd", "csrc")
+    h = hashlib.sha256()
+    seen, todo = set(), [name]
+    while todo:
+        n = todo.pop(0)
+        path = os.path.join(csrc, n)
+        if n in seen or not os.path.isfile(path):
+            continue
+        seen.add(n)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(n.encode() + b"\0" + data)
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', data)]
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_src, per_launch_key):
