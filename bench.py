@@ -709,13 +709,13 @@ PMC_PATHS = {  # bench path -> (kernel name fragment, source file, algorithmic b
                             lambda: lora_producer_bytes(8, 4096, 40)),
     "finch_lora_wkv": ("wkv_chunk_kernel<true, 8, false, false, true>", "wkv_chunk.hip",
                        lambda: lora_wkv_bytes(8, 4096, 40)),
-    "finch_decode": ("wkv_step_kernel<true>", "wkv_step.hip",
+    "finch_decode": ("wkv_step_kernel<true, false>", "wkv_step.hip",
                      lambda: decode_bytes_per_step(256, 64)),
-    "eagle_decode": ("wkv_step_kernel<false>", "wkv_step.hip",
+    "eagle_decode": ("wkv_step_kernel<false, false>", "wkv_step.hip",
                      lambda: eagle_decode_bytes_per_step(256, 64)),
     "rwkv4_decode": ("rwkv4_decode4_kernel", "rwkv4_step.hip",
                      lambda: rwkv4_decode_bytes_per_step(256, 4096)),
-    "finch_decode_B1024": ("wkv_step_kernel<true>", "wkv_step.hip",
+    "finch_decode_B1024": ("wkv_step_kernel<true, true>", "wkv_step.hip",
                            lambda: decode_bytes_per_step(1024, 64)),
 }
 PMC_DIRS = {"finch_fwd": "finch", "eagle_fwd": "eagle", "rwkv4_fwd": "rwkv4",

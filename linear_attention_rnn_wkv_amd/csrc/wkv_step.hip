@@ -27,6 +27,14 @@ namespace {
 
 constexpr int kN = 64;
 constexpr int kHeadsPerBlock = 4;
+// States larger than this are loaded and stored non-temporal.  A state that
+// (mostly) fits the 256 MiB last-level cache is partly served from it on the
+// next step, and the non-temporal accesses would forgo that; past about 1.4
+// times the cache nothing of it survives until the next step, and they stream
+// faster.  Measured per step at 64 heads: 320 MiB state 118.1 us plain against
+// 121.3 us non-temporal, 384 MiB 151.9 against 146.0 us, 1 GiB 417 against
+// 399 us.
+constexpr size_t kStreamStateBytes = (size_t)352 << 20;
 
 __device__ __forceinline__ float wave_sum(float s) {
 #pragma unroll
@@ -34,7 +42,7 @@ __device__ __forceinline__ float wave_sum(float s) {
     return s;
 }
 
-template <bool PT>
+template <bool PT, bool NT>
 __global__ __launch_bounds__(256) void wkv_step_kernel(
     int BH, int T, int H, const uint16_t *__restrict__ r, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ x, const float *__restrict__ u,
@@ -50,7 +58,10 @@ __global__ __launch_bounds__(256) void wkv_step_kernel(
     float *sp = state + (size_t)head * kN * kN + g * kN + 4 * c4;
     f32x4 S[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) S[m] = *(const f32x4 *)(sp + m * 4 * kN);
+    for (int m = 0; m < 16; ++m) {
+        const f32x4 *src = (const f32x4 *)(sp + m * 4 * kN);
+        S[m] = NT ? __builtin_nontemporal_load(src) : *src;
+    }
 
     const float uu = u[h * kN + lane];
     const float w_head = PT ? 0.0f : exp_fast(-exp_fast(x[h * kN + lane]));
@@ -90,7 +101,11 @@ __global__ __launch_bounds__(256) void wkv_step_kernel(
     }
 
 #pragma unroll
-    for (int m = 0; m < 16; ++m) *(f32x4 *)(sp + m * 4 * kN) = S[m];
+    for (int m = 0; m < 16; ++m) {
+        f32x4 *dst = (f32x4 *)(sp + m * 4 * kN);
+        if (NT) __builtin_nontemporal_store(S[m], dst);
+        else *dst = S[m];
+    }
 }
 
 }  // namespace
@@ -100,12 +115,11 @@ hipError_t launch_wkv_step(bool per_token_decay, int B, int T, int H, const uint
                            const float *u, float *state, uint16_t *o, hipStream_t stream) {
     const int64_t BH = (int64_t)B * H;
     const int64_t blocks = (BH + kHeadsPerBlock - 1) / kHeadsPerBlock;
-    if (per_token_decay)
-        hipLaunchKernelGGL(wkv_step_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (int)BH, T, H, r, k, v, x, u, state, o);
-    else
-        hipLaunchKernelGGL(wkv_step_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                           stream, (int)BH, T, H, r, k, v, x, u, state, o);
+    const bool nt = (size_t)BH * kN * kN * sizeof(float) > kStreamStateBytes;
+    auto kernel = per_token_decay ? (nt ? wkv_step_kernel<true, true> : wkv_step_kernel<true, false>)
+                                  : (nt ? wkv_step_kernel<false, true> : wkv_step_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (int)BH, T, H, r, k,
+                       v, x, u, state, o);
     return hipGetLastError();
 }
 

@@ -490,6 +490,38 @@ def test_step_split_anywhere_is_bitwise(per_token):
 
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
+def test_step_large_state_same_bits(per_token):
+    # 384 sequences x 64 heads: a 384 MiB state, above the size from which the
+    # step loads and stores its state non-temporal.  Every (sequence, head) is
+    # independent, so sequences 0, 1, 382 and 383 must come out bit-identical
+    # to a call on those four alone, whose 4 MiB state takes plain accesses.
+    print(f"step large state {'finch' if per_token else 'eagle'}", flush=True)
+    B, T, H, N = 384, 2, 64, 64
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device="cuda")
+
+    r, k, v = ((rnd(B, T, H, N) / 8).bfloat16() for _ in range(3))
+    x = (torch.rand(B, T, H, N, generator=gen, device="cuda") if per_token
+         else torch.rand(H, N, generator=gen, device="cuda")) * -5.5 - 0.5
+    u = rnd(H, N) * 0.5
+    s0 = rnd(B, H, N, N) * 0.1
+    fn = W.rwkv6_wkv_step if per_token else W.rwkv5_wkv_step
+    big = s0.clone()
+    o_big = fn(r, k, v, x, u, big)
+    pick = torch.tensor([0, 1, B - 2, B - 1], device="cuda")
+
+    def sel(t):
+        return t.index_select(0, pick).contiguous()
+
+    small = sel(s0)
+    o_small = fn(sel(r), sel(k), sel(v), sel(x) if per_token else x, u, small)
+    sync()
+    assert torch.equal(o_small, sel(o_big)) and torch.equal(small, sel(big))
+
+
+@pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 @pytest.mark.parametrize("T", [64, 200])
 def test_step_and_chunked_agree(per_token, T):
     # The two modes carry one fp32 state layout; the chunked mode sums in
