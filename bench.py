@@ -790,7 +790,8 @@ def measure_stream(torch, nbytes=1 << 30, reps=10):
     """Achievable HBM bandwidth on this GPU: plain streaming kernels
     (libstream_probe.so: 16-byte loads / stores, eight in flight per thread)
     reading, copying and writing 1 GiB buffers (four times the last-level
-    cache), best launch shape of a small sweep, median of `reps` launches."""
+    cache), best launch shape and cache policy (plain or non-temporal loads
+    and stores) of a small sweep, median of `reps` launches."""
     import ctypes
     from linear_attention_rnn_wkv_amd import _build
     L = ctypes.CDLL(_build.PROBE_LIBRARY)
@@ -802,12 +803,18 @@ def measure_stream(torch, nbytes=1 << 30, reps=10):
     sink = torch.empty(1 << 14, dtype=torch.uint8, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = {"kind": "plain streaming kernels of this repository over 1 GiB buffers "
-                   "(read; copy = read + write; write), best of a launch-shape sweep",
+                   "(read; copy = read + write; write), best of a launch-shape and "
+                   "cache-policy sweep",
            "bytes": nbytes}
-    for kind, name, moved in ((0, "read", nbytes), (1, "copy", 2 * nbytes), (2, "write", nbytes)):
+    # probe kinds per operation: (kind, cache policy)
+    kinds = {"read": ((0, "plain"), (3, "non-temporal")),
+             "copy": ((1, "plain"), (6, "non-temporal loads"), (4, "non-temporal")),
+             "write": ((2, "plain"), (5, "non-temporal"))}
+    for name, moved in (("read", nbytes), ("copy", 2 * nbytes), ("write", nbytes)):
         best = None
-        for blocks, threads in ((1024, 256), (2048, 256), (4096, 256), (2048, 512)):
-            dst = sink if kind == 0 else b
+        for (kind, policy), (blocks, threads) in ((kp, bt) for kp in kinds[name] for bt in (
+                (1024, 256), (2048, 256), (4096, 256), (2048, 512))):
+            dst = sink if name == "read" else b
 
             def go():
                 st = L.stream_probe(kind, a.data_ptr(), dst.data_ptr(), nbytes, blocks, threads,
@@ -829,10 +836,11 @@ def measure_stream(torch, nbytes=1 << 30, reps=10):
             ms.sort()
             gbs = moved / (ms[len(ms) // 2] / 1e3) / 1e9
             if best is None or gbs > best[0]:
-                best = (gbs, blocks, threads)
+                best = (gbs, blocks, threads, policy)
         out[f"{name}_GBps"] = best[0]
         out[f"{name}_frac_of_peak"] = best[0] / HBM_PEAK_GBS
         out[f"{name}_launch"] = [best[1], best[2]]
+        out[f"{name}_policy"] = best[3]
     out["copy_GBps_torch"] = measure_torch_copy(torch, a, b, reps)
     del a, b
     return out

@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
 #pragma unroll
             for (int j = 0; j < (GST ? Raw<NW>::NV : 1); ++j)
                 graw[j] = __builtin_amdgcn_raw_buffer_load_b128(rg, cx.off_v + j * 8 * NW * cx.tokb,
-                                                                0, 0);
+                                                                0, kReadOnce);
         }
     };
     auto gate_lds = [&](int set) {
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
         const uint32_t off = (uint32_t)(16 * p + c) * cx.tokb + 2 * (16 * NT * hf + 4 * g);
 #pragma unroll
         for (int ni = 0; ni < (EPI ? NT : 1); ++ni)
-            gq[ni] = __builtin_amdgcn_raw_buffer_load_b64(rg, off + 32 * ni, 0, 0);
+            gq[ni] = __builtin_amdgcn_raw_buffer_load_b64(rg, off + 32 * ni, 0, kReadOnce);
     };
     auto silu = [](float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_fast(-z)); };
 
@@ -871,7 +871,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void wkv_chunk_kernel(
             const uint32_t off = (uint32_t)tok * cx.tokb + 2 * (CPT * qq);
 #pragma unroll
             for (int hh = 0; hh < CPT / 8; ++hh) {
-                const u32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16 * hh, 0, 0);
+                const u32x4 gv =
+                    __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16 * hh, 0, kReadOnce);
                 const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
                 u32x4 out;
 #pragma unroll

@@ -114,9 +114,10 @@ __device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
 }
 
-// cache policy of the loads of r, k, v and the decay logits, each byte of
-// which a kernel reads once: non-temporal (measured 1 % faster on the Finch
-// forward and 3.5 % on the Eagle forward, the same bytes read)
+// cache policy of the loads of r, k, v, the decay logits and the gate, each
+// byte of which a kernel reads once: non-temporal (measured 1 % faster on the
+// Finch forward, 3.5 % on the Eagle forward and 0.4 % on the forward with the
+// epilogue, the same bytes read)
 constexpr int kReadOnce = 2;
 
 struct Ctx {
