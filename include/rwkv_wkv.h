@@ -135,7 +135,10 @@ int rwkv_wkv_workspace_status(void *workspace, size_t workspace_bytes, hipStream
  *              RWKV_E_ALIGN / RWKV_E_ALIAS as for the tensors.
  *
  * Pointers need 4-byte alignment (the workspace 16).  C = H*N must be at
- * most 2^20 and B * C below 2^36, else RWKV_E_UNSUPPORTED.
+ * most 2^20 and B * C below 2^36, else RWKV_E_UNSUPPORTED.  Values of v up
+ * to about 1e25 in magnitude are handled: where every channel of a wave's
+ * 32-channel block has |u - w| <= 30, a token's output is formed with its
+ * value scaled by e^{u-w}.
  *
  * The 256-token passes of a sequence's block of 32 channels run in separate
  * workgroups that hand the state on through the workspace (1.5 KiB of
