@@ -191,6 +191,11 @@ def test_rwkv4_extreme_decay_and_bonus():
     d["u"] = d["u"].copy()
     d["w"][40], d["w"][41], d["u"][45] = 60.0, 300.0, 40.0
     rwkv4_check(d)
+    # the same in two calls, the state handed over between them
+    head = {n: d[n][:, :277] if n in "kv" else d[n] for n in d}
+    tail = {n: d[n][:, 277:] if n in "kv" else d[n] for n in d}
+    _, s1, _ = rwkv4_check(head)
+    rwkv4_check(tail, state_in=s1.cpu().numpy())
 
 
 def test_rwkv4_state_handoff():
