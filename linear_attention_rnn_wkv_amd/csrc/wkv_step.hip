@@ -64,14 +64,28 @@ __global__ __launch_bounds__(256) void wkv_step_kernel(
     }
 
     const float uu = u[h * kN + lane];
-    const float w_head = PT ? 0.0f : exp_fast(-exp_fast(x[h * kN + lane]));
+    const float xo = PT ? 0.0f : x[h * kN + lane];
+    // Eagle's per-channel decay: with a state streamed from HBM (NT) it is
+    // formed before the first token's loads, which then wait for it and the
+    // state (measured 390 against 401 us per step at 1024 sequences); with a
+    // cached state, after them (see the loop: 84.1 against 80.8 us at 256)
+    const float w_head = (PT || !NT) ? 0.0f : exp_fast(-exp_fast(xo));
+
     for (int t = 0; t < T; ++t) {
         const size_t base = (((size_t)b * T + t) * H + h) * kN;
         const float ri = bf16_to_f32(r[base + lane]);
         const float ki = bf16_to_f32(k[base + lane]);
         const u32x2 vp = *(const u32x2 *)(v + base + 4 * c4);
         const float vj[4] = {bf16_lo(vp.x), bf16_hi(vp.x), bf16_lo(vp.y), bf16_hi(vp.y)};
-        const float wi = PT ? exp_fast(-exp_fast(x[base + lane])) : w_head;
+        float xt = PT ? x[base + lane] : xo;
+        // Eagle with a cached state: the decay is formed here, after the
+        // token's loads, and is not hoisted ahead of them (its wait, which
+        // also waits for the state, would hold them back by a round trip)
+        if (!PT && !NT) {
+            __builtin_amdgcn_sched_barrier(0);
+            __asm__ volatile("" : "+v"(xt));
+        }
+        const float wi = (PT || !NT) ? exp_fast(-exp_fast(xt)) : w_head;
         const float bonus = wave_sum(ri * uu * ki);
 
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
