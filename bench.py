@@ -873,8 +873,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the operator shards by sequence and head with no exchange; see the "
-              "design notes)", file=sys.stderr)
+              "(the operator shards by sequence and head, with no exchange between "
+              "GPUs)", file=sys.stderr)
         return 2
     import numpy as np
     import torch
